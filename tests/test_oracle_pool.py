@@ -1,0 +1,94 @@
+"""Pins for the pool / relayout oracle.
+
+* the slot rule on hand-computed positions ("PD 分离与 KV 传输", section
+  "实现": slot = block id * block size + offset);
+* the documented pool layout on a hand-placed element;
+* write-then-gather returns the logical rows; relayout keeps the logical
+  rows bit for bit and never touches slots past the request;
+* a 16 -> 32 -> 16 round trip through the inverse tables is the identity;
+* bytes moved equal the closed form layers x 2 x heads x dim x bytes x tokens.
+"""
+
+import numpy as np
+
+from conftest import kv_fields, read_golden
+from decode_paged_kv_amd import inputs
+from oracle import accounting, pool
+
+
+def test_slot_rule_hand_values():
+    bt = [5, 2, 9]
+    assert pool.slots_for(bt, 16, [0, 15, 16, 17, 40]) == [80, 95, 32, 33, 152]
+    assert pool.slots_for([3, 0], 32, [0, 31, 32, 63]) == [96, 127, 0, 31]
+
+
+def test_layout_of_one_written_row():
+    pm = pool.PoolModel(num_blocks=4, block_size=16, num_kv_heads=4, num_shards=2, head_dim=8, elem=np.float32)
+    k = np.arange(2 * 4 * 8, dtype=np.float32).reshape(2, 4, 8)
+    v = -k
+    pool.write(pm, k, v, [17, 3])          # token 0 -> slot 17 = block 1, offset 1
+    # head 3 lives in shard 1 as local head 1
+    assert np.array_equal(pm.k[1][1, 1, 1, :], k[0, 3])
+    assert np.array_equal(pm.v[1][1, 1, :, 1], v[0, 3])
+    # head 0 of token 1: shard 0, local 0, block 0, offset 3
+    assert np.array_equal(pm.k[0][0, 0, 3, :], k[1, 0])
+    assert np.array_equal(pm.v[0][0, 0, :, 3], v[1, 0])
+    # negative slots are skipped
+    pm2 = pool.PoolModel(4, 16, 4, 2, 8, np.float32)
+    pool.write(pm2, k, v, [-1, -5])
+    assert all(not a.any() for a in pm2.k + pm2.v)
+
+
+def _filled_pool(n, bs, shards, blocks, seed, heads=8, d=16, fill=0xDEAD):
+    g = inputs.stream(seed, 99, 0, inputs.T_PERM)
+    bt, _ = inputs.assign_blocks(blocks, [n], bs, g)
+    pm = pool.PoolModel(blocks, bs, heads, shards, d, np.uint16, fill)
+    k = inputs.normal((n, heads, d), 0.5, "bf16", inputs.stream(seed, 99, 0, inputs.T_K))
+    v = inputs.normal((n, heads, d), 0.5, "bf16", inputs.stream(seed, 99, 0, inputs.T_V))
+    pool.write(pm, k, v, pool.slots_for(bt[0], bs, range(n)))
+    return pm, bt[0], k, v
+
+
+def test_write_then_gather_round_trip():
+    pm, bt, k, v = _filled_pool(100, 16, 4, 16, seed=1)
+    gk, gv = pool.gather(pm, bt, 100)
+    assert np.array_equal(gk, k) and np.array_equal(gv, v)
+    assert pool.allocated_untouched(pm, 0xDEAD, pool.slots_for(bt, 16, range(100)))
+
+
+def test_relayout_bit_exact_and_untouched_tail():
+    n = 150
+    src, src_bt, k, v = _filled_pool(n, 16, 4, 16, seed=2)
+    dst = pool.PoolModel(8, 32, 8, 8, 16, np.uint16, fill=0xBEEF)
+    g = inputs.stream(2, 99, 0, inputs.T_DST_PERM)
+    dst_bt, _ = inputs.assign_blocks(8, [n + 1], 32, g)   # room for the next token, as decode reserves
+    moved = pool.relayout(src, src_bt, dst, dst_bt[0], n)
+    gk, gv = pool.gather(dst, dst_bt[0], n)
+    assert np.array_equal(gk, k) and np.array_equal(gv, v)
+    assert pool.allocated_untouched(dst, 0xBEEF, pool.slots_for(dst_bt[0], 32, range(n)))
+    assert moved == accounting.relayout_payload_bytes(n, 8, 16, 2)
+
+
+def test_relayout_round_trip_is_identity():
+    n = 96
+    src, src_bt, _, _ = _filled_pool(n, 16, 4, 8, seed=3)
+    mid = pool.PoolModel(4, 32, 8, 8, 16, np.uint16, fill=0)
+    mid_bt = np.array([2, 0, 3], dtype=np.int32)
+    pool.relayout(src, src_bt, mid, mid_bt, n)
+    back = pool.PoolModel(8, 16, 8, 4, 16, np.uint16, fill=0xDEAD)
+    pool.relayout(mid, mid_bt, back, src_bt, n)
+    for a, b in zip(src.k + src.v, back.k + back.v):
+        assert np.array_equal(a, b)
+
+
+def test_relayout_bytes_match_pages_closed_form():
+    rows = {r[0] + ":" + r[1]: kv_fields(r[2:]) for r in read_golden("kv_bytes.txt") if len(r) > 1}
+    t = rows["transfer:llama3-70b"]
+    per_token = accounting.kv_bytes_per_token(80, 8, 128, 2)
+    assert per_token == int(t["per_token"])
+    total = accounting.kv_bytes(int(t["tokens"]), 80, 8, 128, 2)
+    assert total == 1_342_177_280
+    assert round(total / 1e9, 2) == float(t["gb"])
+    assert round(total / float(t["link"]) * 1e3) == int(t["ms"])
+    # the relayout oracle moves exactly one layer's share per call
+    assert accounting.relayout_payload_bytes(4096, 8, 128, 2) * 80 == total
