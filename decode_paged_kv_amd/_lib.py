@@ -1,0 +1,128 @@
+"""ctypes view of libpkv's C ABI (include/pkv.h).  Marshalling only."""
+
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libpkv.so")
+
+MAX_SHARDS = 16
+F32, BF16 = 0, 1
+OK, EINVAL, EUNSUPPORTED, EHIP, ERANGE = 0, -1, -2, -3, -4
+ERRBIT_BLOCK_ID, ERRBIT_SLOT, ERRBIT_TABLE = 1, 2, 4
+
+
+class PkvLibraryMissing(RuntimeError):
+    """libpkv.so has not been built; there is no fallback implementation."""
+
+
+class PkvError(RuntimeError):
+    def __init__(self, code: int, func: str, msg: str):
+        super().__init__(f"{func} failed with {code}: {msg}")
+        self.code = code
+
+
+class PoolLayer(C.Structure):
+    _fields_ = [
+        ("k", C.c_void_p * MAX_SHARDS),
+        ("v", C.c_void_p * MAX_SHARDS),
+        ("num_blocks", C.c_int32),
+        ("block_size", C.c_int32),
+        ("num_kv_heads", C.c_int32),
+        ("num_shards", C.c_int32),
+        ("head_dim", C.c_int32),
+        ("dtype", C.c_int32),
+        ("err_word", C.c_void_p),
+    ]
+
+
+class DecodeStep(C.Structure):
+    _fields_ = [
+        ("num_layers", C.c_int32),
+        ("pools", C.POINTER(PoolLayer)),
+        ("q", C.POINTER(C.c_void_p)),
+        ("k_new", C.POINTER(C.c_void_p)),
+        ("v_new", C.POINTER(C.c_void_p)),
+        ("out", C.POINTER(C.c_void_p)),
+        ("slots", C.c_void_p),
+        ("block_tables", C.c_void_p),
+        ("bt_stride", C.c_int32),
+        ("context_lens", C.c_void_p),
+        ("batch", C.c_int32),
+        ("max_context_len", C.c_int32),
+        ("num_q_heads", C.c_int32),
+        ("scale", C.c_float),
+        ("workspace", C.c_void_p),
+        ("workspace_bytes", C.c_size_t),
+    ]
+
+
+class PrefillJob(C.Structure):
+    _fields_ = [
+        ("num_layers", C.c_int32),
+        ("pools", C.POINTER(PoolLayer)),
+        ("q", C.POINTER(C.c_void_p)),
+        ("k", C.POINTER(C.c_void_p)),
+        ("v", C.POINTER(C.c_void_p)),
+        ("out", C.POINTER(C.c_void_p)),
+        ("slots", C.c_void_p),
+        ("block_table", C.c_void_p),
+        ("bt_stride", C.c_int32),
+        ("start_loc", C.c_void_p),
+        ("chunk_start", C.c_void_p),
+        ("num_tokens", C.c_int32),
+        ("num_q_heads", C.c_int32),
+        ("scale", C.c_float),
+        ("next_layer", C.c_int32),
+        ("submitted_all", C.c_int32),
+    ]
+
+
+_P = C.c_void_p
+_I = C.c_int32
+_SIGS = {
+    "pkv_last_error": (C.c_char_p, []),
+    "pkv_version": (C.c_int, []),
+    "pkv_slot_mapping": (C.c_int, [_P, _I, _P, _P, _I, _I, _I, _I, _P, _P, _P]),
+    "kv_write": (C.c_int, [C.POINTER(PoolLayer), _P, _P, _P, _I, _P]),
+    "kv_relayout": (C.c_int, [C.POINTER(PoolLayer), _P, C.POINTER(PoolLayer), _P, _I, _P]),
+    "attn_prefill_chunk": (C.c_int, [C.POINTER(PoolLayer), _P, _P, _P, _I, _P, _P, _I, _I, _I, C.c_float, _P]),
+    "pkv_attn_decode_workspace_size": (C.c_size_t, [_I, _I, _I, _I]),
+    "attn_decode": (C.c_int, [C.POINTER(PoolLayer), _P, _P, _P, _I, _P, _I, _I, _I, C.c_float, _P, C.c_size_t, _P]),
+    "pkv_mux_create": (C.c_int, [C.c_int, C.c_int, C.c_int, C.c_int, C.c_int, C.c_int, C.POINTER(_P)]),
+    "pkv_mux_destroy": (None, [_P]),
+    "pkv_mux_groups": (C.c_int, [_P, C.POINTER(_I), C.POINTER(_I), _I, C.POINTER(_I)]),
+    "pkv_mux_choose": (C.c_int, [_P, C.c_int, C.c_int]),
+    "pkv_mux_layers_per_round": (C.c_int, [_P, C.c_int, C.c_int]),
+    "pkv_mux_stream": (_P, [_P, C.c_int, C.c_int]),
+    "pkv_mux_cu_mask": (C.c_int, [_P, C.c_int, C.c_int, C.POINTER(C.c_uint32), _I, C.POINTER(_I)]),
+    "run_mux_round": (C.c_int, [_P, C.POINTER(DecodeStep), C.POINTER(PrefillJob), C.POINTER(_I), C.POINTER(_I)]),
+    "pkv_mux_wait_prefill": (C.c_int, [_P]),
+}
+EXPORTED = tuple(_SIGS)
+
+_lib = None
+
+
+def load(path: str = LIB_PATH) -> C.CDLL:
+    """The loaded library (loaded once).  Raises PkvLibraryMissing if unbuilt."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise PkvLibraryMissing(
+            f"{path} is not built; run `python -m decode_paged_kv_amd.build` (needs hipcc for gfx950)")
+    lib = C.CDLL(path)
+    for name, (res, args) in _SIGS.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def check(rc: int, func: str) -> None:
+    if rc != OK:
+        raise PkvError(rc, func, load().pkv_last_error().decode(errors="replace"))

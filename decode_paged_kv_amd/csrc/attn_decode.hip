@@ -1,0 +1,366 @@
+// Paged GQA decode attention: split-KV, wavefront-parallel, HBM-bound.
+//
+// Pages: "Lecture 7 · Prefill 与 Decode" section 1.1 (a decode step adds one
+// token per request and reads all of its KV, so it is bound by memory
+// traffic); "PD multiplexing: splitting prefill and decode by SM on one GPU"
+// section "Green contexts: carving out SMs for a stream" (decode reaches
+// the bandwidth limit once enough compute units issue loads at once).
+//
+// Work decomposition: one workgroup of 4 waves per (split, KV head,
+// request).  A split covers `split_tokens` consecutive keys of the request.
+// The G = Hq/Hkv q-heads of the KV head share every K/V byte the workgroup
+// reads, so K and V are each read from HBM once per step.
+//
+// Inside a workgroup each wave walks 64-key tiles (tile i of the split goes
+// to wave i % 4):
+//   q.k   lane l owns key l of the tile and reads its K row (16-byte loads
+//         of a block's contiguous rows); the G query rows are broadcast
+//         from LDS; bf16 pairs use v_dot2_f32_bf16 with fp32 accumulation.
+//   soft  online softmax per wave in the exp2 domain (scores pre-scaled by
+//         scale*log2 e): running max m, per-lane partial sums.
+//   p.v   p goes through the wave's own LDS slice; lane l owns head-dim
+//         columns and reads the dim-major V tile (16 keys of one dim are
+//         32 contiguous bytes), multiplying bf16 key pairs with v_dot2.
+// The 4 waves' (m, l, acc) are merged in LDS; with several splits the
+// partials go to the workspace and a second kernel merges them.
+#include "pkv_internal.h"
+
+namespace pkv {
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = kWaves * 64;
+constexpr int kTile = 64;
+constexpr float kLog2e = 1.4426950408889634f;
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c,
+                                         false);
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+// Orders one wave's LDS writes before its later LDS reads (no cross-wave sync).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+template <typename T, int D, int G>
+struct DecodeSmem {
+  static constexpr int QW = (sizeof(T) == 2) ? D / 2 : D;            // q words per head
+  uint32_t q[G][QW];                                                  // bf16 pairs or fp32 bits
+  // p of the current tile per wave: bf16 (packed pairs) or fp32
+  uint32_t p[kWaves][G][(sizeof(T) == 2) ? kTile / 2 : kTile];
+  float red_acc[kWaves][G][D];
+  float red_m[kWaves][G];
+  float red_l[kWaves][G];
+};
+
+template <typename T, int D, int G>
+__global__ void __launch_bounds__(kThreads)
+attn_decode_kernel(PoolDev pool, const T* __restrict__ q, T* __restrict__ out, const int32_t* __restrict__ bt,
+                   int bt_stride, const int32_t* __restrict__ ctx, int num_q_heads, float scale_log2,
+                   int split_tokens, int num_splits, float* __restrict__ part_o, float* __restrict__ part_ml) {
+  constexpr bool kBf16 = sizeof(T) == 2;
+  constexpr int DPL = D / 64;                  // head-dim columns per lane in p.v
+  constexpr int VEC = 16 / sizeof(T);          // elements per 16-byte load
+  using Smem = DecodeSmem<T, D, G>;
+  __shared__ Smem sm;
+
+  const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int L = ctx[b];
+  if (L > (bt_stride << pool.bs_shift)) {        // never index past the request's table
+    if (threadIdx.x == 0 && split == 0 && kvh == 0) flag_error(pool.err, PKV_ERRBIT_TABLE);
+    L = bt_stride << pool.bs_shift;
+  }
+  const int start = split * split_tokens;
+  if (start >= L) return;
+  const int end = min(L, start + split_tokens);
+
+  const int hl = pool.heads_per_shard;
+  const int sh = kvh / hl, lh = kvh - sh * hl;
+  const T* kpool = reinterpret_cast<const T*>(pool.k[sh]);
+  const T* vpool = reinterpret_cast<const T*>(pool.v[sh]);
+  const int bs = pool.block_size;
+  const int32_t* table = bt + (size_t)b * bt_stride;
+
+  // q rows of this KV head's group -> LDS
+  {
+    const uint32_t* qsrc = reinterpret_cast<const uint32_t*>(q + ((size_t)b * num_q_heads + (size_t)kvh * G) * D);
+    uint32_t* qdst = &sm.q[0][0];
+    for (int i = threadIdx.x; i < G * Smem::QW; i += kThreads) qdst[i] = qsrc[i];
+  }
+  __syncthreads();
+
+  float m[G], lsum[G], acc[G][DPL];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    m[g] = -INFINITY;
+    lsum[g] = 0.f;
+#pragma unroll
+    for (int j = 0; j < DPL; ++j) acc[g][j] = 0.f;
+  }
+
+  const int ntiles = (end - start + kTile - 1) / kTile;
+  for (int t = wave; t < ntiles; t += kWaves) {
+    const int k0 = start + t * kTile;
+    // ---- q.k: lane owns key k0 + lane ----
+    const int key = k0 + lane;
+    bool valid = key < end;
+    const T* krow = nullptr;
+    if (valid) {
+      const int blk = table[key >> pool.bs_shift];
+      if (blk < 0 || blk >= pool.num_blocks) {
+        flag_error(pool.err, PKV_ERRBIT_BLOCK_ID);
+        valid = false;
+      } else {
+        krow = kpool + tile_elems(pool, blk, lh) + (size_t)(key & (bs - 1)) * D;
+      }
+    }
+    float s[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) s[g] = 0.f;
+    if (valid) {
+#pragma unroll 4
+      for (int c = 0; c < D / VEC; ++c) {
+        const uint4 kv = *reinterpret_cast<const uint4*>(krow + c * VEC);
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          const uint4 qv = *reinterpret_cast<const uint4*>(&sm.q[g][c * 4]);
+          if constexpr (kBf16) {
+            s[g] = dot2_bf16(kv.x, qv.x, s[g]);
+            s[g] = dot2_bf16(kv.y, qv.y, s[g]);
+            s[g] = dot2_bf16(kv.z, qv.z, s[g]);
+            s[g] = dot2_bf16(kv.w, qv.w, s[g]);
+          } else {
+            s[g] = fmaf(__uint_as_float(kv.x), __uint_as_float(qv.x), s[g]);
+            s[g] = fmaf(__uint_as_float(kv.y), __uint_as_float(qv.y), s[g]);
+            s[g] = fmaf(__uint_as_float(kv.z), __uint_as_float(qv.z), s[g]);
+            s[g] = fmaf(__uint_as_float(kv.w), __uint_as_float(qv.w), s[g]);
+          }
+        }
+      }
+    }
+    // ---- online softmax (exp2 domain) ----
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const float sc = valid ? s[g] * scale_log2 : -INFINITY;
+      const float mn = fmaxf(m[g], wave_max(sc));
+      const float alpha = __builtin_amdgcn_exp2f(m[g] - mn);
+      const float p = __builtin_amdgcn_exp2f(sc - mn);
+      m[g] = mn;
+      lsum[g] = lsum[g] * alpha + p;
+#pragma unroll
+      for (int j = 0; j < DPL; ++j) acc[g][j] *= alpha;
+      if constexpr (kBf16) {
+        reinterpret_cast<bf16_t*>(&sm.p[wave][g][0])[lane] = f32_to_bf16(p);
+      } else {
+        sm.p[wave][g][lane] = __float_as_uint(p);
+      }
+    }
+    wave_lds_sync();
+    // ---- p.v: lane owns head-dim columns lane*DPL .. +DPL ----
+#pragma unroll
+    for (int kk = 0; kk < kTile; kk += 16) {
+      const int key16 = k0 + kk;
+      if (key16 >= end) break;
+      const int blk = table[key16 >> pool.bs_shift];
+      if (blk < 0 || blk >= pool.num_blocks) continue;     // its keys already have p = 0
+      const int nvalid = min(16, end - key16);
+      const T* vtile = vpool + tile_elems(pool, blk, lh) + (key16 & (bs - 1));
+#pragma unroll
+      for (int j = 0; j < DPL; ++j) {
+        const int d = lane * DPL + j;
+        const T* vrow = vtile + (size_t)d * bs;          // 16 keys of dim d
+        uint4 vv[16 / VEC];
+#pragma unroll
+        for (int u = 0; u < 16 / VEC; ++u) vv[u] = *reinterpret_cast<const uint4*>(vrow + u * VEC);
+        uint32_t* vw = reinterpret_cast<uint32_t*>(vv);
+        if (nvalid < 16) {            // keys past the context hold arbitrary bits: zero them
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            if (e >= nvalid) {
+              if constexpr (kBf16) vw[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
+              else vw[e] = 0u;
+            }
+          }
+        }
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          if constexpr (kBf16) {
+            const uint4 p0 = *reinterpret_cast<const uint4*>(&sm.p[wave][g][kk / 2]);
+            const uint4 p1 = *reinterpret_cast<const uint4*>(&sm.p[wave][g][kk / 2 + 4]);
+            float a = acc[g][j];
+            a = dot2_bf16(p0.x, vw[0], a);
+            a = dot2_bf16(p0.y, vw[1], a);
+            a = dot2_bf16(p0.z, vw[2], a);
+            a = dot2_bf16(p0.w, vw[3], a);
+            a = dot2_bf16(p1.x, vw[4], a);
+            a = dot2_bf16(p1.y, vw[5], a);
+            a = dot2_bf16(p1.z, vw[6], a);
+            a = dot2_bf16(p1.w, vw[7], a);
+            acc[g][j] = a;
+          } else {
+            float a = acc[g][j];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              const uint4 pp = *reinterpret_cast<const uint4*>(&sm.p[wave][g][kk + u * 4]);
+              a = fmaf(__uint_as_float(pp.x), __uint_as_float(vw[u * 4 + 0]), a);
+              a = fmaf(__uint_as_float(pp.y), __uint_as_float(vw[u * 4 + 1]), a);
+              a = fmaf(__uint_as_float(pp.z), __uint_as_float(vw[u * 4 + 2]), a);
+              a = fmaf(__uint_as_float(pp.w), __uint_as_float(vw[u * 4 + 3]), a);
+            }
+            acc[g][j] = a;
+          }
+        }
+      }
+    }
+    wave_lds_sync();
+  }
+
+  // ---- merge the 4 waves ----
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const float l = wave_sum(lsum[g]);
+    if (lane == 0) {
+      sm.red_m[wave][g] = m[g];
+      sm.red_l[wave][g] = l;
+    }
+#pragma unroll
+    for (int j = 0; j < DPL; ++j) sm.red_acc[wave][g][lane * DPL + j] = acc[g][j];
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < G * D; i += kThreads) {
+    const int g = i / D, d = i - g * D;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) mx = fmaxf(mx, sm.red_m[w][g]);
+    float l = 0.f, o = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float f = __builtin_amdgcn_exp2f(sm.red_m[w][g] - mx);   // waves without keys: m = -inf -> 0
+      l += sm.red_l[w][g] * f;
+      o += sm.red_acc[w][g][d] * f;
+    }
+    const int h = kvh * G + g;
+    if (num_splits == 1) {
+      const float r = o / l;
+      if constexpr (kBf16) out[((size_t)b * num_q_heads + h) * D + d] = f32_to_bf16(r);
+      else out[((size_t)b * num_q_heads + h) * D + d] = r;
+    } else {
+      const size_t row = ((size_t)b * num_q_heads + h) * num_splits + split;
+      part_o[row * D + d] = o;
+      if (d == 0) {
+        part_ml[row * 2 + 0] = mx;
+        part_ml[row * 2 + 1] = l;
+      }
+    }
+  }
+}
+
+// Merge the split partials of each (request, q-head): rescale each split's
+// (m, l, acc) to the common max and normalise.
+template <typename T, int D>
+__global__ void __launch_bounds__(D)
+attn_decode_merge_kernel(const float* __restrict__ part_o, const float* __restrict__ part_ml,
+                         const int32_t* __restrict__ ctx, T* __restrict__ out, int num_q_heads, int split_tokens,
+                         int num_splits, int max_len) {
+  const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
+  const int L = min(ctx[b], max_len);
+  const int ns = min(num_splits, (L + split_tokens - 1) / split_tokens);
+  const size_t row0 = ((size_t)b * num_q_heads + h) * num_splits;
+  float mx = -INFINITY;
+  for (int s = 0; s < ns; ++s) mx = fmaxf(mx, part_ml[(row0 + s) * 2]);
+  float l = 0.f, o = 0.f;
+  for (int s = 0; s < ns; ++s) {
+    const float f = __builtin_amdgcn_exp2f(part_ml[(row0 + s) * 2] - mx);
+    l += part_ml[(row0 + s) * 2 + 1] * f;
+    o += part_o[(row0 + s) * D + d] * f;
+  }
+  const float r = o / l;
+  if constexpr (sizeof(T) == 2) out[((size_t)b * num_q_heads + h) * D + d] = f32_to_bf16(r);
+  else out[((size_t)b * num_q_heads + h) * D + d] = r;
+}
+
+template <typename T, int D, int G>
+hipError_t launch_typed(const PoolDev& pool, const void* q, void* out, const int32_t* bt, int bt_stride,
+                        const int32_t* ctx, int batch, int num_q_heads, float scale_log2, const DecodePlan& plan,
+                        void* ws, hipStream_t s) {
+  float* part_o = static_cast<float*>(ws);
+  float* part_ml = part_o ? part_o + (size_t)batch * num_q_heads * plan.num_splits * D : nullptr;
+  const dim3 grid(plan.num_splits, num_q_heads / G, batch);
+  hipLaunchKernelGGL((attn_decode_kernel<T, D, G>), grid, dim3(kThreads), 0, s, pool, static_cast<const T*>(q),
+                     static_cast<T*>(out), bt, bt_stride, ctx, num_q_heads, scale_log2, plan.split_tokens,
+                     plan.num_splits, part_o, part_ml);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || plan.num_splits == 1) return e;
+  hipLaunchKernelGGL((attn_decode_merge_kernel<T, D>), dim3(num_q_heads, batch), dim3(D), 0, s, part_o, part_ml,
+                     ctx, static_cast<T*>(out), num_q_heads, plan.split_tokens, plan.num_splits,
+                     bt_stride << pool.bs_shift);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t launch_d(int group, const PoolDev& pool, const void* q, void* out, const int32_t* bt, int bt_stride,
+                    const int32_t* ctx, int batch, int num_q_heads, float scale_log2, const DecodePlan& plan,
+                    void* ws, hipStream_t s) {
+  switch (group) {
+    case 1: return launch_typed<T, D, 1>(pool, q, out, bt, bt_stride, ctx, batch, num_q_heads, scale_log2, plan, ws, s);
+    case 2: return launch_typed<T, D, 2>(pool, q, out, bt, bt_stride, ctx, batch, num_q_heads, scale_log2, plan, ws, s);
+    case 4: return launch_typed<T, D, 4>(pool, q, out, bt, bt_stride, ctx, batch, num_q_heads, scale_log2, plan, ws, s);
+    case 8: return launch_typed<T, D, 8>(pool, q, out, bt, bt_stride, ctx, batch, num_q_heads, scale_log2, plan, ws, s);
+    case 16: return launch_typed<T, D, 16>(pool, q, out, bt, bt_stride, ctx, batch, num_q_heads, scale_log2, plan, ws, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+DecodePlan plan_decode(int batch, int num_q_heads, int num_kv_heads, int max_context_len, int head_dim) {
+  (void)num_q_heads;
+  (void)head_dim;
+  // Aim for at least ~4 workgroups per CU across the chip (256 CUs) while
+  // keeping each split at >= 256 keys so the per-split fixed cost stays small.
+  const long pairs = (long)batch * num_kv_heads;
+  int split = 64;
+  while (split < 4096) {
+    const long wgs = pairs * ((max_context_len + split - 1) / split);
+    if (wgs <= 2048 && split >= 256) break;
+    if (wgs <= 1024) break;
+    split *= 2;
+  }
+  DecodePlan p;
+  p.split_tokens = split;
+  p.num_splits = (max_context_len + split - 1) / split;
+  p.workspace = p.num_splits > 1 ? (size_t)batch * num_q_heads * p.num_splits * (head_dim + 2) * sizeof(float) : 0;
+  return p;
+}
+
+hipError_t launch_attn_decode(const PoolDev& pool, int dtype, const void* q, void* out, const int32_t* bt,
+                              int bt_stride, const int32_t* ctx, int batch, int num_q_heads, float scale,
+                              const DecodePlan& plan, void* workspace, hipStream_t s) {
+  if (batch == 0) return hipSuccess;
+  const int group = num_q_heads / pool.num_kv_heads;
+  const float sl2 = scale * kLog2e;
+  if (dtype == PKV_BF16) {
+    if (pool.head_dim == 128) return launch_d<bf16_t, 128>(group, pool, q, out, bt, bt_stride, ctx, batch, num_q_heads, sl2, plan, workspace, s);
+    return launch_d<bf16_t, 64>(group, pool, q, out, bt, bt_stride, ctx, batch, num_q_heads, sl2, plan, workspace, s);
+  }
+  if (pool.head_dim == 128) return launch_d<float, 128>(group, pool, q, out, bt, bt_stride, ctx, batch, num_q_heads, sl2, plan, workspace, s);
+  return launch_d<float, 64>(group, pool, q, out, bt, bt_stride, ctx, batch, num_q_heads, sl2, plan, workspace, s);
+}
+
+}  // namespace pkv

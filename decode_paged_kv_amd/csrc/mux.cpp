@@ -1,0 +1,360 @@
+// Single-GPU PD multiplexing: CU-masked stream pairs per split level, the
+// level / layers-per-round policy, and the round loop.
+//
+// Page: "PD multiplexing: splitting prefill and decode by SM on one GPU",
+// sections "Green contexts: carving out SMs for a stream" (a stream bound
+// to a subset of compute units; bandwidth and L2 stay shared) and "SGLang's
+// PD multiplexing" (split levels on a granularity grid, the level picked
+// from the decode batch size, prefill cut by layer, the main loop that syncs
+// only the decode stream and changes level only when a prefill starts or
+// ends).  On MI355X a split is a pair of streams created with
+// hipExtStreamCreateWithCUMask over complementary CU masks.
+#include <hip/hip_ext.h>
+
+#include <algorithm>
+#include <array>
+#include <cmath>
+#include <mutex>
+#include <vector>
+
+#include "pkv_internal.h"
+
+namespace pkv {
+int fail(int code, const char* fmt, ...);
+int hip_fail(hipError_t e, const char* where);
+int check_pool(const pkv_pool_layer* p, const char* name, PoolDev* out);
+void clear_error();
+}  // namespace pkv
+
+using namespace pkv;
+
+namespace {
+constexpr int kMaskWords = 8;    // 256 CUs
+constexpr int kXcds = 8;
+}  // namespace
+
+struct pkv_mux {
+  int device = 0;
+  int total_cus = 0;
+  int granularity = 8, min_decode = 32, group_num = 8, divisor = 36, budget = 65536;
+  std::vector<std::pair<int, int>> groups;                 // (prefill CUs, decode CUs)
+  std::vector<std::array<uint32_t, kMaskWords>> pmask, dmask;
+  std::vector<hipStream_t> pstream, dstream;               // created on first use
+  hipStream_t whole = nullptr;                             // ordinary stream: the whole device
+  hipEvent_t prefill_done = nullptr;
+  int level = -1;
+  bool level_with_prefill = false;
+  bool done_pending = false;     // event recorded, completion not yet seen
+  bool prefill_finished = false; // completion seen; the level changes next round
+  std::vector<int> used_levels;
+};
+
+namespace {
+
+// Split levels: prefill takes x CUs, x on the granularity grid from
+// `granularity` to total - granularity, prefill at least half and decode at
+// least min_decode; keep `levels` of them evenly spaced from the smallest,
+// listed largest prefill first.
+std::vector<std::pair<int, int>> split_levels(int total, int granularity, int min_decode, int levels) {
+  std::vector<int> cand;
+  for (int x = granularity; x <= total - granularity; x += granularity)
+    if (2 * x >= total && total - x >= min_decode) cand.push_back(x);
+  if ((int)cand.size() >= levels) {
+    const int stride = std::max<int>(1, (int)cand.size() / levels);
+    std::vector<int> kept;
+    for (size_t i = 0; i < cand.size() && (int)kept.size() < levels; i += stride) kept.push_back(cand[i]);
+    cand = kept;
+  }
+  std::sort(cand.rbegin(), cand.rend());
+  std::vector<std::pair<int, int>> out;
+  for (int x : cand) out.emplace_back(x, total - x);
+  return out;
+}
+
+int choose(int n, int decode_bs, bool has_prefill, int divisor) {
+  if (decode_bs > 0 && has_prefill) return std::min(n - 2, std::max(1, decode_bs * (n - 2) / divisor));
+  if (decode_bs > 0) return n - 1;
+  return 0;
+}
+
+// CU masks: decode takes the same number of CUs on every XCD.  Mask bit i of
+// a queue's CU mask selects CU i / kXcds of XCD i % kXcds (the runtime
+// spreads consecutive mask bits over the XCDs), so decode takes the lowest
+// decode_cus / kXcds CUs of each XCD and prefill the rest.
+void build_masks(int total, int decode_cus, std::array<uint32_t, kMaskWords>& pm, std::array<uint32_t, kMaskWords>& dm) {
+  pm.fill(0);
+  dm.fill(0);
+  const int per_xcd = total / kXcds;
+  const int dec_per_xcd = decode_cus / kXcds;
+  for (int i = 0; i < total; ++i) {
+    const int cu_in_xcd = i / kXcds;
+    auto& m = cu_in_xcd < dec_per_xcd ? dm : pm;
+    m[i / 32] |= 1u << (i % 32);
+  }
+  (void)per_xcd;
+}
+
+int ensure_streams(pkv_mux* m, int level) {
+  const auto& g = m->groups[level];
+  if (g.first == 0 || g.second == 0) return PKV_OK;      // whole-device groups use the ordinary stream
+  if (m->pstream[level] && m->dstream[level]) return PKV_OK;
+  hipError_t e = hipExtStreamCreateWithCUMask(&m->pstream[level], kMaskWords, m->pmask[level].data());
+  if (e != hipSuccess) return hip_fail(e, "hipExtStreamCreateWithCUMask(prefill)");
+  e = hipExtStreamCreateWithCUMask(&m->dstream[level], kMaskWords, m->dmask[level].data());
+  if (e != hipSuccess) return hip_fail(e, "hipExtStreamCreateWithCUMask(decode)");
+  m->used_levels.push_back(level);
+  return PKV_OK;
+}
+
+hipStream_t stream_of(const pkv_mux* m, int level, int which) {
+  const auto& g = m->groups[level];
+  if (g.first == 0 || g.second == 0) return m->whole;
+  return which == 0 ? m->pstream[level] : m->dstream[level];
+}
+
+int sync_level(pkv_mux* m, int level) {
+  if (level < 0) return PKV_OK;
+  for (int w = 0; w < 2; ++w) {
+    hipStream_t s = stream_of(m, level, w);
+    if (!s) continue;
+    hipError_t e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+  }
+  return PKV_OK;
+}
+
+int check_decode_step(const pkv_decode_step* d, std::vector<PoolDev>& pools, DecodePlan& plan) {
+  if (d->num_layers <= 0 || !d->pools || !d->q || !d->k_new || !d->v_new || !d->out)
+    return fail(PKV_EINVAL, "run_mux_round: decode step needs layers and per-layer arrays");
+  if (d->batch <= 0 || d->max_context_len <= 0 || !d->slots || !d->block_tables || !d->context_lens)
+    return fail(PKV_EINVAL, "run_mux_round: decode step batch/context/tables");
+  pools.resize(d->num_layers);
+  for (int l = 0; l < d->num_layers; ++l) {
+    if (int rc = check_pool(&d->pools[l], "run_mux_round(decode pool)", &pools[l])) return rc;
+    if (!d->q[l] || !d->k_new[l] || !d->v_new[l] || !d->out[l])
+      return fail(PKV_EINVAL, "run_mux_round: decode layer %d has a NULL tensor", l);
+  }
+  const PoolDev& p0 = pools[0];
+  if (d->num_q_heads <= 0 || d->num_q_heads % p0.num_kv_heads)
+    return fail(PKV_EINVAL, "run_mux_round: num_q_heads %d", d->num_q_heads);
+  if ((int64_t)d->bt_stride * p0.block_size < d->max_context_len)
+    return fail(PKV_EINVAL, "run_mux_round: decode bt_stride too small");
+  plan = plan_decode(d->batch, d->num_q_heads, p0.num_kv_heads, d->max_context_len, p0.head_dim);
+  if (plan.workspace > 0 && (!d->workspace || d->workspace_bytes < plan.workspace))
+    return fail(PKV_EINVAL, "run_mux_round: decode workspace of %zu bytes needed", plan.workspace);
+  return PKV_OK;
+}
+
+int check_prefill_job(const pkv_prefill_job* p, std::vector<PoolDev>& pools) {
+  if (p->num_layers <= 0 || !p->pools || !p->q || !p->k || !p->v || !p->out)
+    return fail(PKV_EINVAL, "run_mux_round: prefill job needs layers and per-layer arrays");
+  if (p->num_tokens <= 0 || !p->slots || !p->block_table || !p->start_loc || !p->chunk_start)
+    return fail(PKV_EINVAL, "run_mux_round: prefill job tokens/tables");
+  if (p->next_layer < 0 || p->next_layer > p->num_layers) return fail(PKV_EINVAL, "run_mux_round: next_layer");
+  pools.resize(p->num_layers);
+  for (int l = 0; l < p->num_layers; ++l) {
+    if (int rc = check_pool(&p->pools[l], "run_mux_round(prefill pool)", &pools[l])) return rc;
+    if (!p->q[l] || !p->k[l] || !p->v[l] || !p->out[l])
+      return fail(PKV_EINVAL, "run_mux_round: prefill layer %d has a NULL tensor", l);
+  }
+  if (p->num_q_heads <= 0 || p->num_q_heads % pools[0].num_kv_heads)
+    return fail(PKV_EINVAL, "run_mux_round: prefill num_q_heads %d", p->num_q_heads);
+  if ((int64_t)p->bt_stride * pools[0].block_size < p->num_tokens)
+    return fail(PKV_EINVAL, "run_mux_round: prefill bt_stride too small");
+  return PKV_OK;
+}
+
+float scale_or_default(float s, int d) { return s > 0.f ? s : 1.0f / std::sqrt((float)d); }
+
+}  // namespace
+
+extern "C" {
+
+int pkv_mux_create(int device, int cu_granularity, int min_decode_cus, int sm_group_num, int decode_bs_divisor,
+                   int token_budget, pkv_mux** out) {
+  if (!out) return fail(PKV_EINVAL, "pkv_mux_create: out is NULL");
+  *out = nullptr;
+  if (cu_granularity <= 0 || min_decode_cus < 0 || sm_group_num < 3 || decode_bs_divisor <= 0 || token_budget <= 0)
+    return fail(PKV_EINVAL, "pkv_mux_create: bad policy parameter");
+  int cus = 0;
+  hipError_t e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device);
+  if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
+  if (cus > kMaskWords * 32 || cus % kXcds) return fail(PKV_EUNSUPPORTED, "pkv_mux_create: %d CUs", cus);
+  if (cus % cu_granularity || cu_granularity % kXcds)
+    return fail(PKV_EINVAL, "pkv_mux_create: granularity %d must divide %d CUs and be a multiple of %d", cu_granularity,
+                cus, kXcds);
+  e = hipSetDevice(device);
+  if (e != hipSuccess) return hip_fail(e, "hipSetDevice");
+  pkv_mux* m = new pkv_mux();
+  m->device = device;
+  m->total_cus = cus;
+  m->granularity = cu_granularity;
+  m->min_decode = min_decode_cus;
+  m->group_num = sm_group_num;
+  m->divisor = decode_bs_divisor;
+  m->budget = token_budget;
+  m->groups.emplace_back(cus, 0);
+  for (auto& g : split_levels(cus, cu_granularity, min_decode_cus, sm_group_num - 2)) m->groups.push_back(g);
+  m->groups.emplace_back(0, cus);
+  const size_t n = m->groups.size();
+  m->pmask.resize(n);
+  m->dmask.resize(n);
+  m->pstream.assign(n, nullptr);
+  m->dstream.assign(n, nullptr);
+  for (size_t i = 0; i < n; ++i) build_masks(cus, m->groups[i].second, m->pmask[i], m->dmask[i]);
+  e = hipStreamCreateWithFlags(&m->whole, hipStreamNonBlocking);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&m->prefill_done, hipEventDisableTiming);
+  if (e != hipSuccess) {
+    pkv_mux_destroy(m);
+    return hip_fail(e, "pkv_mux_create");
+  }
+  *out = m;
+  return PKV_OK;
+}
+
+void pkv_mux_destroy(pkv_mux* m) {
+  if (!m) return;
+  for (size_t i = 0; i < m->pstream.size(); ++i) {
+    if (m->pstream[i]) { (void)hipStreamSynchronize(m->pstream[i]); (void)hipStreamDestroy(m->pstream[i]); }
+    if (m->dstream[i]) { (void)hipStreamSynchronize(m->dstream[i]); (void)hipStreamDestroy(m->dstream[i]); }
+  }
+  if (m->whole) { (void)hipStreamSynchronize(m->whole); (void)hipStreamDestroy(m->whole); }
+  if (m->prefill_done) (void)hipEventDestroy(m->prefill_done);
+  delete m;
+}
+
+int pkv_mux_groups(const pkv_mux* m, int32_t* prefill_cus, int32_t* decode_cus, int32_t cap, int32_t* n) {
+  if (!m || !n) return fail(PKV_EINVAL, "pkv_mux_groups: NULL argument");
+  *n = (int32_t)m->groups.size();
+  for (int i = 0; i < *n && i < cap; ++i) {
+    if (prefill_cus) prefill_cus[i] = m->groups[i].first;
+    if (decode_cus) decode_cus[i] = m->groups[i].second;
+  }
+  return PKV_OK;
+}
+
+int pkv_mux_choose(const pkv_mux* m, int decode_bs, int has_prefill) {
+  if (!m) return fail(PKV_EINVAL, "pkv_mux_choose: NULL mux");
+  return choose((int)m->groups.size(), decode_bs, has_prefill != 0, m->divisor);
+}
+
+int pkv_mux_layers_per_round(const pkv_mux* m, int prefill_tokens, int num_layers) {
+  if (!m || prefill_tokens <= 0 || num_layers <= 0) return fail(PKV_EINVAL, "pkv_mux_layers_per_round: bad argument");
+  return std::min(num_layers, std::max(1, m->budget / prefill_tokens));
+}
+
+void* pkv_mux_stream(const pkv_mux* mc, int level, int which) {
+  pkv_mux* m = const_cast<pkv_mux*>(mc);
+  if (!m || level < 0 || level >= (int)m->groups.size() || (which != 0 && which != 1)) return nullptr;
+  if (ensure_streams(m, level) != PKV_OK) return nullptr;
+  return stream_of(m, level, which);
+}
+
+int pkv_mux_cu_mask(const pkv_mux* m, int level, int which, uint32_t* words, int32_t cap, int32_t* n) {
+  if (!m || !n || level < 0 || level >= (int)m->groups.size() || (which != 0 && which != 1))
+    return fail(PKV_EINVAL, "pkv_mux_cu_mask: bad argument");
+  const auto& src = which == 0 ? m->pmask[level] : m->dmask[level];
+  *n = kMaskWords;
+  for (int i = 0; i < kMaskWords && i < cap; ++i) words[i] = src[i];
+  return PKV_OK;
+}
+
+int run_mux_round(pkv_mux* m, const pkv_decode_step* d, pkv_prefill_job* p, int32_t* level_out,
+                  int32_t* prefill_done_out) {
+  clear_error();
+  if (!m) return fail(PKV_EINVAL, "run_mux_round: NULL mux");
+  std::vector<PoolDev> dpools, ppools;
+  DecodePlan plan{};
+  if (d)
+    if (int rc = check_decode_step(d, dpools, plan)) return rc;
+  if (p)
+    if (int rc = check_prefill_job(p, ppools)) return rc;
+  const int ng = (int)m->groups.size();
+  const int decode_bs = d ? d->batch : 0;
+  const bool starting = p && p->next_layer == 0 && !p->submitted_all;
+  const bool want_prefill = p && !p->submitted_all;
+  hipError_t e = hipSetDevice(m->device);
+  if (e != hipSuccess) return hip_fail(e, "hipSetDevice");
+
+  // ---- level: changes only when a prefill starts or has finished ----
+  bool rechoose = m->level < 0;
+  if (starting && !m->level_with_prefill) rechoose = true;
+  if (m->prefill_finished && !want_prefill) rechoose = true;
+  if (rechoose) {
+    if (int rc = sync_level(m, m->level)) return rc;
+    m->level = choose(ng, decode_bs, want_prefill, m->divisor);
+    m->level_with_prefill = want_prefill;
+    m->prefill_finished = false;
+  }
+  const int level = m->level;
+  if (int rc = ensure_streams(m, level)) return rc;
+  hipStream_t ds = stream_of(m, level, 1), ps = stream_of(m, level, 0);
+
+  // ---- decode step on the decode stream ----
+  if (d) {
+    const float sc = scale_or_default(d->scale, dpools[0].head_dim);
+    for (int l = 0; l < d->num_layers; ++l) {
+      e = launch_kv_write(dpools[l], d->pools[l].dtype, d->k_new[l], d->v_new[l], d->slots, d->batch, ds);
+      if (e == hipSuccess)
+        e = launch_attn_decode(dpools[l], d->pools[l].dtype, d->q[l], d->out[l], d->block_tables, d->bt_stride,
+                               d->context_lens, d->batch, d->num_q_heads, sc, plan, d->workspace, ds);
+      if (e != hipSuccess) return hip_fail(e, "run_mux_round(decode)");
+    }
+  }
+  // ---- next layers of the prefill on the prefill stream ----
+  if (want_prefill) {
+    const int per_round = std::min(p->num_layers, std::max(1, m->budget / p->num_tokens));
+    const int end = std::min(p->num_layers, p->next_layer + per_round);
+    const float sc = scale_or_default(p->scale, ppools[0].head_dim);
+    for (int l = p->next_layer; l < end; ++l) {
+      e = launch_kv_write(ppools[l], p->pools[l].dtype, p->k[l], p->v[l], p->slots, p->num_tokens, ps);
+      if (e == hipSuccess)
+        e = launch_attn_prefill(ppools[l], p->pools[l].dtype, p->q[l], p->out[l], p->block_table, p->bt_stride,
+                                p->start_loc, p->chunk_start, 1, p->num_tokens, p->num_q_heads, sc, ps);
+      if (e != hipSuccess) return hip_fail(e, "run_mux_round(prefill)");
+    }
+    p->next_layer = end;
+    if (end == p->num_layers) {
+      e = hipEventRecord(m->prefill_done, ps);
+      if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+      p->submitted_all = 1;
+      m->done_pending = true;
+    }
+  }
+  // ---- block on the decode stream only ----
+  if (d) {
+    e = hipStreamSynchronize(ds);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize(decode)");
+  }
+  int done = 0;
+  if (p && p->submitted_all) {
+    if (m->done_pending) {
+      e = hipEventQuery(m->prefill_done);
+      if (e == hipSuccess) {
+        m->done_pending = false;
+        m->prefill_finished = true;
+        done = 1;
+      } else if (e != hipErrorNotReady) {
+        return hip_fail(e, "hipEventQuery");
+      }
+    } else {
+      done = 1;
+    }
+  }
+  if (level_out) *level_out = level;
+  if (prefill_done_out) *prefill_done_out = done;
+  return PKV_OK;
+}
+
+int pkv_mux_wait_prefill(pkv_mux* m) {
+  if (!m) return fail(PKV_EINVAL, "pkv_mux_wait_prefill: NULL mux");
+  if (m->done_pending) {
+    hipError_t e = hipEventSynchronize(m->prefill_done);
+    if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
+    m->done_pending = false;
+    m->prefill_finished = true;
+  }
+  return PKV_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,73 @@
+// Internal declarations shared by the HIP kernels and the C-ABI glue of
+// libpkv.  Nothing here is part of the public ABI (include/pkv.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/pkv.h"
+
+namespace pkv {
+
+// Pool of one layer as passed to kernels (by value, in the kernarg segment).
+struct PoolDev {
+  char* k[PKV_MAX_SHARDS];
+  char* v[PKV_MAX_SHARDS];
+  int num_blocks;
+  int block_size;
+  int bs_shift;          // log2(block_size); block sizes are powers of two
+  int heads_per_shard;
+  int num_kv_heads;
+  int head_dim;
+  int32_t* err;          // optional error word (nullptr = none)
+};
+
+// bfloat16 is carried as raw 16-bit patterns in device buffers.
+typedef uint16_t bf16_t;
+
+#ifdef __HIPCC__
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+__device__ __forceinline__ float bf16_lo(uint32_t pair) { return __uint_as_float(pair << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t pair) { return __uint_as_float(pair & 0xffff0000u); }
+// Round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ bf16_t f32_to_bf16(float x) {
+  __bf16 b = static_cast<__bf16>(x);
+  return __builtin_bit_cast(bf16_t, b);
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+}
+__device__ __forceinline__ void flag_error(int32_t* err, int bit) {
+  if (err) atomicOr(err, bit);
+}
+// Base offset (in elements) of the (block, local head) tile of a shard:
+// K and V tiles both hold block_size * head_dim elements.
+__device__ __forceinline__ size_t tile_elems(const PoolDev& p, int blk, int local_head) {
+  return ((size_t)blk * p.heads_per_shard + local_head) * ((size_t)p.block_size * p.head_dim);
+}
+#endif
+
+// ---- launchers (each validates nothing: the ABI layer has done it) ----
+hipError_t launch_slot_mapping(const int32_t* bt, int bt_stride, const int32_t* start_loc, const int32_t* pos_start,
+                               int batch, int num_tokens, int block_size, int num_blocks, int32_t* slots,
+                               int32_t* err, hipStream_t s);
+hipError_t launch_kv_write(const PoolDev& pool, int dtype, const void* k, const void* v, const int32_t* slots,
+                           int n_tokens, hipStream_t s);
+hipError_t launch_kv_relayout(const PoolDev& src, const int32_t* src_bt, const PoolDev& dst, const int32_t* dst_bt,
+                              int dtype, int n_tokens, hipStream_t s);
+
+struct DecodePlan {
+  int split_tokens;   // keys per split (multiple of 64)
+  int num_splits;     // splits per (request, kv head) at max_context_len
+  size_t workspace;   // bytes of partial results needed (0 when num_splits == 1)
+};
+DecodePlan plan_decode(int batch, int num_q_heads, int num_kv_heads, int max_context_len, int head_dim);
+hipError_t launch_attn_decode(const PoolDev& pool, int dtype, const void* q, void* out, const int32_t* bt,
+                              int bt_stride, const int32_t* ctx, int batch, int num_q_heads, float scale,
+                              const DecodePlan& plan, void* workspace, hipStream_t s);
+hipError_t launch_attn_prefill(const PoolDev& pool, int dtype, const void* q, void* out, const int32_t* bt,
+                               int bt_stride, const int32_t* start_loc, const int32_t* chunk_start, int batch,
+                               int max_chunk_len, int num_q_heads, float scale, hipStream_t s);
+
+}  // namespace pkv

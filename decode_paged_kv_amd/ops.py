@@ -1,0 +1,235 @@
+"""Python binding of libpkv with the C ABI's names.
+
+Only argument marshalling happens here: torch supplies device memory and
+streams, every step of the path runs in the library's HIP kernels, and a
+failed call raises ``PkvError`` with the library's message.  There is no
+CPU fallback; without ``libpkv.so`` every call raises ``PkvLibraryMissing``.
+"""
+
+from __future__ import annotations
+
+import ctypes as C
+
+import torch
+
+from . import _lib
+from ._lib import BF16, F32, DecodeStep, PkvError, PkvLibraryMissing, PoolLayer, PrefillJob  # noqa: F401
+
+_TORCH_DTYPE = {"bf16": torch.bfloat16, "f32": torch.float32}
+_CODE = {"bf16": BF16, "f32": F32}
+
+
+def _ptr(t) -> int | None:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+class PagedPool:
+    """One layer of one instance's KV pool, in the library's layout.
+
+    Shard ``s`` holds KV heads ``[s*H/S, (s+1)*H/S)``:
+    ``k[s]`` is ``[num_blocks, H/S, block_size, head_dim]`` and ``v[s]`` is
+    ``[num_blocks, H/S, head_dim, block_size]``.
+    """
+
+    def __init__(self, num_blocks, block_size, num_kv_heads, num_shards, head_dim, dtype="bf16",
+                 device="cuda", err_word=None, k=None, v=None):
+        self.num_blocks, self.block_size = num_blocks, block_size
+        self.num_kv_heads, self.num_shards, self.head_dim = num_kv_heads, num_shards, head_dim
+        self.dtype = dtype
+        hl = num_kv_heads // num_shards
+        td = _TORCH_DTYPE[dtype]
+        self.k = k if k is not None else [torch.empty((num_blocks, hl, block_size, head_dim), dtype=td, device=device)
+                                          for _ in range(num_shards)]
+        self.v = v if v is not None else [torch.empty((num_blocks, hl, head_dim, block_size), dtype=td, device=device)
+                                          for _ in range(num_shards)]
+        self.err_word = err_word
+
+    def fill_bits(self, pattern: int) -> "PagedPool":
+        """Fill every element with one raw bit pattern (16-bit for bf16, 32-bit for f32)."""
+        for t in self.k + self.v:
+            (t.view(torch.int16) if self.dtype == "bf16" else t.view(torch.int32)).fill_(pattern)
+        return self
+
+    def c(self) -> PoolLayer:
+        s = PoolLayer()
+        for i in range(self.num_shards):
+            s.k[i] = self.k[i].data_ptr()
+            s.v[i] = self.v[i].data_ptr()
+        s.num_blocks, s.block_size = self.num_blocks, self.block_size
+        s.num_kv_heads, s.num_shards, s.head_dim = self.num_kv_heads, self.num_shards, self.head_dim
+        s.dtype = _CODE[self.dtype]
+        s.err_word = _ptr(self.err_word)
+        return s
+
+
+def slot_mapping(block_tables, start_loc, pos_start, num_tokens, block_size, num_blocks, out=None,
+                 err_word=None, stream=None):
+    lib = _lib.load()
+    if out is None:
+        out = torch.empty(num_tokens, dtype=torch.int32, device=block_tables.device)
+    batch = start_loc.numel() - 1
+    rc = lib.pkv_slot_mapping(_ptr(block_tables), block_tables.shape[-1], _ptr(start_loc), _ptr(pos_start), batch,
+                              num_tokens, block_size, num_blocks, _ptr(out), _ptr(err_word), _stream(stream))
+    _lib.check(rc, "pkv_slot_mapping")
+    return out
+
+
+def kv_write(pool: PagedPool, k, v, slots, stream=None):
+    lib = _lib.load()
+    c = pool.c()
+    _lib.check(lib.kv_write(C.byref(c), _ptr(k), _ptr(v), _ptr(slots), slots.numel(), _stream(stream)), "kv_write")
+
+
+def kv_relayout(src: PagedPool, src_bt, dst: PagedPool, dst_bt, n_tokens: int, stream=None):
+    lib = _lib.load()
+    cs, cd = src.c(), dst.c()
+    _lib.check(lib.kv_relayout(C.byref(cs), _ptr(src_bt), C.byref(cd), _ptr(dst_bt), n_tokens, _stream(stream)),
+               "kv_relayout")
+
+
+def attn_prefill_chunk(pool: PagedPool, q, out, block_tables, start_loc, chunk_start, max_chunk_len: int,
+                       num_q_heads: int, scale: float = 0.0, stream=None):
+    lib = _lib.load()
+    c = pool.c()
+    batch = chunk_start.numel()
+    rc = lib.attn_prefill_chunk(C.byref(c), _ptr(q), _ptr(out), _ptr(block_tables), block_tables.shape[-1],
+                                _ptr(start_loc), _ptr(chunk_start), batch, max_chunk_len, num_q_heads, scale,
+                                _stream(stream))
+    _lib.check(rc, "attn_prefill_chunk")
+
+
+def attn_decode_workspace_size(batch: int, num_q_heads: int, max_context_len: int, head_dim: int) -> int:
+    return int(_lib.load().pkv_attn_decode_workspace_size(batch, num_q_heads, max_context_len, head_dim))
+
+
+def attn_decode(pool: PagedPool, q, out, block_tables, context_lens, max_context_len: int, num_q_heads: int,
+                scale: float = 0.0, workspace=None, stream=None):
+    lib = _lib.load()
+    c = pool.c()
+    batch = context_lens.numel()
+    if workspace is None:
+        nbytes = attn_decode_workspace_size(batch, num_q_heads, max_context_len, pool.head_dim)
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    rc = lib.attn_decode(C.byref(c), _ptr(q), _ptr(out), _ptr(block_tables), block_tables.shape[-1],
+                         _ptr(context_lens), batch, max_context_len, num_q_heads, scale, _ptr(workspace),
+                         workspace.numel() * workspace.element_size(), _stream(stream))
+    _lib.check(rc, "attn_decode")
+
+
+def _ptr_array(tensors):
+    arr = (C.c_void_p * len(tensors))()
+    for i, t in enumerate(tensors):
+        arr[i] = _ptr(t)
+    return arr
+
+
+def _pool_array(pools):
+    arr = (PoolLayer * len(pools))()
+    for i, p in enumerate(pools):
+        arr[i] = p.c()
+    return arr
+
+
+class DecodeStepArgs:
+    """Keeps the ctypes arrays of one decode step alive while it is in use."""
+
+    def __init__(self, pools, q, k_new, v_new, out, slots, block_tables, context_lens, max_context_len,
+                 num_q_heads, workspace, scale=0.0):
+        self._keep = (_pool_array(pools), _ptr_array(q), _ptr_array(k_new), _ptr_array(v_new), _ptr_array(out))
+        self.c = DecodeStep(len(pools), C.cast(self._keep[0], C.POINTER(PoolLayer)),
+                            C.cast(self._keep[1], C.POINTER(C.c_void_p)), C.cast(self._keep[2], C.POINTER(C.c_void_p)),
+                            C.cast(self._keep[3], C.POINTER(C.c_void_p)), C.cast(self._keep[4], C.POINTER(C.c_void_p)),
+                            _ptr(slots), _ptr(block_tables), block_tables.shape[-1], _ptr(context_lens),
+                            context_lens.numel(), max_context_len, num_q_heads, scale, _ptr(workspace),
+                            workspace.numel() * workspace.element_size())
+        self._tensors = (slots, block_tables, context_lens, workspace)
+
+
+class PrefillJobArgs:
+    """A whole-prompt, layer-by-layer prefill job; ``c.next_layer`` is the cursor."""
+
+    def __init__(self, pools, q, k, v, out, slots, block_table, start_loc, chunk_start, num_tokens, num_q_heads,
+                 scale=0.0):
+        self._keep = (_pool_array(pools), _ptr_array(q), _ptr_array(k), _ptr_array(v), _ptr_array(out))
+        self.c = PrefillJob(len(pools), C.cast(self._keep[0], C.POINTER(PoolLayer)),
+                            C.cast(self._keep[1], C.POINTER(C.c_void_p)), C.cast(self._keep[2], C.POINTER(C.c_void_p)),
+                            C.cast(self._keep[3], C.POINTER(C.c_void_p)), C.cast(self._keep[4], C.POINTER(C.c_void_p)),
+                            _ptr(slots), _ptr(block_table), block_table.shape[-1], _ptr(start_loc), _ptr(chunk_start),
+                            num_tokens, num_q_heads, scale, 0, 0)
+        self._tensors = (slots, block_table, start_loc, chunk_start)
+
+    @property
+    def done_submitting(self) -> bool:
+        return bool(self.c.submitted_all)
+
+
+class Mux:
+    """CU-masked stream pairs per split level and the multiplexing round loop."""
+
+    def __init__(self, device=0, cu_granularity=8, min_decode_cus=32, sm_group_num=8, decode_bs_divisor=36,
+                 token_budget=65536):
+        lib = _lib.load()
+        h = C.c_void_p()
+        _lib.check(lib.pkv_mux_create(device, cu_granularity, min_decode_cus, sm_group_num, decode_bs_divisor,
+                                      token_budget, C.byref(h)), "pkv_mux_create")
+        self._h = h
+
+    def close(self):
+        if self._h:
+            _lib.load().pkv_mux_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def groups(self):
+        lib = _lib.load()
+        cap = 64
+        p, d, n = (C.c_int32 * cap)(), (C.c_int32 * cap)(), C.c_int32()
+        _lib.check(lib.pkv_mux_groups(self._h, p, d, cap, C.byref(n)), "pkv_mux_groups")
+        return [(p[i], d[i]) for i in range(n.value)]
+
+    def choose(self, decode_bs: int, has_prefill: bool) -> int:
+        return int(_lib.load().pkv_mux_choose(self._h, decode_bs, int(has_prefill)))
+
+    def layers_per_round(self, prefill_tokens: int, num_layers: int) -> int:
+        return int(_lib.load().pkv_mux_layers_per_round(self._h, prefill_tokens, num_layers))
+
+    def stream(self, level: int, which: int) -> int:
+        return int(_lib.load().pkv_mux_stream(self._h, level, which) or 0)
+
+    def cu_mask(self, level: int, which: int):
+        lib = _lib.load()
+        words, n = (C.c_uint32 * 16)(), C.c_int32()
+        _lib.check(lib.pkv_mux_cu_mask(self._h, level, which, words, 16, C.byref(n)), "pkv_mux_cu_mask")
+        return [words[i] for i in range(n.value)]
+
+    def run_round(self, decode: DecodeStepArgs | None, prefill: PrefillJobArgs | None):
+        """One round; returns (level, prefill_done)."""
+        lib = _lib.load()
+        lvl, done = C.c_int32(), C.c_int32()
+        rc = lib.run_mux_round(self._h, C.byref(decode.c) if decode else None,
+                               C.byref(prefill.c) if prefill else None, C.byref(lvl), C.byref(done))
+        _lib.check(rc, "run_mux_round")
+        return lvl.value, bool(done.value)
+
+    def wait_prefill(self):
+        _lib.check(_lib.load().pkv_mux_wait_prefill(self._h), "pkv_mux_wait_prefill")
+
+
+run_mux_round = Mux.run_round

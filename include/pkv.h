@@ -1,0 +1,280 @@
+/*
+ * pkv.h - C ABI of libpkv: paged-KV GQA attention, KV relayout and
+ * single-GPU PD multiplexing for AMD Instinct MI355X (gfx950).
+ *
+ * Pages cited (titles as on the pages):
+ *   [MUX]    "PD multiplexing: splitting prefill and decode by SM on one GPU"
+ *   [DISAGG] "PD 分离与 KV 传输" (PD disaggregation and KV transfer)
+ *   [L7]     "Lecture 7 · Prefill 与 Decode：分块 prefill、解耦与 NVIDIA Dynamo"
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Every pointer argument documented as "device" points to device memory
+ *   owned by the caller.  The library keeps no pointer after a call returns,
+ *   except the multiplexing jobs (see run_mux_round).
+ * - Every call except run_mux_round only enqueues work on the given stream
+ *   (NULL = the null stream) and returns at once.
+ * - Return codes: PKV_OK (0) or a negative PKV_E* code.  Arguments are
+ *   validated on the host before any HIP call; on failure nothing is
+ *   enqueued.  pkv_last_error() describes the last failure of the calling
+ *   thread.  No call throws across the ABI.
+ * - Element types: PKV_BF16 (bfloat16, fp32 accumulation, bf16 output
+ *   rounded to nearest even) or PKV_F32 (fp32 throughout).
+ * - Supported shapes: head_dim 64 or 128; block_size 16, 32, 64 or 128;
+ *   num_shards dividing num_kv_heads, at most PKV_MAX_SHARDS; num_q_heads a
+ *   multiple of num_kv_heads with at most 16 q-heads per KV head.
+ *
+ * Pool layout (one layer of one instance)
+ * ---------------------------------------
+ * The pages view a layer's KV pool as [slot, kv_heads, head_dim] with
+ * slot = block_id * block_size + offset ([DISAGG] "实现").  Here the heads
+ * of a layer are cut into num_shards contiguous ranges of H/S heads (the
+ * TP 4 / TP 8 split of [DISAGG] "布局转换"); shard s stores heads
+ * [s*H/S, (s+1)*H/S) as
+ *     k[s]: [num_blocks][H/S][block_size][head_dim]   (token rows)
+ *     v[s]: [num_blocks][H/S][head_dim][block_size]   (dim-major in a block)
+ * so one (block, head) of K or V is one contiguous block_size*head_dim run.
+ * V is stored dim-major so that consecutive keys of one dim are adjacent:
+ * the P*V product then reads whole 16-byte runs of keys.  All shards of an
+ * instance share a request's block table.
+ *
+ * Out-of-range indices: every kernel checks each block id it reads from a
+ * block table against [0, num_blocks) and each slot against the pool; a row
+ * with a bad index is skipped (attention treats the key as absent) and, when
+ * err_word is non-NULL, the kernel ORs a PKV_ERRBIT_* bit into it.  No bad
+ * index is ever dereferenced.
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PKV_MAX_SHARDS 16
+#define PKV_VERSION 1
+
+enum { PKV_F32 = 0, PKV_BF16 = 1 };
+
+enum {
+  PKV_OK = 0,
+  PKV_EINVAL = -1,        /* bad argument, found on the host before any HIP call */
+  PKV_EUNSUPPORTED = -2,  /* valid but unsupported shape or element type          */
+  PKV_EHIP = -3,          /* a HIP runtime call failed; pkv_last_error names it    */
+  PKV_ERANGE = -4         /* a size exceeds a documented limit                     */
+};
+
+enum { PKV_ERRBIT_BLOCK_ID = 1, PKV_ERRBIT_SLOT = 2, PKV_ERRBIT_TABLE = 4 };
+
+/* One layer of one instance's paged KV pool (see "Pool layout" above). */
+typedef struct pkv_pool_layer {
+  void* k[PKV_MAX_SHARDS];   /* device, shard s: [num_blocks][H/S][block_size][head_dim] */
+  void* v[PKV_MAX_SHARDS];   /* device, shard s: [num_blocks][H/S][head_dim][block_size] */
+  int32_t num_blocks;
+  int32_t block_size;
+  int32_t num_kv_heads;      /* H, all shards together */
+  int32_t num_shards;        /* S */
+  int32_t head_dim;
+  int32_t dtype;             /* PKV_F32 or PKV_BF16 */
+  int32_t* err_word;         /* optional device int32, see "Out-of-range indices" */
+} pkv_pool_layer;
+
+/* Description of the last failure on the calling thread ("" if none). */
+const char* pkv_last_error(void);
+
+/* PKV_VERSION of the built library. */
+int pkv_version(void);
+
+/*
+ * pkv_slot_mapping - slot of every token about to be written.
+ * [DISAGG] "实现": token p of a request with block table bt lives at
+ * slot = bt[p / bs] * bs + p % bs.
+ *
+ * Tokens are packed request by request: token i of request b (start_loc[b]
+ * <= i < start_loc[b+1]) sits at position pos_start[b] + (i - start_loc[b]).
+ *   block_tables  device int32 [batch][bt_stride]
+ *   start_loc     device int32 [batch + 1], non-decreasing, start_loc[0] = 0,
+ *                 start_loc[batch] = num_tokens
+ *   pos_start     device int32 [batch]
+ *   slots_out     device int32 [num_tokens]; a token whose block-table index
+ *                 is past bt_stride or whose block id is out of range gets
+ *                 slot -1 (and sets PKV_ERRBIT_TABLE / _BLOCK_ID in err_word).
+ *   num_blocks    pool size used for the range check.
+ * Decode uses start_loc = 0,1,..,B and pos_start = context_len - 1; a
+ * prefill chunk of T tokens at S uses start_loc = {0, T}, pos_start = {S}.
+ */
+int pkv_slot_mapping(const int32_t* block_tables, int32_t bt_stride, const int32_t* start_loc,
+                     const int32_t* pos_start, int32_t batch, int32_t num_tokens, int32_t block_size,
+                     int32_t num_blocks, int32_t* slots_out, int32_t* err_word, hipStream_t stream);
+
+/*
+ * kv_write - scatter new K/V rows of one layer into the pool.
+ * [DISAGG] "实现" (the per-layer write of the admit step): row i of k and v
+ * goes to slots[i], every head to its shard.
+ *   k, v    device [n_tokens][num_kv_heads][head_dim], element type of the pool
+ *   slots   device int32 [n_tokens]; slot < 0 means "skip this row"
+ */
+int kv_write(const pkv_pool_layer* pool, const void* k, const void* v, const int32_t* slots,
+             int32_t n_tokens, hipStream_t stream);
+
+/*
+ * kv_relayout - move one layer of one request from a source pool into a
+ * destination pool with another block size and/or head-shard split.
+ * [DISAGG] self-test answer 3 and "布局转换": gather through the source
+ * block table, redistribute by the destination's head split, write at the
+ * destination block table's positions.  Submitted once per layer so that a
+ * layer can move as soon as it is computed ([DISAGG] "流程").
+ *   src_bt  device int32, at least ceil(n_tokens / src->block_size) entries
+ *   dst_bt  device int32, at least ceil(n_tokens / dst->block_size) entries
+ * Requires equal num_kv_heads, head_dim and dtype.  Only the first n_tokens
+ * slots of the destination are written; the destination may hold more
+ * blocks (decode reserves room for the next token).  src and dst must not
+ * overlap.
+ */
+int kv_relayout(const pkv_pool_layer* src, const int32_t* src_bt, const pkv_pool_layer* dst,
+                const int32_t* dst_bt, int32_t n_tokens, hipStream_t stream);
+
+/*
+ * attn_prefill_chunk - causal GQA attention for one chunk of each request.
+ * [L7] section 2.3: the queries of a chunk starting at S attend to every key
+ * of the earlier chunks and, under a causal mask, to the keys of their own
+ * chunk, so chunking is lossless.  Query i of the chunk (absolute position
+ * S+i) sees keys [0, S+i]; q-head h reads KV head h / (Hq/Hkv).
+ *   q, out        device [sum T][num_q_heads][head_dim], packed request by
+ *                 request (start_loc)
+ *   block_tables  device int32 [batch][bt_stride]
+ *   start_loc     device int32 [batch + 1] offsets of each request's chunk
+ *   chunk_start   device int32 [batch] S of each request
+ *   max_chunk_len host upper bound of every T (sizes the grid)
+ * The chunk's own K/V must already be in the pool (kv_write); keys
+ * [0, S+T) are read from the pool only.  scale <= 0 selects 1/sqrt(head_dim).
+ */
+int attn_prefill_chunk(const pkv_pool_layer* pool, const void* q, void* out, const int32_t* block_tables,
+                       int32_t bt_stride, const int32_t* start_loc, const int32_t* chunk_start,
+                       int32_t batch, int32_t max_chunk_len, int32_t num_q_heads, float scale,
+                       hipStream_t stream);
+
+/*
+ * attn_decode - one query per request over its whole cached context.
+ * [L7] section 1.1: each decode step adds one token per request and reads
+ * all of its KV.  The query sits at position L-1 and sees keys [0, L) with
+ * L = context_lens[b] (its own K/V already written at L-1).
+ *   q, out          device [batch][num_q_heads][head_dim]
+ *   block_tables    device int32 [batch][bt_stride]
+ *   context_lens    device int32 [batch], each in [1, max_context_len]
+ *   max_context_len host upper bound of every L (sizes the grid)
+ *   workspace       device scratch of at least
+ *                   pkv_attn_decode_workspace_size(...) bytes for the
+ *                   split-KV partial results; caller-owned, may be NULL
+ *                   when that size is 0.  Calls that share a workspace must
+ *                   be ordered on one stream.
+ * scale <= 0 selects 1/sqrt(head_dim).
+ */
+size_t pkv_attn_decode_workspace_size(int32_t batch, int32_t num_q_heads, int32_t max_context_len,
+                                      int32_t head_dim);
+int attn_decode(const pkv_pool_layer* pool, const void* q, void* out, const int32_t* block_tables,
+                int32_t bt_stride, const int32_t* context_lens, int32_t batch, int32_t max_context_len,
+                int32_t num_q_heads, float scale, void* workspace, size_t workspace_bytes,
+                hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * PD multiplexing on one GPU ([MUX] "SGLang's PD multiplexing").
+ *
+ * The device's compute units are cut into split levels: prefill gets x CUs
+ * and decode the rest, x on a grid of cu_granularity, prefill at least half,
+ * decode at least min_decode_cus; sm_group_num - 2 levels are kept, evenly
+ * spaced.  Group 0 runs everything on the whole device as prefill, the last
+ * group as decode.  A split level is a pair of HIP streams created with
+ * complementary CU masks (hipExtStreamCreateWithCUMask), the local analogue
+ * of a green-context SM split.  The level follows the decode batch size:
+ * clamp(decode_bs * levels / decode_bs_divisor, 1, levels) when both
+ * phases are present.  Prefill advances token_budget / prompt_tokens layers
+ * per round (at least one).
+ * ------------------------------------------------------------------------- */
+typedef struct pkv_mux pkv_mux;
+
+/* Builds the CU-masked stream pairs of every level on `device`.  The total
+ * CU count is the device's; cu_granularity must divide it. */
+int pkv_mux_create(int device, int cu_granularity, int min_decode_cus, int sm_group_num,
+                   int decode_bs_divisor, int token_budget, pkv_mux** out);
+void pkv_mux_destroy(pkv_mux* mux);
+/* (prefill CUs, decode CUs) of each group; *n = group count (<= cap written). */
+int pkv_mux_groups(const pkv_mux* mux, int32_t* prefill_cus, int32_t* decode_cus, int32_t cap, int32_t* n);
+/* Group index the policy picks. */
+int pkv_mux_choose(const pkv_mux* mux, int decode_bs, int has_prefill);
+/* Layers per round for a prompt of prefill_tokens tokens. */
+int pkv_mux_layers_per_round(const pkv_mux* mux, int prefill_tokens, int num_layers);
+/* Stream of a group: which = 0 prefill, 1 decode (a hipStream_t). */
+void* pkv_mux_stream(const pkv_mux* mux, int level, int which);
+/* The 32-bit words of a group's CU mask (which = 0 prefill, 1 decode). */
+int pkv_mux_cu_mask(const pkv_mux* mux, int level, int which, uint32_t* words, int32_t cap, int32_t* n);
+
+/* One decode step of a batch over all layers: per layer, write the new
+ * token's K/V at its slot, then decode attention. Host arrays of per-layer
+ * device pointers. */
+typedef struct pkv_decode_step {
+  int32_t num_layers;
+  const pkv_pool_layer* pools;     /* host [num_layers] */
+  const void* const* q;            /* host [num_layers] of device [B][Hq][D] */
+  const void* const* k_new;        /* host [num_layers] of device [B][Hkv][D] */
+  const void* const* v_new;
+  void* const* out;                /* host [num_layers] of device [B][Hq][D] */
+  const int32_t* slots;            /* device [B] slot of each request's new token */
+  const int32_t* block_tables;     /* device [B][bt_stride] */
+  int32_t bt_stride;
+  const int32_t* context_lens;     /* device [B] */
+  int32_t batch;
+  int32_t max_context_len;
+  int32_t num_q_heads;
+  float scale;
+  void* workspace;                 /* device, pkv_attn_decode_workspace_size bytes */
+  size_t workspace_bytes;
+} pkv_decode_step;
+
+/* A whole-prompt prefill cut by layer ([MUX]: prefill runs layers
+ * [start, end) per round).  next_layer is the cursor the library advances. */
+typedef struct pkv_prefill_job {
+  int32_t num_layers;
+  const pkv_pool_layer* pools;     /* host [num_layers] */
+  const void* const* q;            /* host [num_layers] of device [N][Hq][D] */
+  const void* const* k;            /* host [num_layers] of device [N][Hkv][D] */
+  const void* const* v;
+  void* const* out;                /* host [num_layers] of device [N][Hq][D] */
+  const int32_t* slots;            /* device [N] */
+  const int32_t* block_table;      /* device [1][bt_stride] */
+  int32_t bt_stride;
+  const int32_t* start_loc;        /* device [2] = {0, N} */
+  const int32_t* chunk_start;      /* device [1] = {0} */
+  int32_t num_tokens;              /* N */
+  int32_t num_q_heads;
+  float scale;
+  int32_t next_layer;              /* in/out: first layer not yet submitted */
+  int32_t submitted_all;           /* out: 1 once every layer is enqueued */
+} pkv_prefill_job;
+
+/*
+ * run_mux_round - one round of the multiplexing loop ([MUX] "SGLang's PD
+ * multiplexing", the main loop).  Enqueues the decode step `d` on the
+ * decode stream of the current level, then the next layers of `p` on the
+ * prefill stream, records the prefill-done event after the last layer, and
+ * blocks on the decode stream only.  The level is re-chosen (after syncing
+ * both streams of the old level) only when a prefill starts or finishes.
+ * Either d or p may be NULL.  The job and every buffer it names must stay
+ * alive until *prefill_done_out is 1 or pkv_mux_wait_prefill returns.
+ *   level_out          group index used this round
+ *   prefill_done_out   1 once the last prefill layer has finished on the GPU
+ */
+int run_mux_round(pkv_mux* mux, const pkv_decode_step* d, pkv_prefill_job* p, int32_t* level_out,
+                  int32_t* prefill_done_out);
+/* Blocks until every submitted prefill layer has finished. */
+int pkv_mux_wait_prefill(pkv_mux* mux);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

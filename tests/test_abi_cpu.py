@@ -1,0 +1,139 @@
+"""Boundary checks that need no GPU.
+
+* libpkv.so loads and exports every function include/pkv.h declares;
+* the binding's signature table covers exactly those functions;
+* invalid arguments are rejected on the host with the documented codes,
+  before any HIP call (nothing here touches a device).
+"""
+
+import ctypes as C
+import os
+import re
+import subprocess
+
+import pytest
+
+from conftest import ROOT
+
+lib_mod = pytest.importorskip("decode_paged_kv_amd._lib")
+
+
+def _lib():
+    if not os.path.exists(lib_mod.LIB_PATH):
+        pytest.skip("libpkv.so not built (run python -m decode_paged_kv_amd.build)")
+    return lib_mod.load()
+
+
+def _declared_functions():
+    text = open(os.path.join(ROOT, "include", "pkv.h"), encoding="utf-8").read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"typedef struct \w+ \{.*?\} \w+;", "", text, flags=re.S)
+    names = re.findall(r"^[A-Za-z_][\w\s\*]*?\b([A-Za-z_]\w*)\s*\([^;{]*\)\s*;", text, flags=re.M)
+    return sorted(set(n for n in names if n not in ("defined",)))
+
+
+def test_every_declared_symbol_is_exported():
+    _lib()
+    declared = _declared_functions()
+    assert "kv_write" in declared and "run_mux_round" in declared and len(declared) == 17
+    out = subprocess.run(["nm", "-D", "--defined-only", lib_mod.LIB_PATH], capture_output=True, text=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    missing = [n for n in declared if n not in exported]
+    assert not missing, missing
+    assert sorted(lib_mod.EXPORTED) == declared
+
+
+def _pool(**kw):
+    p = lib_mod.PoolLayer()
+    p.num_blocks, p.block_size, p.num_kv_heads, p.num_shards, p.head_dim = 8, 16, 8, 4, 128
+    p.dtype = lib_mod.BF16
+    for s in range(4):
+        p.k[s] = 0x10000 * (s + 1)
+        p.v[s] = 0x10000 * (s + 10)
+    for k, v in kw.items():
+        setattr(p, k, v)
+    return p
+
+
+def _err(lib):
+    return lib.pkv_last_error().decode()
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("block_size", 24, -2), ("block_size", 8, -2), ("head_dim", 96, -2), ("num_shards", 3, -2),
+    ("num_shards", 0, -1), ("num_shards", 17, -1), ("num_blocks", 0, -1), ("dtype", 7, -2), ("num_kv_heads", 0, -1),
+])
+def test_kv_write_rejects_bad_pool(field, value, code):
+    lib = _lib()
+    p = _pool(**{field: value})
+    rc = lib.kv_write(C.byref(p), 0x1000, 0x2000, 0x3000, 4, None)
+    assert rc == code, _err(lib)
+    assert _err(lib)
+
+
+def test_null_and_misaligned_pointers():
+    lib = _lib()
+    assert lib.kv_write(None, 0x1000, 0x2000, 0x3000, 4, None) == -1
+    p = _pool()
+    p.k[2] = 0
+    assert lib.kv_write(C.byref(p), 0x1000, 0x2000, 0x3000, 4, None) == -1
+    p = _pool()
+    p.v[1] = 0x10008
+    assert lib.kv_write(C.byref(p), 0x1000, 0x2000, 0x3000, 4, None) == -1
+    assert lib.kv_write(C.byref(_pool()), 0x1004, 0x2000, 0x3000, 4, None) == -1
+    assert lib.kv_write(C.byref(_pool()), 0, 0x2000, 0x3000, 4, None) == -1
+    assert lib.kv_write(C.byref(_pool()), 0x1000, 0x2000, 0x3000, -1, None) == -1
+    # zero tokens is a valid no-op
+    assert lib.kv_write(C.byref(_pool()), 0, 0, 0, 0, None) == 0
+
+
+def test_relayout_validation():
+    lib = _lib()
+    src = _pool()
+    dst = _pool(block_size=32, num_shards=8)
+    for s in range(8):
+        dst.k[s] = 0x100000 * (s + 1)
+        dst.v[s] = 0x100000 * (s + 20)
+    bad = _pool(head_dim=64)
+    assert lib.kv_relayout(C.byref(src), 0x10, C.byref(bad), 0x20, 16, None) == -1
+    other = _pool(dtype=lib_mod.F32)
+    assert lib.kv_relayout(C.byref(src), 0x10, C.byref(other), 0x20, 16, None) == -2
+    assert lib.kv_relayout(C.byref(src), 0, C.byref(dst), 0x20, 16, None) == -1
+    assert lib.kv_relayout(C.byref(src), 0x10, C.byref(dst), 0x20, 8 * 16 + 1, None) == -1   # does not fit
+    same = _pool(block_size=32)
+    assert lib.kv_relayout(C.byref(src), 0x10, C.byref(same), 0x20, 16, None) == -1           # shared buffers
+    assert lib.kv_relayout(C.byref(src), 0x10, C.byref(dst), 0x20, 0, None) == 0
+
+
+def test_attention_validation():
+    lib = _lib()
+    p = _pool()
+    # q-heads not a multiple of kv heads, or an unsupported group
+    assert lib.attn_decode(C.byref(p), 0x100, 0x200, 0x300, 8, 0x400, 2, 64, 12, 0.0, 0x500, 1 << 20, None) == -1
+    assert lib.attn_decode(C.byref(p), 0x100, 0x200, 0x300, 8, 0x400, 2, 64, 8 * 32, 0.0, 0x500, 1 << 20, None) == -2
+    # table too narrow for the context
+    assert lib.attn_decode(C.byref(p), 0x100, 0x200, 0x300, 2, 0x400, 2, 64, 32, 0.0, 0x500, 1 << 20, None) == -1
+    # workspace too small when splits are needed
+    need = lib.pkv_attn_decode_workspace_size(64, 32, 8192, 128)
+    assert need > 0
+    assert lib.attn_decode(C.byref(p), 0x100, 0x200, 0x300, 512, 0x400, 64, 8192, 32, 0.0, 0x500, 16, None) == -1
+    assert lib.attn_decode(C.byref(p), 0x100, 0x200, 0x300, 512, 0x400, 64, 8192, 32, float("inf"), 0x500,
+                           need, None) == -1
+    assert lib.attn_decode(C.byref(p), 0x100, 0x200, 0x300, 8, 0x400, 0, 64, 32, 0.0, 0, 0, None) == 0
+    assert lib.attn_prefill_chunk(C.byref(p), 0x100, 0x200, 0x300, 8, 0x400, 0x500, 1, 64, 30, 0.0, None) == -1
+    assert lib.attn_prefill_chunk(C.byref(p), 0x108, 0x200, 0x300, 8, 0x400, 0x500, 1, 64, 32, 0.0, None) == -1
+    assert lib.attn_prefill_chunk(C.byref(p), 0x100, 0x200, 0x300, 8, 0x400, 0x500, 0, 64, 32, 0.0, None) == 0
+
+
+def test_slot_mapping_validation():
+    lib = _lib()
+    assert lib.pkv_slot_mapping(0x10, 4, 0x20, 0x30, 0, 5, 16, 64, 0x40, None, None) == -1
+    assert lib.pkv_slot_mapping(0x10, 4, 0x20, 0x30, 1, 5, 24, 64, 0x40, None, None) == -2
+    assert lib.pkv_slot_mapping(0x10, 0, 0x20, 0x30, 1, 5, 16, 64, 0x40, None, None) == -1
+    assert lib.pkv_slot_mapping(0, 0, 0, 0, 0, 0, 16, 64, 0, None, None) == 0
+
+
+def test_workspace_size_is_zero_for_single_split():
+    lib = _lib()
+    assert lib.pkv_attn_decode_workspace_size(4, 4, 64, 64) == 0
+    assert lib.pkv_attn_decode_workspace_size(0, 4, 128, 64) == 0

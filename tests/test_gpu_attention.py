@@ -1,0 +1,193 @@
+"""GPU parity of decode and chunked-prefill attention against the fp64 oracle.
+
+Tolerances (written here, applied to every case): bf16 max |err| <= 2e-2
+and rel-L2 <= 5e-3; fp32 max |err| <= 1e-5 and rel-L2 <= 1e-5.  The
+oracle never chunks: every chunk the GPU computes is compared with rows
+S..S+T-1 of the oracle's one-shot prefill ("Lecture 7" section 2.3:
+chunked prefill is lossless).  Pools are filled with NaN sentinels first,
+so any read of a slot that was never written would poison the output.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from decode_paged_kv_amd import inputs, ops, workloads
+from gpu_common import Scenario, assert_close, from_dev, i32, to_dev
+from oracle import attention as oa
+
+pytestmark = pytest.mark.gpu
+
+
+def _q(sc, shape, tid=inputs.T_Q, idx=0, scale=1.0):
+    g = inputs.stream(sc.seed, sc.cfg, sc.layer, tid, idx)
+    return inputs.normal(shape, scale, sc.dtype, g)
+
+
+def _tdtype(dtype):
+    return torch.bfloat16 if dtype == "bf16" else torch.float32
+
+
+def run_decode(sc: Scenario, q_np, max_ctx=None):
+    b = len(sc.lengths)
+    q = to_dev(q_np, sc.dtype)
+    out = torch.empty((b, sc.hq, sc.d), dtype=_tdtype(sc.dtype), device="cuda")
+    ops.attn_decode(sc.pool, q, out, sc.bt_dev, i32(sc.lengths), max_ctx or max(sc.lengths), sc.hq)
+    torch.cuda.synchronize()
+    return inputs.as_float(from_dev(out, sc.dtype), sc.dtype)
+
+
+def oracle_decode(sc: Scenario, q_np):
+    qf = inputs.as_float(q_np, sc.dtype)
+    return np.stack([oa.decode(qf[r], sc.kf(r), sc.vf(r)) for r in range(len(sc.lengths))])
+
+
+@pytest.mark.parametrize("dtype,hq,hkv,d,bs,shards,lengths", [
+    ("f32", 4, 2, 64, 16, 1, [37, 64, 100, 128]),          # the tiny check's decode requests
+    ("bf16", 32, 8, 128, 16, 1, [1, 2, 15, 16, 17, 63, 64, 65, 300, 511, 1000, 1537]),
+    ("bf16", 64, 8, 128, 16, 1, [2048, 8192, 3001, 4097]),
+    ("bf16", 16, 16, 128, 32, 4, [129, 700]),              # G = 1, several shards
+    ("bf16", 32, 2, 64, 64, 2, [1, 333, 2000]),            # G = 16, head dim 64
+    ("bf16", 8, 4, 128, 128, 1, [5, 256, 1025]),
+    ("f32", 8, 2, 128, 32, 2, [1, 90, 513]),
+])
+def test_decode_matches_oracle(dtype, hq, hkv, d, bs, shards, lengths):
+    nblk = sum(-(-n // bs) for n in lengths) + 3
+    sc = Scenario(num_q_heads=hq, num_kv_heads=hkv, head_dim=d, block_size=bs, dtype=dtype, lengths=lengths,
+                  pool_blocks=nblk, num_shards=shards, scale=0.5 if dtype == "bf16" else 1.0, seed=5)
+    sc.write_all()
+    q = _q(sc, (len(lengths), hq, d), scale=0.5 if dtype == "bf16" else 1.0)
+    got = run_decode(sc, q)
+    assert_close(got, oracle_decode(sc, q), dtype, "decode")
+
+
+def test_decode_single_key_is_exact():
+    # one key: the softmax weight is exactly 1, so the output is v0 itself
+    for dtype in ("f32", "bf16"):
+        sc = Scenario(num_q_heads=8, num_kv_heads=2, head_dim=128, block_size=16, dtype=dtype, lengths=[1, 1, 1],
+                      pool_blocks=8, seed=6)
+        sc.write_all()
+        got = run_decode(sc, _q(sc, (3, 8, 128)))
+        for r in range(3):
+            for h in range(8):
+                assert np.array_equal(got[r, h], sc.vf(r)[0, h // 4])
+
+
+def test_decode_longer_max_context_than_needed():
+    # grid sized by a larger max_context_len: extra splits must be idle
+    sc = Scenario(num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=16, dtype="bf16", lengths=[100, 700],
+                  pool_blocks=64, scale=0.5, seed=7, table_pad=260)
+    sc.write_all()
+    q = _q(sc, (2, 32, 128), scale=0.5)
+    got = run_decode(sc, q, max_ctx=4000)
+    assert_close(got, oracle_decode(sc, q), "bf16", "decode(max_ctx 4000)")
+
+
+def run_prefill_chunks(sc: Scenario, q_np, chunk, req=0):
+    """Write + attend chunk by chunk for one request; returns the stacked GPU rows."""
+    n = sc.lengths[req]
+    outs = []
+    for s in range(0, n, chunk):
+        t = min(chunk, n - s)
+        sc.write_tokens(sc.k[req][s:s + t], sc.v[req][s:s + t], np.array([0, t], np.int32), np.array([s], np.int32),
+                        tables=sc.bt_dev[req:req + 1])
+        q = to_dev(q_np[s:s + t], sc.dtype)
+        out = torch.empty((t, sc.hq, sc.d), dtype=_tdtype(sc.dtype), device="cuda")
+        ops.attn_prefill_chunk(sc.pool, q, out, sc.bt_dev[req:req + 1], i32([0, t]), i32([s]), t, sc.hq)
+        outs.append(out)
+    torch.cuda.synchronize()
+    return np.concatenate([inputs.as_float(from_dev(o, sc.dtype), sc.dtype) for o in outs])
+
+
+@pytest.mark.parametrize("dtype,hq,hkv,d,bs,n,chunk", [
+    ("f32", 4, 2, 64, 16, 256, 64),          # the tiny check: 4 causal chunks of 64
+    ("bf16", 32, 8, 128, 16, 1024, 512),     # Llama-3-8B shape, 2 chunks of 512 (all rows)
+    ("bf16", 32, 8, 128, 16, 1024, 1024),    # same prompt one-shot
+    ("bf16", 8, 2, 128, 16, 300, 77),        # ragged chunks and tail
+    ("bf16", 16, 1, 64, 32, 517, 200),       # G = 16, head dim 64
+    ("bf16", 4, 4, 128, 64, 130, 130),       # G = 1, one chunk of 130
+    ("bf16", 8, 8, 64, 128, 1, 1),           # a single token
+    ("f32", 4, 2, 128, 32, 70, 33),
+])
+def test_chunked_prefill_matches_one_shot_oracle(dtype, hq, hkv, d, bs, n, chunk):
+    sc = Scenario(num_q_heads=hq, num_kv_heads=hkv, head_dim=d, block_size=bs, dtype=dtype, lengths=[n],
+                  pool_blocks=-(-n // bs) + 2, scale=0.5 if dtype == "bf16" else 1.0, seed=8)
+    q = _q(sc, (n, hq, d), scale=0.5 if dtype == "bf16" else 1.0)
+    got = run_prefill_chunks(sc, q, chunk)
+    ref = oa.prefill(inputs.as_float(q, dtype), sc.kf(0), sc.vf(0))
+    assert_close(got, ref, dtype, f"prefill chunk {chunk}")
+
+
+def test_prefill_varlen_batch():
+    # three requests with different chunk starts and lengths in one launch
+    lengths = [700, 129, 1500]
+    starts = [500, 0, 1024]
+    sc = Scenario(num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=16, dtype="bf16", lengths=lengths,
+                  pool_blocks=200, scale=0.5, seed=9)
+    sc.write_all()
+    qs = [_q(sc, (n - s, 32, 128), idx=r, scale=0.5) for r, (n, s) in enumerate(zip(lengths, starts))]
+    tl = [n - s for n, s in zip(lengths, starts)]
+    start_loc = np.concatenate([[0], np.cumsum(tl)]).astype(np.int32)
+    q = to_dev(np.concatenate(qs), "bf16")
+    out = torch.empty((int(start_loc[-1]), 32, 128), dtype=torch.bfloat16, device="cuda")
+    ops.attn_prefill_chunk(sc.pool, q, out, sc.bt_dev, i32(start_loc), i32(starts), max(tl), 32)
+    torch.cuda.synchronize()
+    got = inputs.as_float(from_dev(out, "bf16"), "bf16")
+    for r in range(3):
+        ref = oa.prefill_chunk(inputs.as_float(qs[r], "bf16"), sc.kf(r), sc.vf(r), starts[r])
+        assert_close(got[start_loc[r]:start_loc[r + 1]], ref, "bf16", f"request {r}")
+
+
+def test_single_token_chunk_equals_decode():
+    # a T=1 chunk at S is the decode query at L = S+1: the two kernels agree
+    L = 777
+    sc = Scenario(num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=16, dtype="bf16", lengths=[L],
+                  pool_blocks=60, scale=0.5, seed=10)
+    sc.write_all()
+    q = _q(sc, (1, 32, 128), scale=0.5)
+    dec = run_decode(sc, q)
+    out = torch.empty((1, 32, 128), dtype=torch.bfloat16, device="cuda")
+    ops.attn_prefill_chunk(sc.pool, to_dev(q, "bf16"), out, sc.bt_dev, i32([0, 1]), i32([L - 1]), 1, 32)
+    torch.cuda.synchronize()
+    pre = inputs.as_float(from_dev(out, "bf16"), "bf16")
+    ref = oracle_decode(sc, q)
+    assert_close(dec, ref, "bf16", "decode")
+    assert_close(pre, ref, "bf16", "prefill T=1")
+    assert np.abs(dec - pre).max() <= 2e-2
+
+
+def test_tiny_config_relayout_then_decode_unchanged():
+    """The tiny check: prompt prefilled in 64-token chunks, decode, relayout to bs 32 (1 -> 2 shards), decode again."""
+    w = workloads.TINY
+    ctx = list(w.decode_context)
+    lengths = [w.prompt_len] + ctx
+    sc = Scenario(num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads, head_dim=w.head_dim,
+                  block_size=w.block_size, dtype=w.dtype, lengths=lengths, pool_blocks=w.pool_blocks,
+                  num_shards=w.src_shards, scale=w.input_scale, seed=w.seed, config_id=w.config_id)
+    assert sum(-(-n // 16) for n in lengths) == 38
+    qp = _q(sc, (w.prompt_len, w.num_q_heads, w.head_dim))
+    got = run_prefill_chunks(sc, qp, w.chunk_sizes[0], req=0)
+    assert_close(got, oa.prefill(qp, sc.kf(0), sc.vf(0)), "f32", "tiny prefill")
+    sc.write_all([0] + ctx)      # decode requests' K/V (the prompt is already written)
+    sc_dec_lengths = sc.lengths
+    qd = _q(sc, (len(ctx), w.num_q_heads, w.head_dim), tid=inputs.T_Q_DECODE)
+    tables = sc.bt_dev[1:]
+    out = torch.empty((len(ctx), w.num_q_heads, w.head_dim), dtype=torch.float32, device="cuda")
+    ops.attn_decode(sc.pool, to_dev(qd, "f32"), out, tables, i32(ctx), max(ctx), w.num_q_heads)
+    ref = np.stack([oa.decode(qd[i], sc.kf(i + 1), sc.vf(i + 1)) for i in range(len(ctx))])
+    before = out.cpu().numpy().astype(np.float64)
+    assert_close(before, ref, "f32", "tiny decode (bs 16)")
+    # relayout every request to block size 32, 2 shards x 1 head
+    g = inputs.stream(w.seed, w.config_id, 0, inputs.T_DST_PERM)
+    dst_bt, _ = inputs.assign_blocks(w.dst_pool_blocks, sc_dec_lengths, w.dst_block_size, g)
+    dst = ops.PagedPool(w.dst_pool_blocks, w.dst_block_size, w.num_kv_heads, w.dst_shards, w.head_dim, "f32")
+    dst.fill_bits(0x7FC0DEAD)
+    dst_bt_dev = i32(dst_bt)
+    for r, n in enumerate(sc_dec_lengths):
+        ops.kv_relayout(sc.pool, sc.bt_dev[r], dst, dst_bt_dev[r], n)
+    out2 = torch.empty_like(out)
+    ops.attn_decode(dst, to_dev(qd, "f32"), out2, dst_bt_dev[1:], i32(ctx), max(ctx), w.num_q_heads)
+    torch.cuda.synchronize()
+    after = out2.cpu().numpy().astype(np.float64)
+    assert_close(after, ref, "f32", "tiny decode (bs 32, 2 shards)")
+    assert np.abs(after - before).max() <= 1e-6

@@ -1,0 +1,127 @@
+"""GPU parity of slot mapping, kv_write and kv_relayout: bit-exact against the oracle.
+
+The oracle's pool model (``oracle.pool``) is filled by its own naive loops
+from the same logical K/V; the GPU pools are copied back and compared byte
+for byte, including every slot that must stay untouched (sentinel bits).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from decode_paged_kv_amd import inputs, ops, workloads
+from gpu_common import SENTINEL, Scenario, from_dev, i32, to_dev
+from oracle import accounting, pool as opool
+
+pytestmark = pytest.mark.gpu
+
+
+def _elem(dtype):
+    return np.uint16 if dtype == "bf16" else np.float32
+
+
+def _oracle_pool_from(sc: Scenario, num_shards=None, lengths=None):
+    pm = opool.PoolModel(sc.pool.num_blocks, sc.bs, sc.hkv, num_shards or sc.pool.num_shards, sc.d,
+                         _elem(sc.dtype), fill=_fill_value(sc.dtype))
+    for r, n in enumerate(lengths or sc.lengths):
+        opool.write(pm, sc.k[r][:n], sc.v[r][:n], opool.slots_for(sc.tables[r], sc.bs, range(n)))
+    return pm
+
+
+def _fill_value(dtype):
+    return SENTINEL[dtype] if dtype == "bf16" else np.array([SENTINEL[dtype]], np.uint32).view(np.float32)[0]
+
+
+def _assert_pool_equal(gpu_pool: ops.PagedPool, pm: opool.PoolModel):
+    for s in range(pm.num_shards):
+        gk, gv = from_dev(gpu_pool.k[s], gpu_pool.dtype), from_dev(gpu_pool.v[s], gpu_pool.dtype)
+        # compare raw bits (NaN sentinels compare equal this way)
+        assert np.array_equal(gk.view(np.uint8), pm.k[s].view(np.uint8)), f"K shard {s}"
+        assert np.array_equal(gv.view(np.uint8), pm.v[s].view(np.uint8)), f"V shard {s}"
+
+
+def test_slot_mapping_matches_oracle():
+    sc = Scenario(num_q_heads=4, num_kv_heads=2, head_dim=64, block_size=16, dtype="f32",
+                  lengths=[37, 64, 100, 128, 1], pool_blocks=64, seed=3)
+    start = np.concatenate([[0], np.cumsum(sc.lengths)]).astype(np.int32)
+    # decode-style: one token per request at position L-1; prefill-style: all tokens
+    pos = np.array(sc.lengths, np.int32) - 1
+    slots = ops.slot_mapping(sc.bt_dev, i32(np.arange(len(sc.lengths) + 1)), i32(pos), len(sc.lengths), 16, 64)
+    ref = [opool.slots_for(sc.tables[r], 16, [int(pos[r])])[0] for r in range(len(sc.lengths))]
+    assert slots.cpu().tolist() == ref
+    slots = ops.slot_mapping(sc.bt_dev, i32(start), i32(np.zeros(5)), int(start[-1]), 16, 64)
+    ref = sum((opool.slots_for(sc.tables[r], 16, range(n)) for r, n in enumerate(sc.lengths)), [])
+    assert slots.cpu().tolist() == ref
+
+
+@pytest.mark.parametrize("dtype,bs,shards,hkv,d", [("f32", 16, 1, 2, 64), ("bf16", 16, 4, 8, 128),
+                                                  ("bf16", 32, 8, 8, 128), ("bf16", 64, 2, 4, 64),
+                                                  ("f32", 128, 2, 2, 128)])
+def test_kv_write_bit_exact(dtype, bs, shards, hkv, d):
+    sc = Scenario(num_q_heads=hkv, num_kv_heads=hkv, head_dim=d, block_size=bs, dtype=dtype,
+                  lengths=[37, 130, 5], pool_blocks=24, num_shards=shards, seed=11)
+    sc.write_all()
+    torch.cuda.synchronize()
+    _assert_pool_equal(sc.pool, _oracle_pool_from(sc))
+
+
+def test_kv_write_skips_negative_slots():
+    sc = Scenario(num_q_heads=2, num_kv_heads=2, head_dim=64, block_size=16, dtype="bf16", lengths=[20],
+                  pool_blocks=4, seed=12)
+    slots = np.array(opool.slots_for(sc.tables[0], 16, range(20)), np.int32)
+    slots[::3] = -1
+    ops.kv_write(sc.pool, to_dev(sc.k[0], "bf16"), to_dev(sc.v[0], "bf16"), i32(slots))
+    torch.cuda.synchronize()
+    pm = opool.PoolModel(4, 16, 2, 1, 64, np.uint16, fill=SENTINEL["bf16"])
+    opool.write(pm, sc.k[0], sc.v[0], slots.tolist())
+    _assert_pool_equal(sc.pool, pm)
+
+
+def _relayout_case(dtype, n, src_bs, src_shards, src_blocks, dst_bs, dst_shards, dst_blocks, hkv, d, seed,
+                   layers=1):
+    out = []
+    for layer in range(layers):
+        sc = Scenario(num_q_heads=hkv, num_kv_heads=hkv, head_dim=d, block_size=src_bs, dtype=dtype, lengths=[n],
+                      pool_blocks=src_blocks, num_shards=src_shards, seed=seed, layer=layer)
+        sc.write_all()
+        g = inputs.stream(seed, 0, layer, inputs.T_DST_PERM)
+        dst_bt, _ = inputs.assign_blocks(dst_blocks, [n], dst_bs, g)
+        dst = ops.PagedPool(dst_blocks, dst_bs, hkv, dst_shards, d, dtype).fill_bits(SENTINEL[dtype])
+        out.append((sc, dst, dst_bt))
+    for sc, dst, dst_bt in out:            # back to back, as layer-wise submission does
+        ops.kv_relayout(sc.pool, sc.bt_dev[0], dst, i32(dst_bt[0]), n)
+    torch.cuda.synchronize()
+    return out
+
+
+@pytest.mark.parametrize("dtype,n,sbs,ssh,sblk,dbs,dsh,dblk,hkv,d", [
+    ("f32", 256, 16, 1, 64, 32, 2, 32, 2, 64),          # the tiny check: 1 shard x 2 heads -> 2 x 1, bs 16 -> 32
+    ("bf16", 4096, 16, 4, 256, 32, 8, 128, 8, 128),     # the 70B shape, one layer at full size
+    ("bf16", 1000, 32, 8, 40, 16, 4, 70, 8, 128),       # the inverse direction, ragged tail
+    ("bf16", 77, 16, 2, 8, 64, 1, 4, 4, 64),
+    ("f32", 300, 128, 1, 4, 16, 2, 30, 2, 128),
+])
+def test_relayout_bit_exact(dtype, n, sbs, ssh, sblk, dbs, dsh, dblk, hkv, d):
+    (sc, dst, dst_bt), = _relayout_case(dtype, n, sbs, ssh, sblk, dbs, dsh, dblk, hkv, d, seed=21)
+    pm_src = _oracle_pool_from(sc)
+    pm_dst = opool.PoolModel(dblk, dbs, hkv, dsh, d, _elem(dtype), fill=_fill_value(dtype))
+    moved = opool.relayout(pm_src, sc.tables[0], pm_dst, dst_bt[0], n)
+    assert moved == accounting.relayout_payload_bytes(n, hkv, d, 2 if dtype == "bf16" else 4)
+    _assert_pool_equal(dst, pm_dst)
+    # logical content equals the request's K/V
+    gk, gv = opool.gather(pm_dst, dst_bt[0], n)
+    assert np.array_equal(gk, sc.k[0]) and np.array_equal(gv, sc.v[0])
+
+
+def test_relayout_70b_layers_back_to_back():
+    w = workloads.RELAYOUT_70B
+    layers = 6
+    cases = _relayout_case("bf16", w.prompt_len, w.block_size, w.src_shards, w.pool_blocks, w.dst_block_size,
+                           w.dst_shards, w.dst_pool_blocks, w.num_kv_heads, w.head_dim, seed=w.seed, layers=layers)
+    for sc, dst, dst_bt in cases:
+        # logical check through the oracle's gather on a host copy of the GPU pool
+        pm = opool.PoolModel(w.dst_pool_blocks, w.dst_block_size, 8, 8, 128, np.uint16)
+        pm.k = [from_dev(t, "bf16") for t in dst.k]
+        pm.v = [from_dev(t, "bf16") for t in dst.v]
+        gk, gv = opool.gather(pm, dst_bt[0], w.prompt_len)
+        assert np.array_equal(gk, sc.k[0]) and np.array_equal(gv, sc.v[0])
