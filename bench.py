@@ -244,8 +244,209 @@ def cpu_baseline_decode(w):
                       f"workload), repeated {reps} times in {dt:.1f} s; bf16 K/V/q/out bytes / wall time"}
 
 
+# --------------------------------------------------------- qwen3-32b ----
+def bench_qwen3_32b(args):
+    w = workloads.QWEN3_32B
+    L, hq, hkv, d, bs = w.layers, w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size
+    ctxs = [int(x) for x in w.decode_contexts()]
+    B, N = len(ctxs), w.prompt_len
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(w.seed)
+    stream = torch.cuda.Stream()
+    tables = make_tables(w, ctxs + [N], bs, w.pool_blocks)
+    dec_bt, pr_bt = i32(tables[:B]), i32(tables[B:B + 1])
+    pools = [ops.PagedPool(w.pool_blocks, bs, hkv, 1, d, "bf16") for _ in range(L)]
+    for p in pools:
+        fill_pool_random(p, gen)
+    maxc = max(ctxs)
+    q_dec = [rand_bf16((B, hq, d), gen) for _ in range(L)]
+    kn = [rand_bf16((B, hkv, d), gen) for _ in range(L)]
+    vn = [rand_bf16((B, hkv, d), gen) for _ in range(L)]
+    o_dec = [torch.empty((B, hq, d), dtype=torch.bfloat16, device="cuda") for _ in range(L)]
+    q_pr = [rand_bf16((N, hq, d), gen) for _ in range(L)]
+    k_pr = [rand_bf16((N, hkv, d), gen) for _ in range(L)]
+    v_pr = [rand_bf16((N, hkv, d), gen) for _ in range(L)]
+    o_pr = [torch.empty((N, hq, d), dtype=torch.bfloat16, device="cuda") for _ in range(L)]
+    ctx_t = i32(ctxs)
+    ws = torch.empty(max(16, ops.attn_decode_workspace_size(B, hq, maxc, d)), dtype=torch.uint8, device="cuda")
+    dec_start, dec_pos = i32(np.arange(B + 1)), i32([c - 1 for c in ctxs])
+    dec_slots = torch.empty(B, dtype=torch.int32, device="cuda")
+    plans = {}
+    for c in w.chunk_sizes:
+        chunks = [(s, min(c, N - s)) for s in range(0, N, c)]
+        plans[c] = [(s, t, i32([0, t]), i32([s]), torch.empty(t, dtype=torch.int32, device="cuda")) for s, t in chunks]
+    timer = Timer(stream)
+
+    def step(timed):
+        tk = timer if timed else None
+        with torch.cuda.stream(stream):
+            if tk: tk.start("step")
+            if tk: tk.start("decode_step")
+            ops.slot_mapping(dec_bt, dec_start, dec_pos, B, bs, w.pool_blocks, out=dec_slots, stream=stream)
+            for l in range(L):
+                ops.kv_write(pools[l], kn[l], vn[l], dec_slots, stream=stream)
+                if tk: tk.start("attn_decode")
+                ops.attn_decode(pools[l], q_dec[l], o_dec[l], dec_bt, ctx_t, maxc, hq, workspace=ws, stream=stream)
+                if tk: tk.stop("attn_decode")
+            if tk: tk.stop("decode_step")
+            for c, plan in plans.items():
+                if tk: tk.start(f"prefill_c{c}")
+                for s, t, sl, cs, slots in plan:
+                    ops.slot_mapping(pr_bt, sl, cs, t, bs, w.pool_blocks, out=slots, stream=stream)
+                    for l in range(L):
+                        ops.kv_write(pools[l], k_pr[l][s:s + t], v_pr[l][s:s + t], slots, stream=stream)
+                        ops.attn_prefill_chunk(pools[l], q_pr[l][s:s + t], o_pr[l][s:s + t], pr_bt, sl, cs, t, hq,
+                                               stream=stream)
+                if tk: tk.stop(f"prefill_c{c}")
+            if tk: tk.stop("step")
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    step_ms = float(np.mean(timer.ms("step")))
+    dec_ms = float(np.mean(timer.ms("attn_decode")))
+    dbytes = decode_bytes(ctxs, hkv, d, hq)
+    dec_gbps = dbytes / (dec_ms * 1e-3) / 1e9
+    per = {}
+    tot_flops = tot_ms = 0.0
+    for c, plan in plans.items():
+        fl = L * sum(prefill_flops(hq, d, t, s) for s, t, *_ in plan)
+        ms = float(np.mean(timer.ms(f"prefill_c{c}")))
+        per[c] = (fl, ms)
+        tot_flops += fl
+        tot_ms += ms
+    tflops = tot_flops / (tot_ms * 1e-3) / 1e12
+    result = {
+        "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(step_ms, 3), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "qwen3-32b-attn: 64 layers, 64/8 heads, d128, bs16; decode 16 x U[2048,8192]; "
+                               "prompt 16384 prefilled at chunk 2048 and at chunk 512 (slot mapping + kv_write + "
+                               "attn_prefill_chunk per chunk and layer)",
+                   "decode_contexts": ctxs, "prompt": N, "chunks": list(w.chunk_sizes),
+                   "value_is": "prefill attention TFLOP/s over both chunkings (pages' flop count / prefill time, "
+                               "kv_write included)"},
+        "roofline": {"kernel": "attn_prefill_chunk", "bound": "mfma", "achieved": round(tflops, 2),
+                     "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tflops / BF16_PEAK_TFLOPS, 4),
+                     "traffic": None, "flops_per_step": tot_flops},
+        "metrics": {
+            "decode_attn_gbps": round(dec_gbps, 1), "decode_attn_frac_hbm": round(dec_gbps / HBM_PEAK_GBPS, 4),
+            "decode_launch_ms": round(dec_ms, 5), "decode_step_ms": round(float(np.mean(timer.ms("decode_step"))), 3),
+            **{f"prefill_c{c}_tflops": round(fl / (ms * 1e-3) / 1e12, 2) for c, (fl, ms) in per.items()},
+            **{f"prefill_c{c}_ms": round(ms, 3) for c, (fl, ms) in per.items()},
+        },
+    }
+    if args.cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline_prefill(w)
+    return result
+
+
+def cpu_baseline_prefill(w):
+    from oracle import attention as oa
+    hq, hkv, d, N = w.num_q_heads, w.num_kv_heads, w.head_dim, w.prompt_len
+    t, s = 512, N - 512
+    g = lambda tid: inputs.stream(w.seed, w.config_id, 0, tid)  # noqa: E731
+    k = inputs.as_float(inputs.normal((N, hkv, d), 0.5, "bf16", g(inputs.T_K)), "bf16")
+    v = inputs.as_float(inputs.normal((N, hkv, d), 0.5, "bf16", g(inputs.T_V)), "bf16")
+    q = inputs.as_float(inputs.normal((t, hq, d), 0.5, "bf16", g(inputs.T_Q)), "bf16")
+    t0 = time.perf_counter()
+    reps = 0
+    while True:
+        oa.prefill_chunk(q, k, v, s)
+        reps += 1
+        if time.perf_counter() - t0 > 10.0:
+            break
+    dt = time.perf_counter() - t0
+    fl = prefill_flops(hq, d, t, s) * reps
+    return {"value": round(fl / dt / 1e12, 5), "unit": "TFLOP/s", "cores": cores_used(), "kind": "oracle",
+            "sample": f"oracle prefill of the last 512-token chunk (S={s}) of one layer, {hq}/{hkv} heads, repeated "
+                      f"{reps} times in {dt:.1f} s; pages' flop count / wall time"}
+
+
+# ------------------------------------------------------ relayout-70b ----
+def bench_relayout_70b(args):
+    w = workloads.RELAYOUT_70B
+    L, hkv, d, N = w.layers, w.num_kv_heads, w.head_dim, w.prompt_len
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(w.seed)
+    stream = torch.cuda.Stream()
+    src_bt = i32(make_tables(w, [N], w.block_size, w.pool_blocks))
+    dst_bt = i32(make_tables(w, [N], w.dst_block_size, w.dst_pool_blocks, inputs.T_DST_PERM))
+    srcs = [ops.PagedPool(w.pool_blocks, w.block_size, hkv, w.src_shards, d, "bf16") for _ in range(L)]
+    dsts = [ops.PagedPool(w.dst_pool_blocks, w.dst_block_size, hkv, w.dst_shards, d, "bf16") for _ in range(L)]
+    for p in srcs:
+        fill_pool_random(p, gen)
+    timer = Timer(stream)
+
+    def step(mode):
+        with torch.cuda.stream(stream):
+            if mode: timer.start("step_" + mode)
+            for l in range(L):
+                if mode == "per_launch": timer.start("launch")
+                ops.kv_relayout(srcs[l], src_bt, dsts[l], dst_bt, N, stream=stream)
+                if mode == "per_launch": timer.stop("launch")
+            if mode: timer.stop("step_" + mode)
+
+    for _ in range(args.warmup):
+        step(None)
+    torch.cuda.synchronize()
+    for _ in range(args.steps):
+        step("back_to_back")
+    for _ in range(args.steps):
+        step("per_launch")
+    torch.cuda.synchronize()
+    step_ms = float(np.mean(timer.ms("step_back_to_back")))
+    launch_ms = float(np.mean(timer.ms("launch")))
+    per_layer = relayout_bytes(N, hkv, d)
+    gbps = per_layer * L / (step_ms * 1e-3) / 1e9
+    launch_gbps = per_layer / (launch_ms * 1e-3) / 1e9
+    result = {
+        "metric": METRIC, "value": round(gbps, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(step_ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "relayout-llama3-70b: 80 layers x one 4096-token request, 8 kv heads, d128; "
+                               "bs16 / 4 shards x 2 heads -> bs32 / 8 shards x 1 head; 80 kv_relayout calls back to "
+                               "back", "payload_bytes": per_layer // 2 * L,
+                   "value_is": "relayout HBM GB/s = 2 x payload / time of the 80 back-to-back calls"},
+        "roofline": {"kernel": "kv_relayout", "bound": "hbm", "achieved": round(launch_gbps, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(launch_gbps / HBM_PEAK_GBPS, 4),
+                     "traffic": None, "bytes_per_launch": per_layer, "launch_ms": round(launch_ms, 5)},
+        "metrics": {"relayout_gbps_back_to_back": round(gbps, 1), "relayout_frac_hbm": round(gbps / HBM_PEAK_GBPS, 4),
+                    "relayout_launch_gbps": round(launch_gbps, 1), "relayout_launch_ms": round(launch_ms, 5)},
+    }
+    if args.cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline_relayout(w)
+    return result
+
+
+def cpu_baseline_relayout(w):
+    from oracle import pool as opool
+    hkv, d, N = w.num_kv_heads, w.head_dim, w.prompt_len
+    g = lambda tid: inputs.stream(w.seed, w.config_id, 0, tid)  # noqa: E731
+    src_bt, _ = inputs.assign_blocks(w.pool_blocks, [N], w.block_size, g(inputs.T_PERM))
+    dst_bt, _ = inputs.assign_blocks(w.dst_pool_blocks, [N], w.dst_block_size, g(inputs.T_DST_PERM))
+    src = opool.PoolModel(w.pool_blocks, w.block_size, hkv, w.src_shards, d, np.uint16)
+    for a in src.k + src.v:
+        a[...] = inputs.normal(a.shape, 0.5, "bf16", g(inputs.T_K))
+    t0 = time.perf_counter()
+    reps = 0
+    while True:
+        dst = opool.PoolModel(w.dst_pool_blocks, w.dst_block_size, hkv, w.dst_shards, d, np.uint16)
+        opool.relayout(src, src_bt[0], dst, dst_bt[0], N)
+        reps += 1
+        if time.perf_counter() - t0 > 10.0:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": round(relayout_bytes(N, hkv, d) * reps / dt / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "kind": "oracle", "sample": f"oracle naive relayout of one layer (4096 tokens x 8 heads), repeated {reps} "
+                                         f"times in {dt:.1f} s; 2 x payload / wall time"}
+
+
 # --------------------------------------------------------------- main ----
-BENCHES = {"llama3-8b": bench_llama3_8b}
+BENCHES = {"llama3-8b": bench_llama3_8b, "qwen3-32b": bench_qwen3_32b, "relayout-70b": bench_relayout_70b}
 
 
 def main():
