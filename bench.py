@@ -29,7 +29,6 @@ from __future__ import annotations
 
 import argparse
 import json
-import math
 import os
 import sys
 import time
@@ -64,28 +63,50 @@ def relayout_bytes(n, hkv, d, esize=2):
 
 
 # ------------------------------------------------------------- helpers ----
-class Timer:
-    """Pairs of HIP events on one stream; durations in ms after a sync."""
+class PhaseGraphs:
+    """HIP graphs of the step's phases, captured once and replayed.
+
+    The library launches every kernel on the stream it is given; under
+    capture those launches become graph nodes, so a replay runs them back
+    to back with no host work between kernels.  Durations come from HIP
+    events recorded around each replay on the replaying stream.
+    """
 
     def __init__(self, stream):
         self.stream = stream
-        self.pairs = {}
+        self.graphs = {}
 
-    def start(self, key):
-        e = torch.cuda.Event(enable_timing=True)
-        e.record(self.stream)
-        self.pairs.setdefault(key, []).append([e, None])
+    def capture(self, name, fn):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(self.stream):
+            fn()                                  # eager run first (warms up code objects)
+        self.stream.synchronize()
+        with torch.cuda.graph(g, stream=self.stream):
+            fn()
+        self.graphs[name] = g
 
-    def stop(self, key):
-        e = torch.cuda.Event(enable_timing=True)
-        e.record(self.stream)
-        self.pairs[key][-1][1] = e
+    def replay(self, name):
+        with torch.cuda.stream(self.stream):
+            self.graphs[name].replay()
 
-    def ms(self, key):
-        return [a.elapsed_time(b) for a, b in self.pairs.get(key, [])]
 
-    def reset(self):
-        self.pairs = {}
+def time_replays(pg: PhaseGraphs, names, steps, warmup):
+    """Mean ms of each named graph over `steps` timed rounds (all replayed in order each round)."""
+    for _ in range(warmup):
+        for n in names:
+            pg.replay(n)
+    torch.cuda.synchronize()
+    ev = {n: [] for n in names}
+    for _ in range(steps):
+        for n in names:
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(pg.stream)
+            pg.replay(n)
+            b.record(pg.stream)
+            ev[n].append((a, b))
+    torch.cuda.synchronize()
+    return {n: float(np.mean([a.elapsed_time(b) for a, b in ev[n]])) for n in names}
 
 
 def rand_bf16(shape, gen, scale=0.5):
@@ -141,79 +162,79 @@ def bench_llama3_8b(args):
     v_pr = [rand_bf16((N, hkv, d), gen) for _ in range(L)]
     o_pr = [torch.empty((N, hq, d), dtype=torch.bfloat16, device="cuda") for _ in range(L)]
     ctx_t = i32([ctx] * B)
-    ws = torch.empty(max(16, ops.attn_decode_workspace_size(B, hq, ctx, d)), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(max(16, ops.attn_decode_workspace_size(B, hq, ctx, d)), dtype=torch.uint8, device="cuda")
     dec_start, dec_pos = i32(np.arange(B + 1)), i32([ctx - 1] * B)
     dec_slots = torch.empty(B, dtype=torch.int32, device="cuda")
     chunks = [(s, min(chunk, N - s)) for s in range(0, N, chunk)]
     ch_args = [(i32([0, t]), i32([s]), torch.empty(t, dtype=torch.int32, device="cuda")) for s, t in chunks]
-    timer = Timer(stream)
+    sh = stream.cuda_stream
 
-    def step(timed):
-        tk = timer if timed else None
-        with torch.cuda.stream(stream):
-            if tk: tk.start("step")
-            if tk: tk.start("decode_step")
-            ops.slot_mapping(dec_bt, dec_start, dec_pos, B, bs, w.pool_blocks, out=dec_slots, stream=stream)
+    def decode_attn():
+        for l in range(L):
+            ops.attn_decode(pools[l], q_dec[l], o_dec[l], dec_bt, ctx_t, ctx, hq, workspace=ws, stream=sh)
+
+    def decode_step():
+        ops.slot_mapping(dec_bt, dec_start, dec_pos, B, bs, w.pool_blocks, out=dec_slots, stream=sh)
+        for l in range(L):
+            ops.kv_write(pools[l], kn[l], vn[l], dec_slots, stream=sh)
+            ops.attn_decode(pools[l], q_dec[l], o_dec[l], dec_bt, ctx_t, ctx, hq, workspace=ws, stream=sh)
+
+    def prefill_attn():
+        for (s, t), (sl, cs, _) in zip(chunks, ch_args):
             for l in range(L):
-                ops.kv_write(pools[l], kn[l], vn[l], dec_slots, stream=stream)
-                if tk: tk.start("attn_decode")
-                ops.attn_decode(pools[l], q_dec[l], o_dec[l], dec_bt, ctx_t, ctx, hq, workspace=ws, stream=stream)
-                if tk: tk.stop("attn_decode")
-            if tk: tk.stop("decode_step")
-            if tk: tk.start("prefill")
-            for (s, t), (sl, cs, slots) in zip(chunks, ch_args):
-                ops.slot_mapping(pr_bt, sl, cs, t, bs, w.pool_blocks, out=slots, stream=stream)
-                for l in range(L):
-                    ops.kv_write(pools[l], k_pr[l][s:s + t], v_pr[l][s:s + t], slots, stream=stream)
-                    if tk: tk.start(f"attn_prefill_{s}")
-                    ops.attn_prefill_chunk(pools[l], q_pr[l][s:s + t], o_pr[l][s:s + t], pr_bt, sl, cs, t, hq,
-                                           stream=stream)
-                    if tk: tk.stop(f"attn_prefill_{s}")
-            if tk: tk.stop("prefill")
-            if tk: tk.start("relayout")
+                ops.attn_prefill_chunk(pools[l], q_pr[l][s:s + t], o_pr[l][s:s + t], pr_bt, sl, cs, t, hq, stream=sh)
+
+    def prefill():
+        for (s, t), (sl, cs, slots) in zip(chunks, ch_args):
+            ops.slot_mapping(pr_bt, sl, cs, t, bs, w.pool_blocks, out=slots, stream=sh)
             for l in range(L):
-                ops.kv_relayout(pools[l], pr_bt, dsts[l], dst_bt, N, stream=stream)
-            if tk: tk.stop("relayout")
-            if tk: tk.stop("step")
+                ops.kv_write(pools[l], k_pr[l][s:s + t], v_pr[l][s:s + t], slots, stream=sh)
+                ops.attn_prefill_chunk(pools[l], q_pr[l][s:s + t], o_pr[l][s:s + t], pr_bt, sl, cs, t, hq, stream=sh)
 
-    for _ in range(args.warmup):
-        step(False)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step(True)
-    torch.cuda.synchronize()
-    wall = (time.perf_counter() - t0) * 1e3 / args.steps
+    def relayout():
+        for l in range(L):
+            ops.kv_relayout(pools[l], pr_bt, dsts[l], dst_bt, N, stream=sh)
 
-    step_ms = float(np.mean(timer.ms("step")))
-    dec_launch_ms = float(np.mean(timer.ms("attn_decode")))
+    def step():
+        decode_step()
+        prefill()
+        relayout()
+
+    pg = PhaseGraphs(stream)
+    for name, fn in (("step", step), ("decode_attn", decode_attn), ("prefill_attn", prefill_attn),
+                     ("relayout", relayout), ("decode_step", decode_step)):
+        pg.capture(name, fn)
+    t_step = time_replays(pg, ["step"], args.steps, args.warmup)["step"]
+    t = time_replays(pg, ["decode_attn", "prefill_attn", "relayout", "decode_step"], args.steps, args.warmup)
+
+    dec_launch_ms = t["decode_attn"] / L
     dbytes = decode_bytes([ctx] * B, hkv, d, hq)
     dec_gbps = dbytes / (dec_launch_ms * 1e-3) / 1e9
-    pf_flops = sum(prefill_flops(hq, d, t, s) for s, t in chunks)
-    pf_ms = sum(float(np.mean(timer.ms(f"attn_prefill_{s}"))) for s, _ in chunks)   # per layer, both chunks
-    pf_tflops = pf_flops / (pf_ms * 1e-3) / 1e12
-    rl_ms = float(np.mean(timer.ms("relayout"))) / L
+    pf_flops = L * sum(prefill_flops(hq, d, tt, s) for s, tt in chunks)
+    pf_tflops = pf_flops / (t["prefill_attn"] * 1e-3) / 1e12
+    rl_ms = t["relayout"] / L
     rl_gbps = relayout_bytes(N, hkv, d) / (rl_ms * 1e-3) / 1e9
     result = {
         "metric": METRIC, "value": round(dec_gbps, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(step_ms, 4), "higher_is_better": True, "scaling": "weak",
+        "warmup": args.warmup, "ms_per_step": round(t_step, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "llama3-8b-attn: 32 layers, 32/8 heads, d128, bs16; decode 64x512 + prompt 1024 "
                                "in 2 chunks of 512 + relayout 1024 tokens bs16/4 shards -> bs32/8 shards",
                    "layers": L, "decode_batch": B, "decode_context": ctx, "prompt": N, "chunk": chunk,
-                   "value_is": "attn_decode HBM GB/s (algorithmic K/V + q/out bytes per launch / mean launch time)"},
-        "roofline": {"kernel": "attn_decode (split + merge)", "bound": "hbm", "achieved": round(dec_gbps, 1),
+                   "timing": "each phase captured once as a HIP graph and replayed; HIP events around replays",
+                   "value_is": "attn_decode HBM GB/s (algorithmic K/V + q/out bytes per launch / mean launch time "
+                               "over 32 back-to-back launches)"},
+        "roofline": {"kernel": "attn_decode", "bound": "hbm", "achieved": round(dec_gbps, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(dec_gbps / HBM_PEAK_GBPS, 4),
                      "traffic": None, "bytes_per_launch": dbytes, "launch_ms": round(dec_launch_ms, 5)},
         "metrics": {
             "decode_attn_gbps": round(dec_gbps, 1),
-            "decode_step_ms": round(float(np.mean(timer.ms("decode_step"))), 4),
+            "decode_step_ms": round(t["decode_step"], 4),
             "prefill_attn_tflops": round(pf_tflops, 2),
             "prefill_attn_frac_bf16_peak": round(pf_tflops / BF16_PEAK_TFLOPS, 4),
-            "prefill_layer_ms": round(pf_ms, 5),
+            "prefill_attn_ms_per_layer": round(t["prefill_attn"] / L, 5),
             "relayout_gbps": round(rl_gbps, 1),
             "relayout_layer_ms": round(rl_ms, 5),
-            "wall_ms_per_step": round(wall, 3),
         },
     }
     if args.cpu_baseline:
@@ -253,6 +274,7 @@ def bench_qwen3_32b(args):
     gen = torch.Generator(device="cuda")
     gen.manual_seed(w.seed)
     stream = torch.cuda.Stream()
+    sh = stream.cuda_stream
     tables = make_tables(w, ctxs + [N], bs, w.pool_blocks)
     dec_bt, pr_bt = i32(tables[:B]), i32(tables[B:B + 1])
     pools = [ops.PagedPool(w.pool_blocks, bs, hkv, 1, d, "bf16") for _ in range(L)]
@@ -268,53 +290,55 @@ def bench_qwen3_32b(args):
     v_pr = [rand_bf16((N, hkv, d), gen) for _ in range(L)]
     o_pr = [torch.empty((N, hq, d), dtype=torch.bfloat16, device="cuda") for _ in range(L)]
     ctx_t = i32(ctxs)
-    ws = torch.empty(max(16, ops.attn_decode_workspace_size(B, hq, maxc, d)), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(max(16, ops.attn_decode_workspace_size(B, hq, maxc, d)), dtype=torch.uint8, device="cuda")
     dec_start, dec_pos = i32(np.arange(B + 1)), i32([c - 1 for c in ctxs])
     dec_slots = torch.empty(B, dtype=torch.int32, device="cuda")
     plans = {}
     for c in w.chunk_sizes:
         chunks = [(s, min(c, N - s)) for s in range(0, N, c)]
         plans[c] = [(s, t, i32([0, t]), i32([s]), torch.empty(t, dtype=torch.int32, device="cuda")) for s, t in chunks]
-    timer = Timer(stream)
 
-    def step(timed):
-        tk = timer if timed else None
-        with torch.cuda.stream(stream):
-            if tk: tk.start("step")
-            if tk: tk.start("decode_step")
-            ops.slot_mapping(dec_bt, dec_start, dec_pos, B, bs, w.pool_blocks, out=dec_slots, stream=stream)
-            for l in range(L):
-                ops.kv_write(pools[l], kn[l], vn[l], dec_slots, stream=stream)
-                if tk: tk.start("attn_decode")
-                ops.attn_decode(pools[l], q_dec[l], o_dec[l], dec_bt, ctx_t, maxc, hq, workspace=ws, stream=stream)
-                if tk: tk.stop("attn_decode")
-            if tk: tk.stop("decode_step")
-            for c, plan in plans.items():
-                if tk: tk.start(f"prefill_c{c}")
-                for s, t, sl, cs, slots in plan:
-                    ops.slot_mapping(pr_bt, sl, cs, t, bs, w.pool_blocks, out=slots, stream=stream)
-                    for l in range(L):
-                        ops.kv_write(pools[l], k_pr[l][s:s + t], v_pr[l][s:s + t], slots, stream=stream)
-                        ops.attn_prefill_chunk(pools[l], q_pr[l][s:s + t], o_pr[l][s:s + t], pr_bt, sl, cs, t, hq,
-                                               stream=stream)
-                if tk: tk.stop(f"prefill_c{c}")
-            if tk: tk.stop("step")
+    def decode_attn():
+        for l in range(L):
+            ops.attn_decode(pools[l], q_dec[l], o_dec[l], dec_bt, ctx_t, maxc, hq, workspace=ws, stream=sh)
 
-    for _ in range(args.warmup):
-        step(False)
-    torch.cuda.synchronize()
-    for _ in range(args.steps):
-        step(True)
-    torch.cuda.synchronize()
-    step_ms = float(np.mean(timer.ms("step")))
-    dec_ms = float(np.mean(timer.ms("attn_decode")))
+    def decode_step():
+        ops.slot_mapping(dec_bt, dec_start, dec_pos, B, bs, w.pool_blocks, out=dec_slots, stream=sh)
+        for l in range(L):
+            ops.kv_write(pools[l], kn[l], vn[l], dec_slots, stream=sh)
+            ops.attn_decode(pools[l], q_dec[l], o_dec[l], dec_bt, ctx_t, maxc, hq, workspace=ws, stream=sh)
+
+    def prefill(c, with_write=True):
+        def run():
+            for s, t, sl, cs, slots in plans[c]:
+                if with_write:
+                    ops.slot_mapping(pr_bt, sl, cs, t, bs, w.pool_blocks, out=slots, stream=sh)
+                for l in range(L):
+                    if with_write:
+                        ops.kv_write(pools[l], k_pr[l][s:s + t], v_pr[l][s:s + t], slots, stream=sh)
+                    ops.attn_prefill_chunk(pools[l], q_pr[l][s:s + t], o_pr[l][s:s + t], pr_bt, sl, cs, t, hq,
+                                           stream=sh)
+        return run
+
+    pg = PhaseGraphs(stream)
+    pg.capture("decode_step", decode_step)
+    pg.capture("decode_attn", decode_attn)
+    for c in plans:
+        pg.capture(f"prefill_c{c}", prefill(c))          # writes the prompt's K/V too
+    for c in plans:
+        pg.capture(f"prefill_attn_c{c}", prefill(c, with_write=False))
+    names = ["decode_step"] + [f"prefill_c{c}" for c in plans]
+    t_step = time_replays(pg, names, args.steps, args.warmup)
+    step_ms = sum(t_step.values())
+    t = time_replays(pg, ["decode_attn"] + [f"prefill_attn_c{c}" for c in plans], args.steps, args.warmup)
+    dec_ms = t["decode_attn"] / L
     dbytes = decode_bytes(ctxs, hkv, d, hq)
     dec_gbps = dbytes / (dec_ms * 1e-3) / 1e9
     per = {}
     tot_flops = tot_ms = 0.0
     for c, plan in plans.items():
-        fl = L * sum(prefill_flops(hq, d, t, s) for s, t, *_ in plan)
-        ms = float(np.mean(timer.ms(f"prefill_c{c}")))
+        fl = L * sum(prefill_flops(hq, d, tt, s) for s, tt, *_ in plan)
+        ms = t[f"prefill_attn_c{c}"]
         per[c] = (fl, ms)
         tot_flops += fl
         tot_ms += ms
@@ -327,16 +351,19 @@ def bench_qwen3_32b(args):
                                "prompt 16384 prefilled at chunk 2048 and at chunk 512 (slot mapping + kv_write + "
                                "attn_prefill_chunk per chunk and layer)",
                    "decode_contexts": ctxs, "prompt": N, "chunks": list(w.chunk_sizes),
-                   "value_is": "prefill attention TFLOP/s over both chunkings (pages' flop count / prefill time, "
-                               "kv_write included)"},
+                   "timing": "each phase captured once as a HIP graph and replayed; HIP events around replays",
+                   "value_is": "attn_prefill_chunk TFLOP/s over both chunkings (pages' flop count / time of the "
+                               "back-to-back prefill launches)"},
         "roofline": {"kernel": "attn_prefill_chunk", "bound": "mfma", "achieved": round(tflops, 2),
                      "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tflops / BF16_PEAK_TFLOPS, 4),
-                     "traffic": None, "flops_per_step": tot_flops},
+                     "traffic": None, "flops_per_step": tot_flops,
+                     "launch_ms": round(tot_ms / sum(L * len(p) for p in plans.values()), 5)},
         "metrics": {
             "decode_attn_gbps": round(dec_gbps, 1), "decode_attn_frac_hbm": round(dec_gbps / HBM_PEAK_GBPS, 4),
-            "decode_launch_ms": round(dec_ms, 5), "decode_step_ms": round(float(np.mean(timer.ms("decode_step"))), 3),
+            "decode_launch_ms": round(dec_ms, 5), "decode_step_ms": round(t_step["decode_step"], 3),
             **{f"prefill_c{c}_tflops": round(fl / (ms * 1e-3) / 1e12, 2) for c, (fl, ms) in per.items()},
-            **{f"prefill_c{c}_ms": round(ms, 3) for c, (fl, ms) in per.items()},
+            **{f"prefill_c{c}_attn_ms": round(ms, 3) for c, (fl, ms) in per.items()},
+            **{f"prefill_c{c}_with_writes_ms": round(t_step[f"prefill_c{c}"], 3) for c in plans},
         },
     }
     if args.cpu_baseline:
@@ -373,36 +400,24 @@ def bench_relayout_70b(args):
     gen = torch.Generator(device="cuda")
     gen.manual_seed(w.seed)
     stream = torch.cuda.Stream()
+    sh = stream.cuda_stream
     src_bt = i32(make_tables(w, [N], w.block_size, w.pool_blocks))
     dst_bt = i32(make_tables(w, [N], w.dst_block_size, w.dst_pool_blocks, inputs.T_DST_PERM))
     srcs = [ops.PagedPool(w.pool_blocks, w.block_size, hkv, w.src_shards, d, "bf16") for _ in range(L)]
     dsts = [ops.PagedPool(w.dst_pool_blocks, w.dst_block_size, hkv, w.dst_shards, d, "bf16") for _ in range(L)]
     for p in srcs:
         fill_pool_random(p, gen)
-    timer = Timer(stream)
 
-    def step(mode):
-        with torch.cuda.stream(stream):
-            if mode: timer.start("step_" + mode)
-            for l in range(L):
-                if mode == "per_launch": timer.start("launch")
-                ops.kv_relayout(srcs[l], src_bt, dsts[l], dst_bt, N, stream=stream)
-                if mode == "per_launch": timer.stop("launch")
-            if mode: timer.stop("step_" + mode)
+    def relayout_all():
+        for l in range(L):
+            ops.kv_relayout(srcs[l], src_bt, dsts[l], dst_bt, N, stream=sh)
 
-    for _ in range(args.warmup):
-        step(None)
-    torch.cuda.synchronize()
-    for _ in range(args.steps):
-        step("back_to_back")
-    for _ in range(args.steps):
-        step("per_launch")
-    torch.cuda.synchronize()
-    step_ms = float(np.mean(timer.ms("step_back_to_back")))
-    launch_ms = float(np.mean(timer.ms("launch")))
+    pg = PhaseGraphs(stream)
+    pg.capture("relayout", relayout_all)
+    step_ms = time_replays(pg, ["relayout"], args.steps, args.warmup)["relayout"]
     per_layer = relayout_bytes(N, hkv, d)
-    gbps = per_layer * L / (step_ms * 1e-3) / 1e9
-    launch_gbps = per_layer / (launch_ms * 1e-3) / 1e9
+    launch_ms = step_ms / L
+    gbps = per_layer / (launch_ms * 1e-3) / 1e9
     result = {
         "metric": METRIC, "value": round(gbps, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(step_ms, 4), "higher_is_better": True, "scaling": "weak",
@@ -410,12 +425,13 @@ def bench_relayout_70b(args):
         "config": {"workload": "relayout-llama3-70b: 80 layers x one 4096-token request, 8 kv heads, d128; "
                                "bs16 / 4 shards x 2 heads -> bs32 / 8 shards x 1 head; 80 kv_relayout calls back to "
                                "back", "payload_bytes": per_layer // 2 * L,
+                   "timing": "the 80 calls captured once as a HIP graph and replayed; HIP events around replays",
                    "value_is": "relayout HBM GB/s = 2 x payload / time of the 80 back-to-back calls"},
-        "roofline": {"kernel": "kv_relayout", "bound": "hbm", "achieved": round(launch_gbps, 1),
-                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(launch_gbps / HBM_PEAK_GBPS, 4),
+        "roofline": {"kernel": "kv_relayout", "bound": "hbm", "achieved": round(gbps, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4),
                      "traffic": None, "bytes_per_launch": per_layer, "launch_ms": round(launch_ms, 5)},
-        "metrics": {"relayout_gbps_back_to_back": round(gbps, 1), "relayout_frac_hbm": round(gbps / HBM_PEAK_GBPS, 4),
-                    "relayout_launch_gbps": round(launch_gbps, 1), "relayout_launch_ms": round(launch_ms, 5)},
+        "metrics": {"relayout_gbps": round(gbps, 1), "relayout_frac_hbm": round(gbps / HBM_PEAK_GBPS, 4),
+                    "relayout_launch_ms": round(launch_ms, 5)},
     }
     if args.cpu_baseline:
         result["cpu_baseline"] = cpu_baseline_relayout(w)

@@ -23,6 +23,8 @@
 //         32 contiguous bytes), multiplying bf16 key pairs with v_dot2.
 // The 4 waves' (m, l, acc) are merged in LDS; with several splits the
 // partials go to the workspace and a second kernel merges them.
+#include <cstdlib>
+
 #include "pkv_internal.h"
 
 namespace pkv {
@@ -271,6 +273,271 @@ attn_decode_kernel(PoolDev pool, const T* __restrict__ q, T* __restrict__ out, c
   }
 }
 
+// ------------------------------------------------------------------------
+// bf16 kernel.  Same work decomposition (one workgroup of 4 waves per
+// (split, KV head, request)); each wave walks 32-key tiles (tile i of the
+// split to wave i % 4) and every global load instruction reads 1 KB of
+// consecutive bytes:
+//   K     a (block, head) K tile is block_size contiguous rows; one load
+//         instruction takes 64 lanes x 16 B = 1024/(2D) whole rows.  The
+//         rows go to the wave's LDS slice (rows padded by 16 B so the
+//         row-per-lane reads below hit distinct banks).
+//   q.k   lanes l and l+32 own key l%32, each half of the head dim; the
+//         wave's q rows are broadcast from LDS (two addresses per read);
+//         partial dots of the two halves meet through v_permlane32_swap.
+//   soft  per-tile max over the 32 keys with DPP row steps and one
+//         v_permlane16_swap; exp2 domain; p stored to LDS as bf16 pairs.
+//   V     the dim-major V tile gives 16 keys of one dim as 32 contiguous
+//         bytes; two lanes split those, one instruction covers 32 dims
+//         (1 KB).  p.v multiplies bf16 key pairs with v_dot2.
+// ------------------------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+// v[l] + v[l ^ 32]
+__device__ __forceinline__ float sum_halves(float v) {
+  auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+// max over the 32 lanes of each half-wave
+__device__ __forceinline__ float max_half(float v) {
+  v = fmaxf(v, dpp<0xB1>(v));     // quad_perm [1,0,3,2]
+  v = fmaxf(v, dpp<0x4E>(v));     // quad_perm [2,3,0,1]
+  v = fmaxf(v, dpp<0x141>(v));    // row_half_mirror
+  v = fmaxf(v, dpp<0x140>(v));    // row_mirror
+  auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+
+template <int D, int G>
+struct DecodeBf16Smem {
+  static constexpr int TK = 32, KROW = D + 8;
+  uint32_t q[G][D / 2];                         // bf16 pairs
+  union {
+    struct {
+      bf16_t k[kWaves][TK * KROW];              // per-wave K tile
+      uint32_t p[kWaves][G][TK / 2];            // per-wave p, bf16 pairs
+    } t;
+    struct {
+      float acc[kWaves][G][D];
+      float m[kWaves][G];
+      float l[kWaves][G];
+    } r;
+  } u;
+};
+
+template <int D, int G>
+__global__ void __launch_bounds__(kThreads)
+attn_decode_bf16_kernel(PoolDev pool, const bf16_t* __restrict__ q, bf16_t* __restrict__ out,
+                        const int32_t* __restrict__ bt, int bt_stride, const int32_t* __restrict__ ctx,
+                        int num_q_heads, float scale_log2, int split_tokens, int num_splits,
+                        float* __restrict__ part_o, float* __restrict__ part_ml) {
+  using Smem = DecodeBf16Smem<D, G>;
+  constexpr int TK = Smem::TK, KROW = Smem::KROW;
+  constexpr int LPR = D / 8;            // lanes per K row in a coalesced load
+  constexpr int KPI = 64 / LPR;         // K rows per load instruction
+  constexpr int KLOADS = TK / KPI;
+  constexpr int HALF = D / 2;
+  constexpr int DPL = D / 32;           // V dims per lane
+  __shared__ Smem sm;
+
+  const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int L = ctx[b];
+  if (L > (bt_stride << pool.bs_shift)) {
+    if (threadIdx.x == 0 && split == 0 && kvh == 0) flag_error(pool.err, PKV_ERRBIT_TABLE);
+    L = bt_stride << pool.bs_shift;
+  }
+  const int start = split * split_tokens;
+  if (start >= L) return;
+  const int end = min(L, start + split_tokens);
+  const int hl = pool.heads_per_shard;
+  const int sh = kvh / hl, lh = kvh - sh * hl;
+  const bf16_t* kpool = reinterpret_cast<const bf16_t*>(pool.k[sh]);
+  const bf16_t* vpool = reinterpret_cast<const bf16_t*>(pool.v[sh]);
+  const int bs = pool.block_size;
+  const int32_t* table = bt + (size_t)b * bt_stride;
+
+  {
+    const uint32_t* qsrc = reinterpret_cast<const uint32_t*>(q + ((size_t)b * num_q_heads + (size_t)kvh * G) * D);
+    uint32_t* qdst = &sm.q[0][0];
+    for (int i = threadIdx.x; i < G * D / 2; i += kThreads) qdst[i] = qsrc[i];
+  }
+  __syncthreads();
+
+  float m[G], lsum[G], acc[G][DPL];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    m[g] = -INFINITY;
+    lsum[g] = 0.f;
+#pragma unroll
+    for (int j = 0; j < DPL; ++j) acc[g][j] = 0.f;
+  }
+  const int kk = lane & 31, hh = lane >> 5;
+  bf16_t* ktile = sm.u.t.k[wave];
+
+  const int ntiles = (end - start + TK - 1) / TK;
+  for (int t = wave; t < ntiles; t += kWaves) {
+    const int k0 = start + t * TK;
+    // ---- K: coalesced loads -> LDS ----
+    {
+      uint4 kr[KLOADS];
+#pragma unroll
+      for (int i = 0; i < KLOADS; ++i) {
+        const int key = k0 + i * KPI + lane / LPR;
+        kr[i] = make_uint4(0, 0, 0, 0);
+        if (key < end) {
+          const int blk = table[key >> pool.bs_shift];
+          if (blk >= 0 && blk < pool.num_blocks)
+            kr[i] = load_nt16(kpool + tile_elems(pool, blk, lh) + (size_t)(key & (bs - 1)) * D + (lane % LPR) * 8);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < KLOADS; ++i)
+        *reinterpret_cast<uint4*>(&ktile[(i * KPI + lane / LPR) * KROW + (lane % LPR) * 8]) = kr[i];
+    }
+    wave_lds_sync();
+    // ---- q.k: key kk, head-dim half hh ----
+    float s[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) s[g] = 0.f;
+    {
+      // the key's half row stays in registers; q rows stream from LDS one
+      // head at a time (the empty asm keeps the compiler from hoisting the
+      // reads of every head at once, which would cost G*HALF/2 registers)
+      uint4 kv[HALF / 8];
+      const bf16_t* krow = &ktile[kk * KROW + hh * HALF];
+#pragma unroll
+      for (int c = 0; c < HALF / 8; ++c) kv[c] = *reinterpret_cast<const uint4*>(krow + c * 8);
+      int zero = 0;     // opaque 0 tied to the previous head's score (orders the q reads)
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const uint32_t* qrow = &sm.q[g][hh * HALF / 2] + zero;
+#pragma unroll
+        for (int c = 0; c < HALF / 8; ++c) {
+          const uint4 qv = *reinterpret_cast<const uint4*>(qrow + c * 4);
+          s[g] = dot2_bf16(kv[c].x, qv.x, s[g]);
+          s[g] = dot2_bf16(kv[c].y, qv.y, s[g]);
+          s[g] = dot2_bf16(kv[c].z, qv.z, s[g]);
+          s[g] = dot2_bf16(kv[c].w, qv.w, s[g]);
+        }
+        asm volatile("v_mov_b32 %0, 0" : "=v"(zero) : "v"(s[g]));
+      }
+    }
+    bool valid = k0 + kk < end;
+    if (valid) {
+      const int blk = table[(k0 + kk) >> pool.bs_shift];
+      valid = blk >= 0 && blk < pool.num_blocks;
+    }
+    // ---- online softmax over the tile's 32 keys ----
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const float sc = valid ? sum_halves(s[g]) * scale_log2 : -INFINITY;
+      const float mn = fmaxf(m[g], max_half(sc));
+      const float alpha = __builtin_amdgcn_exp2f(m[g] - mn);
+      const float p = __builtin_amdgcn_exp2f(sc - mn);
+      m[g] = mn;
+      lsum[g] = lsum[g] * alpha + (hh == 0 ? p : 0.f);
+#pragma unroll
+      for (int j = 0; j < DPL; ++j) acc[g][j] *= alpha;
+      const float pn = dpp<0xB1>(p);                    // the odd neighbour's p
+      if ((kk & 1) == 0 && hh == (g & 1)) sm.u.t.p[wave][g][kk >> 1] = pack_bf16x2(p, pn);
+    }
+    wave_lds_sync();
+    // ---- V: coalesced loads, held in registers until p.v ----
+    uint4 vr[2][DPL];
+#pragma unroll
+    for (int grp = 0; grp < 2; ++grp) {
+      const int key16 = k0 + 16 * grp;
+      const int blk = key16 < end ? table[key16 >> pool.bs_shift] : -1;
+      const bool ok = blk >= 0 && blk < pool.num_blocks;
+      if (key16 < end && !ok) flag_error(pool.err, PKV_ERRBIT_BLOCK_ID);
+      const bf16_t* vbase = ok ? vpool + tile_elems(pool, blk, lh) + (key16 & (bs - 1)) + (lane & 1) * 8 : nullptr;
+      const int nvalid = end - key16 - (lane & 1) * 8;    // valid keys among this lane's 8
+#pragma unroll
+      for (int i = 0; i < DPL; ++i) {
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (ok && nvalid > 0) {
+          v = load_nt16(vbase + (size_t)(lane / 2 + 32 * i) * bs);
+          if (nvalid < 8) {        // keys past the context hold arbitrary bits
+            uint32_t* w = reinterpret_cast<uint32_t*>(&v);
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+              if (e >= nvalid) w[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
+          }
+        }
+        vr[grp][i] = v;
+      }
+    }
+    // ---- p.v: lane holds dims lane/2 + 32i of keys 16grp + (lane&1)*8 .. +8 ----
+#pragma unroll
+    for (int grp = 0; grp < 2; ++grp) {
+      if (k0 + 16 * grp >= end) break;
+      int zero = 0;
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const uint4 pp = *reinterpret_cast<const uint4*>(&sm.u.t.p[wave][g][grp * 8 + (lane & 1) * 4] + zero);
+#pragma unroll
+        for (int i = 0; i < DPL; ++i) {
+          float a = acc[g][i];
+          a = dot2_bf16(pp.x, vr[grp][i].x, a);
+          a = dot2_bf16(pp.y, vr[grp][i].y, a);
+          a = dot2_bf16(pp.z, vr[grp][i].z, a);
+          a = dot2_bf16(pp.w, vr[grp][i].w, a);
+          acc[g][i] = a;
+        }
+        if (g % 4 == 3) asm volatile("v_mov_b32 %0, 0" : "=v"(zero) : "v"(acc[g][0]));
+      }
+    }
+    wave_lds_sync();
+  }
+
+  // ---- merge the lane pairs (two key halves), then the 4 waves ----
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+#pragma unroll
+    for (int i = 0; i < DPL; ++i) acc[g][i] += dpp<0xB1>(acc[g][i]);
+  __syncthreads();              // the tile buffers are reused for the reduction below
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const float l = wave_sum(lsum[g]);
+    if (lane == 0) {
+      sm.u.r.m[wave][g] = m[g];
+      sm.u.r.l[wave][g] = l;
+    }
+    if ((lane & 1) == 0) {
+#pragma unroll
+      for (int i = 0; i < DPL; ++i) sm.u.r.acc[wave][g][lane / 2 + 32 * i] = acc[g][i];
+    }
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < G * D; i += kThreads) {
+    const int g = i / D, d = i - g * D;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) mx = fmaxf(mx, sm.u.r.m[w][g]);
+    float l = 0.f, o = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float f = __builtin_amdgcn_exp2f(sm.u.r.m[w][g] - mx);
+      l += sm.u.r.l[w][g] * f;
+      o += sm.u.r.acc[w][g][d] * f;
+    }
+    const int h = kvh * G + g;
+    if (num_splits == 1) {
+      out[((size_t)b * num_q_heads + h) * D + d] = f32_to_bf16(o / l);
+    } else {
+      const size_t row = ((size_t)b * num_q_heads + h) * num_splits + split;
+      part_o[row * D + d] = o;
+      if (d == 0) {
+        part_ml[row * 2 + 0] = mx;
+        part_ml[row * 2 + 1] = l;
+      }
+    }
+  }
+}
+
 // Merge the split partials of each (request, q-head): rescale each split's
 // (m, l, acc) to the common max and normalise.
 template <typename T, int D>
@@ -302,9 +569,14 @@ hipError_t launch_typed(const PoolDev& pool, const void* q, void* out, const int
   float* part_o = static_cast<float*>(ws);
   float* part_ml = part_o ? part_o + (size_t)batch * num_q_heads * plan.num_splits * D : nullptr;
   const dim3 grid(plan.num_splits, num_q_heads / G, batch);
-  hipLaunchKernelGGL((attn_decode_kernel<T, D, G>), grid, dim3(kThreads), 0, s, pool, static_cast<const T*>(q),
-                     static_cast<T*>(out), bt, bt_stride, ctx, num_q_heads, scale_log2, plan.split_tokens,
-                     plan.num_splits, part_o, part_ml);
+  if constexpr (sizeof(T) == 2)
+    hipLaunchKernelGGL((attn_decode_bf16_kernel<D, G>), grid, dim3(kThreads), 0, s, pool,
+                       static_cast<const bf16_t*>(q), static_cast<bf16_t*>(out), bt, bt_stride, ctx, num_q_heads,
+                       scale_log2, plan.split_tokens, plan.num_splits, part_o, part_ml);
+  else
+    hipLaunchKernelGGL((attn_decode_kernel<T, D, G>), grid, dim3(kThreads), 0, s, pool, static_cast<const T*>(q),
+                       static_cast<T*>(out), bt, bt_stride, ctx, num_q_heads, scale_log2, plan.split_tokens,
+                       plan.num_splits, part_o, part_ml);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || plan.num_splits == 1) return e;
   hipLaunchKernelGGL((attn_decode_merge_kernel<T, D>), dim3(num_q_heads, batch), dim3(D), 0, s, part_o, part_ml,
@@ -335,13 +607,20 @@ DecodePlan plan_decode(int batch, int num_q_heads, int num_kv_heads, int max_con
   // Aim for at least ~4 workgroups per CU across the chip (256 CUs) while
   // keeping each split at >= 256 keys so the per-split fixed cost stays small.
   const long pairs = (long)batch * num_kv_heads;
-  int split = 64;
-  while (split < 4096) {
+  int split = 128;                     // one 32-key tile per wave per pass
+  while (split < 8192) {
     const long wgs = pairs * ((max_context_len + split - 1) / split);
     if (wgs <= 2048 && split >= 256) break;
     if (wgs <= 1024) break;
     split *= 2;
   }
+  // tuning override (keys per split, a multiple of 128)
+  static const int forced = [] {
+    const char* e = getenv("PKV_DECODE_SPLIT_TOKENS");
+    const int v = e ? atoi(e) : 0;
+    return (v >= 128 && v % 128 == 0) ? v : 0;
+  }();
+  if (forced) split = forced;
   DecodePlan p;
   p.split_tokens = split;
   p.num_splits = (max_context_len + split - 1) / split;

@@ -92,55 +92,97 @@ kv_write_kernel(PoolDev pool, const T* __restrict__ k, const T* __restrict__ v,
 }
 
 // ------------------------------------------------------------- relayout ----
-// One workgroup per (destination block j of the request, head, K or V).
-// The destination (block, head) tile is one contiguous run of
-// block_size * head_dim elements; each thread fills 16-byte vectors of it,
-// reading the matching 16 bytes of the source tile.  Block sizes are powers
-// of two >= 16, so a 16-byte run of keys of one dim (V) never straddles a
-// source block.  Tokens at or past n_tokens are not written.
+// One workgroup per (destination block j of the request, head).  The
+// destination (block, head) K tile and V tile are each one contiguous run
+// of block_size * head_dim elements; every thread fills 16-byte vectors of
+// both from the matching 16 bytes of the source tiles.  The source block ids
+// of the tokens in this destination block are read from the table once, into
+// LDS; the shard base pointers are uniform per workgroup; each thread issues
+// all its loads (K and V) before its non-temporal stores.  Block sizes are
+// powers of two >= 16, so a 16-byte run of keys of one dim (V) never
+// straddles a source block.  Tokens at or past n_tokens are not written.
+constexpr int kRelayoutVpt = 2;    // vectors per thread per tile and round
+
 template <typename T>
 __global__ void __launch_bounds__(kThreads)
 kv_relayout_kernel(PoolDev src, const int32_t* __restrict__ src_bt, PoolDev dst,
                    const int32_t* __restrict__ dst_bt, int n_tokens) {
   constexpr int VEC = 16 / sizeof(T);
-  const int j = blockIdx.x;               // destination block index within the request
+  __shared__ int sblk[128 / 16];           // source blocks covering one destination block
+  const int j = blockIdx.x;                // destination block index within the request
   const int h = blockIdx.y;
-  const bool is_v = blockIdx.z != 0;
   const int D = dst.head_dim;
   const int bsd = dst.block_size, bss = src.block_size;
   const int p0 = j * bsd;
-  const int valid = min(bsd, n_tokens - p0);    // tokens of this block that exist
+  const int valid = min(bsd, n_tokens - p0);     // tokens of this block that exist
   const int dblk = dst_bt[j];
   if (dblk < 0 || dblk >= dst.num_blocks) {
     if (threadIdx.x == 0) flag_error(dst.err, PKV_ERRBIT_BLOCK_ID);
     return;
   }
+  const int first = p0 >> src.bs_shift;
+  const int nsrc = ((p0 + valid - 1) >> src.bs_shift) - first + 1;
+  if ((int)threadIdx.x < nsrc) {
+    int b = src_bt[first + threadIdx.x];
+    if (b < 0 || b >= src.num_blocks) {
+      flag_error(src.err, PKV_ERRBIT_BLOCK_ID);
+      b = -1;
+    }
+    sblk[threadIdx.x] = b;
+  }
+  __syncthreads();
   const int dsh = h / dst.heads_per_shard, dlh = h - dsh * dst.heads_per_shard;
   const int ssh = h / src.heads_per_shard, slh = h - ssh * src.heads_per_shard;
-  T* dtile = reinterpret_cast<T*>(is_v ? dst.v[dsh] : dst.k[dsh]) + tile_elems(dst, dblk, dlh);
-  const T* sbase = reinterpret_cast<const T*>(is_v ? src.v[ssh] : src.k[ssh]);
-  const int nvec = bsd * D / VEC;
-  for (int e = threadIdx.x; e < nvec; e += kThreads) {
-    int o, d;                             // token offset in the block, first dim
-    if (!is_v) { o = (e * VEC) / D; d = (e * VEC) % D; }
-    else       { d = (e * VEC) / bsd; o = (e * VEC) % bsd; }
-    if (o >= valid) continue;
-    const int p = p0 + o;
-    const int sblk = src_bt[p >> src.bs_shift];
-    if (sblk < 0 || sblk >= src.num_blocks) {
-      flag_error(src.err, PKV_ERRBIT_BLOCK_ID);
-      continue;
+  const T* sk = reinterpret_cast<const T*>(src.k[ssh]);
+  const T* sv = reinterpret_cast<const T*>(src.v[ssh]);
+  T* dk = reinterpret_cast<T*>(dst.k[dsh]) + tile_elems(dst, dblk, dlh);
+  T* dv = reinterpret_cast<T*>(dst.v[dsh]) + tile_elems(dst, dblk, dlh);
+  const int off0 = p0 & (bss - 1);               // p0's offset in its source block (bss > bsd only)
+  const int vpr_shift = __builtin_ctz(D / VEC);  // K: vectors per row
+  const int vpk_shift = __builtin_ctz(bsd / VEC);// V: vectors per dim row
+  const int nv = (bsd * D) / VEC;                // vectors per tile
+  const size_t stile = (size_t)bss * D;
+  for (int base = threadIdx.x; base < nv; base += kThreads * kRelayoutVpt) {
+    uint4 kv[kRelayoutVpt], vv[kRelayoutVpt];
+    bool kok[kRelayoutVpt], vok[kRelayoutVpt];
+    int kdo[kRelayoutVpt], vdo[kRelayoutVpt];
+#pragma unroll
+    for (int u = 0; u < kRelayoutVpt; ++u) {
+      const int e = base + u * kThreads;
+      // K vector e: token o, dims d..d+VEC
+      {
+        const int o = e >> vpr_shift, d = (e & ((1 << vpr_shift) - 1)) * VEC;
+        const int r = off0 + o;
+        const int b = (e < nv && o < valid) ? sblk[r >> src.bs_shift] : -1;
+        kok[u] = b >= 0;
+        kdo[u] = o * D + d;
+        kv[u] = kok[u] ? load_nt16(sk + ((size_t)b * src.heads_per_shard + slh) * stile +
+                                   (size_t)(r & (bss - 1)) * D + d)
+                       : make_uint4(0, 0, 0, 0);
+      }
+      // V vector e: dim d, tokens o..o+VEC
+      {
+        const int d = e >> vpk_shift, o = (e & ((1 << vpk_shift) - 1)) * VEC;
+        const int r = off0 + o;
+        const int b = (e < nv && o + VEC <= valid) ? sblk[r >> src.bs_shift] : -1;
+        vok[u] = b >= 0;
+        vdo[u] = d * bsd + o;
+        vv[u] = vok[u] ? load_nt16(sv + ((size_t)b * src.heads_per_shard + slh) * stile + (size_t)d * bss +
+                                   (r & (bss - 1)))
+                       : make_uint4(0, 0, 0, 0);
+        if (!vok[u] && e < nv && o < valid) {        // ragged tail of the request: element copies
+          const int sb = sblk[r >> src.bs_shift];
+          if (sb >= 0) {
+            const T* sp = sv + ((size_t)sb * src.heads_per_shard + slh) * stile + (size_t)d * bss + (r & (bss - 1));
+            for (int t = 0; t < valid - o; ++t) dv[d * bsd + o + t] = sp[t];
+          }
+        }
+      }
     }
-    const int so = p & (bss - 1);
-    const T* stile = sbase + tile_elems(src, sblk, slh);
-    if (!is_v) {
-      *reinterpret_cast<uint4*>(dtile + (size_t)o * D + d) =
-          *reinterpret_cast<const uint4*>(stile + (size_t)so * D + d);
-    } else if (o + VEC <= valid) {
-      *reinterpret_cast<uint4*>(dtile + (size_t)d * bsd + o) =
-          *reinterpret_cast<const uint4*>(stile + (size_t)d * bss + so);
-    } else {
-      for (int t = 0; t < valid - o; ++t) dtile[(size_t)d * bsd + o + t] = stile[(size_t)d * bss + so + t];
+#pragma unroll
+    for (int u = 0; u < kRelayoutVpt; ++u) {
+      if (kok[u]) store_nt16(dk + kdo[u], kv[u]);
+      if (vok[u]) store_nt16(dv + vdo[u], vv[u]);
     }
   }
 }
@@ -175,7 +217,7 @@ hipError_t launch_kv_write(const PoolDev& pool, int dtype, const void* k, const 
 hipError_t launch_kv_relayout(const PoolDev& src, const int32_t* src_bt, const PoolDev& dst, const int32_t* dst_bt,
                               int dtype, int n_tokens, hipStream_t s) {
   if (n_tokens == 0) return hipSuccess;
-  const dim3 grid((n_tokens + dst.block_size - 1) / dst.block_size, dst.num_kv_heads, 2);
+  const dim3 grid((n_tokens + dst.block_size - 1) / dst.block_size, dst.num_kv_heads);
   if (dtype == PKV_BF16)
     hipLaunchKernelGGL(kv_relayout_kernel<bf16_t>, grid, dim3(kThreads), 0, s, src, src_bt, dst, dst_bt, n_tokens);
   else

@@ -94,10 +94,23 @@ void build_masks(int total, int decode_cus, std::array<uint32_t, kMaskWords>& pm
   (void)per_xcd;
 }
 
+// A queue whose mask leaves some XCD without a CU can never run the share of
+// its workgroups dispatched there; every mask used must keep >= 1 CU per XCD.
+bool every_xcd_has_a_cu(const std::array<uint32_t, kMaskWords>& m, int total) {
+  int per[kXcds] = {0};
+  for (int i = 0; i < total; ++i)
+    if ((m[i / 32] >> (i % 32)) & 1u) per[i % kXcds]++;
+  for (int x = 0; x < kXcds; ++x)
+    if (per[x] == 0) return false;
+  return true;
+}
+
 int ensure_streams(pkv_mux* m, int level) {
   const auto& g = m->groups[level];
   if (g.first == 0 || g.second == 0) return PKV_OK;      // whole-device groups use the ordinary stream
   if (m->pstream[level] && m->dstream[level]) return PKV_OK;
+  if (!every_xcd_has_a_cu(m->pmask[level], m->total_cus) || !every_xcd_has_a_cu(m->dmask[level], m->total_cus))
+    return fail(PKV_EINVAL, "CU masks of level %d leave an XCD without a CU", level);
   hipError_t e = hipExtStreamCreateWithCUMask(&m->pstream[level], kMaskWords, m->pmask[level].data());
   if (e != hipSuccess) return hip_fail(e, "hipExtStreamCreateWithCUMask(prefill)");
   e = hipExtStreamCreateWithCUMask(&m->dstream[level], kMaskWords, m->dmask[level].data());

@@ -38,6 +38,19 @@ __device__ __forceinline__ bf16_t f32_to_bf16(float x) {
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
 }
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(1))) u32x4_t global_u32x4_t;
+// 16-byte non-temporal store (the data is not read back soon).  The cast to
+// the global address space keeps it a global_store rather than a flat one.
+__device__ __forceinline__ void store_nt16(void* p, const uint4& v) {
+  u32x4_t w = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(w, (global_u32x4_t*)p);
+}
+// 16-byte non-temporal load: streamed data that this kernel reads once.
+__device__ __forceinline__ uint4 load_nt16(const void* p) {
+  const u32x4_t w = __builtin_nontemporal_load((const global_u32x4_t*)p);
+  return make_uint4(w.x, w.y, w.z, w.w);
+}
 __device__ __forceinline__ void flag_error(int32_t* err, int bit) {
   if (err) atomicOr(err, bit);
 }

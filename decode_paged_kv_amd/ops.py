@@ -56,6 +56,10 @@ class PagedPool:
                                           for _ in range(num_shards)]
         self.err_word = err_word
 
+    def set_err_word(self, err_word) -> None:
+        self.err_word = err_word
+        self._c = None
+
     def fill_bits(self, pattern: int) -> "PagedPool":
         """Fill every element with one raw bit pattern (16-bit for bf16, 32-bit for f32)."""
         for t in self.k + self.v:
@@ -63,6 +67,12 @@ class PagedPool:
         return self
 
     def c(self) -> PoolLayer:
+        """The C descriptor (built once; the pool's tensors never change)."""
+        if getattr(self, "_c", None) is None:
+            self._c = self._build_c()
+        return self._c
+
+    def _build_c(self) -> PoolLayer:
         s = PoolLayer()
         for i in range(self.num_shards):
             s.k[i] = self.k[i].data_ptr()
@@ -88,15 +98,14 @@ def slot_mapping(block_tables, start_loc, pos_start, num_tokens, block_size, num
 
 def kv_write(pool: PagedPool, k, v, slots, stream=None):
     lib = _lib.load()
-    c = pool.c()
-    _lib.check(lib.kv_write(C.byref(c), _ptr(k), _ptr(v), _ptr(slots), slots.numel(), _stream(stream)), "kv_write")
+    _lib.check(lib.kv_write(C.byref(pool.c()), _ptr(k), _ptr(v), _ptr(slots), slots.numel(), _stream(stream)),
+               "kv_write")
 
 
 def kv_relayout(src: PagedPool, src_bt, dst: PagedPool, dst_bt, n_tokens: int, stream=None):
     lib = _lib.load()
-    cs, cd = src.c(), dst.c()
-    _lib.check(lib.kv_relayout(C.byref(cs), _ptr(src_bt), C.byref(cd), _ptr(dst_bt), n_tokens, _stream(stream)),
-               "kv_relayout")
+    _lib.check(lib.kv_relayout(C.byref(src.c()), _ptr(src_bt), C.byref(dst.c()), _ptr(dst_bt), n_tokens,
+                               _stream(stream)), "kv_relayout")
 
 
 def attn_prefill_chunk(pool: PagedPool, q, out, block_tables, start_loc, chunk_start, max_chunk_len: int,
