@@ -461,8 +461,173 @@ def cpu_baseline_relayout(w):
                                          f"times in {dt:.1f} s; 2 x payload / wall time"}
 
 
+# ------------------------------------------------------------- pdmux ----
+def bench_pdmux(args):
+    """PD multiplexing on one GPU, Llama-3-8B attention shape, 32 layers, bf16, block size 16.
+
+    Decode batch 128 at context 2048 (slot of the new token rewritten each
+    step, so every step does the same work).  Arms:
+      A  solo decode: rounds with no prefill (whole device);
+      B  multiplexed: rounds of decode on the CU-masked decode stream while a
+         prompt (32768 tokens, 2 layers per round, and a 16384-token variant,
+         4 layers per round) is prefilled layer by layer on the complementary
+         CUs; the level comes from the batch-size rule (128 : 128 CUs), and a
+         sweep fixes each level 1..6 for the 16K prompt;
+      C  chunked prefill on the whole device: each step runs the decode step
+         and then one chunk (2048 or 512 tokens) through all layers, on one
+         stream;
+      D  prefill alone on the whole device (one stream).
+    A decode step's time is the host wall time of one round, which blocks on
+    the decode stream (the inter-token interval a serving loop would see).
+    """
+    w = workloads.PDMUX_8B
+    L, hq, hkv, d, bs = w.layers, w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size
+    B, ctx = w.decode_batch, w.decode_context[0]
+    prompts = {"32k": w.prompt_len, "16k": w.extra["prompt_variant"]}
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(w.seed)
+    tables = make_tables(w, [ctx] * B + [w.prompt_len], bs, w.pool_blocks)
+    dec_bt, pr_bt = i32(tables[:B]), i32(tables[B:B + 1])
+    pools = [ops.PagedPool(w.pool_blocks, bs, hkv, 1, d, "bf16") for _ in range(L)]
+    for p in pools:
+        fill_pool_random(p, gen)
+    q_dec = [rand_bf16((B, hq, d), gen) for _ in range(L)]
+    kn = [rand_bf16((B, hkv, d), gen) for _ in range(L)]
+    vn = [rand_bf16((B, hkv, d), gen) for _ in range(L)]
+    o_dec = [torch.empty((B, hq, d), dtype=torch.bfloat16, device="cuda") for _ in range(L)]
+    Nmax = w.prompt_len
+    q_pr = [rand_bf16((Nmax, hq, d), gen) for _ in range(L)]
+    k_pr = [rand_bf16((Nmax, hkv, d), gen) for _ in range(L)]
+    v_pr = [rand_bf16((Nmax, hkv, d), gen) for _ in range(L)]
+    o_pr = [torch.empty((Nmax, hq, d), dtype=torch.bfloat16, device="cuda") for _ in range(L)]
+    ctx_t = i32([ctx] * B)
+    ws = torch.zeros(max(16, ops.attn_decode_workspace_size(B, hq, ctx, d)), dtype=torch.uint8, device="cuda")
+    dec_slots = ops.slot_mapping(dec_bt, i32(np.arange(B + 1)), i32([ctx - 1] * B), B, bs, w.pool_blocks)
+    decode = ops.DecodeStepArgs(pools, q_dec, kn, vn, o_dec, dec_slots, dec_bt, ctx_t, ctx, hq, ws)
+    pr_slots = {k: ops.slot_mapping(pr_bt, i32([0, n]), i32([0]), n, bs, w.pool_blocks) for k, n in prompts.items()}
+    torch.cuda.synchronize()
+    mux = ops.Mux(0, w.extra["cu_granularity"], w.extra["min_decode_cus"], w.extra["group_num"],
+                  w.extra["decode_bs_divisor"], w.extra["token_budget"])
+    groups = mux.groups()
+
+    def job(key):
+        n = prompts[key]
+        return ops.PrefillJobArgs(pools, [t[:n] for t in q_pr], [t[:n] for t in k_pr], [t[:n] for t in v_pr],
+                                  [t[:n] for t in o_pr], pr_slots[key], pr_bt, i32([0, n]), i32([0]), n, hq)
+
+    def solo(rounds):
+        ts = []
+        for _ in range(rounds):
+            t0 = time.perf_counter()
+            mux.run_round(decode, None)
+            ts.append((time.perf_counter() - t0) * 1e3)
+        return ts
+
+    def muxed(key, level=-1):
+        mux.set_level_override(level)
+        j = job(key)
+        ts, levels = [], []
+        t_start = time.perf_counter()
+        done = False
+        while not done:
+            t0 = time.perf_counter()
+            lvl, done = mux.run_round(decode, j)
+            ts.append((time.perf_counter() - t0) * 1e3)
+            levels.append(lvl)
+            if len(ts) > 5000:
+                raise RuntimeError("prefill did not finish")
+        mux.wait_prefill()
+        t_pf = (time.perf_counter() - t_start) * 1e3
+        mux.run_round(decode, None)           # the level returns to decode-only
+        mux.set_level_override(-1)
+        return ts, t_pf, sorted(set(levels))
+
+    stream = torch.cuda.Stream()
+    sh = stream.cuda_stream
+
+    def chunked(key, c):
+        n = prompts[key]
+        chunks = [(s0, min(c, n - s0)) for s0 in range(0, n, c)]
+        args_ = [(i32([0, t]), i32([s0]), ops.slot_mapping(pr_bt, i32([0, t]), i32([s0]), t, bs, w.pool_blocks))
+                 for s0, t in chunks]
+        torch.cuda.synchronize()
+        ts = []
+        t_start = time.perf_counter()
+        for (s0, t), (sl, cs, slots) in zip(chunks, args_):
+            t0 = time.perf_counter()
+            for l in range(L):
+                ops.kv_write(pools[l], kn[l], vn[l], dec_slots, stream=sh)
+                ops.attn_decode(pools[l], q_dec[l], o_dec[l], dec_bt, ctx_t, ctx, hq, workspace=ws, stream=sh)
+            for l in range(L):
+                ops.kv_write(pools[l], k_pr[l][s0:s0 + t], v_pr[l][s0:s0 + t], slots, stream=sh)
+                ops.attn_prefill_chunk(pools[l], q_pr[l][s0:s0 + t], o_pr[l][s0:s0 + t], pr_bt, sl, cs, t, hq,
+                                       stream=sh)
+            stream.synchronize()
+            ts.append((time.perf_counter() - t0) * 1e3)
+        return ts, (time.perf_counter() - t_start) * 1e3
+
+    def prefill_alone(key):
+        n = prompts[key]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for l in range(L):
+            ops.kv_write(pools[l], k_pr[l][:n], v_pr[l][:n], pr_slots[key], stream=sh)
+            ops.attn_prefill_chunk(pools[l], q_pr[l][:n], o_pr[l][:n], pr_bt, i32([0, n]), i32([0]), n, hq, stream=sh)
+        stream.synchronize()
+        return (time.perf_counter() - t0) * 1e3
+
+    def stats(ts):
+        a = np.array(ts)
+        return {"median_ms": round(float(np.median(a)), 3), "p99_ms": round(float(np.percentile(a, 99)), 3),
+                "max_ms": round(float(a.max()), 3), "n": int(a.size)}
+
+    solo(max(2, args.warmup))                    # warm-up (also creates the level's streams)
+    prefill_alone("16k")
+    A = solo(max(10, args.steps))
+    B16, pf16, lv16 = muxed("16k")
+    B32, pf32, lv32 = muxed("32k")
+    sweep = {}
+    for lvl in range(1, len(groups) - 1):
+        ts, pf, _ = muxed("16k", lvl)
+        sweep[f"{groups[lvl][0]}:{groups[lvl][1]}"] = {"decode_median_ms": round(float(np.median(ts)), 3),
+                                                        "prefill_ms": round(pf, 2)}
+    C = {}
+    for key in ("16k", "32k"):
+        for c in w.chunk_sizes:
+            ts, tot = chunked(key, c)
+            C[f"{key}_c{c}"] = {**stats(ts), "prefill_ms": round(tot, 2)}
+    D = {key: round(prefill_alone(key), 2) for key in prompts}
+    mux.close()
+    solo_med = float(np.median(A))
+    mux_med = float(np.median(B16))
+    result = {
+        "metric": METRIC, "value": round(mux_med, 3), "unit": "ms", "n_gpus": 1, "steps": len(B16),
+        "warmup": args.warmup, "ms_per_step": round(mux_med, 3), "higher_is_better": False, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "pdmux-llama3-8b: 32 layers, 32/8 heads, d128, bs16; decode 128 x 2048 on a CU-masked "
+                               "stream while a 16384-token prompt is prefilled layer-wise on the complementary CUs",
+                   "groups": [f"{p}:{q}" for p, q in groups], "level_16k": [f"{groups[x][0]}:{groups[x][1]}" for x in lv16],
+                   "level_32k": [f"{groups[x][0]}:{groups[x][1]}" for x in lv32],
+                   "value_is": "median decode step (32 layers: kv_write + attn_decode) wall time per round while the "
+                               "16K prefill runs"},
+        "metrics": {
+            "solo_decode": stats(A),
+            "mux_16k_decode": stats(B16), "mux_16k_prefill_ms": round(pf16, 2),
+            "mux_32k_decode": stats(B32), "mux_32k_prefill_ms": round(pf32, 2),
+            "mux_over_solo_16k": round(mux_med / solo_med, 3),
+            "mux_over_solo_32k": round(float(np.median(B32)) / solo_med, 3),
+            "level_sweep_16k": sweep,
+            "chunked_whole_gpu": C,
+            "prefill_alone_ms": D,
+            "decode_bytes_per_step": decode_bytes([ctx] * B, hkv, d, hq) * L,
+        },
+    }
+    return result
+
+
 # --------------------------------------------------------------- main ----
-BENCHES = {"llama3-8b": bench_llama3_8b, "qwen3-32b": bench_qwen3_32b, "relayout-70b": bench_relayout_70b}
+BENCHES = {"llama3-8b": bench_llama3_8b, "qwen3-32b": bench_qwen3_32b, "relayout-70b": bench_relayout_70b,
+           "pdmux": bench_pdmux}
 
 
 def main():

@@ -91,11 +91,15 @@ _SIGS = {
     "attn_prefill_chunk": (C.c_int, [C.POINTER(PoolLayer), _P, _P, _P, _I, _P, _P, _I, _I, _I, C.c_float, _P]),
     "pkv_attn_decode_workspace_size": (C.c_size_t, [_I, _I, _I, _I]),
     "attn_decode": (C.c_int, [C.POINTER(PoolLayer), _P, _P, _P, _I, _P, _I, _I, _I, C.c_float, _P, C.c_size_t, _P]),
+    "pkv_mux_policy_groups_grid": (C.c_int, [C.c_int] * 5 + [C.POINTER(_I), C.POINTER(_I), _I, C.POINTER(_I)]),
+    "pkv_mux_policy_choose": (C.c_int, [C.c_int] * 4),
+    "pkv_mux_policy_layers_per_round": (C.c_int, [C.c_int] * 3),
     "pkv_mux_create": (C.c_int, [C.c_int, C.c_int, C.c_int, C.c_int, C.c_int, C.c_int, C.POINTER(_P)]),
     "pkv_mux_destroy": (None, [_P]),
     "pkv_mux_groups": (C.c_int, [_P, C.POINTER(_I), C.POINTER(_I), _I, C.POINTER(_I)]),
     "pkv_mux_choose": (C.c_int, [_P, C.c_int, C.c_int]),
     "pkv_mux_layers_per_round": (C.c_int, [_P, C.c_int, C.c_int]),
+    "pkv_mux_set_level_override": (C.c_int, [_P, C.c_int]),
     "pkv_mux_stream": (_P, [_P, C.c_int, C.c_int]),
     "pkv_mux_cu_mask": (C.c_int, [_P, C.c_int, C.c_int, C.POINTER(C.c_uint32), _I, C.POINTER(_I)]),
     "run_mux_round": (C.c_int, [_P, C.POINTER(DecodeStep), C.POINTER(PrefillJob), C.POINTER(_I), C.POINTER(_I)]),

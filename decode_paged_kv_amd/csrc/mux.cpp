@@ -43,6 +43,7 @@ struct pkv_mux {
   hipStream_t whole = nullptr;                             // ordinary stream: the whole device
   hipEvent_t prefill_done = nullptr;
   int level = -1;
+  int override_level = -1;       // fixed level while a prefill runs (-1: the batch-size rule)
   bool level_with_prefill = false;
   bool done_pending = false;     // event recorded, completion not yet seen
   bool prefill_finished = false; // completion seen; the level changes next round
@@ -55,9 +56,9 @@ namespace {
 // `granularity` to total - granularity, prefill at least half and decode at
 // least min_decode; keep `levels` of them evenly spaced from the smallest,
 // listed largest prefill first.
-std::vector<std::pair<int, int>> split_levels(int total, int granularity, int min_decode, int levels) {
+std::vector<std::pair<int, int>> split_levels(int total, int min_part, int granularity, int min_decode, int levels) {
   std::vector<int> cand;
-  for (int x = granularity; x <= total - granularity; x += granularity)
+  for (int x = min_part; x <= total - min_part; x += granularity)
     if (2 * x >= total && total - x >= min_decode) cand.push_back(x);
   if ((int)cand.size() >= levels) {
     const int stride = std::max<int>(1, (int)cand.size() / levels);
@@ -183,6 +184,32 @@ float scale_or_default(float s, int d) { return s > 0.f ? s : 1.0f / std::sqrt((
 
 extern "C" {
 
+int pkv_mux_policy_groups_grid(int total_units, int min_part, int granularity, int min_decode, int group_num,
+                               int32_t* prefill_units, int32_t* decode_units, int32_t cap, int32_t* n) {
+  if (!n || total_units <= 0 || min_part <= 0 || granularity <= 0 || min_decode < 0 || group_num < 3)
+    return fail(PKV_EINVAL, "pkv_mux_policy_groups_grid: bad argument");
+  std::vector<std::pair<int, int>> g{{total_units, 0}};
+  for (auto& x : split_levels(total_units, min_part, granularity, min_decode, group_num - 2)) g.push_back(x);
+  g.emplace_back(0, total_units);
+  *n = (int32_t)g.size();
+  for (int i = 0; i < *n && i < cap; ++i) {
+    if (prefill_units) prefill_units[i] = g[i].first;
+    if (decode_units) decode_units[i] = g[i].second;
+  }
+  return PKV_OK;
+}
+
+int pkv_mux_policy_choose(int num_groups, int decode_bs, int has_prefill, int decode_bs_divisor) {
+  if (num_groups < 3 || decode_bs < 0 || decode_bs_divisor <= 0) return fail(PKV_EINVAL, "pkv_mux_policy_choose");
+  return choose(num_groups, decode_bs, has_prefill != 0, decode_bs_divisor);
+}
+
+int pkv_mux_policy_layers_per_round(int prefill_tokens, int num_layers, int token_budget) {
+  if (prefill_tokens <= 0 || num_layers <= 0 || token_budget <= 0)
+    return fail(PKV_EINVAL, "pkv_mux_policy_layers_per_round");
+  return std::min(num_layers, std::max(1, token_budget / prefill_tokens));
+}
+
 int pkv_mux_create(int device, int cu_granularity, int min_decode_cus, int sm_group_num, int decode_bs_divisor,
                    int token_budget, pkv_mux** out) {
   if (!out) return fail(PKV_EINVAL, "pkv_mux_create: out is NULL");
@@ -207,7 +234,8 @@ int pkv_mux_create(int device, int cu_granularity, int min_decode_cus, int sm_gr
   m->divisor = decode_bs_divisor;
   m->budget = token_budget;
   m->groups.emplace_back(cus, 0);
-  for (auto& g : split_levels(cus, cu_granularity, min_decode_cus, sm_group_num - 2)) m->groups.push_back(g);
+  for (auto& g : split_levels(cus, cu_granularity, cu_granularity, min_decode_cus, sm_group_num - 2))
+    m->groups.push_back(g);
   m->groups.emplace_back(0, cus);
   const size_t n = m->groups.size();
   m->pmask.resize(n);
@@ -251,6 +279,14 @@ int pkv_mux_choose(const pkv_mux* m, int decode_bs, int has_prefill) {
   return choose((int)m->groups.size(), decode_bs, has_prefill != 0, m->divisor);
 }
 
+int pkv_mux_set_level_override(pkv_mux* m, int level) {
+  if (!m) return fail(PKV_EINVAL, "pkv_mux_set_level_override: NULL mux");
+  if (level != -1 && (level < 1 || level > (int)m->groups.size() - 2))
+    return fail(PKV_EINVAL, "pkv_mux_set_level_override: level %d outside 1..%d", level, (int)m->groups.size() - 2);
+  m->override_level = level;
+  return PKV_OK;
+}
+
 int pkv_mux_layers_per_round(const pkv_mux* m, int prefill_tokens, int num_layers) {
   if (!m || prefill_tokens <= 0 || num_layers <= 0) return fail(PKV_EINVAL, "pkv_mux_layers_per_round: bad argument");
   return std::min(num_layers, std::max(1, m->budget / prefill_tokens));
@@ -289,13 +325,18 @@ int run_mux_round(pkv_mux* m, const pkv_decode_step* d, pkv_prefill_job* p, int3
   hipError_t e = hipSetDevice(m->device);
   if (e != hipSuccess) return hip_fail(e, "hipSetDevice");
 
-  // ---- level: changes only when a prefill starts or has finished ----
+  // ---- level: while a prefill is in flight it changes only when the prefill
+  // starts or has finished; with no prefill it follows the decode batch ----
   bool rechoose = m->level < 0;
   if (starting && !m->level_with_prefill) rechoose = true;
   if (m->prefill_finished && !want_prefill) rechoose = true;
+  if (!want_prefill && !m->level_with_prefill) rechoose = true;
   if (rechoose) {
-    if (int rc = sync_level(m, m->level)) return rc;
-    m->level = choose(ng, decode_bs, want_prefill, m->divisor);
+    int next = choose(ng, decode_bs, want_prefill, m->divisor);
+    if (want_prefill && decode_bs > 0 && m->override_level > 0) next = m->override_level;
+    if (next != m->level)
+      if (int rc = sync_level(m, m->level)) return rc;    // both streams of the old level drain first
+    m->level = next;
     m->level_with_prefill = want_prefill;
     m->prefill_finished = false;
   }

@@ -219,6 +219,9 @@ class Mux:
     def layers_per_round(self, prefill_tokens: int, num_layers: int) -> int:
         return int(_lib.load().pkv_mux_layers_per_round(self._h, prefill_tokens, num_layers))
 
+    def set_level_override(self, level: int) -> None:
+        _lib.check(_lib.load().pkv_mux_set_level_override(self._h, level), "pkv_mux_set_level_override")
+
     def stream(self, level: int, which: int) -> int:
         return int(_lib.load().pkv_mux_stream(self._h, level, which) or 0)
 

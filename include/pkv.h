@@ -201,6 +201,18 @@ int attn_decode(const pkv_pool_layer* pool, const void* q, void* out, const int3
  * ------------------------------------------------------------------------- */
 typedef struct pkv_mux pkv_mux;
 
+/* The policy alone, as pure host functions (no device, no streams): the
+ * split levels of `total_units` units on a grid of `granularity` (also the
+ * minimum part), decode keeping at least `min_decode` units; then the group
+ * index for a decode batch, and the layers per round of a prompt.  The
+ * pages' SM tables follow from the same rule with (total, minimum part,
+ * granularity) = (132, 8, 8), (108, 4, 2), (78, 8, 8) and min_decode 16;
+ * pkv_mux_policy_groups_grid takes the minimum part separately for them. */
+int pkv_mux_policy_groups_grid(int total_units, int min_part, int granularity, int min_decode, int group_num,
+                               int32_t* prefill_units, int32_t* decode_units, int32_t cap, int32_t* n);
+int pkv_mux_policy_choose(int num_groups, int decode_bs, int has_prefill, int decode_bs_divisor);
+int pkv_mux_policy_layers_per_round(int prefill_tokens, int num_layers, int token_budget);
+
 /* Builds the CU-masked stream pairs of every level on `device`.  The total
  * CU count is the device's; cu_granularity must divide it. */
 int pkv_mux_create(int device, int cu_granularity, int min_decode_cus, int sm_group_num,
@@ -212,6 +224,11 @@ int pkv_mux_groups(const pkv_mux* mux, int32_t* prefill_cus, int32_t* decode_cus
 int pkv_mux_choose(const pkv_mux* mux, int decode_bs, int has_prefill);
 /* Layers per round for a prompt of prefill_tokens tokens. */
 int pkv_mux_layers_per_round(const pkv_mux* mux, int prefill_tokens, int num_layers);
+/* Fixes the level used while a prefill runs (1 .. group count - 2), in
+ * place of the batch-size rule; -1 restores the rule.  The analogue of
+ * spelling out the level per decode load by hand ([MUX] "SGLang's PD
+ * multiplexing", manual divisions), used for level sweeps. */
+int pkv_mux_set_level_override(pkv_mux* mux, int level);
 /* Stream of a group: which = 0 prefill, 1 decode (a hipStream_t). */
 void* pkv_mux_stream(const pkv_mux* mux, int level, int which);
 /* The 32-bit words of a group's CU mask (which = 0 prefill, 1 decode). */

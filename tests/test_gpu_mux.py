@@ -1,0 +1,162 @@
+"""GPU tests of the single-GPU PD-multiplexing runtime.
+
+* The split levels and the CU masks the library builds: complementary,
+  the right sizes, and balanced over the 8 XCDs (mask bit i selects a CU of
+  XCD i % 8).
+* A multi-round run: decode steps of a small batch on the decode stream of
+  the chosen level while a prompt is prefilled layer by layer on the prefill
+  stream ("PD multiplexing" page, "SGLang's PD multiplexing": the main
+  loop).  Every decode and prefill output is checked against the oracle,
+  and the level changes only when the prefill starts and after it finishes.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from decode_paged_kv_amd import inputs, ops
+from gpu_common import assert_close, from_dev, i32, to_dev
+from oracle import attention as oa
+from oracle import policy
+
+pytestmark = pytest.mark.gpu
+
+
+def _popcount(words):
+    return sum(bin(w).count("1") for w in words)
+
+
+def _bits(words):
+    return [i for i in range(len(words) * 32) if (words[i // 32] >> (i % 32)) & 1]
+
+
+def test_levels_and_cu_masks():
+    mux = ops.Mux(0, cu_granularity=8, min_decode_cus=32, sm_group_num=8, decode_bs_divisor=36, token_budget=65536)
+    try:
+        groups = mux.groups()
+        assert groups == policy.mi355x_stream_groups()
+        assert mux.choose(128, True) == policy.choose_level(len(groups), 128, True) == 6
+        assert mux.choose(5, False) == len(groups) - 1 and mux.choose(0, True) == 0
+        assert mux.layers_per_round(32768, 32) == 2
+        for lvl, (pcu, dcu) in enumerate(groups):
+            if pcu == 0 or dcu == 0:
+                continue
+            pm, dm = mux.cu_mask(lvl, 0), mux.cu_mask(lvl, 1)
+            assert _popcount(pm) == pcu and _popcount(dm) == dcu
+            assert all((a & b) == 0 for a, b in zip(pm, dm))
+            assert all((a | b) == 0xFFFFFFFF for a, b in zip(pm, dm))
+            for bits, n in ((_bits(pm), pcu), (_bits(dm), dcu)):
+                per_xcd = [sum(1 for b in bits if b % 8 == x) for x in range(8)]
+                assert per_xcd == [n // 8] * 8
+            assert mux.stream(lvl, 0) and mux.stream(lvl, 1) and mux.stream(lvl, 0) != mux.stream(lvl, 1)
+    finally:
+        mux.close()
+
+
+class _MuxCase:
+    """A few layers with a decode batch and one prompt sharing each layer's pool."""
+
+    def __init__(self, layers=3, hq=8, hkv=2, d=128, bs=16, ctx=(100, 37, 300, 64), prompt=500, seed=31):
+        self.L, self.hq, self.hkv, self.d, self.bs = layers, hq, hkv, d, bs
+        self.ctx = list(ctx)
+        self.N = prompt
+        B = len(ctx)
+        nblk = sum(-(-c // bs) for c in ctx) + -(-prompt // bs) + 4
+        g = lambda t, i=0, l=0: inputs.stream(seed, 50, l, t, i)  # noqa: E731
+        tables, _ = inputs.assign_blocks(nblk, self.ctx + [prompt], bs, g(inputs.T_PERM))
+        self.dec_bt, self.pr_bt = i32(tables[:B]), i32(tables[B:])
+        self.pools, self.hist_k, self.hist_v = [], [], []
+        self.kn, self.vn, self.qd, self.qp, self.kp, self.vp = [], [], [], [], [], []
+        for l in range(layers):
+            pool = ops.PagedPool(nblk, bs, hkv, 1, d, "bf16").fill_bits(0x7FBF)
+            hk = [inputs.normal((c - 1, hkv, d), 0.5, "bf16", g(inputs.T_K, r, l)) for r, c in enumerate(self.ctx)]
+            hv = [inputs.normal((c - 1, hkv, d), 0.5, "bf16", g(inputs.T_V, r, l)) for r, c in enumerate(self.ctx)]
+            start = np.concatenate([[0], np.cumsum([c - 1 for c in self.ctx])]).astype(np.int32)
+            slots = ops.slot_mapping(self.dec_bt, i32(start), i32(np.zeros(B)), int(start[-1]), bs, nblk)
+            ops.kv_write(pool, to_dev(np.concatenate(hk), "bf16"), to_dev(np.concatenate(hv), "bf16"), slots)
+            self.pools.append(pool)
+            self.hist_k.append(hk)
+            self.hist_v.append(hv)
+            self.kn.append(inputs.normal((B, hkv, d), 0.5, "bf16", g(inputs.T_K_DECODE, 0, l)))
+            self.vn.append(inputs.normal((B, hkv, d), 0.5, "bf16", g(inputs.T_V_DECODE, 0, l)))
+            self.qd.append(inputs.normal((B, hq, d), 0.5, "bf16", g(inputs.T_Q_DECODE, 0, l)))
+            self.qp.append(inputs.normal((prompt, hq, d), 0.5, "bf16", g(inputs.T_Q, 0, l)))
+            self.kp.append(inputs.normal((prompt, hkv, d), 0.5, "bf16", g(inputs.T_K, 99, l)))
+            self.vp.append(inputs.normal((prompt, hkv, d), 0.5, "bf16", g(inputs.T_V, 99, l)))
+        self.dec_slots = ops.slot_mapping(self.dec_bt, i32(np.arange(B + 1)), i32([c - 1 for c in self.ctx]), B, bs,
+                                          nblk)
+        self.pr_slots = ops.slot_mapping(self.pr_bt, i32([0, prompt]), i32([0]), prompt, bs, nblk)
+        torch.cuda.synchronize()
+        self.o_dec = [torch.zeros((B, hq, d), dtype=torch.bfloat16, device="cuda") for _ in range(layers)]
+        self.o_pr = [torch.zeros((prompt, hq, d), dtype=torch.bfloat16, device="cuda") for _ in range(layers)]
+        self.dev = dict(qd=[to_dev(x, "bf16") for x in self.qd], kn=[to_dev(x, "bf16") for x in self.kn],
+                        vn=[to_dev(x, "bf16") for x in self.vn], qp=[to_dev(x, "bf16") for x in self.qp],
+                        kp=[to_dev(x, "bf16") for x in self.kp], vp=[to_dev(x, "bf16") for x in self.vp])
+        ws = torch.zeros(max(16, ops.attn_decode_workspace_size(B, hq, max(self.ctx), d)), dtype=torch.uint8,
+                         device="cuda")
+        self.decode = ops.DecodeStepArgs(self.pools, self.dev["qd"], self.dev["kn"], self.dev["vn"], self.o_dec,
+                                         self.dec_slots, self.dec_bt, i32(self.ctx), max(self.ctx), hq, ws)
+        self.prefill = ops.PrefillJobArgs(self.pools, self.dev["qp"], self.dev["kp"], self.dev["vp"], self.o_pr,
+                                          self.pr_slots, self.pr_bt, i32([0, prompt]), i32([0]), prompt, hq)
+
+    def check_decode(self):
+        f = lambda x: inputs.as_float(x, "bf16")  # noqa: E731
+        for l in range(self.L):
+            got = f(from_dev(self.o_dec[l], "bf16"))
+            for r in range(len(self.ctx)):
+                k = np.concatenate([f(self.hist_k[l][r]), f(self.kn[l][r:r + 1])])
+                v = np.concatenate([f(self.hist_v[l][r]), f(self.vn[l][r:r + 1])])
+                assert_close(got[r], oa.decode(f(self.qd[l][r]), k, v), "bf16", f"decode layer {l} request {r}")
+
+    def check_prefill(self):
+        f = lambda x: inputs.as_float(x, "bf16")  # noqa: E731
+        for l in range(self.L):
+            got = f(from_dev(self.o_pr[l], "bf16"))
+            assert_close(got, oa.prefill(f(self.qp[l]), f(self.kp[l]), f(self.vp[l])), "bf16", f"prefill layer {l}")
+
+
+def test_mux_rounds_match_oracle_and_follow_the_level_rule():
+    case = _MuxCase()
+    # budget 1000 with a 500-token prompt: 2 layers per round, 3 layers -> 2 rounds
+    mux = ops.Mux(0, cu_granularity=8, min_decode_cus=32, sm_group_num=8, decode_bs_divisor=36, token_budget=1000)
+    try:
+        groups = mux.groups()
+        with_prefill = policy.choose_level(len(groups), 4, True)
+        decode_only = policy.choose_level(len(groups), 4, False)
+        levels, done = [], False
+        for _ in range(10):
+            lvl, done = mux.run_round(case.decode, case.prefill)
+            levels.append(lvl)
+            if done:
+                break
+        assert case.prefill.done_submitting and done
+        assert case.prefill.c.next_layer == case.L
+        assert levels[0] == with_prefill and all(x == with_prefill for x in levels)
+        assert len(levels) >= 2          # 2 layers per round for 3 layers
+        # after the prefill finished, the next round changes level (decode only)
+        lvl, done = mux.run_round(case.decode, None)
+        assert lvl == decode_only and not done
+        mux.wait_prefill()
+        torch.cuda.synchronize()
+        case.check_decode()
+        case.check_prefill()
+    finally:
+        mux.close()
+
+
+def test_mux_prefill_only_and_decode_only():
+    case = _MuxCase(layers=2, ctx=(40, 33), prompt=300)
+    mux = ops.Mux(0, token_budget=65536)
+    try:
+        lvl, done = mux.run_round(None, case.prefill)       # prefill alone: group 0, whole device
+        assert lvl == 0
+        mux.wait_prefill()
+        lvl, done = mux.run_round(None, case.prefill)       # already submitted: reports done
+        assert done
+        lvl, _ = mux.run_round(case.decode, None)
+        assert lvl == len(mux.groups()) - 1
+        torch.cuda.synchronize()
+        case.check_decode()
+        case.check_prefill()
+    finally:
+        mux.close()
