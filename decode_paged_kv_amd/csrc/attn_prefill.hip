@@ -60,9 +60,17 @@ struct PrefillCfg {
   static constexpr int DT = D / 32;     // 32-dim output tiles
   static constexpr int KROW = D + 8;    // LDS K row stride (elements)
   static constexpr int VROW = BN + 8;   // LDS V^T row stride (elements)
-  static constexpr int KCH = BN * D / 8 / THREADS;   // 16-byte K chunks per thread per tile
-  static constexpr int VCH = D * BN / 8 / THREADS;   // 16-byte V chunks per thread per tile
+  static constexpr int GROUPS = BN / 16;            // 16-key groups per tile (each inside one block)
+  static constexpr int KLANES = D / 8;              // lanes per K row in a group load
+  static constexpr int KACTIVE = 16 * KLANES;       // threads that load K rows of a group (256 for D=128)
+  static constexpr int SK = BN * KROW;              // one K buffer (elements)
+  static constexpr int SV = D * VROW;               // one V buffer
 };
+
+// Running max update rule: the max used for exp2 moves only when a tile's
+// max exceeds it by more than this (log2 units), so p <= 2^8 and the O
+// accumulators are rescaled rarely.
+constexpr float kRescaleSlack = 8.0f;
 
 template <int D>
 __global__ void __launch_bounds__(256, 2)
@@ -71,8 +79,9 @@ attn_prefill_bf16_kernel(PoolDev pool, const bf16_t* __restrict__ q, bf16_t* __r
                          const int32_t* __restrict__ chunk_start, int batch, int ntiles, int num_q_heads,
                          int group, float scale_log2, int total_items) {
   using C = PrefillCfg<D>;
-  __shared__ __attribute__((aligned(16))) bf16_t sk[C::BN * C::KROW];
-  __shared__ __attribute__((aligned(16))) bf16_t sv[D * C::VROW];
+  // double-buffered K and V^T tiles
+  __shared__ __attribute__((aligned(16))) bf16_t sk[2 * C::SK];
+  __shared__ __attribute__((aligned(16))) bf16_t sv[2 * C::SV];
 
   // ---- work item (XCD-contiguous runs) ----
   const int per_xcd = gridDim.x / kXcds;
@@ -95,13 +104,18 @@ attn_prefill_bf16_kernel(PoolDev pool, const bf16_t* __restrict__ q, bf16_t* __r
   if (S + T > (bt_stride << pool.bs_shift) && threadIdx.x == 0) flag_error(pool.err, PKV_ERRBIT_TABLE);
   const int kend = min(kv_len, S + min(T, (qt + 1) * C::BM));   // one past the last query's position
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);    // wave-uniform (lets branches on it stay scalar)
   const int half = lane >> 5, l32 = lane & 31;
   const int hl = pool.heads_per_shard;
   const int sh = kvh / hl, lh = kvh - sh * hl;
   const bf16_t* kpool = reinterpret_cast<const bf16_t*>(pool.k[sh]);
   const bf16_t* vpool = reinterpret_cast<const bf16_t*>(pool.v[sh]);
   const int bs = pool.block_size;
+  const size_t tile_stride = (size_t)bs * D;                     // elements per (block, head) tile
+  const size_t head_off = (size_t)lh * tile_stride;
+  const size_t block_stride = (size_t)hl * tile_stride;
   const int32_t* table = bt + (size_t)b * bt_stride;
 
   // ---- this lane's query row and its Q fragments (B operand of S^T) ----
@@ -116,57 +130,55 @@ attn_prefill_bf16_kernel(PoolDev pool, const bf16_t* __restrict__ q, bf16_t* __r
   }
   const int wave_first_q = S + qt * C::BM + wave * 32;
 
-  // ---- tile loader: global -> registers (next tile), registers -> LDS ----
-  uint4 rk[C::KCH], rv[C::VCH];
+  // ---- tile loader.  Group r of a tile is keys 16r..16r+15, which lie in one
+  // block: its block id is uniform.  K: thread t loads row t / KLANES of the
+  // group, dims (t % KLANES) * 8 (threads >= KACTIVE idle for D = 64).  V:
+  // thread t loads dim t >> 1, keys 8 * (t & 1) of the dim-major tile. ----
+  const int k_row = tid / C::KLANES, k_col = (tid % C::KLANES) * 8;
+  const int v_dim = tid >> 1, v_key = (tid & 1) * 8;
+  const bool k_act = tid < C::KACTIVE, v_act = v_dim < D;
+  uint4 rk[C::GROUPS], rv[C::GROUPS];
   auto load_tile = [&](int kt) {
     const int kbase = kt * C::BN;
+    const bool full = kbase + C::BN <= kv_len;
 #pragma unroll
-    for (int r = 0; r < C::KCH; ++r) {
-      const int c = threadIdx.x + r * C::THREADS;
-      const int key = c / (D / 8), dc = c % (D / 8);
-      const int ka = kbase + key;
-      uint4 val = make_uint4(0, 0, 0, 0);
-      if (ka < kv_len) {
-        const int blk = table[ka >> pool.bs_shift];
-        if (blk >= 0 && blk < pool.num_blocks)
-          val = *reinterpret_cast<const uint4*>(kpool + tile_elems(pool, blk, lh) + (size_t)(ka & (bs - 1)) * D + dc * 8);
-        else
-          flag_error(pool.err, PKV_ERRBIT_BLOCK_ID);
+    for (int r = 0; r < C::GROUPS; ++r) {
+      const int key16 = kbase + 16 * r;
+      rk[r] = make_uint4(0, 0, 0, 0);
+      rv[r] = make_uint4(0, 0, 0, 0);
+      if (key16 >= kv_len) continue;                                   // uniform
+      const int blk = __builtin_amdgcn_readfirstlane(table[key16 >> pool.bs_shift]);
+      if (blk < 0 || blk >= pool.num_blocks) {                         // uniform
+        if (tid == 0) flag_error(pool.err, PKV_ERRBIT_BLOCK_ID);
+        continue;
       }
-      rk[r] = val;
-    }
+      const size_t tbase = (size_t)blk * block_stride + head_off;
+      const int off = key16 & (bs - 1);
+      if (full) {
+        if (k_act) rk[r] = *reinterpret_cast<const uint4*>(kpool + tbase + (size_t)(off + k_row) * D + k_col);
+        if (v_act) rv[r] = *reinterpret_cast<const uint4*>(vpool + tbase + (size_t)v_dim * bs + off + v_key);
+      } else {                                                         // the request's last tile
+        if (k_act && key16 + k_row < kv_len)
+          rk[r] = *reinterpret_cast<const uint4*>(kpool + tbase + (size_t)(off + k_row) * D + k_col);
+        const int nvalid = kv_len - key16 - v_key;                     // keys past the request hold arbitrary bits
+        if (v_act && nvalid > 0) {
+          uint4 val = *reinterpret_cast<const uint4*>(vpool + tbase + (size_t)v_dim * bs + off + v_key);
+          uint32_t* w = reinterpret_cast<uint32_t*>(&val);
 #pragma unroll
-    for (int r = 0; r < C::VCH; ++r) {
-      const int c = threadIdx.x + r * C::THREADS;
-      const int dim = c / (C::BN / 8), kc = c % (C::BN / 8);
-      const int ka = kbase + kc * 8;
-      uint4 val = make_uint4(0, 0, 0, 0);
-      if (ka < kv_len) {
-        const int blk = table[ka >> pool.bs_shift];
-        if (blk >= 0 && blk < pool.num_blocks) {
-          val = *reinterpret_cast<const uint4*>(vpool + tile_elems(pool, blk, lh) + (size_t)dim * bs + (ka & (bs - 1)));
-          const int nvalid = kv_len - ka;          // keys past the request hold arbitrary bits
-          if (nvalid < 8) {
-            uint32_t* w = reinterpret_cast<uint32_t*>(&val);
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-              if (e >= nvalid) w[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
-          }
+          for (int e = 0; e < 8; ++e)
+            if (e >= nvalid) w[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
+          rv[r] = val;
         }
       }
-      rv[r] = val;
     }
   };
-  auto store_tile = [&]() {
+  auto store_tile = [&](int buf) {
+    bf16_t* kb = sk + buf * C::SK;
+    bf16_t* vb = sv + buf * C::SV;
 #pragma unroll
-    for (int r = 0; r < C::KCH; ++r) {
-      const int c = threadIdx.x + r * C::THREADS;
-      *reinterpret_cast<uint4*>(&sk[(c / (D / 8)) * C::KROW + (c % (D / 8)) * 8]) = rk[r];
-    }
-#pragma unroll
-    for (int r = 0; r < C::VCH; ++r) {
-      const int c = threadIdx.x + r * C::THREADS;
-      *reinterpret_cast<uint4*>(&sv[(c / (C::BN / 8)) * C::VROW + (c % (C::BN / 8)) * 8]) = rv[r];
+    for (int r = 0; r < C::GROUPS; ++r) {
+      if (k_act) *reinterpret_cast<uint4*>(&kb[(16 * r + k_row) * C::KROW + k_col]) = rk[r];
+      if (v_act) *reinterpret_cast<uint4*>(&vb[v_dim * C::VROW + 16 * r + v_key]) = rv[r];
     }
   };
 
@@ -177,19 +189,20 @@ attn_prefill_bf16_kernel(PoolDev pool, const bf16_t* __restrict__ q, bf16_t* __r
 
   const int nkt = (kend + C::BN - 1) / C::BN;
   load_tile(0);
+  store_tile(0);
+  __syncthreads();
   for (int kt = 0; kt < nkt; ++kt) {
-    __syncthreads();                 // previous tile's LDS reads are done
-    store_tile();
-    __syncthreads();
-    if (kt + 1 < nkt) load_tile(kt + 1);   // in flight during this tile's math
-
+    const int buf = kt & 1;
+    if (kt + 1 < nkt) load_tile(kt + 1);           // in flight during this tile's math
+    const bf16_t* kb = sk + buf * C::SK;
+    const bf16_t* vb = sv + buf * C::SV;
     const int kbase = kt * C::BN;
     // ---- S^T = K Q^T over two 32-key halves ----
     f32x16_t st[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       st[i] = f32x16_t{};
-      const bf16_t* krow = &sk[(32 * i + key_perm(l32)) * C::KROW + 8 * half];
+      const bf16_t* krow = &kb[(32 * i + key_perm(l32)) * C::KROW + 8 * half];
 #pragma unroll
       for (int s = 0; s < C::KS; ++s) st[i] = mfma32(*reinterpret_cast<const uint4*>(krow + 16 * s), qf[s], st[i]);
     }
@@ -208,11 +221,18 @@ attn_prefill_bf16_kernel(PoolDev pool, const bf16_t* __restrict__ q, bf16_t* __r
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st[i][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float mnew = fmaxf(m, mx * scale_log2);
-    const float alpha = __builtin_amdgcn_exp2f(m - mnew);
-    m = mnew;
+      for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(st[i][r], st[i][r + 1]));
+    mx = fmaxf(mx, __shfl_xor(mx, 32)) * scale_log2;
+    // move the running max only when this tile exceeds it by the slack
+    const bool grow = mx > m + kRescaleSlack;
+    if (__builtin_amdgcn_ballot_w64(grow)) {         // wave-uniform branch
+      const float mnew = grow ? mx : m;
+      const float alpha = __builtin_amdgcn_exp2f(m - mnew);     // 0 on the first tile (m = -inf)
+      m = mnew;
+      lsum *= alpha;
+#pragma unroll
+      for (int t = 0; t < C::DT; ++t) o[t] *= alpha;
+    }
     float psum = 0.f;
     uint4 pf[2][2];
 #pragma unroll
@@ -222,15 +242,13 @@ attn_prefill_bf16_kernel(PoolDev pool, const bf16_t* __restrict__ q, bf16_t* __r
         float p[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          p[e] = __builtin_amdgcn_exp2f(fmaf(st[i][8 * sp + e], scale_log2, -mnew));
+          p[e] = __builtin_amdgcn_exp2f(fmaf(st[i][8 * sp + e], scale_log2, -m));
           psum += p[e];
         }
         pf[i][sp] = make_uint4(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
                                pack_bf16x2(p[6], p[7]));
       }
-    lsum = lsum * alpha + psum;
-#pragma unroll
-    for (int t = 0; t < C::DT; ++t) o[t] *= alpha;
+    lsum += psum;
     // ---- O^T += V^T P^T ----
 #pragma unroll
     for (int i = 0; i < 2; ++i)
@@ -238,10 +256,12 @@ attn_prefill_bf16_kernel(PoolDev pool, const bf16_t* __restrict__ q, bf16_t* __r
       for (int sp = 0; sp < 2; ++sp) {
 #pragma unroll
         for (int t = 0; t < C::DT; ++t) {
-          const uint4 va = *reinterpret_cast<const uint4*>(&sv[(32 * t + l32) * C::VROW + 32 * i + 16 * sp + 8 * half]);
+          const uint4 va = *reinterpret_cast<const uint4*>(&vb[(32 * t + l32) * C::VROW + 32 * i + 16 * sp + 8 * half]);
           o[t] = mfma32(va, pf[i][sp], o[t]);
         }
       }
+    if (kt + 1 < nkt) store_tile(buf ^ 1);           // the other buffer was last read before the previous barrier
+    __syncthreads();
   }
 
   // ---- normalise and store: lane holds dims 32t + 8a + 4*half + 0..3 of its query ----

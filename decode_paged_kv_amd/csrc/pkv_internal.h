@@ -35,8 +35,12 @@ __device__ __forceinline__ bf16_t f32_to_bf16(float x) {
   __bf16 b = static_cast<__bf16>(x);
   return __builtin_bit_cast(bf16_t, b);
 }
+// Two floats to a bf16 pair (lo in bits 0-15), one v_cvt_pk_bf16_f32.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_v));
 }
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(1))) u32x4_t global_u32x4_t;
