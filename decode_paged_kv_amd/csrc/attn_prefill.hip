@@ -23,7 +23,9 @@
 //   permuted so that the 8 consecutive accumulator registers a lane
 //   converts to bf16 are 8 consecutive keys; the second MFMA's A operand
 //   then reads those same 8 keys as one 16-byte run of the dim-major V
-//   tile.  Online softmax in the exp2 domain, fp32 accumulation.
+//   tile.  The permutation is applied when K rows are written to LDS, so
+//   the MFMA reads consecutive LDS rows (bank-conflict free with the
+//   16-byte row padding).  Online softmax in the exp2 domain, fp32 accumulation.
 //   Work items are ordered (KV head, query tile from the heaviest, q-head
 //   in the group) and dealt out so that each XCD (consecutive workgroup ids
 //   go round-robin over the 8 XCDs) gets one contiguous run: the q-heads of
@@ -131,53 +133,66 @@ attn_prefill_bf16_kernel(PoolDev pool, const bf16_t* __restrict__ q, bf16_t* __r
   const int wave_first_q = S + qt * C::BM + wave * 32;
 
   // ---- tile loader.  Group r of a tile is keys 16r..16r+15, which lie in one
-  // block: its block id is uniform.  K: thread t loads row t / KLANES of the
-  // group, dims (t % KLANES) * 8 (threads >= KACTIVE idle for D = 64).  V:
-  // thread t loads dim t >> 1, keys 8 * (t & 1) of the dim-major tile. ----
+  // block: its block id is uniform, so each group is read through a buffer
+  // descriptor on that block's (block, head) tile and a lane adds only its
+  // fixed offset.  K: thread t loads row t / KLANES of the group, dims
+  // (t % KLANES) * 8 (threads >= KACTIVE idle for D = 64).  V: thread t loads
+  // dim t >> 1, keys 8 * (t & 1) of the dim-major tile.  A group with a bad
+  // block id (or wholly past the request) gets a zero-size descriptor, reads
+  // zeros, and its bit in the returned mask marks its keys absent. ----
   const int k_row = tid / C::KLANES, k_col = (tid % C::KLANES) * 8;
+  const int k_row_perm = key_perm(k_row);     // LDS row of this key (key_perm is its own inverse)
   const int v_dim = tid >> 1, v_key = (tid & 1) * 8;
-  const bool k_act = tid < C::KACTIVE, v_act = v_dim < D;
+  const bool k_act = C::KACTIVE >= C::THREADS || tid < C::KACTIVE;
+  const bool v_act = 2 * D >= C::THREADS || v_dim < D;
+  const int k_voff = (k_row * D + k_col) * 2, v_voff = (v_dim * bs + v_key) * 2;   // bytes
+  const int tile_bytes = bs * D * 2;
   uint4 rk[C::GROUPS], rv[C::GROUPS];
-  auto load_tile = [&](int kt) {
+  auto load_tile = [&](int kt) -> uint32_t {
     const int kbase = kt * C::BN;
-    const bool full = kbase + C::BN <= kv_len;
+    int blk[C::GROUPS];
 #pragma unroll
     for (int r = 0; r < C::GROUPS; ++r) {
       const int key16 = kbase + 16 * r;
-      rk[r] = make_uint4(0, 0, 0, 0);
-      rv[r] = make_uint4(0, 0, 0, 0);
-      if (key16 >= kv_len) continue;                                   // uniform
-      const int blk = __builtin_amdgcn_readfirstlane(table[key16 >> pool.bs_shift]);
-      if (blk < 0 || blk >= pool.num_blocks) {                         // uniform
-        if (tid == 0) flag_error(pool.err, PKV_ERRBIT_BLOCK_ID);
-        continue;
-      }
-      const size_t tbase = (size_t)blk * block_stride + head_off;
-      const int off = key16 & (bs - 1);
-      if (full) {
-        if (k_act) rk[r] = *reinterpret_cast<const uint4*>(kpool + tbase + (size_t)(off + k_row) * D + k_col);
-        if (v_act) rv[r] = *reinterpret_cast<const uint4*>(vpool + tbase + (size_t)v_dim * bs + off + v_key);
-      } else {                                                         // the request's last tile
-        if (k_act && key16 + k_row < kv_len)
-          rk[r] = *reinterpret_cast<const uint4*>(kpool + tbase + (size_t)(off + k_row) * D + k_col);
-        const int nvalid = kv_len - key16 - v_key;                     // keys past the request hold arbitrary bits
-        if (v_act && nvalid > 0) {
-          uint4 val = *reinterpret_cast<const uint4*>(vpool + tbase + (size_t)v_dim * bs + off + v_key);
-          uint32_t* w = reinterpret_cast<uint32_t*>(&val);
+      blk[r] = key16 < kv_len ? __builtin_amdgcn_readfirstlane(table[key16 >> pool.bs_shift]) : -1;
+    }
+    uint32_t absent = 0;
 #pragma unroll
-          for (int e = 0; e < 8; ++e)
-            if (e >= nvalid) w[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
-          rv[r] = val;
-        }
+    for (int r = 0; r < C::GROUPS; ++r) {
+      const int key16 = kbase + 16 * r;
+      const bool ok = blk[r] >= 0 && blk[r] < pool.num_blocks;      // uniform
+      if (!ok) {
+        absent |= 1u << r;
+        if (key16 < kv_len && tid == 0) flag_error(pool.err, PKV_ERRBIT_BLOCK_ID);
+      }
+      const size_t tbase = ok ? (size_t)blk[r] * block_stride + head_off : 0;
+      const int off = key16 & (bs - 1);
+      const buffer_rsrc_t rsk = buffer_rsrc(kpool + tbase, ok ? tile_bytes : 0);
+      const buffer_rsrc_t rsv = buffer_rsrc(vpool + tbase, ok ? tile_bytes : 0);
+      if (k_act) rk[r] = buffer_load16(rsk, k_voff, off * D * 2);
+      if (v_act) rv[r] = buffer_load16(rsv, v_voff, off * 2);
+    }
+    // the request's last tile: keys past kv_len hold arbitrary bits; their
+    // scores are masked by causality, their V entries must be zero (p = 0
+    // times a NaN pattern would still poison the sum)
+    if (kbase + C::BN > kv_len && v_act) {
+#pragma unroll
+      for (int r = 0; r < C::GROUPS; ++r) {
+        const int nvalid = kv_len - (kbase + 16 * r) - v_key;
+        uint32_t* w = reinterpret_cast<uint32_t*>(&rv[r]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (e >= nvalid) w[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
       }
     }
+    return absent;
   };
   auto store_tile = [&](int buf) {
     bf16_t* kb = sk + buf * C::SK;
     bf16_t* vb = sv + buf * C::SV;
 #pragma unroll
     for (int r = 0; r < C::GROUPS; ++r) {
-      if (k_act) *reinterpret_cast<uint4*>(&kb[(16 * r + k_row) * C::KROW + k_col]) = rk[r];
+      if (k_act) *reinterpret_cast<uint4*>(&kb[(16 * r + k_row_perm) * C::KROW + k_col]) = rk[r];
       if (v_act) *reinterpret_cast<uint4*>(&vb[v_dim * C::VROW + 16 * r + v_key]) = rv[r];
     }
   };
@@ -185,27 +200,46 @@ attn_prefill_bf16_kernel(PoolDev pool, const bf16_t* __restrict__ q, bf16_t* __r
   f32x16_t o[C::DT];
 #pragma unroll
   for (int t = 0; t < C::DT; ++t) o[t] = f32x16_t{};
-  float m = -INFINITY, lsum = 0.f;
+  // running max (log2 units): finite start, so a tile whose keys are all
+  // masked or absent gives p = exp2(-inf) = 0 rather than exp2(-inf + inf)
+  float m = -1e30f, lsum = 0.f;
 
   const int nkt = (kend + C::BN - 1) / C::BN;
-  load_tile(0);
+  uint32_t absent = load_tile(0);
   store_tile(0);
   __syncthreads();
   for (int kt = 0; kt < nkt; ++kt) {
     const int buf = kt & 1;
-    if (kt + 1 < nkt) load_tile(kt + 1);           // in flight during this tile's math
+    uint32_t absent_next = 0;
+    if (kt + 1 < nkt) absent_next = load_tile(kt + 1);   // in flight during this tile's math
     const bf16_t* kb = sk + buf * C::SK;
     const bf16_t* vb = sv + buf * C::SV;
     const int kbase = kt * C::BN;
     // ---- S^T = K Q^T over two 32-key halves ----
+    // all K fragments are read before the first MFMA so the LDS latency is
+    // paid once per tile, not once per MFMA
     f32x16_t st[2];
+    uint4 kf[2][C::KS];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const bf16_t* krow = &kb[(32 * i + l32) * C::KROW + 8 * half];
+#pragma unroll
+      for (int s = 0; s < C::KS; ++s) kf[i][s] = *reinterpret_cast<const uint4*>(krow + 16 * s);
+    }
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       st[i] = f32x16_t{};
-      const bf16_t* krow = &kb[(32 * i + key_perm(l32)) * C::KROW + 8 * half];
 #pragma unroll
-      for (int s = 0; s < C::KS; ++s) st[i] = mfma32(*reinterpret_cast<const uint4*>(krow + 16 * s), qf[s], st[i]);
+      for (int s = 0; s < C::KS; ++s) st[i] = mfma32(kf[i][s], qf[s], st[i]);
     }
+    // schedule: 8 reads ahead, then one read behind each MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+    for (int j = 0; j < 2 * C::KS - 8; ++j) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
     // ---- causal mask (only where the tile reaches past this wave's first query) ----
     if (kbase + C::BN - 1 > wave_first_q) {
 #pragma unroll
@@ -215,6 +249,14 @@ attn_prefill_bf16_kernel(PoolDev pool, const bf16_t* __restrict__ q, bf16_t* __r
           const int key = kbase + 32 * i + 16 * (r >> 3) + 8 * half + (r & 7);
           if (key > qpos) st[i][r] = -INFINITY;
         }
+    }
+    // ---- keys of groups with a bad block id are absent ----
+    if (absent) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if ((absent >> (2 * i + (r >> 3))) & 1) st[i][r] = -INFINITY;
     }
     // ---- online softmax for query l32 (keys split over lanes l and l^32) ----
     float mx = -INFINITY;
@@ -227,13 +269,16 @@ attn_prefill_bf16_kernel(PoolDev pool, const bf16_t* __restrict__ q, bf16_t* __r
     const bool grow = mx > m + kRescaleSlack;
     if (__builtin_amdgcn_ballot_w64(grow)) {         // wave-uniform branch
       const float mnew = grow ? mx : m;
-      const float alpha = __builtin_amdgcn_exp2f(m - mnew);     // 0 on the first tile (m = -inf)
+      const float alpha = __builtin_amdgcn_exp2f(m - mnew);     // 0 on the first tile
       m = mnew;
       lsum *= alpha;
 #pragma unroll
       for (int t = 0; t < C::DT; ++t) o[t] *= alpha;
     }
-    float psum = 0.f;
+    // p in bf16 (the MFMA operand); the row sum adds those same rounded
+    // values, two per v_dot2 against (1, 1)
+    constexpr uint32_t kOnes = 0x3F803F80u;
+    float psum[2] = {0.f, 0.f};
     uint4 pf[2][2];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
@@ -241,14 +286,15 @@ attn_prefill_bf16_kernel(PoolDev pool, const bf16_t* __restrict__ q, bf16_t* __r
       for (int sp = 0; sp < 2; ++sp) {
         float p[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          p[e] = __builtin_amdgcn_exp2f(fmaf(st[i][8 * sp + e], scale_log2, -m));
-          psum += p[e];
-        }
+        for (int e = 0; e < 8; ++e) p[e] = __builtin_amdgcn_exp2f(fmaf(st[i][8 * sp + e], scale_log2, -m));
         pf[i][sp] = make_uint4(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
                                pack_bf16x2(p[6], p[7]));
+        psum[sp] = dot2_bf16(pf[i][sp].x, kOnes, psum[sp]);
+        psum[sp] = dot2_bf16(pf[i][sp].y, kOnes, psum[sp]);
+        psum[sp] = dot2_bf16(pf[i][sp].z, kOnes, psum[sp]);
+        psum[sp] = dot2_bf16(pf[i][sp].w, kOnes, psum[sp]);
       }
-    lsum += psum;
+    lsum += psum[0] + psum[1];
     // ---- O^T += V^T P^T ----
 #pragma unroll
     for (int i = 0; i < 2; ++i)
@@ -261,6 +307,7 @@ attn_prefill_bf16_kernel(PoolDev pool, const bf16_t* __restrict__ q, bf16_t* __r
         }
       }
     if (kt + 1 < nkt) store_tile(buf ^ 1);           // the other buffer was last read before the previous barrier
+    absent = absent_next;
     __syncthreads();
   }
 

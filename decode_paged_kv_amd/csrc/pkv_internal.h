@@ -42,6 +42,11 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   const f32x2_t v = {lo, hi};
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_v));
 }
+// c + a.lo*b.lo + a.hi*b.hi over bf16 pairs, fp32 accumulate (v_dot2_f32_bf16).
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_v, a), __builtin_bit_cast(bf16x2_v, b), c, false);
+}
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(1))) u32x4_t global_u32x4_t;
 // 16-byte non-temporal store (the data is not read back soon).  The cast to
@@ -53,6 +58,19 @@ __device__ __forceinline__ void store_nt16(void* p, const uint4& v) {
 // 16-byte non-temporal load: streamed data that this kernel reads once.
 __device__ __forceinline__ uint4 load_nt16(const void* p) {
   const u32x4_t w = __builtin_nontemporal_load((const global_u32x4_t*)p);
+  return make_uint4(w.x, w.y, w.z, w.w);
+}
+// Raw buffer view of one contiguous range whose base and size are
+// wave-uniform: the descriptor sits in scalar registers and a lane adds only
+// a 32-bit offset, so a load costs no vector address arithmetic.  Bytes past
+// `bytes` read as zero (bytes = 0: every load reads zero, nothing is touched).
+// Descriptor word 3 = untyped 32-bit elements (the gfx9 raw-buffer setting).
+typedef __amdgpu_buffer_rsrc_t buffer_rsrc_t;
+__device__ __forceinline__ buffer_rsrc_t buffer_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+__device__ __forceinline__ uint4 buffer_load16(buffer_rsrc_t r, int voffset, int soffset) {
+  const u32x4_t w = __builtin_amdgcn_raw_buffer_load_b128(r, voffset, soffset, 0);
   return make_uint4(w.x, w.y, w.z, w.w);
 }
 __device__ __forceinline__ void flag_error(int32_t* err, int bit) {

@@ -191,3 +191,45 @@ def test_tiny_config_relayout_then_decode_unchanged():
     after = out2.cpu().numpy().astype(np.float64)
     assert_close(after, ref, "f32", "tiny decode (bs 32, 2 shards)")
     assert np.abs(after - before).max() <= 1e-6
+
+
+def test_bad_block_id_makes_its_keys_absent():
+    """A block-table entry outside [0, num_blocks) is never dereferenced: its
+    keys drop out of the softmax (decode and prefill alike) and the error
+    word gets the block-id bit.  Reference: the oracle over the remaining keys."""
+    bs, hq, hkv, d = 16, 16, 4, 128
+    lengths = [300, 200]
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    sc = Scenario(num_q_heads=hq, num_kv_heads=hkv, head_dim=d, block_size=bs, dtype="bf16", lengths=lengths,
+                  pool_blocks=40, scale=0.5, seed=12, err_word=err)
+    sc.write_all()
+    bad = {0: [3, 10], 1: [5]}                      # logical block indices made invalid
+    tables = sc.tables.copy()
+    for r, js in bad.items():
+        for j in js:
+            tables[r, j] = 40 + 7 * j               # out of range
+    sc.bt_dev = i32(tables)
+    f = lambda x: inputs.as_float(x, "bf16")  # noqa: E731
+
+    def present(r, upto):
+        keep = [p for p in range(upto) if p // bs not in bad[r]]
+        return sc.kf(r)[keep], sc.vf(r)[keep]
+
+    # decode: every request's last position
+    q = _q(sc, (2, hq, d), scale=0.5)
+    got = run_decode(sc, q)
+    for r in range(2):
+        k, v = present(r, lengths[r])
+        assert_close(got[r], oa.decode(f(q)[r], k, v), "bf16", f"decode request {r}")
+    assert int(err.item()) & 1
+    # prefill: request 0, one chunk covering positions 100..299 (a bad block on each side of 100)
+    err.zero_()
+    s0, t = 100, 200
+    qp = _q(sc, (t, hq, d), tid=inputs.T_Q, idx=1, scale=0.5)
+    out = torch.empty((t, hq, d), dtype=torch.bfloat16, device="cuda")
+    ops.attn_prefill_chunk(sc.pool, to_dev(qp, "bf16"), out, sc.bt_dev[0:1], i32([0, t]), i32([s0]), t, hq)
+    torch.cuda.synchronize()
+    got = f(from_dev(out, "bf16"))
+    ref = np.stack([oa.decode(f(qp)[i], *present(0, s0 + i + 1)) for i in range(t)])
+    assert_close(got, ref, "bf16", "prefill with absent keys")
+    assert int(err.item()) & 1
