@@ -21,8 +21,9 @@
 //   p.v   p goes through the wave's own LDS slice; lane l owns head-dim
 //         columns and reads the dim-major V tile (16 keys of one dim are
 //         32 contiguous bytes), multiplying bf16 key pairs with v_dot2.
-// The 4 waves' (m, l, acc) are merged in LDS; with several splits the
-// partials go to the workspace and a second kernel merges them.
+// The 4 waves' (m, l, acc) are merged in LDS.  A request whose context
+// fits one split writes its output there; otherwise the split partials go
+// to the workspace and a second kernel merges them.
 #include <cstdlib>
 
 #include "pkv_internal.h"
@@ -251,7 +252,7 @@ attn_decode_kernel(PoolDev pool, const T* __restrict__ q, T* __restrict__ out, c
       o += sm.red_acc[w][g][d] * f;
     }
     const int h = kvh * G + g;
-    if (num_splits == 1) {
+    if (L <= split_tokens) {                   // the request's only split: final output
       const float r = o / l;
       if constexpr (kBf16) out[((size_t)b * num_q_heads + h) * D + d] = f32_to_bf16(r);
       else out[((size_t)b * num_q_heads + h) * D + d] = r;
@@ -269,12 +270,15 @@ attn_decode_kernel(PoolDev pool, const T* __restrict__ q, T* __restrict__ out, c
 // ------------------------------------------------------------------------
 // bf16 kernel.  Same work decomposition (one workgroup of 4 waves per
 // (split, KV head, request)); each wave walks 32-key tiles (tile i of the
-// split to wave i % 4) and every global load instruction reads 1 KB of
-// consecutive bytes:
-//   K     a (block, head) K tile is block_size contiguous rows; one load
-//         instruction takes 64 lanes x 16 B = 1024/(2D) whole rows.  The
-//         rows go to the wave's LDS slice (rows padded by 16 B so the
-//         row-per-lane reads below hit distinct banks).
+// split to wave i % 4).  A tile is two 16-key groups, each inside one block,
+// so a group's block id is wave-uniform: it is read with a scalar load and
+// the group's (block, head) K and V tiles are addressed through buffer
+// descriptors in scalar registers; a lane adds only a fixed offset.  Every
+// load instruction reads 1 KB of consecutive bytes:
+//   K     one instruction takes 64 lanes x 16 B = 1024/(2D) whole rows of
+//         the block's contiguous K rows.  The rows go to the wave's LDS
+//         slice (rows padded by 16 B so the row-per-lane reads below hit
+//         distinct banks).
 //   q.k   lanes l and l+32 own key l%32, each half of the head dim; the
 //         wave's q rows are broadcast from LDS (two addresses per read);
 //         partial dots of the two halves meet through v_permlane32_swap.
@@ -283,6 +287,14 @@ attn_decode_kernel(PoolDev pool, const T* __restrict__ q, T* __restrict__ out, c
 //   V     the dim-major V tile gives 16 keys of one dim as 32 contiguous
 //         bytes; two lanes split those, one instruction covers 32 dims
 //         (1 KB).  p.v multiplies bf16 key pairs with v_dot2.
+// Loads run one tile ahead: the next tile's K is issued as soon as this
+// tile's K sits in LDS, its V as soon as this tile's p.v has consumed the
+// V registers, so HBM latency overlaps the arithmetic.
+// A request whose context fits one split writes its output directly;
+// otherwise each split writes its partial (m, l, acc) and the merge kernel
+// combines them (a device-wide handoff inside the kernel would need L2
+// write-back and invalidation on this multi-XCD part, costlier than a
+// second launch).
 // ------------------------------------------------------------------------
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {
@@ -330,13 +342,14 @@ attn_decode_bf16_kernel(PoolDev pool, const bf16_t* __restrict__ q, bf16_t* __re
   constexpr int TK = Smem::TK, KROW = Smem::KROW;
   constexpr int LPR = D / 8;            // lanes per K row in a coalesced load
   constexpr int KPI = 64 / LPR;         // K rows per load instruction
-  constexpr int KLOADS = TK / KPI;
+  constexpr int KPG = 16 / KPI;         // K load instructions per 16-key group
   constexpr int HALF = D / 2;
   constexpr int DPL = D / 32;           // V dims per lane
   __shared__ Smem sm;
 
   const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   int L = ctx[b];
   if (L > (bt_stride << pool.bs_shift)) {
     if (threadIdx.x == 0 && split == 0 && kvh == 0) flag_error(pool.err, PKV_ERRBIT_TABLE);
@@ -345,11 +358,15 @@ attn_decode_bf16_kernel(PoolDev pool, const bf16_t* __restrict__ q, bf16_t* __re
   const int start = split * split_tokens;
   if (start >= L) return;
   const int end = min(L, start + split_tokens);
+  const int nsplit = (L + split_tokens - 1) / split_tokens;   // splits holding keys of this request
   const int hl = pool.heads_per_shard;
   const int sh = kvh / hl, lh = kvh - sh * hl;
   const bf16_t* kpool = reinterpret_cast<const bf16_t*>(pool.k[sh]);
   const bf16_t* vpool = reinterpret_cast<const bf16_t*>(pool.v[sh]);
   const int bs = pool.block_size;
+  const size_t head_off = (size_t)lh * bs * D;                  // elements
+  const size_t block_stride = (size_t)hl * bs * D;
+  const int tile_bytes = bs * D * 2;
   const int32_t* table = bt + (size_t)b * bt_stride;
 
   {
@@ -370,27 +387,68 @@ attn_decode_bf16_kernel(PoolDev pool, const bf16_t* __restrict__ q, bf16_t* __re
   const int kk = lane & 31, hh = lane >> 5;
   bf16_t* ktile = sm.u.t.k[wave];
 
+  // ---- loads of one tile (two 16-key groups, uniform block ids) ----
+  const int k_voff = ((lane / LPR) * D + (lane % LPR) * 8) * 2;        // bytes within a group's rows
+  const int v_voff = ((lane >> 1) * bs + (lane & 1) * 8) * 2;          // dim lane/2, keys (lane&1)*8
+  uint4 kr[2][KPG], vr[2][DPL];
+  int nblk[2];                                  // block ids of the tile in flight (-1: absent)
+  auto fetch_ids = [&](int k0) {
+#pragma unroll
+    for (int grp = 0; grp < 2; ++grp) {
+      const int key16 = k0 + 16 * grp;
+      int blk = key16 < end ? table[key16 >> pool.bs_shift] : -1;
+      blk = __builtin_amdgcn_readfirstlane(blk);
+      if (key16 < end && (blk < 0 || blk >= pool.num_blocks)) {
+        if (lane == 0) flag_error(pool.err, PKV_ERRBIT_BLOCK_ID);
+        blk = -1;
+      }
+      nblk[grp] = blk;
+    }
+  };
+  auto issue_k = [&](int k0) {
+#pragma unroll
+    for (int grp = 0; grp < 2; ++grp) {
+      const bool ok = nblk[grp] >= 0;
+      const buffer_rsrc_t rs = buffer_rsrc(kpool + (ok ? (size_t)nblk[grp] * block_stride + head_off : 0),
+                                           ok ? tile_bytes : 0);
+      const int soff = ((k0 + 16 * grp) & (bs - 1)) * D * 2;
+#pragma unroll
+      for (int j = 0; j < KPG; ++j) kr[grp][j] = buffer_load16(rs, k_voff + j * KPI * D * 2, soff);
+    }
+  };
+  auto issue_v = [&](int k0) {
+#pragma unroll
+    for (int grp = 0; grp < 2; ++grp) {
+      const bool ok = nblk[grp] >= 0;
+      const buffer_rsrc_t rs = buffer_rsrc(vpool + (ok ? (size_t)nblk[grp] * block_stride + head_off : 0),
+                                           ok ? tile_bytes : 0);
+      const int soff = ((k0 + 16 * grp) & (bs - 1)) * 2;
+#pragma unroll
+      for (int i = 0; i < DPL; ++i) vr[grp][i] = buffer_load16(rs, v_voff, soff + i * 64 * bs);
+    }
+  };
+
   const int ntiles = (end - start + TK - 1) / TK;
+  if (wave < ntiles) {
+    fetch_ids(start + wave * TK);
+    issue_k(start + wave * TK);
+    issue_v(start + wave * TK);
+  }
   for (int t = wave; t < ntiles; t += kWaves) {
     const int k0 = start + t * TK;
-    // ---- K: coalesced loads -> LDS ----
-    {
-      uint4 kr[KLOADS];
+    const bool grp_ok[2] = {nblk[0] >= 0, nblk[1] >= 0};
+    // ---- K -> LDS, then the next tile's K loads ----
 #pragma unroll
-      for (int i = 0; i < KLOADS; ++i) {
-        const int key = k0 + i * KPI + lane / LPR;
-        kr[i] = make_uint4(0, 0, 0, 0);
-        if (key < end) {
-          const int blk = table[key >> pool.bs_shift];
-          if (blk >= 0 && blk < pool.num_blocks)
-            kr[i] = load_nt16(kpool + tile_elems(pool, blk, lh) + (size_t)(key & (bs - 1)) * D + (lane % LPR) * 8);
-        }
-      }
+    for (int grp = 0; grp < 2; ++grp)
 #pragma unroll
-      for (int i = 0; i < KLOADS; ++i)
-        *reinterpret_cast<uint4*>(&ktile[(i * KPI + lane / LPR) * KROW + (lane % LPR) * 8]) = kr[i];
-    }
+      for (int j = 0; j < KPG; ++j)
+        *reinterpret_cast<uint4*>(&ktile[(16 * grp + j * KPI + lane / LPR) * KROW + (lane % LPR) * 8]) = kr[grp][j];
     wave_lds_sync();
+    const int tn = t + kWaves;
+    if (tn < ntiles) {
+      fetch_ids(start + tn * TK);
+      issue_k(start + tn * TK);
+    }
     // ---- q.k: key kk, head-dim half hh ----
     float s[G];
 #pragma unroll
@@ -418,11 +476,7 @@ attn_decode_bf16_kernel(PoolDev pool, const bf16_t* __restrict__ q, bf16_t* __re
         asm volatile("v_mov_b32 %0, 0" : "=v"(zero) : "v"(s[g]));
       }
     }
-    bool valid = k0 + kk < end;
-    if (valid) {
-      const int blk = table[(k0 + kk) >> pool.bs_shift];
-      valid = blk >= 0 && blk < pool.num_blocks;
-    }
+    const bool valid = k0 + kk < end && grp_ok[kk >> 4];
     // ---- online softmax over the tile's 32 keys ----
 #pragma unroll
     for (int g = 0; g < G; ++g) {
@@ -438,35 +492,24 @@ attn_decode_bf16_kernel(PoolDev pool, const bf16_t* __restrict__ q, bf16_t* __re
       if ((kk & 1) == 0 && hh == (g & 1)) sm.u.t.p[wave][g][kk >> 1] = pack_bf16x2(p, pn);
     }
     wave_lds_sync();
-    // ---- V: coalesced loads, held in registers until p.v ----
-    uint4 vr[2][DPL];
+    // ---- the request's last tile: V entries of keys past the context hold
+    // arbitrary bits and must be zero (p = 0 times a NaN pattern is NaN) ----
+    if (k0 + TK > end) {
 #pragma unroll
-    for (int grp = 0; grp < 2; ++grp) {
-      const int key16 = k0 + 16 * grp;
-      const int blk = key16 < end ? table[key16 >> pool.bs_shift] : -1;
-      const bool ok = blk >= 0 && blk < pool.num_blocks;
-      if (key16 < end && !ok) flag_error(pool.err, PKV_ERRBIT_BLOCK_ID);
-      const bf16_t* vbase = ok ? vpool + tile_elems(pool, blk, lh) + (key16 & (bs - 1)) + (lane & 1) * 8 : nullptr;
-      const int nvalid = end - key16 - (lane & 1) * 8;    // valid keys among this lane's 8
+      for (int grp = 0; grp < 2; ++grp) {
+        const int nvalid = end - (k0 + 16 * grp) - (lane & 1) * 8;
 #pragma unroll
-      for (int i = 0; i < DPL; ++i) {
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (ok && nvalid > 0) {
-          v = load_nt16(vbase + (size_t)(lane / 2 + 32 * i) * bs);
-          if (nvalid < 8) {        // keys past the context hold arbitrary bits
-            uint32_t* w = reinterpret_cast<uint32_t*>(&v);
+        for (int i = 0; i < DPL; ++i) {
+          uint32_t* w = reinterpret_cast<uint32_t*>(&vr[grp][i]);
 #pragma unroll
-            for (int e = 0; e < 8; ++e)
-              if (e >= nvalid) w[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
-          }
+          for (int e = 0; e < 8; ++e)
+            if (e >= nvalid) w[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
         }
-        vr[grp][i] = v;
       }
     }
     // ---- p.v: lane holds dims lane/2 + 32i of keys 16grp + (lane&1)*8 .. +8 ----
 #pragma unroll
     for (int grp = 0; grp < 2; ++grp) {
-      if (k0 + 16 * grp >= end) break;
       int zero = 0;
 #pragma unroll
       for (int g = 0; g < G; ++g) {
@@ -483,6 +526,7 @@ attn_decode_bf16_kernel(PoolDev pool, const bf16_t* __restrict__ q, bf16_t* __re
         if (g % 4 == 3) asm volatile("v_mov_b32 %0, 0" : "=v"(zero) : "v"(acc[g][0]));
       }
     }
+    if (tn < ntiles) issue_v(start + tn * TK);
     wave_lds_sync();
   }
 
@@ -518,7 +562,7 @@ attn_decode_bf16_kernel(PoolDev pool, const bf16_t* __restrict__ q, bf16_t* __re
       o += sm.u.r.acc[w][g][d] * f;
     }
     const int h = kvh * G + g;
-    if (num_splits == 1) {
+    if (nsplit == 1) {
       out[((size_t)b * num_q_heads + h) * D + d] = f32_to_bf16(o / l);
     } else {
       const size_t row = ((size_t)b * num_q_heads + h) * num_splits + split;
@@ -532,7 +576,8 @@ attn_decode_bf16_kernel(PoolDev pool, const bf16_t* __restrict__ q, bf16_t* __re
 }
 
 // Merge the split partials of each (request, q-head): rescale each split's
-// (m, l, acc) to the common max and normalise.
+// (m, l, acc) to the common max and normalise.  Requests with one split
+// were finished by the attention kernel.
 template <typename T, int D>
 __global__ void __launch_bounds__(D)
 attn_decode_merge_kernel(const float* __restrict__ part_o, const float* __restrict__ part_ml,
@@ -541,6 +586,7 @@ attn_decode_merge_kernel(const float* __restrict__ part_o, const float* __restri
   const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
   const int L = min(ctx[b], max_len);
   const int ns = min(num_splits, (L + split_tokens - 1) / split_tokens);
+  if (ns <= 1) return;                         // written by the attention kernel itself
   const size_t row0 = ((size_t)b * num_q_heads + h) * num_splits;
   float mx = -INFINITY;
   for (int s = 0; s < ns; ++s) mx = fmaxf(mx, part_ml[(row0 + s) * 2]);
@@ -595,28 +641,26 @@ hipError_t launch_d(int group, const PoolDev& pool, const void* q, void* out, co
 }  // namespace
 
 DecodePlan plan_decode(int batch, int num_q_heads, int num_kv_heads, int max_context_len, int head_dim) {
-  (void)num_q_heads;
-  (void)head_dim;
-  // Aim for at least ~4 workgroups per CU across the chip (256 CUs) while
-  // keeping each split at >= 256 keys so the per-split fixed cost stays small.
+  // About two workgroups per CU (256 CUs) keep enough loads in flight to
+  // saturate HBM; below that a (request, KV head) is split into more
+  // workgroups, each split at least 256 keys so its fixed cost stays small.
+  // Splits are whole 32-key tiles.
   const long pairs = (long)batch * num_kv_heads;
-  int split = 128;                     // one 32-key tile per wave per pass
-  while (split < 8192) {
-    const long wgs = pairs * ((max_context_len + split - 1) / split);
-    if (wgs <= 2048 && split >= 256) break;
-    if (wgs <= 1024) break;
-    split *= 2;
-  }
-  // tuning override (keys per split, a multiple of 128)
+  const long splits = pairs >= 512 ? 1 : (512 + pairs - 1) / pairs;
+  long split = (max_context_len + splits - 1) / splits;
+  split = split < 256 ? 256 : split;
+  split = (split + 31) / 32 * 32;
+  // tuning override (keys per split, a multiple of 32)
   static const int forced = [] {
     const char* e = getenv("PKV_DECODE_SPLIT_TOKENS");
     const int v = e ? atoi(e) : 0;
-    return (v >= 128 && v % 128 == 0) ? v : 0;
+    return (v >= 32 && v % 32 == 0) ? v : 0;
   }();
   if (forced) split = forced;
   DecodePlan p;
-  p.split_tokens = split;
-  p.num_splits = (max_context_len + split - 1) / split;
+  p.split_tokens = (int)split;
+  p.num_splits = (int)((max_context_len + split - 1) / split);
+  // partial (acc, m, l) per (request, q-head, split)
   p.workspace = p.num_splits > 1 ? (size_t)batch * num_q_heads * p.num_splits * (head_dim + 2) * sizeof(float) : 0;
   return p;
 }

@@ -130,7 +130,7 @@ def attn_decode(pool: PagedPool, q, out, block_tables, context_lens, max_context
     batch = context_lens.numel()
     if workspace is None:
         nbytes = attn_decode_workspace_size(batch, num_q_heads, max_context_len, pool.head_dim)
-        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+        workspace = torch.zeros(max(nbytes, 16), dtype=torch.uint8, device=q.device)
     rc = lib.attn_decode(C.byref(c), _ptr(q), _ptr(out), _ptr(block_tables), block_tables.shape[-1],
                          _ptr(context_lens), batch, max_context_len, num_q_heads, scale, _ptr(workspace),
                          workspace.numel() * workspace.element_size(), _stream(stream))

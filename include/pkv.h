@@ -175,8 +175,10 @@ int attn_prefill_chunk(const pkv_pool_layer* pool, const void* q, void* out, con
  * scale <= 0 selects 1/sqrt(head_dim).
  * The library picks the split size (keys per workgroup) from the batch,
  * KV-head count and max_context_len; the environment variable
- * PKV_DECODE_SPLIT_TOKENS (a multiple of 128, read once) overrides it for
- * tuning; pkv_attn_decode_workspace_size accounts for it.
+ * PKV_DECODE_SPLIT_TOKENS (a multiple of 32, read once) overrides it for
+ * tuning; pkv_attn_decode_workspace_size accounts for it.  A request whose
+ * context fits one split is finished by the attention kernel; the others
+ * are merged by a second kernel on the same stream.
  */
 size_t pkv_attn_decode_workspace_size(int32_t batch, int32_t num_q_heads, int32_t max_context_len,
                                       int32_t head_dim);

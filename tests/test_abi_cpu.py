@@ -114,10 +114,10 @@ def test_attention_validation():
     # table too narrow for the context
     assert lib.attn_decode(C.byref(p), 0x100, 0x200, 0x300, 2, 0x400, 2, 64, 32, 0.0, 0x500, 1 << 20, None) == -1
     # workspace too small when splits are needed
-    need = lib.pkv_attn_decode_workspace_size(64, 32, 8192, 128)
+    need = lib.pkv_attn_decode_workspace_size(4, 32, 8192, 128)
     assert need > 0
-    assert lib.attn_decode(C.byref(p), 0x100, 0x200, 0x300, 512, 0x400, 64, 8192, 32, 0.0, 0x500, 16, None) == -1
-    assert lib.attn_decode(C.byref(p), 0x100, 0x200, 0x300, 512, 0x400, 64, 8192, 32, float("inf"), 0x500,
+    assert lib.attn_decode(C.byref(p), 0x100, 0x200, 0x300, 512, 0x400, 4, 8192, 32, 0.0, 0x500, 16, None) == -1
+    assert lib.attn_decode(C.byref(p), 0x100, 0x200, 0x300, 512, 0x400, 4, 8192, 32, float("inf"), 0x500,
                            need, None) == -1
     assert lib.attn_decode(C.byref(p), 0x100, 0x200, 0x300, 8, 0x400, 0, 64, 32, 0.0, 0, 0, None) == 0
     assert lib.attn_prefill_chunk(C.byref(p), 0x100, 0x200, 0x300, 8, 0x400, 0x500, 1, 64, 30, 0.0, None) == -1
