@@ -270,67 +270,85 @@ attn_decode_kernel(PoolDev pool, const T* __restrict__ q, T* __restrict__ out, c
 // ------------------------------------------------------------------------
 // bf16 kernel.  Same work decomposition (one workgroup of 4 waves per
 // (split, KV head, request)); each wave walks 32-key tiles (tile i of the
-// split to wave i % 4).  A tile is two 16-key groups, each inside one block,
-// so a group's block id is wave-uniform: it is read with a scalar load and
-// the group's (block, head) K and V tiles are addressed through buffer
-// descriptors in scalar registers; a lane adds only a fixed offset.  Every
-// load instruction reads 1 KB of consecutive bytes:
-//   K     one instruction takes 64 lanes x 16 B = 1024/(2D) whole rows of
-//         the block's contiguous K rows.  The rows go to the wave's LDS
-//         slice (rows padded by 16 B so the row-per-lane reads below hit
-//         distinct banks).
-//   q.k   lanes l and l+32 own key l%32, each half of the head dim; the
-//         wave's q rows are broadcast from LDS (two addresses per read);
-//         partial dots of the two halves meet through v_permlane32_swap.
-//   soft  per-tile max over the 32 keys with DPP row steps and one
-//         v_permlane16_swap; exp2 domain; p stored to LDS as bf16 pairs.
-//   V     the dim-major V tile gives 16 keys of one dim as 32 contiguous
-//         bytes; two lanes split those, one instruction covers 32 dims
-//         (1 KB).  p.v multiplies bf16 key pairs with v_dot2.
-// Loads run one tile ahead: the next tile's K is issued as soon as this
-// tile's K sits in LDS, its V as soon as this tile's p.v has consumed the
-// V registers, so HBM latency overlaps the arithmetic.
+// split to wave i % 4).  A tile is two 16-key halves, each inside one block,
+// so a half's block id is wave-uniform: it is read with a scalar load and
+// the half's (block, head) K and V tiles are addressed through buffer
+// descriptors in scalar registers; a lane adds only a fixed offset.
+//
+// The GQA group's contraction runs on the matrix cores, in transposed form
+// so the G <= 16 q-heads are the 16 columns of 16x16 MFMA tiles:
+//   S^T = K Q^T    v_mfma_f32_16x16x32_bf16 per (half, 32 head dims):
+//                  A = 16 K rows (lane l: key l%16, dims 8(l/16)..+7 of the
+//                  chunk, one 16-byte load), B = q (lane l: head l%16).
+//   softmax        lane l holds keys 4(l/16)..+3 of each half for head
+//                  l%16; the per-head max over the tile needs two lane swaps
+//                  (v_permlane16_swap, v_permlane32_swap); exp2 domain; the
+//                  running max moves only by more than a slack, so the
+//                  accumulators are rescaled rarely.
+//   O^T += V^T P^T v_mfma_f32_16x16x16_bf16 per (half, 16 head dims): the
+//                  S^T accumulator layout is already P's operand layout (4
+//                  keys per lane), and A = the dim-major V tile (lane l: dim
+//                  l%16, keys 4(l/16)..+3: 8 bytes; one instruction reads 16
+//                  whole 32-byte dim rows, 512 contiguous bytes).
+// Nothing goes through LDS until the final 4-wave merge.  The operand
+// registers of a wave's tile are refilled with its next tile as soon as
+// they are consumed: K right after S^T, V right after P V.  Two waves per
+// SIMD keep about 16 KB each in flight.
 // A request whose context fits one split writes its output directly;
 // otherwise each split writes its partial (m, l, acc) and the merge kernel
 // combines them (a device-wide handoff inside the kernel would need L2
 // write-back and invalidation on this multi-XCD part, costlier than a
 // second launch).
 // ------------------------------------------------------------------------
-template <int CTRL>
-__device__ __forceinline__ float dpp(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4_t mfma_qk(const uint4& a, const uint4& b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
+                                                 0, 0, 0);
 }
-// v[l] + v[l ^ 32]
-__device__ __forceinline__ float sum_halves(float v) {
-  auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+__device__ __forceinline__ f32x4_t mfma_pv(const uint2& a, const uint2& b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, a), __builtin_bit_cast(s16x4_t, b), c,
+                                                   0, 0, 0);
 }
-// max over the 32 lanes of each half-wave
-__device__ __forceinline__ float max_half(float v) {
-  v = fmaxf(v, dpp<0xB1>(v));     // quad_perm [1,0,3,2]
-  v = fmaxf(v, dpp<0x4E>(v));     // quad_perm [2,3,0,1]
-  v = fmaxf(v, dpp<0x141>(v));    // row_half_mirror
-  v = fmaxf(v, dpp<0x140>(v));    // row_mirror
-  auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+__device__ __forceinline__ uint2 buffer_load8(buffer_rsrc_t r, int voffset, int soffset) {
+  typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+  const u32x2_t w = __builtin_amdgcn_raw_buffer_load_b64(r, voffset, soffset, 0);
+  return make_uint2(w.x, w.y);
 }
+// reduce over the four lanes l, l^16, l^32, l^48 (one MFMA column)
+__device__ __forceinline__ float col_max(float v) {
+  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto c = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(c[0]), __uint_as_float(c[1]));
+}
+__device__ __forceinline__ float col_sum(float v) {
+  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto c = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(c[0]) + __uint_as_float(c[1]);
+}
+
+// One 32-key tile's MFMA operands and its two block ids (-1: absent).
+template <int D>
+struct DecodeTile {
+  uint4 k[2][D / 32];       // A of S^T: key 16h + l%16, dims 32c + 8(l/16) .. +7
+  uint2 v[2][D / 16];       // A of O^T: dim 16m + l%16, keys 16h + 4(l/16) .. +3
+  int blk[2];
+};
 
 template <int D, int G>
 struct DecodeBf16Smem {
-  static constexpr int TK = 32, KROW = D + 8;
-  uint32_t q[G][D / 2];                         // bf16 pairs
-  union {
-    struct {
-      bf16_t k[kWaves][TK * KROW];              // per-wave K tile
-      uint32_t p[kWaves][G][TK / 2];            // per-wave p, bf16 pairs
-    } t;
-    struct {
-      float acc[kWaves][G][D];
-      float m[kWaves][G];
-      float l[kWaves][G];
-    } r;
-  } u;
+  float acc[kWaves][G][D];
+  float m[kWaves][G];
+  float l[kWaves][G];
 };
+
+// Running max update rule (log2 units): the max used for exp2 moves only
+// when a tile's max exceeds it by more than this, so p <= 2^8.
+constexpr float kDecodeSlack = 8.0f;
 
 template <int D, int G>
 __global__ void __launch_bounds__(kThreads)
@@ -338,18 +356,14 @@ attn_decode_bf16_kernel(PoolDev pool, const bf16_t* __restrict__ q, bf16_t* __re
                         const int32_t* __restrict__ bt, int bt_stride, const int32_t* __restrict__ ctx,
                         int num_q_heads, float scale_log2, int split_tokens, int num_splits,
                         float* __restrict__ part_o, float* __restrict__ part_ml) {
-  using Smem = DecodeBf16Smem<D, G>;
-  constexpr int TK = Smem::TK, KROW = Smem::KROW;
-  constexpr int LPR = D / 8;            // lanes per K row in a coalesced load
-  constexpr int KPI = 64 / LPR;         // K rows per load instruction
-  constexpr int KPG = 16 / KPI;         // K load instructions per 16-key group
-  constexpr int HALF = D / 2;
-  constexpr int DPL = D / 32;           // V dims per lane
-  __shared__ Smem sm;
+  static_assert(G >= 1 && G <= 16, "the q-heads of a KV head are the 16 MFMA columns");
+  constexpr int KC = D / 32, DT = D / 16, TK = 32;
+  __shared__ DecodeBf16Smem<D, G> sm;
 
   const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int l16 = lane & 15, j4 = lane >> 4;
   int L = ctx[b];
   if (L > (bt_stride << pool.bs_shift)) {
     if (threadIdx.x == 0 && split == 0 && kvh == 0) flag_error(pool.err, PKV_ERRBIT_TABLE);
@@ -358,7 +372,6 @@ attn_decode_bf16_kernel(PoolDev pool, const bf16_t* __restrict__ q, bf16_t* __re
   const int start = split * split_tokens;
   if (start >= L) return;
   const int end = min(L, start + split_tokens);
-  const int nsplit = (L + split_tokens - 1) / split_tokens;   // splits holding keys of this request
   const int hl = pool.heads_per_shard;
   const int sh = kvh / hl, lh = kvh - sh * hl;
   const bf16_t* kpool = reinterpret_cast<const bf16_t*>(pool.k[sh]);
@@ -369,204 +382,175 @@ attn_decode_bf16_kernel(PoolDev pool, const bf16_t* __restrict__ q, bf16_t* __re
   const int tile_bytes = bs * D * 2;
   const int32_t* table = bt + (size_t)b * bt_stride;
 
+  // q as the B operand of S^T: head l16 (zero columns past G), dims 32c + 8 j4
+  uint4 qf[KC];
   {
-    const uint32_t* qsrc = reinterpret_cast<const uint32_t*>(q + ((size_t)b * num_q_heads + (size_t)kvh * G) * D);
-    uint32_t* qdst = &sm.q[0][0];
-    for (int i = threadIdx.x; i < G * D / 2; i += kThreads) qdst[i] = qsrc[i];
+    const bool hv = l16 < G;
+    const bf16_t* qrow = q + ((size_t)b * num_q_heads + (size_t)kvh * G + (hv ? l16 : 0)) * D + 8 * j4;
+#pragma unroll
+    for (int c = 0; c < KC; ++c) qf[c] = hv ? *reinterpret_cast<const uint4*>(qrow + 32 * c) : make_uint4(0, 0, 0, 0);
   }
-  __syncthreads();
 
-  float m[G], lsum[G], acc[G][DPL];
+  const int k_voff = (l16 * D + 8 * j4) * 2;                    // bytes within a half's 16 K rows
+  const int v_voff = (l16 * bs + 4 * j4) * 2;                   // dim l16 of a 16-dim slab, 4 keys
+  auto fetch_ids = [&](int k0, DecodeTile<D>& r) {
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    m[g] = -INFINITY;
-    lsum[g] = 0.f;
-#pragma unroll
-    for (int j = 0; j < DPL; ++j) acc[g][j] = 0.f;
-  }
-  const int kk = lane & 31, hh = lane >> 5;
-  bf16_t* ktile = sm.u.t.k[wave];
-
-  // ---- loads of one tile (two 16-key groups, uniform block ids) ----
-  const int k_voff = ((lane / LPR) * D + (lane % LPR) * 8) * 2;        // bytes within a group's rows
-  const int v_voff = ((lane >> 1) * bs + (lane & 1) * 8) * 2;          // dim lane/2, keys (lane&1)*8
-  uint4 kr[2][KPG], vr[2][DPL];
-  int nblk[2];                                  // block ids of the tile in flight (-1: absent)
-  auto fetch_ids = [&](int k0) {
-#pragma unroll
-    for (int grp = 0; grp < 2; ++grp) {
-      const int key16 = k0 + 16 * grp;
+    for (int h = 0; h < 2; ++h) {
+      const int key16 = k0 + 16 * h;
       int blk = key16 < end ? table[key16 >> pool.bs_shift] : -1;
       blk = __builtin_amdgcn_readfirstlane(blk);
       if (key16 < end && (blk < 0 || blk >= pool.num_blocks)) {
         if (lane == 0) flag_error(pool.err, PKV_ERRBIT_BLOCK_ID);
         blk = -1;
       }
-      nblk[grp] = blk;
+      r.blk[h] = blk;
     }
   };
-  auto issue_k = [&](int k0) {
+  auto issue_k = [&](int k0, DecodeTile<D>& r) {
 #pragma unroll
-    for (int grp = 0; grp < 2; ++grp) {
-      const bool ok = nblk[grp] >= 0;
-      const buffer_rsrc_t rs = buffer_rsrc(kpool + (ok ? (size_t)nblk[grp] * block_stride + head_off : 0),
+    for (int h = 0; h < 2; ++h) {
+      const bool ok = r.blk[h] >= 0;
+      const buffer_rsrc_t rs = buffer_rsrc(kpool + (ok ? (size_t)r.blk[h] * block_stride + head_off : 0),
                                            ok ? tile_bytes : 0);
-      const int soff = ((k0 + 16 * grp) & (bs - 1)) * D * 2;
+      const int soff = ((k0 + 16 * h) & (bs - 1)) * D * 2;
 #pragma unroll
-      for (int j = 0; j < KPG; ++j) kr[grp][j] = buffer_load16(rs, k_voff + j * KPI * D * 2, soff);
+      for (int c = 0; c < KC; ++c) r.k[h][c] = buffer_load16(rs, k_voff + 64 * c, soff);
     }
   };
-  auto issue_v = [&](int k0) {
+  auto issue_v = [&](int k0, DecodeTile<D>& r) {
 #pragma unroll
-    for (int grp = 0; grp < 2; ++grp) {
-      const bool ok = nblk[grp] >= 0;
-      const buffer_rsrc_t rs = buffer_rsrc(vpool + (ok ? (size_t)nblk[grp] * block_stride + head_off : 0),
+    for (int h = 0; h < 2; ++h) {
+      const bool ok = r.blk[h] >= 0;
+      const buffer_rsrc_t rs = buffer_rsrc(vpool + (ok ? (size_t)r.blk[h] * block_stride + head_off : 0),
                                            ok ? tile_bytes : 0);
-      const int soff = ((k0 + 16 * grp) & (bs - 1)) * 2;
+      const int soff = ((k0 + 16 * h) & (bs - 1)) * 2;
 #pragma unroll
-      for (int i = 0; i < DPL; ++i) vr[grp][i] = buffer_load16(rs, v_voff, soff + i * 64 * bs);
+      for (int mm = 0; mm < DT; ++mm) r.v[h][mm] = buffer_load8(rs, v_voff, soff + mm * 32 * bs);
     }
+  };
+
+  f32x4_t o[DT];
+#pragma unroll
+  for (int mm = 0; mm < DT; ++mm) o[mm] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  // running max of head l16 (log2 units; finite start, so a tile whose keys
+  // are all absent gives p = exp2(-inf) = 0) and this lane's share of the sum
+  float m = -1e30f, lsum = 0.f;
+  constexpr uint32_t kOnes = 0x3F803F80u;       // bf16 (1, 1)
+
+  // one tile: S^T, softmax, P V; the registers are refilled with the tile
+  // at k0_next (< 0: none) as they are consumed
+  auto process = [&](int k0, DecodeTile<D>& r, int k0_next) {
+    f32x4_t st[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      st[h] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < KC; ++c) st[h] = mfma_qk(r.k[h][c], qf[c], st[h]);
+    }
+    const bool ok0 = r.blk[0] >= 0, ok1 = r.blk[1] >= 0;
+    if (k0_next >= 0) {
+      fetch_ids(k0_next, r);
+      issue_k(k0_next, r);
+    }
+    float x[2][4];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int key = k0 + 16 * h + 4 * j4 + rr;
+        const bool valid = key < end && (h ? ok1 : ok0);
+        x[h][rr] = valid ? st[h][rr] : -INFINITY;
+        mx = fmaxf(mx, x[h][rr]);
+      }
+    mx = col_max(mx) * scale_log2;
+    const bool grow = mx > m + kDecodeSlack;
+    if (__builtin_amdgcn_ballot_w64(grow)) {          // wave-uniform branch
+      const float mnew = grow ? mx : m;
+      const float alpha = __builtin_amdgcn_exp2f(m - mnew);
+      m = mnew;
+      lsum *= alpha;
+#pragma unroll
+      for (int mm = 0; mm < DT; ++mm) o[mm] *= alpha;
+    }
+    uint2 pb[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      float p[4];
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) p[rr] = __builtin_amdgcn_exp2f(fmaf(x[h][rr], scale_log2, -m));
+      pb[h] = make_uint2(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]));
+      lsum = dot2_bf16(pb[h].x, kOnes, lsum);         // the sum of the same bf16 p the MFMA uses
+      lsum = dot2_bf16(pb[h].y, kOnes, lsum);
+    }
+    // the request's last tile: V entries of keys past the context hold
+    // arbitrary bits and must be zero (p = 0 times a NaN pattern is NaN)
+    if (k0 + TK > end) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int nvalid = end - (k0 + 16 * h + 4 * j4);
+#pragma unroll
+        for (int mm = 0; mm < DT; ++mm) {
+          if (nvalid <= 0) r.v[h][mm] = make_uint2(0, 0);
+          else if (nvalid < 4) {
+            uint32_t* w = reinterpret_cast<uint32_t*>(&r.v[h][mm]);
+#pragma unroll
+            for (int e = 1; e < 4; ++e)
+              if (e >= nvalid) w[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int mm = 0; mm < DT; ++mm) o[mm] = mfma_pv(r.v[h][mm], pb[h], o[mm]);
+    if (k0_next >= 0) issue_v(k0_next, r);
   };
 
   const int ntiles = (end - start + TK - 1) / TK;
+  DecodeTile<D> r;
   if (wave < ntiles) {
-    fetch_ids(start + wave * TK);
-    issue_k(start + wave * TK);
-    issue_v(start + wave * TK);
+    fetch_ids(start + wave * TK, r);
+    issue_k(start + wave * TK, r);
+    issue_v(start + wave * TK, r);
   }
   for (int t = wave; t < ntiles; t += kWaves) {
-    const int k0 = start + t * TK;
-    const bool grp_ok[2] = {nblk[0] >= 0, nblk[1] >= 0};
-    // ---- K -> LDS, then the next tile's K loads ----
-#pragma unroll
-    for (int grp = 0; grp < 2; ++grp)
-#pragma unroll
-      for (int j = 0; j < KPG; ++j)
-        *reinterpret_cast<uint4*>(&ktile[(16 * grp + j * KPI + lane / LPR) * KROW + (lane % LPR) * 8]) = kr[grp][j];
-    wave_lds_sync();
     const int tn = t + kWaves;
-    if (tn < ntiles) {
-      fetch_ids(start + tn * TK);
-      issue_k(start + tn * TK);
-    }
-    // ---- q.k: key kk, head-dim half hh ----
-    float s[G];
-#pragma unroll
-    for (int g = 0; g < G; ++g) s[g] = 0.f;
-    {
-      // the key's half row stays in registers; q rows stream from LDS one
-      // head at a time (the empty asm keeps the compiler from hoisting the
-      // reads of every head at once, which would cost G*HALF/2 registers)
-      uint4 kv[HALF / 8];
-      const bf16_t* krow = &ktile[kk * KROW + hh * HALF];
-#pragma unroll
-      for (int c = 0; c < HALF / 8; ++c) kv[c] = *reinterpret_cast<const uint4*>(krow + c * 8);
-      int zero = 0;     // opaque 0 tied to the previous head's score (orders the q reads)
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        const uint32_t* qrow = &sm.q[g][hh * HALF / 2] + zero;
-#pragma unroll
-        for (int c = 0; c < HALF / 8; ++c) {
-          const uint4 qv = *reinterpret_cast<const uint4*>(qrow + c * 4);
-          s[g] = dot2_bf16(kv[c].x, qv.x, s[g]);
-          s[g] = dot2_bf16(kv[c].y, qv.y, s[g]);
-          s[g] = dot2_bf16(kv[c].z, qv.z, s[g]);
-          s[g] = dot2_bf16(kv[c].w, qv.w, s[g]);
-        }
-        asm volatile("v_mov_b32 %0, 0" : "=v"(zero) : "v"(s[g]));
-      }
-    }
-    const bool valid = k0 + kk < end && grp_ok[kk >> 4];
-    // ---- online softmax over the tile's 32 keys ----
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const float sc = valid ? sum_halves(s[g]) * scale_log2 : -INFINITY;
-      const float mn = fmaxf(m[g], max_half(sc));
-      const float alpha = __builtin_amdgcn_exp2f(m[g] - mn);
-      const float p = __builtin_amdgcn_exp2f(sc - mn);
-      m[g] = mn;
-      lsum[g] = lsum[g] * alpha + (hh == 0 ? p : 0.f);
-#pragma unroll
-      for (int j = 0; j < DPL; ++j) acc[g][j] *= alpha;
-      const float pn = dpp<0xB1>(p);                    // the odd neighbour's p
-      if ((kk & 1) == 0 && hh == (g & 1)) sm.u.t.p[wave][g][kk >> 1] = pack_bf16x2(p, pn);
-    }
-    wave_lds_sync();
-    // ---- the request's last tile: V entries of keys past the context hold
-    // arbitrary bits and must be zero (p = 0 times a NaN pattern is NaN) ----
-    if (k0 + TK > end) {
-#pragma unroll
-      for (int grp = 0; grp < 2; ++grp) {
-        const int nvalid = end - (k0 + 16 * grp) - (lane & 1) * 8;
-#pragma unroll
-        for (int i = 0; i < DPL; ++i) {
-          uint32_t* w = reinterpret_cast<uint32_t*>(&vr[grp][i]);
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            if (e >= nvalid) w[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
-        }
-      }
-    }
-    // ---- p.v: lane holds dims lane/2 + 32i of keys 16grp + (lane&1)*8 .. +8 ----
-#pragma unroll
-    for (int grp = 0; grp < 2; ++grp) {
-      int zero = 0;
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        const uint4 pp = *reinterpret_cast<const uint4*>(&sm.u.t.p[wave][g][grp * 8 + (lane & 1) * 4] + zero);
-#pragma unroll
-        for (int i = 0; i < DPL; ++i) {
-          float a = acc[g][i];
-          a = dot2_bf16(pp.x, vr[grp][i].x, a);
-          a = dot2_bf16(pp.y, vr[grp][i].y, a);
-          a = dot2_bf16(pp.z, vr[grp][i].z, a);
-          a = dot2_bf16(pp.w, vr[grp][i].w, a);
-          acc[g][i] = a;
-        }
-        if (g % 4 == 3) asm volatile("v_mov_b32 %0, 0" : "=v"(zero) : "v"(acc[g][0]));
-      }
-    }
-    if (tn < ntiles) issue_v(start + tn * TK);
-    wave_lds_sync();
+    process(start + t * TK, r, tn < ntiles ? start + tn * TK : -1);
   }
 
-  // ---- merge the lane pairs (two key halves), then the 4 waves ----
-#pragma unroll
-  for (int g = 0; g < G; ++g)
-#pragma unroll
-    for (int i = 0; i < DPL; ++i) acc[g][i] += dpp<0xB1>(acc[g][i]);
-  __syncthreads();              // the tile buffers are reused for the reduction below
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    const float l = wave_sum(lsum[g]);
-    if (lane == 0) {
-      sm.u.r.m[wave][g] = m[g];
-      sm.u.r.l[wave][g] = l;
+  // ---- merge the 4 waves ----
+  lsum = col_sum(lsum);
+  if (l16 < G) {
+    if (j4 == 0) {
+      sm.m[wave][l16] = m;
+      sm.l[wave][l16] = lsum;
     }
-    if ((lane & 1) == 0) {
 #pragma unroll
-      for (int i = 0; i < DPL; ++i) sm.u.r.acc[wave][g][lane / 2 + 32 * i] = acc[g][i];
-    }
+    for (int mm = 0; mm < DT; ++mm)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) sm.acc[wave][l16][16 * mm + 4 * j4 + rr] = o[mm][rr];
   }
   __syncthreads();
   for (int i = threadIdx.x; i < G * D; i += kThreads) {
     const int g = i / D, d = i - g * D;
     float mx = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) mx = fmaxf(mx, sm.u.r.m[w][g]);
-    float l = 0.f, o = 0.f;
+    for (int w = 0; w < kWaves; ++w) mx = fmaxf(mx, sm.m[w][g]);
+    float l = 0.f, acc = 0.f;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
-      const float f = __builtin_amdgcn_exp2f(sm.u.r.m[w][g] - mx);
-      l += sm.u.r.l[w][g] * f;
-      o += sm.u.r.acc[w][g][d] * f;
+      const float f = __builtin_amdgcn_exp2f(sm.m[w][g] - mx);
+      l += sm.l[w][g] * f;
+      acc += sm.acc[w][g][d] * f;
     }
     const int h = kvh * G + g;
-    if (nsplit == 1) {
-      out[((size_t)b * num_q_heads + h) * D + d] = f32_to_bf16(o / l);
+    if (L <= split_tokens) {                    // the request's only split: final output
+      out[((size_t)b * num_q_heads + h) * D + d] = f32_to_bf16(acc / l);
     } else {
       const size_t row = ((size_t)b * num_q_heads + h) * num_splits + split;
-      part_o[row * D + d] = o;
+      part_o[row * D + d] = acc;
       if (d == 0) {
         part_ml[row * 2 + 0] = mx;
         part_ml[row * 2 + 1] = l;
