@@ -273,7 +273,8 @@ attn_decode_kernel(PoolDev pool, const T* __restrict__ q, T* __restrict__ out, c
 // split to wave i % 4).  A tile is two 16-key halves, each inside one block,
 // so a half's block id is wave-uniform: it is read with a scalar load and
 // the half's (block, head) K and V tiles are addressed through buffer
-// descriptors in scalar registers; a lane adds only a fixed offset.
+// descriptors in scalar registers; a lane adds only a fixed offset.  Every
+// K/V byte is read once, so the loads carry the non-temporal hint.
 //
 // The GQA group's contraction runs on the matrix cores, in transposed form
 // so the G <= 16 q-heads are the 16 columns of 16x16 MFMA tiles:
@@ -292,7 +293,7 @@ attn_decode_kernel(PoolDev pool, const T* __restrict__ q, T* __restrict__ out, c
 //                  whole 32-byte dim rows, 512 contiguous bytes).
 // Nothing goes through LDS until the final 4-wave merge.  The operand
 // registers of a wave's tile are refilled with its next tile as soon as
-// they are consumed: K right after S^T, V right after P V.  Two waves per
+// they are consumed: K right after S^T, V right after P V.  Three waves per
 // SIMD keep about 16 KB each in flight.
 // A request whose context fits one split writes its output directly;
 // otherwise each split writes its partial (m, l, acc) and the merge kernel
@@ -311,11 +312,6 @@ __device__ __forceinline__ f32x4_t mfma_qk(const uint4& a, const uint4& b, f32x4
 __device__ __forceinline__ f32x4_t mfma_pv(const uint2& a, const uint2& b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, a), __builtin_bit_cast(s16x4_t, b), c,
                                                    0, 0, 0);
-}
-__device__ __forceinline__ uint2 buffer_load8(buffer_rsrc_t r, int voffset, int soffset) {
-  typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
-  const u32x2_t w = __builtin_amdgcn_raw_buffer_load_b64(r, voffset, soffset, 0);
-  return make_uint2(w.x, w.y);
 }
 // reduce over the four lanes l, l^16, l^32, l^48 (one MFMA column)
 __device__ __forceinline__ float col_max(float v) {
@@ -351,7 +347,7 @@ struct DecodeBf16Smem {
 constexpr float kDecodeSlack = 8.0f;
 
 template <int D, int G>
-__global__ void __launch_bounds__(kThreads)
+__global__ void __launch_bounds__(kThreads, 2)
 attn_decode_bf16_kernel(PoolDev pool, const bf16_t* __restrict__ q, bf16_t* __restrict__ out,
                         const int32_t* __restrict__ bt, int bt_stride, const int32_t* __restrict__ ctx,
                         int num_q_heads, float scale_log2, int split_tokens, int num_splits,
@@ -393,7 +389,8 @@ attn_decode_bf16_kernel(PoolDev pool, const bf16_t* __restrict__ q, bf16_t* __re
 
   const int k_voff = (l16 * D + 8 * j4) * 2;                    // bytes within a half's 16 K rows
   const int v_voff = (l16 * bs + 4 * j4) * 2;                   // dim l16 of a 16-dim slab, 4 keys
-  auto fetch_ids = [&](int k0, DecodeTile<D>& r) {
+  // block ids of the tile at k0 (-1: past the split or out of range)
+  auto fetch_ids = [&](int k0, int (&ids)[2]) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int key16 = k0 + 16 * h;
@@ -403,7 +400,7 @@ attn_decode_bf16_kernel(PoolDev pool, const bf16_t* __restrict__ q, bf16_t* __re
         if (lane == 0) flag_error(pool.err, PKV_ERRBIT_BLOCK_ID);
         blk = -1;
       }
-      r.blk[h] = blk;
+      ids[h] = blk;
     }
   };
   auto issue_k = [&](int k0, DecodeTile<D>& r) {
@@ -414,7 +411,7 @@ attn_decode_bf16_kernel(PoolDev pool, const bf16_t* __restrict__ q, bf16_t* __re
                                            ok ? tile_bytes : 0);
       const int soff = ((k0 + 16 * h) & (bs - 1)) * D * 2;
 #pragma unroll
-      for (int c = 0; c < KC; ++c) r.k[h][c] = buffer_load16(rs, k_voff + 64 * c, soff);
+      for (int c = 0; c < KC; ++c) r.k[h][c] = buffer_load16<kStream>(rs, k_voff + 64 * c, soff);
     }
   };
   auto issue_v = [&](int k0, DecodeTile<D>& r) {
@@ -425,7 +422,7 @@ attn_decode_bf16_kernel(PoolDev pool, const bf16_t* __restrict__ q, bf16_t* __re
                                            ok ? tile_bytes : 0);
       const int soff = ((k0 + 16 * h) & (bs - 1)) * 2;
 #pragma unroll
-      for (int mm = 0; mm < DT; ++mm) r.v[h][mm] = buffer_load8(rs, v_voff, soff + mm * 32 * bs);
+      for (int mm = 0; mm < DT; ++mm) r.v[h][mm] = buffer_load8<kStream>(rs, v_voff, soff + mm * 32 * bs);
     }
   };
 
@@ -438,8 +435,10 @@ attn_decode_bf16_kernel(PoolDev pool, const bf16_t* __restrict__ q, bf16_t* __re
   constexpr uint32_t kOnes = 0x3F803F80u;       // bf16 (1, 1)
 
   // one tile: S^T, softmax, P V; the registers are refilled with the tile
-  // at k0_next (< 0: none) as they are consumed
-  auto process = [&](int k0, DecodeTile<D>& r, int k0_next) {
+  // at k0_next (< 0: none) as they are consumed, whose block ids were read
+  // one tile earlier into ids_next; then the ids of the tile at k0_next2
+  int ids_next[2] = {-1, -1};
+  auto process = [&](int k0, DecodeTile<D>& r, int k0_next, int k0_next2) {
     f32x4_t st[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -449,8 +448,10 @@ attn_decode_bf16_kernel(PoolDev pool, const bf16_t* __restrict__ q, bf16_t* __re
     }
     const bool ok0 = r.blk[0] >= 0, ok1 = r.blk[1] >= 0;
     if (k0_next >= 0) {
-      fetch_ids(k0_next, r);
+      r.blk[0] = ids_next[0];
+      r.blk[1] = ids_next[1];
       issue_k(k0_next, r);
+      if (k0_next2 >= 0) fetch_ids(k0_next2, ids_next);
     }
     float x[2][4];
     float mx = -INFINITY;
@@ -509,15 +510,24 @@ attn_decode_bf16_kernel(PoolDev pool, const bf16_t* __restrict__ q, bf16_t* __re
   };
 
   const int ntiles = (end - start + TK - 1) / TK;
-  DecodeTile<D> r;
+  // two tiles in flight per wave: ra holds tiles wave + 8i, rb tiles wave + 8i + 4
+  DecodeTile<D> ra, rb;
+  constexpr int W = kWaves;
   if (wave < ntiles) {
-    fetch_ids(start + wave * TK, r);
-    issue_k(start + wave * TK, r);
-    issue_v(start + wave * TK, r);
+    fetch_ids(start + wave * TK, ra.blk);
+    issue_k(start + wave * TK, ra);
+    issue_v(start + wave * TK, ra);
   }
-  for (int t = wave; t < ntiles; t += kWaves) {
-    const int tn = t + kWaves;
-    process(start + t * TK, r, tn < ntiles ? start + tn * TK : -1);
+  if (wave + W < ntiles) {
+    fetch_ids(start + (wave + W) * TK, rb.blk);
+    issue_k(start + (wave + W) * TK, rb);
+    issue_v(start + (wave + W) * TK, rb);
+  }
+  if (wave + 2 * W < ntiles) fetch_ids(start + (wave + 2 * W) * TK, ids_next);
+  auto at = [&](int t) { return t < ntiles ? start + t * TK : -1; };
+  for (int t = wave; t < ntiles; t += 2 * W) {
+    process(start + t * TK, ra, at(t + 2 * W), at(t + 3 * W));
+    if (t + W < ntiles) process(start + (t + W) * TK, rb, at(t + 3 * W), at(t + 4 * W));
   }
 
   // ---- merge the 4 waves ----
@@ -560,8 +570,9 @@ attn_decode_bf16_kernel(PoolDev pool, const bf16_t* __restrict__ q, bf16_t* __re
 }
 
 // Merge the split partials of each (request, q-head): rescale each split's
-// (m, l, acc) to the common max and normalise.  Requests with one split
-// were finished by the attention kernel.
+// (m, l, acc) to the common max and normalise, in one pass with a running
+// max (the loads of four splits at a time are in flight together).
+// Requests with one split were finished by the attention kernel.
 template <typename T, int D>
 __global__ void __launch_bounds__(D)
 attn_decode_merge_kernel(const float* __restrict__ part_o, const float* __restrict__ part_ml,
@@ -572,13 +583,30 @@ attn_decode_merge_kernel(const float* __restrict__ part_o, const float* __restri
   const int ns = min(num_splits, (L + split_tokens - 1) / split_tokens);
   if (ns <= 1) return;                         // written by the attention kernel itself
   const size_t row0 = ((size_t)b * num_q_heads + h) * num_splits;
-  float mx = -INFINITY;
-  for (int s = 0; s < ns; ++s) mx = fmaxf(mx, part_ml[(row0 + s) * 2]);
-  float l = 0.f, o = 0.f;
-  for (int s = 0; s < ns; ++s) {
-    const float f = __builtin_amdgcn_exp2f(part_ml[(row0 + s) * 2] - mx);
-    l += part_ml[(row0 + s) * 2 + 1] * f;
-    o += part_o[(row0 + s) * D + d] * f;
+  const float2* ml = reinterpret_cast<const float2*>(part_ml) + row0;
+  float mx = -INFINITY, l = 0.f, o = 0.f;
+  for (int s0 = 0; s0 < ns; s0 += 4) {
+    float2 v[4];
+    float a[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const bool in = s0 + j < ns;
+      v[j] = in ? ml[s0 + j] : make_float2(-INFINITY, 0.f);
+      a[j] = in ? part_o[(row0 + s0 + j) * D + d] : 0.f;
+    }
+    float mn = mx;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) mn = fmaxf(mn, v[j].x);
+    const float f = __builtin_amdgcn_exp2f(mx - mn);    // 0 on the first pass
+    l *= f;
+    o *= f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float e = __builtin_amdgcn_exp2f(v[j].x - mn);   // 0 for the padding entries
+      l += v[j].y * e;
+      o += a[j] * e;
+    }
+    mx = mn;
   }
   const float r = o / l;
   if constexpr (sizeof(T) == 2) out[((size_t)b * num_q_heads + h) * D + d] = f32_to_bf16(r);
@@ -625,14 +653,19 @@ hipError_t launch_d(int group, const PoolDev& pool, const void* q, void* out, co
 }  // namespace
 
 DecodePlan plan_decode(int batch, int num_q_heads, int num_kv_heads, int max_context_len, int head_dim) {
-  // About two workgroups per CU (256 CUs) keep enough loads in flight to
-  // saturate HBM; below that a (request, KV head) is split into more
-  // workgroups, each split at least 256 keys so its fixed cost stays small.
-  // Splits are whole 32-key tiles.
+  // Two workgroups per CU (256 CUs) already keep enough loads in flight to
+  // saturate HBM, so a batch with that many (request, KV head) pairs runs
+  // one split per pair and needs no merge.  Below that a pair is cut into
+  // splits of at most 512 keys (short workgroups balance uneven contexts as
+  // they finish), shorter still until there are about three workgroups per
+  // CU (the bf16 kernel's occupancy), but no shorter than 128 keys.  Splits
+  // are whole 32-key tiles.
   const long pairs = (long)batch * num_kv_heads;
-  const long splits = pairs >= 512 ? 1 : (512 + pairs - 1) / pairs;
-  long split = (max_context_len + splits - 1) / splits;
-  split = split < 256 ? 256 : split;
+  long split = max_context_len;
+  if (pairs < 512) {
+    split = ((long)max_context_len * pairs + 767) / 768;
+    split = split < 128 ? 128 : (split > 512 ? 512 : split);
+  }
   split = (split + 31) / 32 * 32;
   // tuning override (keys per split, a multiple of 32)
   static const int forced = [] {

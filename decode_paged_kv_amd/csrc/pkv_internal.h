@@ -69,9 +69,19 @@ typedef __amdgpu_buffer_rsrc_t buffer_rsrc_t;
 __device__ __forceinline__ buffer_rsrc_t buffer_rsrc(const void* base, int bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
 }
+// cache policy of a buffer load: kCached for data other workgroups re-read
+// through L2, kStream (the nt bit) for data read once
+enum { kCached = 0, kStream = 2 };
+template <int POLICY = kCached>
 __device__ __forceinline__ uint4 buffer_load16(buffer_rsrc_t r, int voffset, int soffset) {
-  const u32x4_t w = __builtin_amdgcn_raw_buffer_load_b128(r, voffset, soffset, 0);
+  const u32x4_t w = __builtin_amdgcn_raw_buffer_load_b128(r, voffset, soffset, POLICY);
   return make_uint4(w.x, w.y, w.z, w.w);
+}
+template <int POLICY = kCached>
+__device__ __forceinline__ uint2 buffer_load8(buffer_rsrc_t r, int voffset, int soffset) {
+  typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+  const u32x2_t w = __builtin_amdgcn_raw_buffer_load_b64(r, voffset, soffset, POLICY);
+  return make_uint2(w.x, w.y);
 }
 __device__ __forceinline__ void flag_error(int32_t* err, int bit) {
   if (err) atomicOr(err, bit);
