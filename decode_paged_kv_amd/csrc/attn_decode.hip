@@ -391,17 +391,18 @@ attn_decode_bf16_kernel(PoolDev pool, const bf16_t* __restrict__ q, bf16_t* __re
   const int v_voff = (l16 * bs + 4 * j4) * 2;                   // dim l16 of a 16-dim slab, 4 keys
   // block ids of the tile at k0 (-1: past the split or out of range)
   auto fetch_ids = [&](int k0, int (&ids)[2]) {
+    bool bad = false;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int key16 = k0 + 16 * h;
-      int blk = key16 < end ? table[key16 >> pool.bs_shift] : -1;
-      blk = __builtin_amdgcn_readfirstlane(blk);
-      if (key16 < end && (blk < 0 || blk >= pool.num_blocks)) {
-        if (lane == 0) flag_error(pool.err, PKV_ERRBIT_BLOCK_ID);
-        blk = -1;
-      }
-      ids[h] = blk;
+      const int blk = key16 < end ? table[key16 >> pool.bs_shift] : -1;
+      const bool ok = blk >= 0 && blk < pool.num_blocks;
+      bad |= key16 < end && !ok;
+      // the id is wave-uniform; saying so keeps the descriptors built from
+      // it in scalar registers
+      ids[h] = __builtin_amdgcn_readfirstlane(ok ? blk : -1);
     }
+    if (bad && lane == 0) flag_error(pool.err, PKV_ERRBIT_BLOCK_ID);
   };
   auto issue_k = [&](int k0, DecodeTile<D>& r) {
 #pragma unroll

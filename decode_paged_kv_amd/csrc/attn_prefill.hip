@@ -42,6 +42,9 @@ constexpr int kXcds = 8;
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+struct f32x16x2 {
+  f32x16_t v[2];
+};
 
 __device__ __forceinline__ f32x16_t mfma32(const uint4& a, const uint4& b, f32x16_t c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
@@ -58,21 +61,25 @@ __device__ __forceinline__ int key_perm(int m) {
 template <int D>
 struct PrefillCfg {
   static constexpr int BM = 128, BN = 64, THREADS = 256;
-  static constexpr int KS = D / 16;     // MFMA k-steps of q.k
-  static constexpr int DT = D / 32;     // 32-dim output tiles
-  static constexpr int KROW = D + 8;    // LDS K row stride (elements)
-  static constexpr int VROW = BN + 8;   // LDS V^T row stride (elements)
-  static constexpr int GROUPS = BN / 16;            // 16-key groups per tile (each inside one block)
-  static constexpr int KLANES = D / 8;              // lanes per K row in a group load
-  static constexpr int KACTIVE = 16 * KLANES;       // threads that load K rows of a group (256 for D=128)
-  static constexpr int SK = BN * KROW;              // one K buffer (elements)
-  static constexpr int SV = D * VROW;               // one V buffer
+  static constexpr int KS = D / 16;            // MFMA k-steps of q.k
+  static constexpr int DT = D / 32;            // 32-dim output tiles
+  static constexpr int KCH = D / 8;            // 16-byte chunks per K row
+  static constexpr int TILE = BN * D * 2;      // bytes of one K (or V) tile in LDS
+  static constexpr int KRPI = 1024 / (2 * D);  // K rows per 1 KB DMA instruction
+  static constexpr int NDMA = D / 32;          // DMA instructions per wave for its group's K (and V)
+  static constexpr int VGRP = D * 32;          // bytes of one 16-key group of the V tile
 };
 
 // Running max update rule: the max used for exp2 moves only when a tile's
 // max exceeds it by more than this (log2 units), so p <= 2^8 and the O
 // accumulators are rescaled rarely.
 constexpr float kRescaleSlack = 8.0f;
+
+__device__ __forceinline__ void lds_dma16(buffer_rsrc_t r, char* lds, int voffset, int soffset) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voffset, soffset, 0,
+                                           0);
+}
+__device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 template <int D>
 __global__ void __launch_bounds__(256, 2)
@@ -81,9 +88,12 @@ attn_prefill_bf16_kernel(PoolDev pool, const bf16_t* __restrict__ q, bf16_t* __r
                          const int32_t* __restrict__ chunk_start, int batch, int ntiles, int num_q_heads,
                          int group, float scale_log2, int total_items) {
   using C = PrefillCfg<D>;
-  // double-buffered K and V^T tiles
-  __shared__ __attribute__((aligned(16))) bf16_t sk[2 * C::SK];
-  __shared__ __attribute__((aligned(16))) bf16_t sv[2 * C::SV];
+  // double-buffered K and V tiles; four separate arrays so the compiler
+  // sees that a DMA into one buffer never overlaps reads of another
+  __shared__ __attribute__((aligned(1024))) char kb0[C::TILE];
+  __shared__ __attribute__((aligned(1024))) char kb1[C::TILE];
+  __shared__ __attribute__((aligned(1024))) char vb0[C::TILE];
+  __shared__ __attribute__((aligned(1024))) char vb1[C::TILE];
 
   // ---- work item (XCD-contiguous runs) ----
   const int per_xcd = gridDim.x / kXcds;
@@ -108,16 +118,16 @@ attn_prefill_bf16_kernel(PoolDev pool, const bf16_t* __restrict__ q, bf16_t* __r
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);    // wave-uniform (lets branches on it stay scalar)
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);    // wave-uniform
   const int half = lane >> 5, l32 = lane & 31;
   const int hl = pool.heads_per_shard;
   const int sh = kvh / hl, lh = kvh - sh * hl;
-  const bf16_t* kpool = reinterpret_cast<const bf16_t*>(pool.k[sh]);
-  const bf16_t* vpool = reinterpret_cast<const bf16_t*>(pool.v[sh]);
+  const char* kpool = reinterpret_cast<const char*>(pool.k[sh]);
+  const char* vpool = reinterpret_cast<const char*>(pool.v[sh]);
   const int bs = pool.block_size;
-  const size_t tile_stride = (size_t)bs * D;                     // elements per (block, head) tile
-  const size_t head_off = (size_t)lh * tile_stride;
-  const size_t block_stride = (size_t)hl * tile_stride;
+  const int tile_bytes = bs * D * 2;                            // one (block, head) tile
+  const size_t head_off = (size_t)lh * tile_bytes;
+  const size_t block_stride = (size_t)hl * tile_bytes;
   const int32_t* table = bt + (size_t)b * bt_stride;
 
   // ---- this lane's query row and its Q fragments (B operand of S^T) ----
@@ -132,70 +142,95 @@ attn_prefill_bf16_kernel(PoolDev pool, const bf16_t* __restrict__ q, bf16_t* __r
   }
   const int wave_first_q = S + qt * C::BM + wave * 32;
 
-  // ---- tile loader.  Group r of a tile is keys 16r..16r+15, which lie in one
-  // block: its block id is uniform, so each group is read through a buffer
-  // descriptor on that block's (block, head) tile and a lane adds only its
-  // fixed offset.  K: thread t loads row t / KLANES of the group, dims
-  // (t % KLANES) * 8 (threads >= KACTIVE idle for D = 64).  V: thread t loads
-  // dim t >> 1, keys 8 * (t & 1) of the dim-major tile.  A group with a bad
-  // block id (or wholly past the request) gets a zero-size descriptor, reads
-  // zeros, and its bit in the returned mask marks its keys absent. ----
-  const int k_row = tid / C::KLANES, k_col = (tid % C::KLANES) * 8;
-  const int k_row_perm = key_perm(k_row);     // LDS row of this key (key_perm is its own inverse)
-  const int v_dim = tid >> 1, v_key = (tid & 1) * 8;
-  const bool k_act = C::KACTIVE >= C::THREADS || tid < C::KACTIVE;
-  const bool v_act = 2 * D >= C::THREADS || v_dim < D;
-  const int k_voff = (k_row * D + k_col) * 2, v_voff = (v_dim * bs + v_key) * 2;   // bytes
-  const int tile_bytes = bs * D * 2;
-  uint4 rk[C::GROUPS], rv[C::GROUPS];
-  auto load_tile = [&](int kt) -> uint32_t {
-    const int kbase = kt * C::BN;
-    int blk[C::GROUPS];
+  // ---- tile loads: LDS DMA, wave w moves 16-key group w of K and of V ----
+  // K tile in LDS: row r holds key 32(r/32) + key_perm(r%32) (so that the
+  // accumulator registers a lane converts to bf16 are 8 consecutive keys);
+  // its 16-byte chunk c sits at position c ^ (r % KCH), so the MFMA's
+  // row-per-lane reads of one chunk hit distinct banks.  A DMA instruction
+  // fills KRPI whole rows (1 KB); lane t fetches the chunk that belongs at
+  // its slot.
+  int k_voff[C::NDMA];
 #pragma unroll
-    for (int r = 0; r < C::GROUPS; ++r) {
-      const int key16 = kbase + 16 * r;
-      blk[r] = key16 < kv_len ? __builtin_amdgcn_readfirstlane(table[key16 >> pool.bs_shift]) : -1;
+  for (int jj = 0; jj < C::NDMA; ++jj) {
+    const int r = C::KRPI * jj + lane / C::KCH;                 // row within the group (0..15)
+    const int c = (lane % C::KCH) ^ (r & (C::KCH - 1));
+    k_voff[jj] = (key_perm(r) * D + 8 * c) * 2;
+  }
+  // V tile in LDS: [group][dim][16 keys], the two 8-key halves of a dim row
+  // swapped when bit 2 of the dim is set (conflict-free reads of 8 dims).
+  // A DMA instruction fills 32 dims of one group.
+  int v_dim[C::NDMA], v_kh[C::NDMA];
+#pragma unroll
+  for (int jj = 0; jj < C::NDMA; ++jj) {
+    v_dim[jj] = 32 * jj + (lane >> 1);
+    v_kh[jj] = (lane & 1) ^ ((v_dim[jj] >> 2) & 1);
+  }
+  // block ids of tile kt's 4 groups; returns the bits of the absent groups
+  // and this wave's block id in *blk_own
+  auto tile_ids = [&](int kt, int* blk_own) -> uint32_t {
+    uint32_t absent = 0, bad = 0;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int key16 = kt * C::BN + 16 * r;
+      int blk = key16 < kv_len ? table[key16 >> pool.bs_shift] : -1;
+      const bool ok = blk >= 0 && blk < pool.num_blocks;
+      if (!ok) absent |= 1u << r;
+      if (!ok && key16 < kv_len) bad |= 1u << r;
+      // the id is wave-uniform; saying so keeps the descriptors built from
+      // it in scalar registers
+      if (r == wave) *blk_own = __builtin_amdgcn_readfirstlane(ok ? blk : -1);
     }
-    uint32_t absent = 0;
-#pragma unroll
-    for (int r = 0; r < C::GROUPS; ++r) {
-      const int key16 = kbase + 16 * r;
-      const bool ok = blk[r] >= 0 && blk[r] < pool.num_blocks;      // uniform
-      if (!ok) {
-        absent |= 1u << r;
-        if (key16 < kv_len && tid == 0) flag_error(pool.err, PKV_ERRBIT_BLOCK_ID);
-      }
-      const size_t tbase = ok ? (size_t)blk[r] * block_stride + head_off : 0;
-      const int off = key16 & (bs - 1);
-      const buffer_rsrc_t rsk = buffer_rsrc(kpool + tbase, ok ? tile_bytes : 0);
-      const buffer_rsrc_t rsv = buffer_rsrc(vpool + tbase, ok ? tile_bytes : 0);
-      if (k_act) rk[r] = buffer_load16(rsk, k_voff, off * D * 2);
-      if (v_act) rv[r] = buffer_load16(rsv, v_voff, off * 2);
-    }
-    // the request's last tile: keys past kv_len hold arbitrary bits; their
-    // scores are masked by causality, their V entries must be zero (p = 0
-    // times a NaN pattern would still poison the sum)
-    if (kbase + C::BN > kv_len && v_act) {
-#pragma unroll
-      for (int r = 0; r < C::GROUPS; ++r) {
-        const int nvalid = kv_len - (kbase + 16 * r) - v_key;
-        uint32_t* w = reinterpret_cast<uint32_t*>(&rv[r]);
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          if (e >= nvalid) w[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
-      }
-    }
-    return absent;
+    if (((bad >> wave) & 1) && lane == 0) flag_error(pool.err, PKV_ERRBIT_BLOCK_ID);
+    return __builtin_amdgcn_readfirstlane(absent);
   };
-  auto store_tile = [&](int buf) {
-    bf16_t* kb = sk + buf * C::SK;
-    bf16_t* vb = sv + buf * C::SV;
+  auto dma_k = [&](int kt, char* kbuf, int blk) {
+    const int key16 = kt * C::BN + 16 * wave;
+    const bool ok = blk >= 0;
+    const buffer_rsrc_t rs = buffer_rsrc(kpool + (ok ? (size_t)blk * block_stride + head_off : 0), ok ? tile_bytes : 0);
+    const int soff = (key16 & (bs - 1)) * D * 2;
+    char* dst = kbuf + (16 * wave) * 2 * D;
 #pragma unroll
-    for (int r = 0; r < C::GROUPS; ++r) {
-      if (k_act) *reinterpret_cast<uint4*>(&kb[(16 * r + k_row_perm) * C::KROW + k_col]) = rk[r];
-      if (v_act) *reinterpret_cast<uint4*>(&vb[v_dim * C::VROW + 16 * r + v_key]) = rv[r];
+    for (int jj = 0; jj < C::NDMA; ++jj) lds_dma16(rs, dst + jj * 1024, k_voff[jj], soff);
+  };
+  auto dma_v = [&](int kt, char* vbuf, int blk) {
+    const int key16 = kt * C::BN + 16 * wave;
+    const bool ok = blk >= 0;
+    const buffer_rsrc_t rs = buffer_rsrc(vpool + (ok ? (size_t)blk * block_stride + head_off : 0), ok ? tile_bytes : 0);
+    const int soff = (key16 & (bs - 1)) * 2;
+    char* dst = vbuf + wave * C::VGRP;
+#pragma unroll
+    for (int jj = 0; jj < C::NDMA; ++jj) {
+      // an 8-key half wholly past the request reads zeros (out of range)
+      const bool past = key16 + 8 * v_kh[jj] >= kv_len;
+      lds_dma16(rs, dst + jj * 1024, past ? 0x40000000 : (v_dim[jj] * bs + 8 * v_kh[jj]) * 2, soff);
     }
   };
+  // the request's last tile: V entries of keys in [kv_len, next multiple of
+  // 8) sit in the same 16 bytes as valid keys and hold arbitrary bits; the
+  // wave that loaded them zeroes them (p = 0 times a NaN pattern is NaN)
+  auto fix_tail = [&](int kt, char* vbuf) {
+    const int rel = kv_len - kt * C::BN;                        // valid keys in this tile
+    if (rel >= C::BN || (rel & 7) == 0 || (rel >> 4) != wave) return;
+    const int kh = (rel >> 3) & 1, e0 = rel & 7;
+    char* base = vbuf + wave * C::VGRP;
+    for (int d = lane; d < D; d += 64) {
+      uint4* p = reinterpret_cast<uint4*>(base + d * 32 + ((kh ^ ((d >> 2) & 1)) << 4));
+      uint4 v = *p;
+      uint32_t* w = reinterpret_cast<uint32_t*>(&v);
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (e >= e0) w[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
+      *p = v;
+    }
+  };
+
+  // ---- LDS read addresses ----
+  // K: row 32i + l32, chunk 2s + half at position (2s + half) ^ (l32 % KCH):
+  // address = kx ^ 32s ^ (32 rows * i), XORs of disjoint bits with a
+  // per-lane constant
+  const int kx = l32 * 2 * D + (((half ^ (l32 & (C::KCH - 1))) & 1) << 4) + (((l32 & (C::KCH - 1)) >> 1) << 5);
+  // V: dim 32t + l32, keys 32i + 16sp + 8half -> group 2i + sp, half `half`
+  const int vx = l32 * 32 + ((half ^ ((l32 >> 2) & 1)) << 4);
 
   f32x16_t o[C::DT];
 #pragma unroll
@@ -203,81 +238,107 @@ attn_prefill_bf16_kernel(PoolDev pool, const bf16_t* __restrict__ q, bf16_t* __r
   // running max (log2 units): finite start, so a tile whose keys are all
   // masked or absent gives p = exp2(-inf) = 0 rather than exp2(-inf + inf)
   float m = -1e30f, lsum = 0.f;
+  constexpr uint32_t kOnes = 0x3F803F80u;                       // bf16 (1, 1)
 
-  const int nkt = (kend + C::BN - 1) / C::BN;
-  uint32_t absent = load_tile(0);
-  store_tile(0);
-  __syncthreads();
-  for (int kt = 0; kt < nkt; ++kt) {
-    const int buf = kt & 1;
-    uint32_t absent_next = 0;
-    if (kt + 1 < nkt) absent_next = load_tile(kt + 1);   // in flight during this tile's math
-    const bf16_t* kb = sk + buf * C::SK;
-    const bf16_t* vb = sv + buf * C::SV;
-    const int kbase = kt * C::BN;
-    // ---- S^T = K Q^T over two 32-key halves ----
-    // all K fragments are read before the first MFMA so the LDS latency is
-    // paid once per tile, not once per MFMA
-    f32x16_t st[2];
+  auto qk = [&](const char* kbuf) -> f32x16x2 {
+    f32x16x2 st;
     uint4 kf[2][C::KS];
 #pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int s = 0; s < C::KS; ++s)
+        kf[i][s] = *reinterpret_cast<const uint4*>(kbuf + (kx ^ (32 * s) ^ (i * 32 * 2 * D)));
+#pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const bf16_t* krow = &kb[(32 * i + l32) * C::KROW + 8 * half];
+      st.v[i] = f32x16_t{};
 #pragma unroll
-      for (int s = 0; s < C::KS; ++s) kf[i][s] = *reinterpret_cast<const uint4*>(krow + 16 * s);
+      for (int s = 0; s < C::KS; ++s) st.v[i] = mfma32(kf[i][s], qf[s], st.v[i]);
     }
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      st[i] = f32x16_t{};
-#pragma unroll
-      for (int s = 0; s < C::KS; ++s) st[i] = mfma32(kf[i][s], qf[s], st[i]);
-    }
-    // schedule: 8 reads ahead, then one read behind each MFMA
-    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
-#pragma unroll
-    for (int j = 0; j < 2 * C::KS - 8; ++j) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
-    // ---- causal mask (only where the tile reaches past this wave's first query) ----
+    return st;
+  };
+
+  const int nkt = (kend + C::BN - 1) / C::BN;
+  // prologue: K(0), K(1), V(0); S(0)
+  int blk0 = -1, blk1 = -1;
+  uint32_t absent_cur = tile_ids(0, &blk0);
+  dma_k(0, kb0, blk0);
+  dma_v(0, vb0, blk0);
+  uint32_t absent_next = 0;
+  int blk_next = -1;
+  if (nkt > 1) {
+    absent_next = tile_ids(1, &blk1);
+    dma_k(1, kb1, blk1);
+    blk_next = blk1;
+  }
+  wait_dma();
+  __syncthreads();
+  f32x16x2 sa = qk(kb0), sb;
+
+  // one key tile: st = S(kt) on entry; S(kt+1) goes to stn.  kcur holds
+  // K(kt) (free after the barrier, refilled with K(kt+2)), knext K(kt+1),
+  // vcur V(kt), vnext the buffer V(kt+1) goes to.
+  auto step = [&](int kt, char* kcur, const char* knext, const char* vcur, char* vnext, f32x16x2& st,
+                  f32x16x2& stn) {
+    const int kbase = kt * C::BN;
+    // ---- softmax statistics of S(kt) (registers only): masks for causality
+    // (tiles reaching past this wave's first query) and absent groups, the
+    // row max, the rare rescale of O ----
     if (kbase + C::BN - 1 > wave_first_q) {
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = kbase + 32 * i + 16 * (r >> 3) + 8 * half + (r & 7);
-          if (key > qpos) st[i][r] = -INFINITY;
-        }
-    }
-    // ---- keys of groups with a bad block id are absent ----
-    if (absent) {
+      // an opaque copy keeps the compares inside this branch (hoisted, they
+      // would run on every tile)
+      int d;
+      asm volatile("v_mov_b32 %0, %1" : "=v"(d) : "v"(qpos - kbase - 8 * half));
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          if ((absent >> (2 * i + (r >> 3))) & 1) st[i][r] = -INFINITY;
+          if (32 * i + 16 * (r >> 3) + (r & 7) > d) st.v[i][r] = -INFINITY;
     }
-    // ---- online softmax for query l32 (keys split over lanes l and l^32) ----
+    if (absent_cur) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if ((absent_cur >> (2 * i + (r >> 3))) & 1) st.v[i][r] = -INFINITY;
+    }
     float mx = -INFINITY;
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(st[i][r], st[i][r + 1]));
-    mx = fmaxf(mx, __shfl_xor(mx, 32)) * scale_log2;
+      for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(st.v[i][r], st.v[i][r + 1]));
+    {
+      auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+      mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * scale_log2;
+    }
     // move the running max only when this tile exceeds it by the slack
     const bool grow = mx > m + kRescaleSlack;
-    if (__builtin_amdgcn_ballot_w64(grow)) {         // wave-uniform branch
+    if (__builtin_amdgcn_ballot_w64(grow)) {                    // wave-uniform, rare
       const float mnew = grow ? mx : m;
-      const float alpha = __builtin_amdgcn_exp2f(m - mnew);     // 0 on the first tile
+      const float alpha = __builtin_amdgcn_exp2f(m - mnew);    // 0 on the first growth
       m = mnew;
       lsum *= alpha;
 #pragma unroll
       for (int t = 0; t < C::DT; ++t) o[t] *= alpha;
     }
+
+    // ---- K(kt+1) and V(kt) were moved by this wave's DMA one step ago ----
+    wait_dma();
+    fix_tail(kt, const_cast<char*>(vcur));
+    __syncthreads();
+    // every wave is past step kt-1: K(kt)'s buffer and V(kt-1)'s are free
+    uint32_t absent_after = 0;
+    int blk2 = -1;
+    if (kt + 2 < nkt) {
+      absent_after = tile_ids(kt + 2, &blk2);
+      dma_k(kt + 2, kcur, blk2);
+    }
+    if (kt + 1 < nkt) dma_v(kt + 1, vnext, blk_next);
+
+    // ---- one branch-free block: S(kt+1) on the matrix cores while P(kt) is
+    // formed, then O^T += V^T P^T ----
+    stn = qk(knext);
     // p in bf16 (the MFMA operand); the row sum adds those same rounded
     // values, two per v_dot2 against (1, 1)
-    constexpr uint32_t kOnes = 0x3F803F80u;
     float psum[2] = {0.f, 0.f};
     uint4 pf[2][2];
 #pragma unroll
@@ -286,7 +347,7 @@ attn_prefill_bf16_kernel(PoolDev pool, const bf16_t* __restrict__ q, bf16_t* __r
       for (int sp = 0; sp < 2; ++sp) {
         float p[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) p[e] = __builtin_amdgcn_exp2f(fmaf(st[i][8 * sp + e], scale_log2, -m));
+        for (int e = 0; e < 8; ++e) p[e] = __builtin_amdgcn_exp2f(fmaf(st.v[i][8 * sp + e], scale_log2, -m));
         pf[i][sp] = make_uint4(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
                                pack_bf16x2(p[6], p[7]));
         psum[sp] = dot2_bf16(pf[i][sp].x, kOnes, psum[sp]);
@@ -295,20 +356,38 @@ attn_prefill_bf16_kernel(PoolDev pool, const bf16_t* __restrict__ q, bf16_t* __r
         psum[sp] = dot2_bf16(pf[i][sp].w, kOnes, psum[sp]);
       }
     lsum += psum[0] + psum[1];
-    // ---- O^T += V^T P^T ----
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int sp = 0; sp < 2; ++sp) {
+      for (int sp = 0; sp < 2; ++sp)
 #pragma unroll
         for (int t = 0; t < C::DT; ++t) {
-          const uint4 va = *reinterpret_cast<const uint4*>(&vb[(32 * t + l32) * C::VROW + 32 * i + 16 * sp + 8 * half]);
+          const uint4 va = *reinterpret_cast<const uint4*>(vcur + vx + (2 * i + sp) * C::VGRP + t * 1024);
           o[t] = mfma32(va, pf[i][sp], o[t]);
         }
-      }
-    if (kt + 1 < nkt) store_tile(buf ^ 1);           // the other buffer was last read before the previous barrier
-    absent = absent_next;
-    __syncthreads();
+    // schedule of the block: K fragments 8 ahead; each S MFMA with one LDS
+    // read and a share of the softmax arithmetic; then each P V MFMA with
+    // one V read
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+    for (int j = 0; j < 2 * C::KS; ++j) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < 4 * C::DT; ++j) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+    }
+    absent_cur = absent_next;
+    absent_next = absent_after;
+    blk_next = blk2;
+  };
+  for (int kt = 0; kt < nkt; kt += 2) {
+    step(kt, kb0, kb1, vb0, vb1, sa, sb);
+    if (kt + 1 < nkt) step(kt + 1, kb1, kb0, vb1, vb0, sb, sa);
   }
 
   // ---- normalise and store: lane holds dims 32t + 8a + 4*half + 0..3 of its query ----
