@@ -81,8 +81,12 @@ __device__ __forceinline__ void lds_dma16(buffer_rsrc_t r, char* lds, int voffse
 }
 __device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-template <int D>
-__global__ void __launch_bounds__(256, 2)
+// NG = key-tile groups per workgroup.  NG = 1: 4 waves, two workgroups per
+// CU.  NG = 2 (small grids): 8 waves in two groups of 4 that share the
+// queries and walk alternate key tiles with their own buffers, merging
+// their (m, l, O) through LDS at the end; one workgroup per CU.
+template <int D, int NG>
+__global__ void __launch_bounds__(256 * NG, 2 / NG)
 attn_prefill_bf16_kernel(PoolDev pool, const bf16_t* __restrict__ q, bf16_t* __restrict__ out,
                          const int32_t* __restrict__ bt, int bt_stride, const int32_t* __restrict__ start_loc,
                          const int32_t* __restrict__ chunk_start, int batch, int ntiles, int num_q_heads,
@@ -90,10 +94,10 @@ attn_prefill_bf16_kernel(PoolDev pool, const bf16_t* __restrict__ q, bf16_t* __r
   using C = PrefillCfg<D>;
   // double-buffered K and V tiles; four separate arrays so the compiler
   // sees that a DMA into one buffer never overlaps reads of another
-  __shared__ __attribute__((aligned(1024))) char kb0[C::TILE];
-  __shared__ __attribute__((aligned(1024))) char kb1[C::TILE];
-  __shared__ __attribute__((aligned(1024))) char vb0[C::TILE];
-  __shared__ __attribute__((aligned(1024))) char vb1[C::TILE];
+  __shared__ __attribute__((aligned(1024))) char kb0[NG][C::TILE];
+  __shared__ __attribute__((aligned(1024))) char kb1[NG][C::TILE];
+  __shared__ __attribute__((aligned(1024))) char vb0[NG][C::TILE];
+  __shared__ __attribute__((aligned(1024))) char vb1[NG][C::TILE];
 
   // ---- work item (XCD-contiguous runs) ----
   const int per_xcd = gridDim.x / kXcds;
@@ -118,7 +122,8 @@ attn_prefill_bf16_kernel(PoolDev pool, const bf16_t* __restrict__ q, bf16_t* __r
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);    // wave-uniform
+  const int wave8 = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
+  const int grp = wave8 >> 2, wave = wave8 & 3;                 // key-tile group, wave within it
   const int half = lane >> 5, l32 = lane & 31;
   const int hl = pool.heads_per_shard;
   const int sh = kvh / hl, lh = kvh - sh * hl;
@@ -258,32 +263,41 @@ attn_prefill_bf16_kernel(PoolDev pool, const bf16_t* __restrict__ q, bf16_t* __r
   };
 
   const int nkt = (kend + C::BN - 1) / C::BN;
-  // prologue: K(0), K(1), V(0); S(0)
+  char* const k0b = kb0[grp];
+  char* const k1b = kb1[grp];
+  char* const v0b = vb0[grp];
+  char* const v1b = vb1[grp];
+  // prologue: this group's first two K tiles and first V tile; its first S
   int blk0 = -1, blk1 = -1;
-  uint32_t absent_cur = tile_ids(0, &blk0);
-  dma_k(0, kb0, blk0);
-  dma_v(0, vb0, blk0);
-  uint32_t absent_next = 0;
+  uint32_t absent_cur = 0, absent_next = 0;
   int blk_next = -1;
-  if (nkt > 1) {
-    absent_next = tile_ids(1, &blk1);
-    dma_k(1, kb1, blk1);
+  if (grp < nkt) {
+    absent_cur = tile_ids(grp, &blk0);
+    dma_k(grp, k0b, blk0);
+    dma_v(grp, v0b, blk0);
+  }
+  if (grp + NG < nkt) {
+    absent_next = tile_ids(grp + NG, &blk1);
+    dma_k(grp + NG, k1b, blk1);
     blk_next = blk1;
   }
   wait_dma();
   __syncthreads();
-  f32x16x2 sa = qk(kb0), sb;
+  f32x16x2 sa = qk(k0b), sb;
 
-  // one key tile: st = S(kt) on entry; S(kt+1) goes to stn.  kcur holds
-  // K(kt) (free after the barrier, refilled with K(kt+2)), knext K(kt+1),
-  // vcur V(kt), vnext the buffer V(kt+1) goes to.
+  // one key tile of this group: st = S(kt) on entry; S(kt+NG), the group's
+  // next tile, goes to stn.  kcur holds K(kt) (free after the barrier,
+  // refilled with K(kt+2NG)), knext K(kt+NG), vcur V(kt), vnext the buffer
+  // V(kt+NG) goes to.  A step past the group's last tile only keeps the
+  // barrier count equal across the groups.
   auto step = [&](int kt, char* kcur, const char* knext, const char* vcur, char* vnext, f32x16x2& st,
                   f32x16x2& stn) {
+    const bool live = kt < nkt;
     const int kbase = kt * C::BN;
     // ---- softmax statistics of S(kt) (registers only): masks for causality
     // (tiles reaching past this wave's first query) and absent groups, the
     // row max, the rare rescale of O ----
-    if (kbase + C::BN - 1 > wave_first_q) {
+    if (live && kbase + C::BN - 1 > wave_first_q) {
       // an opaque copy keeps the compares inside this branch (hoisted, they
       // would run on every tile)
       int d;
@@ -294,7 +308,7 @@ attn_prefill_bf16_kernel(PoolDev pool, const bf16_t* __restrict__ q, bf16_t* __r
         for (int r = 0; r < 16; ++r)
           if (32 * i + 16 * (r >> 3) + (r & 7) > d) st.v[i][r] = -INFINITY;
     }
-    if (absent_cur) {
+    if (live && absent_cur) {
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -311,7 +325,7 @@ attn_prefill_bf16_kernel(PoolDev pool, const bf16_t* __restrict__ q, bf16_t* __r
       mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * scale_log2;
     }
     // move the running max only when this tile exceeds it by the slack
-    const bool grow = mx > m + kRescaleSlack;
+    const bool grow = live && mx > m + kRescaleSlack;
     if (__builtin_amdgcn_ballot_w64(grow)) {                    // wave-uniform, rare
       const float mnew = grow ? mx : m;
       const float alpha = __builtin_amdgcn_exp2f(m - mnew);    // 0 on the first growth
@@ -321,20 +335,22 @@ attn_prefill_bf16_kernel(PoolDev pool, const bf16_t* __restrict__ q, bf16_t* __r
       for (int t = 0; t < C::DT; ++t) o[t] *= alpha;
     }
 
-    // ---- K(kt+1) and V(kt) were moved by this wave's DMA one step ago ----
+    // ---- K(kt+NG) and V(kt) were moved by this wave's DMA one step ago ----
     wait_dma();
-    fix_tail(kt, const_cast<char*>(vcur));
+    if (live) fix_tail(kt, const_cast<char*>(vcur));
     __syncthreads();
-    // every wave is past step kt-1: K(kt)'s buffer and V(kt-1)'s are free
+    // every wave is past the previous step: K(kt)'s buffer and the buffer of
+    // V(kt-NG) are free
     uint32_t absent_after = 0;
     int blk2 = -1;
-    if (kt + 2 < nkt) {
-      absent_after = tile_ids(kt + 2, &blk2);
-      dma_k(kt + 2, kcur, blk2);
+    if (kt + 2 * NG < nkt) {
+      absent_after = tile_ids(kt + 2 * NG, &blk2);
+      dma_k(kt + 2 * NG, kcur, blk2);
     }
-    if (kt + 1 < nkt) dma_v(kt + 1, vnext, blk_next);
+    if (kt + NG < nkt) dma_v(kt + NG, vnext, blk_next);
+    if (!live) return;
 
-    // ---- one branch-free block: S(kt+1) on the matrix cores while P(kt) is
+    // ---- one branch-free block: S(kt+NG) on the matrix cores while P(kt) is
     // formed, then O^T += V^T P^T ----
     stn = qk(knext);
     // p in bf16 (the MFMA operand); the row sum adds those same rounded
@@ -385,9 +401,37 @@ attn_prefill_bf16_kernel(PoolDev pool, const bf16_t* __restrict__ q, bf16_t* __r
     absent_next = absent_after;
     blk_next = blk2;
   };
-  for (int kt = 0; kt < nkt; kt += 2) {
-    step(kt, kb0, kb1, vb0, vb1, sa, sb);
-    if (kt + 1 < nkt) step(kt + 1, kb1, kb0, vb1, vb0, sb, sa);
+  // every group takes the same number of steps (one barrier each)
+  const int nsteps = (nkt + NG - 1) / NG;
+  for (int u = 0; u < nsteps; u += 2) {
+    step(grp + NG * u, k0b, k1b, v0b, v1b, sa, sb);
+    if (u + 1 < nsteps) step(grp + NG * (u + 1), k1b, k0b, v1b, v0b, sb, sa);
+  }
+
+  if constexpr (NG == 2) {
+    // ---- merge group 1's (m, l, O) into group 0's, lane by lane (both
+    // groups hold the same queries in the same layout) ----
+    float* const ox = reinterpret_cast<float*>(wave < 2 ? &kb0[0][0] : &kb1[0][0]) + (wave & 1) * (16 * C::DT * 64);
+    float* const mlx = reinterpret_cast<float*>(&vb0[0][0]) + wave * 128;
+    __syncthreads();                                            // all buffers free
+    if (grp == 1) {
+#pragma unroll
+      for (int t = 0; t < C::DT; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) ox[(16 * t + r) * 64 + lane] = o[t][r];
+      mlx[lane] = m;
+      mlx[64 + lane] = lsum;
+    }
+    __syncthreads();
+    if (grp == 1) return;
+    const float m1 = mlx[lane], l1 = mlx[64 + lane];
+    const float mn = fmaxf(m, m1);
+    const float a0 = __builtin_amdgcn_exp2f(m - mn), a1 = __builtin_amdgcn_exp2f(m1 - mn);
+    lsum = lsum * a0 + l1 * a1;
+#pragma unroll
+    for (int t = 0; t < C::DT; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[t][r] = o[t][r] * a0 + ox[(16 * t + r) * 64 + lane] * a1;
   }
 
   // ---- normalise and store: lane holds dims 32t + 8a + 4*half + 0..3 of its query ----
@@ -479,14 +523,21 @@ hipError_t launch_attn_prefill(const PoolDev& pool, int dtype, const void* q, vo
     const int ntiles = (max_chunk_len + BM - 1) / BM;
     const int items = pool.num_kv_heads * ntiles * group * batch;
     const int grid = (items + kXcds - 1) / kXcds * kXcds;
-    if (pool.head_dim == 128)
-      hipLaunchKernelGGL(attn_prefill_bf16_kernel<128>, dim3(grid), dim3(256), 0, s, pool,
-                         static_cast<const bf16_t*>(q), static_cast<bf16_t*>(out), bt, bt_stride, start_loc,
-                         chunk_start, batch, ntiles, num_q_heads, group, sl2, items);
-    else
-      hipLaunchKernelGGL(attn_prefill_bf16_kernel<64>, dim3(grid), dim3(256), 0, s, pool,
-                         static_cast<const bf16_t*>(q), static_cast<bf16_t*>(out), bt, bt_stride, start_loc,
-                         chunk_start, batch, ntiles, num_q_heads, group, sl2, items);
+    // fewer than two 4-wave workgroups per CU (256 CUs): split each
+    // workgroup's key tiles over two groups of 4 waves instead
+    const bool split = items < 512;
+#define PKV_PREFILL_LAUNCH(DD, NG)                                                                               \
+    hipLaunchKernelGGL((attn_prefill_bf16_kernel<DD, NG>), dim3(grid), dim3(256 * NG), 0, s, pool,                \
+                       static_cast<const bf16_t*>(q), static_cast<bf16_t*>(out), bt, bt_stride, start_loc,       \
+                       chunk_start, batch, ntiles, num_q_heads, group, sl2, items)
+    if (pool.head_dim == 128) {
+      if (split) PKV_PREFILL_LAUNCH(128, 2);
+      else PKV_PREFILL_LAUNCH(128, 1);
+    } else {
+      if (split) PKV_PREFILL_LAUNCH(64, 2);
+      else PKV_PREFILL_LAUNCH(64, 1);
+    }
+#undef PKV_PREFILL_LAUNCH
     return hipGetLastError();
   }
   const dim3 grid((max_chunk_len + 3) / 4, num_q_heads, batch);

@@ -103,6 +103,7 @@ def run_prefill_chunks(sc: Scenario, q_np, chunk, req=0):
     ("f32", 4, 2, 64, 16, 256, 64),          # the tiny check: 4 causal chunks of 64
     ("bf16", 32, 8, 128, 16, 1024, 512),     # Llama-3-8B shape, 2 chunks of 512 (all rows)
     ("bf16", 32, 8, 128, 16, 1024, 1024),    # same prompt one-shot
+    ("bf16", 64, 8, 128, 16, 1100, 1100),    # >= 512 workgroups: one key-tile group per workgroup
     ("bf16", 8, 2, 128, 16, 300, 77),        # ragged chunks and tail
     ("bf16", 16, 1, 64, 32, 517, 200),       # G = 16, head dim 64
     ("bf16", 4, 4, 128, 64, 130, 130),       # G = 1, one chunk of 130
