@@ -20,6 +20,8 @@ Workloads (all synthetic, seeded, resident in HBM before timing):
   ``value`` is relayout HBM GB/s (read + write).
 * ``pdmux``: the PD-multiplexing round (see ``bench_pdmux``).  ``value`` is
   the multiplexed decode step in ms.
+* ``copy-1gib``: a plain 1 GiB device copy, the known-size kernel that
+  calibrates the FETCH_SIZE / WRITE_SIZE counters behind ``traffic``.
 
 One JSON line is printed.  Kernel times come from HIP events recorded on
 the stream the kernels are launched on.
@@ -28,6 +30,7 @@ the stream the kernels are launched on.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -60,6 +63,44 @@ def prefill_flops(hq, d, t, s):
 def relayout_bytes(n, hkv, d, esize=2):
     """HBM traffic of one layer's relayout: the K/V payload read once and written once."""
     return 2 * n * 2 * hkv * d * esize
+
+
+# ------------------------------------------------------------ traffic ----
+# HBM bytes of each roofline kernel, from two rocprofv3 --pmc runs of this
+# script's own workload (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch,
+# mean over the dispatches of one run), scaled by what the same counters
+# read for a plain 1 GiB copy (torch copy_): FETCH_SIZE reads 0.5 GiB for
+# 1 GiB fetched, WRITE_SIZE 1.0 GiB for 1 GiB written.  Each entry holds the
+# SHA-256 of the sources the kernel is built from when the counters were
+# taken; once they differ the figure no longer describes the kernel and
+# `traffic` is reported as null.  Commands and per-kernel tables are in the
+# profiles/ summaries named for each kernel and workload.
+PMC_SCALE = {"fetch": 2.0, "write": 1.0}
+TRAFFIC = {
+    "attn_decode": {"sources": ['decode_paged_kv_amd/csrc/attn_decode.hip', 'decode_paged_kv_amd/csrc/pkv_internal.h'],
+                    "sha256": "fe06fc0946fb32efb574f5b6e8b49d36999dfa21906de3405f0fd391b0db193c",
+                    "fetch_kib": 66245.56, "write_kib": 512.0},
+    "attn_prefill_chunk": {"sources": ['decode_paged_kv_amd/csrc/attn_prefill.hip', 'decode_paged_kv_amd/csrc/pkv_internal.h'],
+                           "sha256": "a3b2e0b2f08944e6ad638663c0475dba892064673af0a632c045f6af1127c506",
+                           "fetch_kib": 27435.1, "write_kib": 13107.2},
+    "kv_relayout": {"sources": ['decode_paged_kv_amd/csrc/kv_ops.hip', 'decode_paged_kv_amd/csrc/pkv_internal.h'],
+                    "sha256": "ff9075f7713c947e70195c2629ec7733a0a631560f9298edab78b0b71b23b201",
+                    "fetch_kib": 8234.91, "write_kib": 16388.17},
+}
+
+
+def traffic_bytes(kernel):
+    """Measured HBM bytes per launch of `kernel`, or None if its sources changed since the counters were taken."""
+    e = TRAFFIC.get(kernel)
+    if e is None:
+        return None
+    h = hashlib.sha256()
+    for f in e["sources"]:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    if h.hexdigest() != e["sha256"]:
+        return None
+    return int(round(1024 * (e["fetch_kib"] * PMC_SCALE["fetch"] + e["write_kib"] * PMC_SCALE["write"])))
 
 
 # ------------------------------------------------------------- helpers ----
@@ -226,7 +267,8 @@ def bench_llama3_8b(args):
                                "over 32 back-to-back launches)"},
         "roofline": {"kernel": "attn_decode", "bound": "hbm", "achieved": round(dec_gbps, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(dec_gbps / HBM_PEAK_GBPS, 4),
-                     "traffic": None, "bytes_per_launch": dbytes, "launch_ms": round(dec_launch_ms, 5)},
+                     "traffic": traffic_bytes("attn_decode"), "bytes_per_launch": dbytes,
+                     "launch_ms": round(dec_launch_ms, 5)},
         "metrics": {
             "decode_attn_gbps": round(dec_gbps, 1),
             "decode_step_ms": round(t["decode_step"], 4),
@@ -356,7 +398,7 @@ def bench_qwen3_32b(args):
                                "back-to-back prefill launches)"},
         "roofline": {"kernel": "attn_prefill_chunk", "bound": "mfma", "achieved": round(tflops, 2),
                      "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tflops / BF16_PEAK_TFLOPS, 4),
-                     "traffic": None, "flops_per_step": tot_flops,
+                     "traffic": traffic_bytes("attn_prefill_chunk"), "flops_per_step": tot_flops,
                      "launch_ms": round(tot_ms / sum(L * len(p) for p in plans.values()), 5)},
         "metrics": {
             "decode_attn_gbps": round(dec_gbps, 1), "decode_attn_frac_hbm": round(dec_gbps / HBM_PEAK_GBPS, 4),
@@ -429,7 +471,8 @@ def bench_relayout_70b(args):
                    "value_is": "relayout HBM GB/s = 2 x payload / time of the 80 back-to-back calls"},
         "roofline": {"kernel": "kv_relayout", "bound": "hbm", "achieved": round(gbps, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4),
-                     "traffic": None, "bytes_per_launch": per_layer, "launch_ms": round(launch_ms, 5)},
+                     "traffic": traffic_bytes("kv_relayout"), "bytes_per_launch": per_layer,
+                     "launch_ms": round(launch_ms, 5)},
         "metrics": {"relayout_gbps": round(gbps, 1), "relayout_frac_hbm": round(gbps / HBM_PEAK_GBPS, 4),
                     "relayout_launch_ms": round(launch_ms, 5)},
     }
@@ -600,6 +643,7 @@ def bench_pdmux(args):
     mux.close()
     solo_med = float(np.median(A))
     mux_med = float(np.median(B16))
+    dstep_bytes = decode_bytes([ctx] * B, hkv, d, hq) * L
     result = {
         "metric": METRIC, "value": round(mux_med, 3), "unit": "ms", "n_gpus": 1, "steps": len(B16),
         "warmup": args.warmup, "ms_per_step": round(mux_med, 3), "higher_is_better": False, "scaling": "weak",
@@ -610,6 +654,12 @@ def bench_pdmux(args):
                    "level_32k": [f"{groups[x][0]}:{groups[x][1]}" for x in lv32],
                    "value_is": "median decode step (32 layers: kv_write + attn_decode) wall time per round while the "
                                "16K prefill runs"},
+        "roofline": {"kernel": "attn_decode (decode step under multiplexing)", "bound": "hbm",
+                     "achieved": round(dstep_bytes / (mux_med * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(dstep_bytes / (mux_med * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "bytes_per_step": dstep_bytes,
+                     "note": "decode K/V + q/out bytes of the 32-layer step over its median wall time (host "
+                             "clock around each round, kv_write launches included)"},
         "metrics": {
             "solo_decode": stats(A),
             "mux_16k_decode": stats(B16), "mux_16k_prefill_ms": round(pf16, 2),
@@ -625,9 +675,35 @@ def bench_pdmux(args):
     return result
 
 
+# --------------------------------------------------------- copy-1gib ----
+def bench_copy_1gib(args):
+    """A plain device copy of 1 GiB (torch copy_), the reference kernel for reading the
+    FETCH_SIZE / WRITE_SIZE counters: its bytes read and written are known exactly."""
+    n = 1 << 30
+    src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(max(1, args.warmup)):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(args.steps):
+        dst.copy_(src)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / args.steps
+    gbps = 2 * n / (ms * 1e-3) / 1e9
+    return {"metric": "device copy GB/s (read + write)", "value": round(gbps, 1), "unit": "GB/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+            "config": {"workload": "copy-1gib: torch copy_ of 1 GiB, the calibration kernel for the HBM counters"},
+            "roofline": {"kernel": "copy", "bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS,
+                         "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": 2 * n}}
+
+
 # --------------------------------------------------------------- main ----
 BENCHES = {"llama3-8b": bench_llama3_8b, "qwen3-32b": bench_qwen3_32b, "relayout-70b": bench_relayout_70b,
-           "pdmux": bench_pdmux}
+           "pdmux": bench_pdmux, "copy-1gib": bench_copy_1gib}
 
 
 def main():
