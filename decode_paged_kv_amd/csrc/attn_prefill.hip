@@ -170,23 +170,59 @@ attn_prefill_bf16_kernel(PoolDev pool, const bf16_t* __restrict__ q, bf16_t* __r
     v_dim[jj] = 32 * jj + (lane >> 1);
     v_kh[jj] = (lane & 1) ^ ((v_dim[jj] >> 2) & 1);
   }
-  // block ids of tile kt's 4 groups; returns the bits of the absent groups
-  // and this wave's block id in *blk_own
-  auto tile_ids = [&](int kt, int* blk_own) -> uint32_t {
-    uint32_t absent = 0, bad = 0;
+  // ---- block ids, 64 key tiles at a time.  Lane j of idv[P & 1] holds the
+  // block of this wave's 16-key group in tile 64P + j (-1 when the group
+  // lies past the request or its table entry is not a block of the pool);
+  // lane j of absv[P & 1] holds the bits of that tile's absent groups.  The
+  // table entries of period P+1 are read while period P is in use and
+  // turned into these vectors one step later, after the wait that ends
+  // every step's loads, so no step waits on the table. ----
+  const int nkt = (kend + C::BN - 1) / C::BN;
+  const int nper = (nkt + 63) >> 6;
+  const int nbt = max((kv_len + bs - 1) >> pool.bs_shift, 1);   // table entries in use
+  int raw[4];
+  int idv0 = -1, idv1 = -1, absv0 = 0, absv1 = 0;
+  auto load_raw = [&](int period) {
+    const int t = 64 * period + lane;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) raw[r] = table[min((t * C::BN + 16 * r) >> pool.bs_shift, nbt - 1)];
+  };
+  auto convert = [&](int period) {
+    const int t = 64 * period + lane;
+    int own = -1, absent = 0;
+    bool bad = false;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int key16 = kt * C::BN + 16 * r;
-      int blk = key16 < kv_len ? table[key16 >> pool.bs_shift] : -1;
-      const bool ok = blk >= 0 && blk < pool.num_blocks;
-      if (!ok) absent |= 1u << r;
-      if (!ok && key16 < kv_len) bad |= 1u << r;
-      // the id is wave-uniform; saying so keeps the descriptors built from
-      // it in scalar registers
-      if (r == wave) *blk_own = __builtin_amdgcn_readfirstlane(ok ? blk : -1);
+      const bool in = t * C::BN + 16 * r < kv_len;
+      const bool valid = (unsigned)raw[r] < (unsigned)pool.num_blocks;
+      if (!(in && valid)) absent |= 1 << r;
+      if (r == wave) {
+        own = in && valid ? raw[r] : -1;
+        bad = in && !valid && t < nkt;
+      }
     }
-    if (((bad >> wave) & 1) && lane == 0) flag_error(pool.err, PKV_ERRBIT_BLOCK_ID);
-    return __builtin_amdgcn_readfirstlane(absent);
+    if (__builtin_amdgcn_ballot_w64(bad) && lane == 0) flag_error(pool.err, PKV_ERRBIT_BLOCK_ID);
+    if (period & 1) {
+      idv1 = own;
+      absv1 = absent;
+    } else {
+      idv0 = own;
+      absv0 = absent;
+    }
+  };
+  int have = 1;        // periods [0, have) are in idv/absv
+  bool pend = false;   // raw holds the entries of period `have`
+  load_raw(0);
+  convert(0);
+  if (nper > 1) {
+    load_raw(1);
+    pend = true;
+  }
+  // tile u's absent-group bits; this wave's block id in *blk_own
+  auto tile_ids = [&](int u, int* blk_own) -> uint32_t {
+    const bool odd = (u >> 6) & 1;
+    *blk_own = __builtin_amdgcn_readlane(odd ? idv1 : idv0, u & 63);
+    return __builtin_amdgcn_readlane(odd ? absv1 : absv0, u & 63);
   };
   auto dma_k = [&](int kt, char* kbuf, int blk) {
     const int key16 = kt * C::BN + 16 * wave;
@@ -245,6 +281,16 @@ attn_prefill_bf16_kernel(PoolDev pool, const bf16_t* __restrict__ q, bf16_t* __r
   float m = -1e30f, lsum = 0.f;
   constexpr uint32_t kOnes = 0x3F803F80u;                       // bf16 (1, 1)
 
+  // row max of a score tile over both lane halves, in log2 units
+  auto rowmax = [&](const f32x16x2& st) -> float {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(st.v[i][r], st.v[i][r + 1]));
+    auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+    return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * scale_log2;
+  };
   auto qk = [&](const char* kbuf) -> f32x16x2 {
     f32x16x2 st;
     uint4 kf[2][C::KS];
@@ -261,8 +307,15 @@ attn_prefill_bf16_kernel(PoolDev pool, const bf16_t* __restrict__ q, bf16_t* __r
     }
     return st;
   };
+  // fragment qi of the S MFMAs (32-key half qi / KS, k-step qi % KS) and
+  // fragment t of quarter c of the V tile
+  auto ldk = [&](const char* kbuf, int qi) -> uint4 {
+    return *reinterpret_cast<const uint4*>(kbuf + (kx ^ (32 * (qi % C::KS)) ^ ((qi / C::KS) * 32 * 2 * D)));
+  };
+  auto ldv = [&](const char* vbuf, int c, int t) -> uint4 {
+    return *reinterpret_cast<const uint4*>(vbuf + vx + c * C::VGRP + t * 1024);
+  };
 
-  const int nkt = (kend + C::BN - 1) / C::BN;
   char* const k0b = kb0[grp];
   char* const k1b = kb1[grp];
   char* const v0b = vb0[grp];
@@ -285,19 +338,27 @@ attn_prefill_bf16_kernel(PoolDev pool, const bf16_t* __restrict__ q, bf16_t* __r
   __syncthreads();
   f32x16x2 sa = qk(k0b), sb;
 
-  // one key tile of this group: st = S(kt) on entry; S(kt+NG), the group's
-  // next tile, goes to stn.  kcur holds K(kt) (free after the barrier,
-  // refilled with K(kt+2NG)), knext K(kt+NG), vcur V(kt), vnext the buffer
-  // V(kt+NG) goes to.  A step past the group's last tile only keeps the
-  // barrier count equal across the groups.
-  auto step = [&](int kt, char* kcur, const char* knext, const char* vcur, char* vnext, f32x16x2& st,
-                  f32x16x2& stn) {
-    const bool live = kt < nkt;
+  // A step of this group on key tile kt has three phases:
+  //  * stats(kt): softmax statistics of S(kt) in registers: masks for
+  //    causality (tiles reaching past this wave's first query) and for
+  //    absent groups, the row max, the rare rescale of O;
+  //  * sync(kt): K(kt+NG) and V(kt) have arrived (this wave's loads, one
+  //    step old); after the workgroup barrier every wave is past step
+  //    kt-NG, so K(kt)'s buffer (kcur) and the buffer of V(kt-NG) (vnext)
+  //    take the loads of K(kt+2NG) and V(kt+NG);
+  //  * block(kt): S(kt+NG) = K Q^T into stn with the exponentials of P(kt)
+  //    between its MFMAs, each quarter of P followed by its O^T += V^T P^T
+  //    MFMAs, in an order fixed by scheduling fences, every LDS fragment read
+  //    a few MFMAs before its use, at raised wave priority so that the
+  //    matrix cores go to the wave that has work for them.
+  // Group 0 runs sync, block, stats of the next tile; group 1 (NG = 2) runs
+  // sync, stats, block, so that between two barriers one group's softmax
+  // work overlaps the other's MFMAs.  A step past the group's last tile only
+  // keeps the barrier count equal across the groups.
+  auto stats = [&](int kt, f32x16x2& st, uint32_t absent) {
+    if (kt >= nkt) return;
     const int kbase = kt * C::BN;
-    // ---- softmax statistics of S(kt) (registers only): masks for causality
-    // (tiles reaching past this wave's first query) and absent groups, the
-    // row max, the rare rescale of O ----
-    if (live && kbase + C::BN - 1 > wave_first_q) {
+    if (kbase + C::BN - 1 > wave_first_q) {
       // an opaque copy keeps the compares inside this branch (hoisted, they
       // would run on every tile)
       int d;
@@ -308,24 +369,16 @@ attn_prefill_bf16_kernel(PoolDev pool, const bf16_t* __restrict__ q, bf16_t* __r
         for (int r = 0; r < 16; ++r)
           if (32 * i + 16 * (r >> 3) + (r & 7) > d) st.v[i][r] = -INFINITY;
     }
-    if (live && absent_cur) {
+    if (absent) {
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          if ((absent_cur >> (2 * i + (r >> 3))) & 1) st.v[i][r] = -INFINITY;
+          if ((absent >> (2 * i + (r >> 3))) & 1) st.v[i][r] = -INFINITY;
     }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(st.v[i][r], st.v[i][r + 1]));
-    {
-      auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-      mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * scale_log2;
-    }
+    const float mx = rowmax(st);
     // move the running max only when this tile exceeds it by the slack
-    const bool grow = live && mx > m + kRescaleSlack;
+    const bool grow = mx > m + kRescaleSlack;
     if (__builtin_amdgcn_ballot_w64(grow)) {                    // wave-uniform, rare
       const float mnew = grow ? mx : m;
       const float alpha = __builtin_amdgcn_exp2f(m - mnew);    // 0 on the first growth
@@ -334,75 +387,98 @@ attn_prefill_bf16_kernel(PoolDev pool, const bf16_t* __restrict__ q, bf16_t* __r
 #pragma unroll
       for (int t = 0; t < C::DT; ++t) o[t] *= alpha;
     }
-
-    // ---- K(kt+NG) and V(kt) were moved by this wave's DMA one step ago ----
+  };
+  uint32_t absent_after = 0;
+  int blk_after = -1;
+  auto sync = [&](int kt, char* kcur, const char* vcur, char* vnext) {
     wait_dma();
-    if (live) fix_tail(kt, const_cast<char*>(vcur));
+    if (pend) {
+      convert(have);
+      ++have;
+      pend = false;
+    }
+    if (kt < nkt) fix_tail(kt, const_cast<char*>(vcur));
     __syncthreads();
-    // every wave is past the previous step: K(kt)'s buffer and the buffer of
-    // V(kt-NG) are free
-    uint32_t absent_after = 0;
-    int blk2 = -1;
-    if (kt + 2 * NG < nkt) {
-      absent_after = tile_ids(kt + 2 * NG, &blk2);
-      dma_k(kt + 2 * NG, kcur, blk2);
+    absent_after = 0;
+    blk_after = -1;
+    const int u = kt + 2 * NG;
+    if (u < nkt) {
+      absent_after = tile_ids(u, &blk_after);
+      dma_k(u, kcur, blk_after);
+      // entering the last period read so far: read the next one's entries
+      if (!pend && have < nper && (u >> 6) + 1 >= have) {
+        load_raw(have);
+        pend = true;
+      }
     }
     if (kt + NG < nkt) dma_v(kt + NG, vnext, blk_next);
-    if (!live) return;
-
-    // ---- one branch-free block: S(kt+NG) on the matrix cores while P(kt) is
-    // formed, then O^T += V^T P^T ----
-    stn = qk(knext);
-    // p in bf16 (the MFMA operand); the row sum adds those same rounded
-    // values, two per v_dot2 against (1, 1)
-    float psum[2] = {0.f, 0.f};
-    uint4 pf[2][2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int sp = 0; sp < 2; ++sp) {
-        float p[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) p[e] = __builtin_amdgcn_exp2f(fmaf(st.v[i][8 * sp + e], scale_log2, -m));
-        pf[i][sp] = make_uint4(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
-                               pack_bf16x2(p[6], p[7]));
-        psum[sp] = dot2_bf16(pf[i][sp].x, kOnes, psum[sp]);
-        psum[sp] = dot2_bf16(pf[i][sp].y, kOnes, psum[sp]);
-        psum[sp] = dot2_bf16(pf[i][sp].z, kOnes, psum[sp]);
-        psum[sp] = dot2_bf16(pf[i][sp].w, kOnes, psum[sp]);
-      }
-    lsum += psum[0] + psum[1];
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int sp = 0; sp < 2; ++sp)
-#pragma unroll
-        for (int t = 0; t < C::DT; ++t) {
-          const uint4 va = *reinterpret_cast<const uint4*>(vcur + vx + (2 * i + sp) * C::VGRP + t * 1024);
-          o[t] = mfma32(va, pf[i][sp], o[t]);
-        }
-    // schedule of the block: K fragments 8 ahead; each S MFMA with one LDS
-    // read and a share of the softmax arithmetic; then each P V MFMA with
-    // one V read
-    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
-#pragma unroll
-    for (int j = 0; j < 2 * C::KS; ++j) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
-    }
-#pragma unroll
-    for (int j = 0; j < 4 * C::DT; ++j) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
-    }
+  };
+  auto rotate = [&]() {
     absent_cur = absent_next;
     absent_next = absent_after;
-    blk_next = blk2;
+    blk_next = blk_after;
   };
-  // every group takes the same number of steps (one barrier each)
+  auto block = [&](int kt, const char* knext, const char* vcur, const f32x16x2& st, f32x16x2& stn) {
+    if (kt >= nkt) return;
+    constexpr int NQK = 2 * C::KS;                              // S MFMAs: 2 halves x KS k-steps
+    constexpr int QPG = NQK / 4;                                // S MFMAs per quarter of P
+    constexpr int KPF = 4;                                      // K fragments in flight
+    uint4 kr[KPF], vr[C::DT];
+#pragma unroll
+    for (int j = 0; j < KPF; ++j) kr[j] = ldk(knext, j);
+#pragma unroll
+    for (int t = 0; t < C::DT; ++t) vr[t] = ldv(vcur, 0, t);
+    float psum[2] = {0.f, 0.f};
+    __builtin_amdgcn_s_setprio(1);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      // quarter c of P: registers 8(c%2)..8(c%2)+7 of S half c/2
+      const int i = c >> 1, r0 = 8 * (c & 1);
+      float p[8];
+      uint32_t pw[4];
+#pragma unroll
+      for (int j = 0; j < QPG; ++j) {
+        const int qi = c * QPG + j;
+        const int hs = qi / C::KS, ks = qi % C::KS;
+        stn.v[hs] = mfma32(kr[qi % KPF], qf[ks], ks == 0 ? f32x16_t{} : stn.v[hs]);
+        if (qi + KPF < NQK) kr[qi % KPF] = ldk(knext, qi + KPF);
+#pragma unroll
+        for (int e = 8 * j / QPG; e < 8 * (j + 1) / QPG; ++e) {
+          p[e] = __builtin_amdgcn_exp2f(fmaf(st.v[i][r0 + e], scale_log2, -m));
+          if (e & 1) pw[e >> 1] = pack_bf16x2(p[e - 1], p[e]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      const uint4 pf = make_uint4(pw[0], pw[1], pw[2], pw[3]);
+#pragma unroll
+      for (int t = 0; t < C::DT; ++t) {
+        o[t] = mfma32(vr[t], pf, o[t]);
+        if (c < 3) vr[t] = ldv(vcur, c + 1, t);
+        // the row sum adds the same bf16-rounded p, two per v_dot2 against (1, 1)
+#pragma unroll
+        for (int w = 4 * t / C::DT; w < 4 * (t + 1) / C::DT; ++w) psum[w & 1] = dot2_bf16(pw[w], kOnes, psum[w & 1]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    __builtin_amdgcn_s_setprio(0);
+    lsum += psum[0] + psum[1];
+  };
+
+  // every group takes the same number of steps (one barrier each); st is
+  // S(kt) on entry to a step, stn receives S(kt+NG); kcur holds K(kt),
+  // knext K(kt+NG), vcur V(kt), vnext the buffer V(kt+NG) goes to
   const int nsteps = (nkt + NG - 1) / NG;
+  const bool lead = NG == 1 || grp == 0;
+  auto step = [&](int kt, char* kcur, const char* knext, const char* vcur, char* vnext, f32x16x2& st,
+                  f32x16x2& stn) {
+    sync(kt, kcur, vcur, vnext);
+    if (!lead) stats(kt, st, absent_cur);
+    block(kt, knext, vcur, st, stn);
+    rotate();
+    if (lead) stats(kt + NG, stn, absent_cur);
+  };
+  if (lead) stats(grp, sa, absent_cur);
   for (int u = 0; u < nsteps; u += 2) {
     step(grp + NG * u, k0b, k1b, v0b, v1b, sa, sb);
     if (u + 1 < nsteps) step(grp + NG * (u + 1), k1b, k0b, v1b, v0b, sb, sa);
