@@ -81,6 +81,52 @@ __device__ __forceinline__ void lds_dma16(buffer_rsrc_t r, char* lds, int voffse
 }
 __device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// Order of the MFMAs of one step (block) for head dim D: eight groups,
+// S0 S1 S2 PV0 S3 PV1 PV2 PV3, where Sq is quarter q of the S^T = K Q^T
+// MFMAs (QPG each) and PVc the O^T += V^T P^T MFMAs of quarter c of P (DT
+// each).  The 16 pairs of P values a lane forms are spread over the slots
+// so that quarter c is complete before PVc, and the row max of each S half
+// is taken a few slots after its last MFMA.
+template <int D>
+struct BlockPlan {
+  static constexpr int KS = D / 16, DT = D / 32, QPG = KS / 2;
+  static constexpr int NS = 4 * QPG + 4 * DT;                   // MFMA slots
+  static constexpr int gtype(int g) { return (g == 3 || g >= 5) ? 1 : 0; }   // 0: S, 1: PV
+  static constexpr int gq(int g) { return g == 3 ? 0 : g == 4 ? 3 : g == 5 ? 1 : g == 6 ? 2 : g == 7 ? 3 : g; }
+  static constexpr int gstart(int g) {
+    int s = 0;
+    for (int i = 0; i < g; ++i) s += gtype(i) ? DT : QPG;
+    return s;
+  }
+  static constexpr int group_of(int s) {
+    int g = 0;
+    while (g < 7 && gstart(g + 1) <= s) ++g;
+    return g;
+  }
+  static constexpr int pair_slot(int j) { return j * (NS - NS / 8) / 16; }
+  static constexpr int max_slot(int h, int k) {
+    const int start = h ? gstart(5) + 2 : gstart(2) + 2 * (QPG / 2);
+    const int end = h ? NS - 1 : gstart(5);
+    return start + k * (end - start) / 8;
+  }
+  // every quarter of P is complete before its PV group; every half of S is
+  // complete before its max is taken
+  static constexpr bool valid() {
+    for (int j = 0; j < 16; ++j) {
+      const int c = j >> 2;
+      int g = 0;
+      while (!(gtype(g) == 1 && gq(g) == c)) ++g;
+      if (pair_slot(j) >= gstart(g)) return false;
+    }
+    for (int k = 0; k < 8; ++k) {
+      if (max_slot(0, k) < gstart(2) + 1 || max_slot(0, k) >= NS) return false;
+      if (max_slot(1, k) < gstart(5) + 1 || max_slot(1, k) >= NS) return false;
+    }
+    return true;
+  }
+};
+static_assert(BlockPlan<128>::valid() && BlockPlan<64>::valid(), "block schedule");
+
 // NG = key-tile groups per workgroup.  NG = 1: 4 waves, two workgroups per
 // CU.  NG = 2 (small grids): 8 waves in two groups of 4 that share the
 // queries and walk alternate key tiles with their own buffers, merging
@@ -162,13 +208,14 @@ attn_prefill_bf16_kernel(PoolDev pool, const bf16_t* __restrict__ q, bf16_t* __r
     k_voff[jj] = (key_perm(r) * D + 8 * c) * 2;
   }
   // V tile in LDS: [group][dim][16 keys], the two 8-key halves of a dim row
-  // swapped when bit 2 of the dim is set (conflict-free reads of 8 dims).
-  // A DMA instruction fills 32 dims of one group.
+  // swapped when bit 2 xor bit 3 of the dim is set, so that the 16-byte
+  // reads of any 16 consecutive dims (one half each) fall in 16 distinct
+  // bank groups.  A DMA instruction fills 32 dims of one group.
   int v_dim[C::NDMA], v_kh[C::NDMA];
 #pragma unroll
   for (int jj = 0; jj < C::NDMA; ++jj) {
     v_dim[jj] = 32 * jj + (lane >> 1);
-    v_kh[jj] = (lane & 1) ^ ((v_dim[jj] >> 2) & 1);
+    v_kh[jj] = (lane & 1) ^ (((v_dim[jj] >> 2) ^ (v_dim[jj] >> 3)) & 1);
   }
   // ---- block ids, 64 key tiles at a time.  Lane j of idv[P & 1] holds the
   // block of this wave's 16-key group in tile 64P + j (-1 when the group
@@ -255,7 +302,7 @@ attn_prefill_bf16_kernel(PoolDev pool, const bf16_t* __restrict__ q, bf16_t* __r
     const int kh = (rel >> 3) & 1, e0 = rel & 7;
     char* base = vbuf + wave * C::VGRP;
     for (int d = lane; d < D; d += 64) {
-      uint4* p = reinterpret_cast<uint4*>(base + d * 32 + ((kh ^ ((d >> 2) & 1)) << 4));
+      uint4* p = reinterpret_cast<uint4*>(base + d * 32 + ((kh ^ ((d >> 2) ^ (d >> 3)) & 1) << 4));
       uint4 v = *p;
       uint32_t* w = reinterpret_cast<uint32_t*>(&v);
 #pragma unroll
@@ -271,7 +318,7 @@ attn_prefill_bf16_kernel(PoolDev pool, const bf16_t* __restrict__ q, bf16_t* __r
   // per-lane constant
   const int kx = l32 * 2 * D + (((half ^ (l32 & (C::KCH - 1))) & 1) << 4) + (((l32 & (C::KCH - 1)) >> 1) << 5);
   // V: dim 32t + l32, keys 32i + 16sp + 8half -> group 2i + sp, half `half`
-  const int vx = l32 * 32 + ((half ^ ((l32 >> 2) & 1)) << 4);
+  const int vx = l32 * 32 + (((half ^ (l32 >> 2) ^ (l32 >> 3)) & 1) << 4);
 
   f32x16_t o[C::DT];
 #pragma unroll
@@ -279,7 +326,6 @@ attn_prefill_bf16_kernel(PoolDev pool, const bf16_t* __restrict__ q, bf16_t* __r
   // running max (log2 units): finite start, so a tile whose keys are all
   // masked or absent gives p = exp2(-inf) = 0 rather than exp2(-inf + inf)
   float m = -1e30f, lsum = 0.f;
-  constexpr uint32_t kOnes = 0x3F803F80u;                       // bf16 (1, 1)
 
   // row max of a score tile over both lane halves, in log2 units
   auto rowmax = [&](const f32x16x2& st) -> float {
@@ -355,8 +401,9 @@ attn_prefill_bf16_kernel(PoolDev pool, const bf16_t* __restrict__ q, bf16_t* __r
   // sync, stats, block, so that between two barriers one group's softmax
   // work overlaps the other's MFMAs.  A step past the group's last tile only
   // keeps the barrier count equal across the groups.
-  auto stats = [&](int kt, f32x16x2& st, uint32_t absent) {
+  auto stats = [&](int kt, f32x16x2& st, uint32_t absent, float mx_block) {
     if (kt >= nkt) return;
+    bool masked = false;
     const int kbase = kt * C::BN;
     if (kbase + C::BN - 1 > wave_first_q) {
       // an opaque copy keeps the compares inside this branch (hoisted, they
@@ -368,6 +415,7 @@ attn_prefill_bf16_kernel(PoolDev pool, const bf16_t* __restrict__ q, bf16_t* __r
 #pragma unroll
         for (int r = 0; r < 16; ++r)
           if (32 * i + 16 * (r >> 3) + (r & 7) > d) st.v[i][r] = -INFINITY;
+      masked = true;
     }
     if (absent) {
 #pragma unroll
@@ -375,8 +423,10 @@ attn_prefill_bf16_kernel(PoolDev pool, const bf16_t* __restrict__ q, bf16_t* __r
 #pragma unroll
         for (int r = 0; r < 16; ++r)
           if ((absent >> (2 * i + (r >> 3))) & 1) st.v[i][r] = -INFINITY;
+      masked = true;
     }
-    const float mx = rowmax(st);
+    // the block that computed S took its max; a masked tile takes it again
+    const float mx = masked ? rowmax(st) : mx_block;
     // move the running max only when this tile exceeds it by the slack
     const bool grow = mx > m + kRescaleSlack;
     if (__builtin_amdgcn_ballot_w64(grow)) {                    // wave-uniform, rare
@@ -418,51 +468,62 @@ attn_prefill_bf16_kernel(PoolDev pool, const bf16_t* __restrict__ q, bf16_t* __r
     absent_next = absent_after;
     blk_next = blk_after;
   };
-  auto block = [&](int kt, const char* knext, const char* vcur, const f32x16x2& st, f32x16x2& stn) {
+  auto block = [&](int kt, const char* knext, const char* vcur, const f32x16x2& st, f32x16x2& stn, float& mx_stn) {
     if (kt >= nkt) return;
-    constexpr int NQK = 2 * C::KS;                              // S MFMAs: 2 halves x KS k-steps
-    constexpr int QPG = NQK / 4;                                // S MFMAs per quarter of P
-    constexpr int KPF = 4;                                      // K fragments in flight
-    uint4 kr[KPF], vr[C::DT];
+    using BP = BlockPlan<D>;
+    constexpr int R = 4;                                        // LDS fragments in flight
+    // A operand (K or V fragment from LDS) of the MFMA in slot s
+    auto frag = [&](int s) -> uint4 {
+      const int g = BP::group_of(s), j = s - BP::gstart(g);
+      return BP::gtype(g) == 0 ? ldk(knext, BP::gq(g) * BP::QPG + j) : ldv(vcur, BP::gq(g), j);
+    };
+    uint4 fr[R];
 #pragma unroll
-    for (int j = 0; j < KPF; ++j) kr[j] = ldk(knext, j);
-#pragma unroll
-    for (int t = 0; t < C::DT; ++t) vr[t] = ldv(vcur, 0, t);
+    for (int s = 0; s < R; ++s) fr[s] = frag(s);
+    uint32_t pw[4][4];                                          // P in bf16 pairs, by quarter
     float psum[2] = {0.f, 0.f};
+    float mh[2] = {-INFINITY, -INFINITY};
     __builtin_amdgcn_s_setprio(1);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      // quarter c of P: registers 8(c%2)..8(c%2)+7 of S half c/2
-      const int i = c >> 1, r0 = 8 * (c & 1);
-      float p[8];
-      uint32_t pw[4];
-#pragma unroll
-      for (int j = 0; j < QPG; ++j) {
-        const int qi = c * QPG + j;
-        const int hs = qi / C::KS, ks = qi % C::KS;
-        stn.v[hs] = mfma32(kr[qi % KPF], qf[ks], ks == 0 ? f32x16_t{} : stn.v[hs]);
-        if (qi + KPF < NQK) kr[qi % KPF] = ldk(knext, qi + KPF);
-#pragma unroll
-        for (int e = 8 * j / QPG; e < 8 * (j + 1) / QPG; ++e) {
-          p[e] = __builtin_amdgcn_exp2f(fmaf(st.v[i][r0 + e], scale_log2, -m));
-          if (e & 1) pw[e >> 1] = pack_bf16x2(p[e - 1], p[e]);
-        }
-        __builtin_amdgcn_sched_barrier(0);
+    for (int s = 0; s < BP::NS; ++s) {
+      const int g = BP::group_of(s), j = s - BP::gstart(g), c = BP::gq(g);
+      if (BP::gtype(g) == 0) {
+        const int qi = c * BP::QPG + j, hs = qi / C::KS, ks = qi % C::KS;
+        stn.v[hs] = mfma32(fr[s % R], qf[ks], ks == 0 ? f32x16_t{} : stn.v[hs]);
+      } else {
+        o[j] = mfma32(fr[s % R], make_uint4(pw[c][0], pw[c][1], pw[c][2], pw[c][3]), o[j]);
       }
-      const uint4 pf = make_uint4(pw[0], pw[1], pw[2], pw[3]);
+      if (s + R < BP::NS) fr[s % R] = frag(s + R);
+      // the pairs of P placed in this slot: p = 2^(s*scale - m), in bf16
+      // for the MFMA; the row sum adds p in fp32 (plain adds: a v_dot2 of
+      // the rounded pairs stalls next to the MFMAs), which differs from the
+      // sum of the rounded values by unbiased rounding noise only
 #pragma unroll
-      for (int t = 0; t < C::DT; ++t) {
-        o[t] = mfma32(vr[t], pf, o[t]);
-        if (c < 3) vr[t] = ldv(vcur, c + 1, t);
-        // the row sum adds the same bf16-rounded p, two per v_dot2 against (1, 1)
-#pragma unroll
-        for (int w = 4 * t / C::DT; w < 4 * (t + 1) / C::DT; ++w) psum[w & 1] = dot2_bf16(pw[w], kOnes, psum[w & 1]);
-        __builtin_amdgcn_sched_barrier(0);
+      for (int pj = 0; pj < 16; ++pj) {
+        if (BP::pair_slot(pj) != s) continue;
+        const int pc = pj >> 2, w = pj & 3;
+        const int i = pc >> 1, r = 8 * (pc & 1) + 2 * w;
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(st.v[i][r], scale_log2, -m));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(st.v[i][r + 1], scale_log2, -m));
+        pw[pc][w] = pack_bf16x2(p0, p1);
+        psum[0] += p0;
+        psum[1] += p1;
       }
+      // the row max of S(kt+NG), a few registers per slot once each half
+      // is complete
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+          if (BP::max_slot(h, k) == s) mh[h] = fmaxf(mh[h], fmaxf(stn.v[h][2 * k], stn.v[h][2 * k + 1]));
+      __builtin_amdgcn_sched_barrier(0);
     }
     __builtin_amdgcn_s_setprio(0);
     lsum += psum[0] + psum[1];
+    float mx = fmaxf(mh[0], mh[1]);
+    auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+    mx_stn = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * scale_log2;
   };
 
   // every group takes the same number of steps (one barrier each); st is
@@ -471,17 +532,18 @@ attn_prefill_bf16_kernel(PoolDev pool, const bf16_t* __restrict__ q, bf16_t* __r
   const int nsteps = (nkt + NG - 1) / NG;
   const bool lead = NG == 1 || grp == 0;
   auto step = [&](int kt, char* kcur, const char* knext, const char* vcur, char* vnext, f32x16x2& st,
-                  f32x16x2& stn) {
+                  f32x16x2& stn, float mx_st, float& mx_stn) {
     sync(kt, kcur, vcur, vnext);
-    if (!lead) stats(kt, st, absent_cur);
-    block(kt, knext, vcur, st, stn);
+    if (!lead) stats(kt, st, absent_cur, mx_st);
+    block(kt, knext, vcur, st, stn, mx_stn);
     rotate();
-    if (lead) stats(kt + NG, stn, absent_cur);
+    if (lead) stats(kt + NG, stn, absent_cur, mx_stn);
   };
-  if (lead) stats(grp, sa, absent_cur);
+  float mxa = rowmax(sa), mxb = -INFINITY;
+  if (lead) stats(grp, sa, absent_cur, mxa);
   for (int u = 0; u < nsteps; u += 2) {
-    step(grp + NG * u, k0b, k1b, v0b, v1b, sa, sb);
-    if (u + 1 < nsteps) step(grp + NG * (u + 1), k1b, k0b, v1b, v0b, sb, sa);
+    step(grp + NG * u, k0b, k1b, v0b, v1b, sa, sb, mxa, mxb);
+    if (u + 1 < nsteps) step(grp + NG * (u + 1), k1b, k0b, v1b, v0b, sb, sa, mxb, mxa);
   }
 
   if constexpr (NG == 2) {
