@@ -173,14 +173,16 @@ int attn_prefill_chunk(const pkv_pool_layer* pool, const void* q, void* out, con
 
 size_t pkv_attn_decode_workspace_size(int32_t batch, int32_t num_q_heads, int32_t max_context_len,
                                       int32_t head_dim) {
-  // the split plan depends on the KV head count only through pairs; use the
-  // most conservative (one q-head per kv head) when not known
+  // the plan depends on the KV head count and the dtype, which are not
+  // given: the largest need over the group sizes and both dtypes
   if (batch <= 0 || num_q_heads <= 0 || max_context_len <= 0 || head_dim <= 0) return 0;
   size_t worst = 0;
   for (int g = 1; g <= 16 && g <= num_q_heads; g *= 2) {
     if (num_q_heads % g) continue;
-    const DecodePlan p = plan_decode(batch, num_q_heads, num_q_heads / g, max_context_len, head_dim);
-    if (p.workspace > worst) worst = p.workspace;
+    for (int dt : {(int)PKV_F32, (int)PKV_BF16}) {
+      const DecodePlan p = plan_decode(batch, num_q_heads, num_q_heads / g, max_context_len, head_dim, dt);
+      if (p.workspace > worst) worst = p.workspace;
+    }
   }
   return worst;
 }
@@ -200,7 +202,7 @@ int attn_decode(const pkv_pool_layer* pool, const void* q, void* out, const int3
   if (bt_stride <= 0 || (int64_t)bt_stride * pd.block_size < max_context_len)
     return fail(PKV_EINVAL, "attn_decode: bt_stride %d blocks cannot hold %d tokens", bt_stride, max_context_len);
   if (!(scale >= 0.f) || std::isinf(scale)) return fail(PKV_EINVAL, "attn_decode: scale must be finite");
-  const DecodePlan plan = plan_decode(batch, num_q_heads, pd.num_kv_heads, max_context_len, pd.head_dim);
+  const DecodePlan plan = plan_decode(batch, num_q_heads, pd.num_kv_heads, max_context_len, pd.head_dim, pool->dtype);
   if (plan.workspace > 0) {
     if (!workspace || workspace_bytes < plan.workspace)
       return fail(PKV_EINVAL, "attn_decode: workspace of %zu bytes needed, %zu given", plan.workspace,

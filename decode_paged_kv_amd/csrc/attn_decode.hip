@@ -274,7 +274,12 @@ attn_decode_kernel(PoolDev pool, const T* __restrict__ q, T* __restrict__ out, c
 // so a half's block id is wave-uniform: it is read with a scalar load and
 // the half's (block, head) K and V tiles are addressed through buffer
 // descriptors in scalar registers; a lane adds only a fixed offset.  Every
-// K/V byte is read once, so the loads carry the non-temporal hint.
+// K/V byte is read once.  The V loads carry the non-temporal hint (each
+// instruction reads whole lines).  The K loads do not: one instruction
+// reads 64 bytes of each of 16 rows, the other half of every 128-byte line
+// comes with the next instruction, and without the hint the two halves meet
+// in the L1 (on a CU-masked half of the device this is worth about a fifth
+// of the decode bandwidth).
 //
 // The GQA group's contraction runs on the matrix cores, in transposed form
 // so the G <= 16 q-heads are the 16 columns of 16x16 MFMA tiles:
@@ -346,36 +351,89 @@ struct DecodeBf16Smem {
 // when a tile's max exceeds it by more than this, so p <= 2^8.
 constexpr float kDecodeSlack = 8.0f;
 
-template <int D, int G>
+// Stream split bookkeeping.  Request b holds Hkv * ceil(L_b / 32) pair-tiles
+// (L_b clamped to what its table addresses), laid out by request, then KV
+// head, then key.  scan_tiles returns the total, the request holding pair-
+// tile `target` (-1: none) with the index of its first pair-tile, and the
+// index of request rb's first pair-tile; every lane of the wave gets the
+// same values (a wave-wide prefix sum, 64 requests per pass).
+struct TileScan {
+  long long total;
+  int b;
+  long long base;
+  long long base_rb;
+  bool over;                                    // some context exceeds its table
+};
+__device__ __forceinline__ long long uniform64(long long x) {
+  const int lo = __builtin_amdgcn_readfirstlane((int)(unsigned)(unsigned long long)x);
+  const int hi = __builtin_amdgcn_readfirstlane((int)(unsigned)((unsigned long long)x >> 32));
+  return (long long)(((unsigned long long)(unsigned)hi << 32) | (unsigned)lo);
+}
+__device__ TileScan scan_tiles(const int32_t* __restrict__ ctx, int batch, int cap, int hkv, long long target, int rb) {
+  const int lane = threadIdx.x & 63;
+  long long run = 0, base = 0, base_rb = 0;
+  int fb = -1;
+  bool over = false;
+  for (int b0 = 0; b0 < batch; b0 += 64) {
+    const int bb = b0 + lane;
+    const int L = bb < batch ? ctx[bb] : 0;
+    over |= L > cap;
+    const long long x = (long long)hkv * ((max(min(L, cap), 0) + 31) >> 5);
+    long long inc = x;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const long long y = __shfl_up(inc, o);
+      if (lane >= o) inc += y;
+    }
+    const long long excl = run + inc - x;
+    const uint64_t hit = __builtin_amdgcn_ballot_w64(bb < batch && excl <= target && target < excl + x);
+    if (fb < 0 && hit) {
+      const int l = __builtin_ctzll(hit);
+      fb = b0 + l;
+      base = __shfl(excl, l);
+    }
+    if (rb >= b0 && rb < b0 + 64) base_rb = __shfl(excl, rb - b0);
+    run += __shfl(inc, 63);
+  }
+  TileScan r;
+  r.total = uniform64(run);
+  r.b = __builtin_amdgcn_readfirstlane(fb);
+  r.base = uniform64(base);
+  r.base_rb = uniform64(base_rb);
+  r.over = __builtin_amdgcn_ballot_w64(over) != 0;
+  return r;
+}
+// the workgroup whose pair-tile range holds pair-tile x (NW workgroups, W tiles)
+__device__ __forceinline__ long long stream_owner(long long x, long long NW, long long W) {
+  return ((x + 1) * NW + W - 1) / W - 1;
+}
+
+template <int D, int G, bool STREAM>
 __global__ void __launch_bounds__(kThreads, 2)
 attn_decode_bf16_kernel(PoolDev pool, const bf16_t* __restrict__ q, bf16_t* __restrict__ out,
-                        const int32_t* __restrict__ bt, int bt_stride, const int32_t* __restrict__ ctx,
+                        const int32_t* __restrict__ bt, int bt_stride, const int32_t* __restrict__ ctx, int batch,
                         int num_q_heads, float scale_log2, int split_tokens, int num_splits,
                         float* __restrict__ part_o, float* __restrict__ part_ml) {
   static_assert(G >= 1 && G <= 16, "the q-heads of a KV head are the 16 MFMA columns");
   constexpr int KC = D / 32, DT = D / 16, TK = 32;
   __shared__ DecodeBf16Smem<D, G> sm;
 
-  const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l16 = lane & 15, j4 = lane >> 4;
-  int L = ctx[b];
-  if (L > (bt_stride << pool.bs_shift)) {
-    if (threadIdx.x == 0 && split == 0 && kvh == 0) flag_error(pool.err, PKV_ERRBIT_TABLE);
-    L = bt_stride << pool.bs_shift;
-  }
-  const int start = split * split_tokens;
-  if (start >= L) return;
-  const int end = min(L, start + split_tokens);
+  const int cap = bt_stride << pool.bs_shift;                   // keys the table can address
   const int hl = pool.heads_per_shard;
+  const int bs = pool.block_size;
+  const size_t block_stride = (size_t)hl * bs * D;
+  const int tile_bytes = bs * D * 2;
+
+  // keys [start, end) of request b (context L) and KV head kvh; the result
+  // goes to out when final_out, else to the partial rows prow + g * pstride
+  auto segment = [&](int b, int kvh, int L, int start, int end, bool final_out, size_t prow, int pstride) {
   const int sh = kvh / hl, lh = kvh - sh * hl;
   const bf16_t* kpool = reinterpret_cast<const bf16_t*>(pool.k[sh]);
   const bf16_t* vpool = reinterpret_cast<const bf16_t*>(pool.v[sh]);
-  const int bs = pool.block_size;
   const size_t head_off = (size_t)lh * bs * D;                  // elements
-  const size_t block_stride = (size_t)hl * bs * D;
-  const int tile_bytes = bs * D * 2;
   const int32_t* table = bt + (size_t)b * bt_stride;
 
   // q as the B operand of S^T: head l16 (zero columns past G), dims 32c + 8 j4
@@ -412,7 +470,7 @@ attn_decode_bf16_kernel(PoolDev pool, const bf16_t* __restrict__ q, bf16_t* __re
                                            ok ? tile_bytes : 0);
       const int soff = ((k0 + 16 * h) & (bs - 1)) * D * 2;
 #pragma unroll
-      for (int c = 0; c < KC; ++c) r.k[h][c] = buffer_load16<kStream>(rs, k_voff + 64 * c, soff);
+      for (int c = 0; c < KC; ++c) r.k[h][c] = buffer_load16<kCached>(rs, k_voff + 64 * c, soff);
     }
   };
   auto issue_v = [&](int k0, DecodeTile<D>& r) {
@@ -557,14 +615,65 @@ attn_decode_bf16_kernel(PoolDev pool, const bf16_t* __restrict__ q, bf16_t* __re
       acc += sm.acc[w][g][d] * f;
     }
     const int h = kvh * G + g;
-    if (L <= split_tokens) {                    // the request's only split: final output
+    if (final_out) {
       out[((size_t)b * num_q_heads + h) * D + d] = f32_to_bf16(acc / l);
     } else {
-      const size_t row = ((size_t)b * num_q_heads + h) * num_splits + split;
+      const size_t row = prow + (size_t)g * pstride;
       part_o[row * D + d] = acc;
       if (d == 0) {
         part_ml[row * 2 + 0] = mx;
         part_ml[row * 2 + 1] = l;
+      }
+    }
+  }
+  __syncthreads();                              // the merge buffers are free again
+  };
+
+  if constexpr (!STREAM) {
+    // one segment: split blockIdx.x of (request blockIdx.z, KV head blockIdx.y)
+    const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+    int L = ctx[b];
+    if (L > cap) {                              // never index past the request's table
+      if (threadIdx.x == 0 && split == 0 && kvh == 0) flag_error(pool.err, PKV_ERRBIT_TABLE);
+      L = cap;
+    }
+    const int start = split * split_tokens;
+    if (start >= L) return;
+    segment(b, kvh, L, start, min(L, start + split_tokens), L <= split_tokens,
+            ((size_t)b * num_q_heads + (size_t)kvh * G) * num_splits + split, num_splits);
+  } else {
+    // stream split: workgroup w takes the pair-tiles [w W / NW, (w+1) W / NW)
+    // of the W = Hkv * sum_b ceil(L_b / 32) tiles of the batch, ordered by
+    // request, KV head, key; a pair met by several workgroups leaves one
+    // partial per workgroup, in row (w + pair index) * G + g
+    const int hkv = num_q_heads / G;
+    const long long NW = gridDim.x, w = blockIdx.x;
+    const TileScan tot = scan_tiles(ctx, batch, cap, hkv, -1, 0);
+    if (tot.over && w == 0 && threadIdx.x == 0) flag_error(pool.err, PKV_ERRBIT_TABLE);
+    const long long W = tot.total;
+    long long t = w * W / NW;
+    const long long t1 = (w + 1) * W / NW;
+    if (t >= t1) return;
+    const TileScan at = scan_tiles(ctx, batch, cap, hkv, t, 0);
+    int b = at.b;
+    long long base = at.base;
+    while (t < t1) {
+      const int L = min(ctx[b], cap);
+      const int ntb = (L + TK - 1) / TK;
+      if (ntb == 0) {                           // an empty request holds no tiles
+        ++b;
+        continue;
+      }
+      const int kvh = (int)((t - base) / ntb);
+      const long long pstart = base + (long long)kvh * ntb;
+      const long long seg_end = min(t1, pstart + ntb);
+      const bool final_out = stream_owner(pstart, NW, W) == stream_owner(pstart + ntb - 1, NW, W);
+      segment(b, kvh, L, (int)(t - pstart) * TK, min(L, (int)(seg_end - pstart) * TK), final_out,
+              (size_t)(w + (long long)b * hkv + kvh) * G, 1);
+      t = seg_end;
+      if (t == base + (long long)hkv * ntb) {
+        base = t;
+        ++b;
       }
     }
   }
@@ -614,17 +723,78 @@ attn_decode_merge_kernel(const float* __restrict__ part_o, const float* __restri
   else out[((size_t)b * num_q_heads + h) * D + d] = r;
 }
 
+// Merge of the stream split: pair (b, h / G) has one partial per workgroup
+// that met it, rows (w + pair index) * G + g for w in [owner of its first
+// tile, owner of its last]; a pair met by one workgroup is already final.
+template <int D>
+__global__ void __launch_bounds__(D)
+attn_decode_stream_merge_kernel(const float* __restrict__ part_o, const float* __restrict__ part_ml,
+                                const int32_t* __restrict__ ctx, bf16_t* __restrict__ out, int batch,
+                                int num_q_heads, int hkv, int cap, int nwg) {
+  const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
+  const int G = num_q_heads / hkv, kvh = h / G, g = h - kvh * G;
+  const TileScan sc = scan_tiles(ctx, batch, cap, hkv, -1, b);
+  const int L = min(ctx[b], cap);
+  const int ntb = (max(L, 0) + 31) >> 5;
+  if (ntb == 0) return;
+  const long long pstart = sc.base_rb + (long long)kvh * ntb;
+  const long long wlo = stream_owner(pstart, nwg, sc.total), whi = stream_owner(pstart + ntb - 1, nwg, sc.total);
+  if (wlo == whi) return;
+  const size_t row0 = (size_t)(wlo + (long long)b * hkv + kvh) * G + g;
+  const int ns = (int)(whi - wlo + 1);
+  float mx = -INFINITY, l = 0.f, o = 0.f;
+  for (int s0 = 0; s0 < ns; s0 += 4) {
+    float2 v[4];
+    float a[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const bool in = s0 + j < ns;
+      const size_t row = row0 + (size_t)(s0 + j) * G;
+      v[j] = in ? reinterpret_cast<const float2*>(part_ml)[row] : make_float2(-INFINITY, 0.f);
+      a[j] = in ? part_o[row * D + d] : 0.f;
+    }
+    float mn = mx;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) mn = fmaxf(mn, v[j].x);
+    const float f = __builtin_amdgcn_exp2f(mx - mn);    // 0 on the first pass
+    l *= f;
+    o *= f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float e = __builtin_amdgcn_exp2f(v[j].x - mn);   // 0 for the padding entries
+      l += v[j].y * e;
+      o += a[j] * e;
+    }
+    mx = mn;
+  }
+  out[((size_t)b * num_q_heads + h) * D + d] = f32_to_bf16(o / l);
+}
+
 template <typename T, int D, int G>
 hipError_t launch_typed(const PoolDev& pool, const void* q, void* out, const int32_t* bt, int bt_stride,
                         const int32_t* ctx, int batch, int num_q_heads, float scale_log2, const DecodePlan& plan,
                         void* ws, hipStream_t s) {
   float* part_o = static_cast<float*>(ws);
   float* part_ml = part_o ? part_o + (size_t)batch * num_q_heads * plan.num_splits * D : nullptr;
+  if constexpr (sizeof(T) == 2) {
+    if (plan.stream_wgs > 0) {
+      float* ml = static_cast<float*>(ws) + (size_t)(plan.stream_wgs + batch * (num_q_heads / G)) * G * D;
+      hipLaunchKernelGGL((attn_decode_bf16_kernel<D, G, true>), dim3(plan.stream_wgs), dim3(kThreads), 0, s, pool,
+                         static_cast<const bf16_t*>(q), static_cast<bf16_t*>(out), bt, bt_stride, ctx, batch,
+                         num_q_heads, scale_log2, 0, 0, part_o, ml);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL((attn_decode_stream_merge_kernel<D>), dim3(num_q_heads, batch), dim3(D), 0, s, part_o, ml,
+                         ctx, static_cast<bf16_t*>(out), batch, num_q_heads, num_q_heads / G,
+                         bt_stride << pool.bs_shift, plan.stream_wgs);
+      return hipGetLastError();
+    }
+  }
   const dim3 grid(plan.num_splits, num_q_heads / G, batch);
   if constexpr (sizeof(T) == 2)
-    hipLaunchKernelGGL((attn_decode_bf16_kernel<D, G>), grid, dim3(kThreads), 0, s, pool,
-                       static_cast<const bf16_t*>(q), static_cast<bf16_t*>(out), bt, bt_stride, ctx, num_q_heads,
-                       scale_log2, plan.split_tokens, plan.num_splits, part_o, part_ml);
+    hipLaunchKernelGGL((attn_decode_bf16_kernel<D, G, false>), grid, dim3(kThreads), 0, s, pool,
+                       static_cast<const bf16_t*>(q), static_cast<bf16_t*>(out), bt, bt_stride, ctx, batch,
+                       num_q_heads, scale_log2, plan.split_tokens, plan.num_splits, part_o, part_ml);
   else
     hipLaunchKernelGGL((attn_decode_kernel<T, D, G>), grid, dim3(kThreads), 0, s, pool, static_cast<const T*>(q),
                        static_cast<T*>(out), bt, bt_stride, ctx, num_q_heads, scale_log2, plan.split_tokens,
@@ -653,7 +823,7 @@ hipError_t launch_d(int group, const PoolDev& pool, const void* q, void* out, co
 
 }  // namespace
 
-DecodePlan plan_decode(int batch, int num_q_heads, int num_kv_heads, int max_context_len, int head_dim) {
+DecodePlan plan_decode(int batch, int num_q_heads, int num_kv_heads, int max_context_len, int head_dim, int dtype) {
   // Two workgroups per CU (256 CUs) already keep enough loads in flight to
   // saturate HBM, so a batch with that many (request, KV head) pairs runs
   // one split per pair and needs no merge.  Below that a pair is cut into
@@ -678,8 +848,25 @@ DecodePlan plan_decode(int batch, int num_q_heads, int num_kv_heads, int max_con
   DecodePlan p;
   p.split_tokens = (int)split;
   p.num_splits = (int)((max_context_len + split - 1) / split);
+  p.stream_wgs = 0;
   // partial (acc, m, l) per (request, q-head, split)
   p.workspace = p.num_splits > 1 ? (size_t)batch * num_q_heads * p.num_splits * (head_dim + 2) * sizeof(float) : 0;
+  // bf16 with fewer pairs than resident workgroups and contexts long
+  // enough to need splits: the stream split instead (one resident round of
+  // two workgroups per CU, each taking an equal run of 32-key tiles, so
+  // uneven contexts cost no idle tail; partial rows (workgroups + pairs) * G)
+  static const int stream_wgs = [] {
+    const char* e = getenv("PKV_DECODE_STREAM_WGS");
+    const int v = e ? atoi(e) : 0;
+    return v > 0 ? v : 512;
+  }();
+  if (dtype == PKV_BF16 && pairs < 512 && p.num_splits > 1 && !forced) {
+    const long tiles = pairs * (((long)max_context_len + 31) / 32);
+    p.stream_wgs = (int)(tiles < stream_wgs ? tiles : stream_wgs);
+    p.split_tokens = 0;
+    p.num_splits = 0;
+    p.workspace = (size_t)(p.stream_wgs + pairs) * (num_q_heads / num_kv_heads) * (head_dim + 2) * sizeof(float);
+  }
   return p;
 }
 

@@ -153,7 +153,7 @@ int check_decode_step(const pkv_decode_step* d, std::vector<PoolDev>& pools, Dec
     return fail(PKV_EINVAL, "run_mux_round: num_q_heads %d", d->num_q_heads);
   if ((int64_t)d->bt_stride * p0.block_size < d->max_context_len)
     return fail(PKV_EINVAL, "run_mux_round: decode bt_stride too small");
-  plan = plan_decode(d->batch, d->num_q_heads, p0.num_kv_heads, d->max_context_len, p0.head_dim);
+  plan = plan_decode(d->batch, d->num_q_heads, p0.num_kv_heads, d->max_context_len, p0.head_dim, d->pools[0].dtype);
   if (plan.workspace > 0 && (!d->workspace || d->workspace_bytes < plan.workspace))
     return fail(PKV_EINVAL, "run_mux_round: decode workspace of %zu bytes needed", plan.workspace);
   return PKV_OK;

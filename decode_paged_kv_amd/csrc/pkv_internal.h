@@ -103,11 +103,12 @@ hipError_t launch_kv_relayout(const PoolDev& src, const int32_t* src_bt, const P
                               int dtype, int n_tokens, hipStream_t s);
 
 struct DecodePlan {
-  int split_tokens;   // keys per split (multiple of 64)
-  int num_splits;     // splits per (request, kv head) at max_context_len
-  size_t workspace;   // bytes of partial results needed (0 when num_splits == 1)
+  int split_tokens;   // keys per split (multiple of 32); split plan only
+  int num_splits;     // splits per (request, kv head) at max_context_len; split plan only
+  int stream_wgs;     // > 0: stream split over this many workgroups instead
+  size_t workspace;   // bytes of partial results needed (0: none)
 };
-DecodePlan plan_decode(int batch, int num_q_heads, int num_kv_heads, int max_context_len, int head_dim);
+DecodePlan plan_decode(int batch, int num_q_heads, int num_kv_heads, int max_context_len, int head_dim, int dtype);
 hipError_t launch_attn_decode(const PoolDev& pool, int dtype, const void* q, void* out, const int32_t* bt,
                               int bt_stride, const int32_t* ctx, int batch, int num_q_heads, float scale,
                               const DecodePlan& plan, void* workspace, hipStream_t s);

@@ -50,6 +50,8 @@ def oracle_decode(sc: Scenario, q_np):
     ("bf16", 32, 2, 64, 64, 2, [1, 333, 2000]),            # G = 16, head dim 64
     ("bf16", 8, 4, 128, 128, 1, [5, 256, 1025]),
     ("f32", 8, 2, 128, 32, 2, [1, 90, 513]),
+    # 512 (request, KV head) pairs: one workgroup per pair, no partials
+    ("bf16", 32, 8, 128, 16, 1, [int(x) for x in np.random.default_rng(11).integers(1, 600, 64)]),
 ])
 def test_decode_matches_oracle(dtype, hq, hkv, d, bs, shards, lengths):
     nblk = sum(-(-n // bs) for n in lengths) + 3
