@@ -173,12 +173,18 @@ int attn_prefill_chunk(const pkv_pool_layer* pool, const void* q, void* out, con
  *                   when that size is 0.  Calls that share a workspace must
  *                   be ordered on one stream.
  * scale <= 0 selects 1/sqrt(head_dim).
- * The library picks the split size (keys per workgroup) from the batch,
- * KV-head count and max_context_len; the environment variable
- * PKV_DECODE_SPLIT_TOKENS (a multiple of 32, read once) overrides it for
- * tuning; pkv_attn_decode_workspace_size accounts for it.  A request whose
- * context fits one split is finished by the attention kernel; the others
- * are merged by a second kernel on the same stream.
+ * The library picks the work split from the batch, KV-head count,
+ * max_context_len and dtype.  With at least 512 (request, KV head) pairs, or
+ * contexts short enough, every pair is one workgroup and no workspace is
+ * used.  Otherwise fp32 cuts each pair into equal splits of keys, and bf16
+ * uses a stream split: one round of workgroups (512, or the environment
+ * variable PKV_DECODE_STREAM_WGS, read once) each takes an equal run of
+ * 32-key tiles over the whole batch, so uneven contexts leave no idle tail.
+ * PKV_DECODE_SPLIT_TOKENS (a multiple of 32, read once) forces equal splits
+ * of that many keys, for tuning.  pkv_attn_decode_workspace_size accounts
+ * for all of these.  A pair handled by one workgroup is finished by the
+ * attention kernel; the partial results of the others are merged by a
+ * second kernel on the same stream.
  */
 size_t pkv_attn_decode_workspace_size(int32_t batch, int32_t num_q_heads, int32_t max_context_len,
                                       int32_t head_dim);
