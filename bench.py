@@ -78,14 +78,14 @@ def relayout_bytes(n, hkv, d, esize=2):
 PMC_SCALE = {"fetch": 2.0, "write": 1.0}
 TRAFFIC = {
     "attn_decode": {"sources": ['decode_paged_kv_amd/csrc/attn_decode.hip', 'decode_paged_kv_amd/csrc/pkv_internal.h'],
-                    "sha256": "fe06fc0946fb32efb574f5b6e8b49d36999dfa21906de3405f0fd391b0db193c",
-                    "fetch_kib": 66245.56, "write_kib": 512.0},
+                    "sha256": "20daf4a4721e752004cfc8a59b47b3637018cd2577604b4736c42b0af77ea956",
+                    "fetch_kib": 65949.26, "write_kib": 512.0},
     "attn_prefill_chunk": {"sources": ['decode_paged_kv_amd/csrc/attn_prefill.hip', 'decode_paged_kv_amd/csrc/pkv_internal.h'],
-                           "sha256": "a3b2e0b2f08944e6ad638663c0475dba892064673af0a632c045f6af1127c506",
-                           "fetch_kib": 27435.1, "write_kib": 13107.2},
+                           "sha256": "53c0fa6e78cb56acbfb1f2b3e40a3379a2c4dcdef1f5dd2981c3607478d65e90",
+                           "fetch_kib": 27173.41, "write_kib": 13107.73},
     "kv_relayout": {"sources": ['decode_paged_kv_amd/csrc/kv_ops.hip', 'decode_paged_kv_amd/csrc/pkv_internal.h'],
-                    "sha256": "ff9075f7713c947e70195c2629ec7733a0a631560f9298edab78b0b71b23b201",
-                    "fetch_kib": 8234.91, "write_kib": 16388.17},
+                    "sha256": "ad28fef6862dad8395b483ee1c69cb6a6afb7de3af697948e61af46bc73b9a62",
+                    "fetch_kib": 8234.90, "write_kib": 16388.02},
 }
 
 
