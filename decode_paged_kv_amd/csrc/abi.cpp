@@ -214,4 +214,60 @@ int attn_decode(const pkv_pool_layer* pool, const void* q, void* out, const int3
   return e == hipSuccess ? PKV_OK : hip_fail(e, "attn_decode");
 }
 
+int pkv_stall_free_chunk(int32_t token_budget, int32_t num_decode, int32_t prompt_remaining) {
+  g_last_error.clear();
+  if (token_budget < 0 || num_decode < 0 || prompt_remaining < 0)
+    return fail(PKV_EINVAL, "pkv_stall_free_chunk: negative argument");
+  const int32_t left = token_budget > num_decode ? token_budget - num_decode : 0;
+  return prompt_remaining < left ? prompt_remaining : left;
+}
+
+int attn_mixed_batch(const pkv_pool_layer* pool, const void* q_dec, void* out_dec, const int32_t* dec_block_tables,
+                     int32_t dec_bt_stride, const int32_t* context_lens, int32_t num_decode, int32_t max_context_len,
+                     const void* q_pf, void* out_pf, const int32_t* pf_block_tables, int32_t pf_bt_stride,
+                     const int32_t* start_loc, const int32_t* chunk_start, int32_t num_prefill,
+                     int32_t max_chunk_len, int32_t num_q_heads, float scale, void* workspace,
+                     size_t workspace_bytes, hipStream_t stream) {
+  g_last_error.clear();
+  PoolDev pd;
+  if (int rc = check_pool(pool, "attn_mixed_batch", &pd)) return rc;
+  if (int rc = check_heads(pd, num_q_heads)) return rc;
+  if (num_decode < 0 || num_prefill < 0 || max_chunk_len < 0)
+    return fail(PKV_EINVAL, "attn_mixed_batch: negative batch or chunk length");
+  if (!(scale >= 0.f) || std::isinf(scale)) return fail(PKV_EINVAL, "attn_mixed_batch: scale must be finite");
+  MixedDecode d{};
+  MixedPrefill p{};
+  if (num_decode > 0) {
+    if (max_context_len <= 0) return fail(PKV_EINVAL, "attn_mixed_batch: max_context_len %d", max_context_len);
+    if (!q_dec || !out_dec || !dec_block_tables || !context_lens)
+      return fail(PKV_EINVAL, "attn_mixed_batch: NULL decode array");
+    if (!aligned16(q_dec) || !aligned16(out_dec))
+      return fail(PKV_EINVAL, "attn_mixed_batch: decode q/out must be 16-byte aligned");
+    if (dec_bt_stride <= 0 || (int64_t)dec_bt_stride * pd.block_size < max_context_len)
+      return fail(PKV_EINVAL, "attn_mixed_batch: dec_bt_stride %d blocks cannot hold %d tokens", dec_bt_stride,
+                  max_context_len);
+    const DecodePlan plan =
+        plan_decode(num_decode, num_q_heads, pd.num_kv_heads, max_context_len, pd.head_dim, pool->dtype, false);
+    if (plan.workspace > 0) {
+      if (!workspace || workspace_bytes < plan.workspace)
+        return fail(PKV_EINVAL, "attn_mixed_batch: workspace of %zu bytes needed, %zu given", plan.workspace,
+                    workspace ? workspace_bytes : (size_t)0);
+      if (!aligned16(workspace)) return fail(PKV_EINVAL, "attn_mixed_batch: workspace must be 16-byte aligned");
+    }
+    d = MixedDecode{q_dec, out_dec, dec_block_tables, dec_bt_stride, context_lens, num_decode, plan, workspace};
+  }
+  if (num_prefill > 0 && max_chunk_len > 0) {
+    if (!q_pf || !out_pf || !pf_block_tables || !start_loc || !chunk_start)
+      return fail(PKV_EINVAL, "attn_mixed_batch: NULL prefill array");
+    if (!aligned16(q_pf) || !aligned16(out_pf))
+      return fail(PKV_EINVAL, "attn_mixed_batch: prefill q/out must be 16-byte aligned");
+    if (pf_bt_stride <= 0) return fail(PKV_EINVAL, "attn_mixed_batch: pf_bt_stride %d", pf_bt_stride);
+    if ((int64_t)max_chunk_len * 2 > INT32_MAX / 64) return fail(PKV_ERANGE, "attn_mixed_batch: chunk too long");
+    p = MixedPrefill{q_pf, out_pf, pf_block_tables, pf_bt_stride, start_loc, chunk_start, num_prefill, max_chunk_len};
+  }
+  if (d.batch == 0 && p.batch == 0) return PKV_OK;
+  hipError_t e = launch_attn_mixed(pd, pool->dtype, d, p, num_q_heads, resolve_scale(scale, pd.head_dim), stream);
+  return e == hipSuccess ? PKV_OK : hip_fail(e, "attn_mixed_batch");
+}
+
 }  // extern "C"

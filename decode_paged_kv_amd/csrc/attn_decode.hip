@@ -26,13 +26,13 @@
 // to the workspace and a second kernel merges them.
 #include <cstdlib>
 
-#include "pkv_internal.h"
+#include "decode_bf16.h"
 
 namespace pkv {
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kThreads = kWaves * 64;
+using namespace decode_impl;
+
 constexpr int kTile = 64;
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -267,416 +267,14 @@ attn_decode_kernel(PoolDev pool, const T* __restrict__ q, T* __restrict__ out, c
   }
 }
 
-// ------------------------------------------------------------------------
-// bf16 kernel.  Same work decomposition (one workgroup of 4 waves per
-// (split, KV head, request)); each wave walks 32-key tiles (tile i of the
-// split to wave i % 4).  A tile is two 16-key halves, each inside one block,
-// so a half's block id is wave-uniform: it is read with a scalar load and
-// the half's (block, head) K and V tiles are addressed through buffer
-// descriptors in scalar registers; a lane adds only a fixed offset.  Every
-// K/V byte is read once.  The V loads carry the non-temporal hint (each
-// instruction reads whole lines).  The K loads do not: one instruction
-// reads 64 bytes of each of 16 rows, the other half of every 128-byte line
-// comes with the next instruction, and without the hint the two halves meet
-// in the L1 (on a CU-masked half of the device this is worth about a fifth
-// of the decode bandwidth).
-//
-// The GQA group's contraction runs on the matrix cores, in transposed form
-// so the G <= 16 q-heads are the 16 columns of 16x16 MFMA tiles:
-//   S^T = K Q^T    v_mfma_f32_16x16x32_bf16 per (half, 32 head dims):
-//                  A = 16 K rows (lane l: key l%16, dims 8(l/16)..+7 of the
-//                  chunk, one 16-byte load), B = q (lane l: head l%16).
-//   softmax        lane l holds keys 4(l/16)..+3 of each half for head
-//                  l%16; the per-head max over the tile needs two lane swaps
-//                  (v_permlane16_swap, v_permlane32_swap); exp2 domain; the
-//                  running max moves only by more than a slack, so the
-//                  accumulators are rescaled rarely.
-//   O^T += V^T P^T v_mfma_f32_16x16x16_bf16 per (half, 16 head dims): the
-//                  S^T accumulator layout is already P's operand layout (4
-//                  keys per lane), and A = the dim-major V tile (lane l: dim
-//                  l%16, keys 4(l/16)..+3: 8 bytes; one instruction reads 16
-//                  whole 32-byte dim rows, 512 contiguous bytes).
-// Nothing goes through LDS until the final 4-wave merge.  The operand
-// registers of a wave's tile are refilled with its next tile as soon as
-// they are consumed: K right after S^T, V right after P V.  Three waves per
-// SIMD keep about 16 KB each in flight.
-// A request whose context fits one split writes its output directly;
-// otherwise each split writes its partial (m, l, acc) and the merge kernel
-// combines them (a device-wide handoff inside the kernel would need L2
-// write-back and invalidation on this multi-XCD part, costlier than a
-// second launch).
-// ------------------------------------------------------------------------
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef short s16x4_t __attribute__((ext_vector_type(4)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ f32x4_t mfma_qk(const uint4& a, const uint4& b, f32x4_t c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
-                                                 0, 0, 0);
-}
-__device__ __forceinline__ f32x4_t mfma_pv(const uint2& a, const uint2& b, f32x4_t c) {
-  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, a), __builtin_bit_cast(s16x4_t, b), c,
-                                                   0, 0, 0);
-}
-// reduce over the four lanes l, l^16, l^32, l^48 (one MFMA column)
-__device__ __forceinline__ float col_max(float v) {
-  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-  auto c = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(c[0]), __uint_as_float(c[1]));
-}
-__device__ __forceinline__ float col_sum(float v) {
-  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-  auto c = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return __uint_as_float(c[0]) + __uint_as_float(c[1]);
-}
-
-// One 32-key tile's MFMA operands and its two block ids (-1: absent).
-template <int D>
-struct DecodeTile {
-  uint4 k[2][D / 32];       // A of S^T: key 16h + l%16, dims 32c + 8(l/16) .. +7
-  uint2 v[2][D / 16];       // A of O^T: dim 16m + l%16, keys 16h + 4(l/16) .. +3
-  int blk[2];
-};
-
-template <int D, int G>
-struct DecodeBf16Smem {
-  float acc[kWaves][G][D];
-  float m[kWaves][G];
-  float l[kWaves][G];
-};
-
-// Running max update rule (log2 units): the max used for exp2 moves only
-// when a tile's max exceeds it by more than this, so p <= 2^8.
-constexpr float kDecodeSlack = 8.0f;
-
-// Stream split bookkeeping.  Request b holds Hkv * ceil(L_b / 32) pair-tiles
-// (L_b clamped to what its table addresses), laid out by request, then KV
-// head, then key.  scan_tiles returns the total, the request holding pair-
-// tile `target` (-1: none) with the index of its first pair-tile, and the
-// index of request rb's first pair-tile; every lane of the wave gets the
-// same values (a wave-wide prefix sum, 64 requests per pass).
-struct TileScan {
-  long long total;
-  int b;
-  long long base;
-  long long base_rb;
-  bool over;                                    // some context exceeds its table
-};
-__device__ __forceinline__ long long uniform64(long long x) {
-  const int lo = __builtin_amdgcn_readfirstlane((int)(unsigned)(unsigned long long)x);
-  const int hi = __builtin_amdgcn_readfirstlane((int)(unsigned)((unsigned long long)x >> 32));
-  return (long long)(((unsigned long long)(unsigned)hi << 32) | (unsigned)lo);
-}
-__device__ TileScan scan_tiles(const int32_t* __restrict__ ctx, int batch, int cap, int hkv, long long target, int rb) {
-  const int lane = threadIdx.x & 63;
-  long long run = 0, base = 0, base_rb = 0;
-  int fb = -1;
-  bool over = false;
-  for (int b0 = 0; b0 < batch; b0 += 64) {
-    const int bb = b0 + lane;
-    const int L = bb < batch ? ctx[bb] : 0;
-    over |= L > cap;
-    const long long x = (long long)hkv * ((max(min(L, cap), 0) + 31) >> 5);
-    long long inc = x;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const long long y = __shfl_up(inc, o);
-      if (lane >= o) inc += y;
-    }
-    const long long excl = run + inc - x;
-    const uint64_t hit = __builtin_amdgcn_ballot_w64(bb < batch && excl <= target && target < excl + x);
-    if (fb < 0 && hit) {
-      const int l = __builtin_ctzll(hit);
-      fb = b0 + l;
-      base = __shfl(excl, l);
-    }
-    if (rb >= b0 && rb < b0 + 64) base_rb = __shfl(excl, rb - b0);
-    run += __shfl(inc, 63);
-  }
-  TileScan r;
-  r.total = uniform64(run);
-  r.b = __builtin_amdgcn_readfirstlane(fb);
-  r.base = uniform64(base);
-  r.base_rb = uniform64(base_rb);
-  r.over = __builtin_amdgcn_ballot_w64(over) != 0;
-  return r;
-}
-// the workgroup whose pair-tile range holds pair-tile x (NW workgroups, W tiles)
-__device__ __forceinline__ long long stream_owner(long long x, long long NW, long long W) {
-  return ((x + 1) * NW + W - 1) / W - 1;
-}
-
 template <int D, int G, bool STREAM>
 __global__ void __launch_bounds__(kThreads, 2)
 attn_decode_bf16_kernel(PoolDev pool, const bf16_t* __restrict__ q, bf16_t* __restrict__ out,
                         const int32_t* __restrict__ bt, int bt_stride, const int32_t* __restrict__ ctx, int batch,
                         int num_q_heads, float scale_log2, int split_tokens, int num_splits,
                         float* __restrict__ part_o, float* __restrict__ part_ml) {
-  static_assert(G >= 1 && G <= 16, "the q-heads of a KV head are the 16 MFMA columns");
-  constexpr int KC = D / 32, DT = D / 16, TK = 32;
-  __shared__ DecodeBf16Smem<D, G> sm;
-
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int l16 = lane & 15, j4 = lane >> 4;
-  const int cap = bt_stride << pool.bs_shift;                   // keys the table can address
-  const int hl = pool.heads_per_shard;
-  const int bs = pool.block_size;
-  const size_t block_stride = (size_t)hl * bs * D;
-  const int tile_bytes = bs * D * 2;
-
-  // keys [start, end) of request b (context L) and KV head kvh; the result
-  // goes to out when final_out, else to the partial rows prow + g * pstride
-  auto segment = [&](int b, int kvh, int L, int start, int end, bool final_out, size_t prow, int pstride) {
-  const int sh = kvh / hl, lh = kvh - sh * hl;
-  const bf16_t* kpool = reinterpret_cast<const bf16_t*>(pool.k[sh]);
-  const bf16_t* vpool = reinterpret_cast<const bf16_t*>(pool.v[sh]);
-  const size_t head_off = (size_t)lh * bs * D;                  // elements
-  const int32_t* table = bt + (size_t)b * bt_stride;
-
-  // q as the B operand of S^T: head l16 (zero columns past G), dims 32c + 8 j4
-  uint4 qf[KC];
-  {
-    const bool hv = l16 < G;
-    const bf16_t* qrow = q + ((size_t)b * num_q_heads + (size_t)kvh * G + (hv ? l16 : 0)) * D + 8 * j4;
-#pragma unroll
-    for (int c = 0; c < KC; ++c) qf[c] = hv ? *reinterpret_cast<const uint4*>(qrow + 32 * c) : make_uint4(0, 0, 0, 0);
-  }
-
-  const int k_voff = (l16 * D + 8 * j4) * 2;                    // bytes within a half's 16 K rows
-  const int v_voff = (l16 * bs + 4 * j4) * 2;                   // dim l16 of a 16-dim slab, 4 keys
-  // block ids of the tile at k0 (-1: past the split or out of range)
-  auto fetch_ids = [&](int k0, int (&ids)[2]) {
-    bool bad = false;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int key16 = k0 + 16 * h;
-      const int blk = key16 < end ? table[key16 >> pool.bs_shift] : -1;
-      const bool ok = blk >= 0 && blk < pool.num_blocks;
-      bad |= key16 < end && !ok;
-      // the id is wave-uniform; saying so keeps the descriptors built from
-      // it in scalar registers
-      ids[h] = __builtin_amdgcn_readfirstlane(ok ? blk : -1);
-    }
-    if (bad && lane == 0) flag_error(pool.err, PKV_ERRBIT_BLOCK_ID);
-  };
-  auto issue_k = [&](int k0, DecodeTile<D>& r) {
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const bool ok = r.blk[h] >= 0;
-      const buffer_rsrc_t rs = buffer_rsrc(kpool + (ok ? (size_t)r.blk[h] * block_stride + head_off : 0),
-                                           ok ? tile_bytes : 0);
-      const int soff = ((k0 + 16 * h) & (bs - 1)) * D * 2;
-#pragma unroll
-      for (int c = 0; c < KC; ++c) r.k[h][c] = buffer_load16<kCached>(rs, k_voff + 64 * c, soff);
-    }
-  };
-  auto issue_v = [&](int k0, DecodeTile<D>& r) {
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const bool ok = r.blk[h] >= 0;
-      const buffer_rsrc_t rs = buffer_rsrc(vpool + (ok ? (size_t)r.blk[h] * block_stride + head_off : 0),
-                                           ok ? tile_bytes : 0);
-      const int soff = ((k0 + 16 * h) & (bs - 1)) * 2;
-#pragma unroll
-      for (int mm = 0; mm < DT; ++mm) r.v[h][mm] = buffer_load8<kStream>(rs, v_voff, soff + mm * 32 * bs);
-    }
-  };
-
-  f32x4_t o[DT];
-#pragma unroll
-  for (int mm = 0; mm < DT; ++mm) o[mm] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  // running max of head l16 (log2 units; finite start, so a tile whose keys
-  // are all absent gives p = exp2(-inf) = 0) and this lane's share of the sum
-  float m = -1e30f, lsum = 0.f;
-  constexpr uint32_t kOnes = 0x3F803F80u;       // bf16 (1, 1)
-
-  // one tile: S^T, softmax, P V; the registers are refilled with the tile
-  // at k0_next (< 0: none) as they are consumed, whose block ids were read
-  // one tile earlier into ids_next; then the ids of the tile at k0_next2
-  int ids_next[2] = {-1, -1};
-  auto process = [&](int k0, DecodeTile<D>& r, int k0_next, int k0_next2) {
-    f32x4_t st[2];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      st[h] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int c = 0; c < KC; ++c) st[h] = mfma_qk(r.k[h][c], qf[c], st[h]);
-    }
-    const bool ok0 = r.blk[0] >= 0, ok1 = r.blk[1] >= 0;
-    if (k0_next >= 0) {
-      r.blk[0] = ids_next[0];
-      r.blk[1] = ids_next[1];
-      issue_k(k0_next, r);
-      if (k0_next2 >= 0) fetch_ids(k0_next2, ids_next);
-    }
-    float x[2][4];
-    float mx = -INFINITY;
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int key = k0 + 16 * h + 4 * j4 + rr;
-        const bool valid = key < end && (h ? ok1 : ok0);
-        x[h][rr] = valid ? st[h][rr] : -INFINITY;
-        mx = fmaxf(mx, x[h][rr]);
-      }
-    mx = col_max(mx) * scale_log2;
-    const bool grow = mx > m + kDecodeSlack;
-    if (__builtin_amdgcn_ballot_w64(grow)) {          // wave-uniform branch
-      const float mnew = grow ? mx : m;
-      const float alpha = __builtin_amdgcn_exp2f(m - mnew);
-      m = mnew;
-      lsum *= alpha;
-#pragma unroll
-      for (int mm = 0; mm < DT; ++mm) o[mm] *= alpha;
-    }
-    uint2 pb[2];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      float p[4];
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) p[rr] = __builtin_amdgcn_exp2f(fmaf(x[h][rr], scale_log2, -m));
-      pb[h] = make_uint2(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]));
-      lsum = dot2_bf16(pb[h].x, kOnes, lsum);         // the sum of the same bf16 p the MFMA uses
-      lsum = dot2_bf16(pb[h].y, kOnes, lsum);
-    }
-    // the request's last tile: V entries of keys past the context hold
-    // arbitrary bits and must be zero (p = 0 times a NaN pattern is NaN)
-    if (k0 + TK > end) {
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int nvalid = end - (k0 + 16 * h + 4 * j4);
-#pragma unroll
-        for (int mm = 0; mm < DT; ++mm) {
-          if (nvalid <= 0) r.v[h][mm] = make_uint2(0, 0);
-          else if (nvalid < 4) {
-            uint32_t* w = reinterpret_cast<uint32_t*>(&r.v[h][mm]);
-#pragma unroll
-            for (int e = 1; e < 4; ++e)
-              if (e >= nvalid) w[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
-          }
-        }
-      }
-    }
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int mm = 0; mm < DT; ++mm) o[mm] = mfma_pv(r.v[h][mm], pb[h], o[mm]);
-    if (k0_next >= 0) issue_v(k0_next, r);
-  };
-
-  const int ntiles = (end - start + TK - 1) / TK;
-  // two tiles in flight per wave: ra holds tiles wave + 8i, rb tiles wave + 8i + 4
-  DecodeTile<D> ra, rb;
-  constexpr int W = kWaves;
-  if (wave < ntiles) {
-    fetch_ids(start + wave * TK, ra.blk);
-    issue_k(start + wave * TK, ra);
-    issue_v(start + wave * TK, ra);
-  }
-  if (wave + W < ntiles) {
-    fetch_ids(start + (wave + W) * TK, rb.blk);
-    issue_k(start + (wave + W) * TK, rb);
-    issue_v(start + (wave + W) * TK, rb);
-  }
-  if (wave + 2 * W < ntiles) fetch_ids(start + (wave + 2 * W) * TK, ids_next);
-  auto at = [&](int t) { return t < ntiles ? start + t * TK : -1; };
-  for (int t = wave; t < ntiles; t += 2 * W) {
-    process(start + t * TK, ra, at(t + 2 * W), at(t + 3 * W));
-    if (t + W < ntiles) process(start + (t + W) * TK, rb, at(t + 3 * W), at(t + 4 * W));
-  }
-
-  // ---- merge the 4 waves ----
-  lsum = col_sum(lsum);
-  if (l16 < G) {
-    if (j4 == 0) {
-      sm.m[wave][l16] = m;
-      sm.l[wave][l16] = lsum;
-    }
-#pragma unroll
-    for (int mm = 0; mm < DT; ++mm)
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) sm.acc[wave][l16][16 * mm + 4 * j4 + rr] = o[mm][rr];
-  }
-  __syncthreads();
-  for (int i = threadIdx.x; i < G * D; i += kThreads) {
-    const int g = i / D, d = i - g * D;
-    float mx = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) mx = fmaxf(mx, sm.m[w][g]);
-    float l = 0.f, acc = 0.f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const float f = __builtin_amdgcn_exp2f(sm.m[w][g] - mx);
-      l += sm.l[w][g] * f;
-      acc += sm.acc[w][g][d] * f;
-    }
-    const int h = kvh * G + g;
-    if (final_out) {
-      out[((size_t)b * num_q_heads + h) * D + d] = f32_to_bf16(acc / l);
-    } else {
-      const size_t row = prow + (size_t)g * pstride;
-      part_o[row * D + d] = acc;
-      if (d == 0) {
-        part_ml[row * 2 + 0] = mx;
-        part_ml[row * 2 + 1] = l;
-      }
-    }
-  }
-  __syncthreads();                              // the merge buffers are free again
-  };
-
-  if constexpr (!STREAM) {
-    // one segment: split blockIdx.x of (request blockIdx.z, KV head blockIdx.y)
-    const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
-    int L = ctx[b];
-    if (L > cap) {                              // never index past the request's table
-      if (threadIdx.x == 0 && split == 0 && kvh == 0) flag_error(pool.err, PKV_ERRBIT_TABLE);
-      L = cap;
-    }
-    const int start = split * split_tokens;
-    if (start >= L) return;
-    segment(b, kvh, L, start, min(L, start + split_tokens), L <= split_tokens,
-            ((size_t)b * num_q_heads + (size_t)kvh * G) * num_splits + split, num_splits);
-  } else {
-    // stream split: workgroup w takes the pair-tiles [w W / NW, (w+1) W / NW)
-    // of the W = Hkv * sum_b ceil(L_b / 32) tiles of the batch, ordered by
-    // request, KV head, key; a pair met by several workgroups leaves one
-    // partial per workgroup, in row (w + pair index) * G + g
-    const int hkv = num_q_heads / G;
-    const long long NW = gridDim.x, w = blockIdx.x;
-    const TileScan tot = scan_tiles(ctx, batch, cap, hkv, -1, 0);
-    if (tot.over && w == 0 && threadIdx.x == 0) flag_error(pool.err, PKV_ERRBIT_TABLE);
-    const long long W = tot.total;
-    long long t = w * W / NW;
-    const long long t1 = (w + 1) * W / NW;
-    if (t >= t1) return;
-    const TileScan at = scan_tiles(ctx, batch, cap, hkv, t, 0);
-    int b = at.b;
-    long long base = at.base;
-    while (t < t1) {
-      const int L = min(ctx[b], cap);
-      const int ntb = (L + TK - 1) / TK;
-      if (ntb == 0) {                           // an empty request holds no tiles
-        ++b;
-        continue;
-      }
-      const int kvh = (int)((t - base) / ntb);
-      const long long pstart = base + (long long)kvh * ntb;
-      const long long seg_end = min(t1, pstart + ntb);
-      const bool final_out = stream_owner(pstart, NW, W) == stream_owner(pstart + ntb - 1, NW, W);
-      segment(b, kvh, L, (int)(t - pstart) * TK, min(L, (int)(seg_end - pstart) * TK), final_out,
-              (size_t)(w + (long long)b * hkv + kvh) * G, 1);
-      t = seg_end;
-      if (t == base + (long long)hkv * ntb) {
-        base = t;
-        ++b;
-      }
-    }
-  }
+  decode_bf16_block<D, G, STREAM>(pool, q, out, bt, bt_stride, ctx, batch, num_q_heads, scale_log2, split_tokens,
+                                  num_splits, part_o, part_ml, blockIdx.x, blockIdx.y, blockIdx.z, gridDim.x);
 }
 
 // Merge the split partials of each (request, q-head): rescale each split's
@@ -823,7 +421,29 @@ hipError_t launch_d(int group, const PoolDev& pool, const void* q, void* out, co
 
 }  // namespace
 
-DecodePlan plan_decode(int batch, int num_q_heads, int num_kv_heads, int max_context_len, int head_dim, int dtype) {
+hipError_t launch_decode_split_merge(const PoolDev& pool, int dtype, void* out, const int32_t* ctx, int bt_stride,
+                                     int batch, int num_q_heads, const DecodePlan& plan, void* workspace,
+                                     hipStream_t s) {
+  if (batch == 0 || plan.stream_wgs > 0 || plan.num_splits <= 1) return hipSuccess;
+  const float* part_o = static_cast<const float*>(workspace);
+  const float* part_ml = part_o + (size_t)batch * num_q_heads * plan.num_splits * pool.head_dim;
+  const int max_len = bt_stride << pool.bs_shift;
+#define PKV_MERGE(T, DD)                                                                                           \
+  hipLaunchKernelGGL((attn_decode_merge_kernel<T, DD>), dim3(num_q_heads, batch), dim3(DD), 0, s, part_o, part_ml, \
+                     ctx, static_cast<T*>(out), num_q_heads, plan.split_tokens, plan.num_splits, max_len)
+  if (dtype == PKV_BF16) {
+    if (pool.head_dim == 128) PKV_MERGE(bf16_t, 128);
+    else PKV_MERGE(bf16_t, 64);
+  } else {
+    if (pool.head_dim == 128) PKV_MERGE(float, 128);
+    else PKV_MERGE(float, 64);
+  }
+#undef PKV_MERGE
+  return hipGetLastError();
+}
+
+DecodePlan plan_decode(int batch, int num_q_heads, int num_kv_heads, int max_context_len, int head_dim, int dtype,
+                       bool stream_ok) {
   // Two workgroups per CU (256 CUs) already keep enough loads in flight to
   // saturate HBM, so a batch with that many (request, KV head) pairs runs
   // one split per pair and needs no merge.  Below that a pair is cut into
@@ -860,7 +480,7 @@ DecodePlan plan_decode(int batch, int num_q_heads, int num_kv_heads, int max_con
     const int v = e ? atoi(e) : 0;
     return v > 0 ? v : 512;
   }();
-  if (dtype == PKV_BF16 && pairs < 512 && p.num_splits > 1 && !forced) {
+  if (stream_ok && dtype == PKV_BF16 && pairs < 512 && p.num_splits > 1 && !forced) {
     const long tiles = pairs * (((long)max_context_len + 31) / 32);
     p.stream_wgs = (int)(tiles < stream_wgs ? tiles : stream_wgs);
     p.split_tokens = 0;

@@ -108,12 +108,42 @@ struct DecodePlan {
   int stream_wgs;     // > 0: stream split over this many workgroups instead
   size_t workspace;   // bytes of partial results needed (0: none)
 };
-DecodePlan plan_decode(int batch, int num_q_heads, int num_kv_heads, int max_context_len, int head_dim, int dtype);
+// stream_ok = false: never the stream split (equal splits instead)
+DecodePlan plan_decode(int batch, int num_q_heads, int num_kv_heads, int max_context_len, int head_dim, int dtype,
+                       bool stream_ok = true);
+// the merge kernel of an equal-splits plan (no-op for other plans)
+hipError_t launch_decode_split_merge(const PoolDev& pool, int dtype, void* out, const int32_t* ctx, int bt_stride,
+                                     int batch, int num_q_heads, const DecodePlan& plan, void* workspace,
+                                     hipStream_t s);
 hipError_t launch_attn_decode(const PoolDev& pool, int dtype, const void* q, void* out, const int32_t* bt,
                               int bt_stride, const int32_t* ctx, int batch, int num_q_heads, float scale,
                               const DecodePlan& plan, void* workspace, hipStream_t s);
 hipError_t launch_attn_prefill(const PoolDev& pool, int dtype, const void* q, void* out, const int32_t* bt,
                                int bt_stride, const int32_t* start_loc, const int32_t* chunk_start, int batch,
                                int max_chunk_len, int num_q_heads, float scale, hipStream_t s);
+// decode (plan made with stream_ok = false) and prefill chunks of one layer
+// in one launch (bf16), decode workgroups first; fp32 runs the two kernels
+struct MixedDecode {
+  const void* q;
+  void* out;
+  const int32_t* bt;
+  int bt_stride;
+  const int32_t* ctx;
+  int batch;
+  DecodePlan plan;
+  void* workspace;
+};
+struct MixedPrefill {
+  const void* q;
+  void* out;
+  const int32_t* bt;
+  int bt_stride;
+  const int32_t* start_loc;
+  const int32_t* chunk_start;
+  int batch;
+  int max_chunk_len;
+};
+hipError_t launch_attn_mixed(const PoolDev& pool, int dtype, const MixedDecode& d, const MixedPrefill& p,
+                             int num_q_heads, float scale, hipStream_t s);
 
 }  // namespace pkv

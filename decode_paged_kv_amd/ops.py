@@ -137,6 +137,37 @@ def attn_decode(pool: PagedPool, q, out, block_tables, context_lens, max_context
     _lib.check(rc, "attn_decode")
 
 
+def stall_free_chunk(token_budget: int, num_decode: int, prompt_remaining: int) -> int:
+    """Tokens of a prompt that fit a stall-free step: what the decode requests leave of the budget."""
+    rc = int(_lib.load().pkv_stall_free_chunk(token_budget, num_decode, prompt_remaining))
+    _lib.check(rc if rc < 0 else 0, "pkv_stall_free_chunk")
+    return rc
+
+
+def attn_mixed_batch(pool: PagedPool, q_dec, out_dec, dec_block_tables, context_lens, max_context_len: int,
+                     q_pf, out_pf, pf_block_tables, start_loc, chunk_start, max_chunk_len: int, num_q_heads: int,
+                     scale: float = 0.0, workspace=None, stream=None):
+    """Decode attention for every request in context_lens and prefill attention for the chunks described by
+    start_loc / chunk_start, one launch (bf16).  Pass None for the tensors of an empty part."""
+    lib = _lib.load()
+    c = pool.c()
+    nd = 0 if context_lens is None else context_lens.numel()
+    npf = 0 if chunk_start is None else chunk_start.numel()
+    if workspace is None and nd > 0:
+        nbytes = attn_decode_workspace_size(nd, num_q_heads, max_context_len, pool.head_dim)
+        dev = q_dec.device
+        workspace = torch.zeros(max(nbytes, 16), dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    p = lambda t: None if t is None else _ptr(t)  # noqa: E731
+    rc = lib.attn_mixed_batch(C.byref(c), p(q_dec), p(out_dec), p(dec_block_tables),
+                              0 if dec_block_tables is None else dec_block_tables.shape[-1], p(context_lens), nd,
+                              max_context_len, p(q_pf), p(out_pf), p(pf_block_tables),
+                              0 if pf_block_tables is None else pf_block_tables.shape[-1], p(start_loc),
+                              p(chunk_start), npf, max_chunk_len, num_q_heads, scale, p(workspace), ws_bytes,
+                              _stream(stream))
+    _lib.check(rc, "attn_mixed_batch")
+
+
 def _ptr_array(tensors):
     arr = (C.c_void_p * len(tensors))()
     for i, t in enumerate(tensors):

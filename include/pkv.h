@@ -193,6 +193,40 @@ int attn_decode(const pkv_pool_layer* pool, const void* q, void* out, const int3
                 int32_t num_q_heads, float scale, void* workspace, size_t workspace_bytes,
                 hipStream_t stream);
 
+/*
+ * Stall-free mixed batch ([L7] section 2.4): each step takes
+ * every decoding request first, one token each, and fills what is left of a
+ * per-step token budget with prefill chunks, so the step time is bounded and
+ * decode never waits behind a prefill.
+ *
+ * pkv_stall_free_chunk - the chunk a prefill gets in a step:
+ * min(prompt_remaining, max(0, token_budget - num_decode)); 0 means the
+ * decode requests used the whole budget.  Returns -1 (EINVAL) for a negative
+ * argument.
+ */
+int pkv_stall_free_chunk(int32_t token_budget, int32_t num_decode, int32_t prompt_remaining);
+/*
+ * attn_mixed_batch - one layer of such a batch in a single launch: the
+ * decode attention of num_decode requests (arguments as attn_decode) and
+ * the prefill attention of num_prefill chunks (arguments as
+ * attn_prefill_chunk), the two sharing the pool and num_q_heads.  Decode
+ * workgroups are dispatched first and prefill workgroups fill the device as
+ * they finish; the outputs equal those of attn_decode and
+ * attn_prefill_chunk called one after the other.  Either part may be empty
+ * (num_decode = 0, or num_prefill = 0 / max_chunk_len = 0).  The decode part
+ * always uses equal splits of the context (the workspace needed is at most
+ * pkv_attn_decode_workspace_size(num_decode, ...)); when it needs more than
+ * one split, a merge kernel follows on the same stream.  bf16 runs one fused
+ * kernel; fp32 runs the two kernels back to back.  The chunks' own K/V must
+ * be written (kv_write) before the call.
+ */
+int attn_mixed_batch(const pkv_pool_layer* pool, const void* q_dec, void* out_dec, const int32_t* dec_block_tables,
+                     int32_t dec_bt_stride, const int32_t* context_lens, int32_t num_decode, int32_t max_context_len,
+                     const void* q_pf, void* out_pf, const int32_t* pf_block_tables, int32_t pf_bt_stride,
+                     const int32_t* start_loc, const int32_t* chunk_start, int32_t num_prefill,
+                     int32_t max_chunk_len, int32_t num_q_heads, float scale, void* workspace,
+                     size_t workspace_bytes, hipStream_t stream);
+
 /* ---------------------------------------------------------------------------
  * PD multiplexing on one GPU ([MUX] "SGLang's PD multiplexing").
  *

@@ -80,3 +80,21 @@ def choose_level(num_groups: int, decode_bs: int, has_prefill: bool, divisor: in
 def layers_per_round(prefill_tokens: int, num_layers: int, budget: int = 65536) -> int:
     """Layers of prefill submitted per multiplexing round."""
     return min(num_layers, max(1, budget // prefill_tokens))
+
+
+def stall_free_batch(token_budget: int, num_decode: int, prompts_remaining: list[int]) -> tuple[int, list[int]]:
+    """One step of a stall-free batch, following [L7] section 2.4.
+
+    Every decoding request joins the step first, one token each; then each
+    unfinished prompt, in order, takes at most what is left of the token
+    budget.  Returns (decode tokens, chunk per prompt).  Decode requests are
+    never dropped, so a budget at or below the decode count leaves the
+    prompts nothing.
+    """
+    left = max(0, token_budget - num_decode)
+    chunks = []
+    for rem in prompts_remaining:
+        take = min(rem, left)
+        chunks.append(take)
+        left -= take
+    return num_decode, chunks

@@ -35,7 +35,7 @@ def _declared_functions():
 def test_every_declared_symbol_is_exported():
     _lib()
     declared = _declared_functions()
-    assert "kv_write" in declared and "run_mux_round" in declared and len(declared) == 21
+    assert "kv_write" in declared and "run_mux_round" in declared and len(declared) == 23
     out = subprocess.run(["nm", "-D", "--defined-only", lib_mod.LIB_PATH], capture_output=True, text=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
     missing = [n for n in declared if n not in exported]
@@ -123,6 +123,19 @@ def test_attention_validation():
     assert lib.attn_prefill_chunk(C.byref(p), 0x100, 0x200, 0x300, 8, 0x400, 0x500, 1, 64, 30, 0.0, None) == -1
     assert lib.attn_prefill_chunk(C.byref(p), 0x108, 0x200, 0x300, 8, 0x400, 0x500, 1, 64, 32, 0.0, None) == -1
     assert lib.attn_prefill_chunk(C.byref(p), 0x100, 0x200, 0x300, 8, 0x400, 0x500, 0, 64, 32, 0.0, None) == 0
+    # mixed batch: both parts empty is a no-op; each part is validated like its own entry point
+    assert lib.attn_mixed_batch(C.byref(p), None, None, None, 0, None, 0, 0, None, None, None, 0, None, None, 0, 0,
+                                32, 0.0, None, 0, None) == 0
+    assert lib.attn_mixed_batch(C.byref(p), 0x100, 0x200, None, 8, 0x400, 2, 64, None, None, None, 0, None, None,
+                                0, 0, 32, 0.0, 0x500, 1 << 20, None) == -1          # NULL decode table
+    assert lib.attn_mixed_batch(C.byref(p), 0x100, 0x200, 0x300, 2, 0x400, 2, 64, None, None, None, 0, None, None,
+                                0, 0, 32, 0.0, 0x500, 1 << 20, None) == -1          # table too narrow
+    assert lib.attn_mixed_batch(C.byref(p), None, None, None, 0, None, 0, 0, 0x108, 0x200, 0x300, 8, 0x400,
+                                0x500, 1, 64, 32, 0.0, None, 0, None) == -1         # misaligned prefill q
+    assert lib.attn_mixed_batch(C.byref(p), None, None, None, 0, None, 0, 0, 0x100, 0x200, 0x300, 8, 0x400,
+                                0x500, 1, 64, 30, 0.0, None, 0, None) == -1         # heads not a multiple
+    assert lib.attn_mixed_batch(C.byref(p), 0x100, 0x200, 0x300, 512, 0x400, 4, 8192, None, None, None, 0, None,
+                                None, 0, 0, 32, 0.0, 0x500, 16, None) == -1         # workspace too small
 
 
 def test_slot_mapping_validation():
