@@ -519,7 +519,12 @@ def bench_pdmux(args):
       C  chunked prefill on the whole device: each step runs the decode step
          and then one chunk (2048 or 512 tokens) through all layers, on one
          stream;
-      D  prefill alone on the whole device (one stream).
+      D  prefill alone on the whole device (one stream);
+      E  stall-free batches on the whole device: each step takes every decode
+         request and the prompt's share of a token budget (2048 and 512, the
+         pages' loose and strict settings), per layer one attn_mixed_batch
+         launch, and for comparison the same chunks as attn_decode then
+         attn_prefill_chunk.
     A decode step's time is the host wall time of one round, which blocks on
     the decode stream (the inter-token interval a serving loop would see).
     """
@@ -609,6 +614,38 @@ def bench_pdmux(args):
             ts.append((time.perf_counter() - t0) * 1e3)
         return ts, (time.perf_counter() - t_start) * 1e3
 
+    def stall_free(key, budget, fused=True):
+        """Stall-free steps: every decode request plus the prompt's share of the token budget, per layer one
+        attn_mixed_batch launch (fused) or attn_decode then attn_prefill_chunk (same chunks, two launches)."""
+        n = prompts[key]
+        steps, s0 = [], 0
+        while s0 < n:
+            t = ops.stall_free_chunk(budget, B, n - s0)
+            if t <= 0:
+                raise RuntimeError("the decode requests fill the whole token budget")
+            steps.append((s0, t))
+            s0 += t
+        args_ = [(i32([0, t]), i32([s0]), ops.slot_mapping(pr_bt, i32([0, t]), i32([s0]), t, bs, w.pool_blocks))
+                 for s0, t in steps]
+        torch.cuda.synchronize()
+        ts = []
+        t_start = time.perf_counter()
+        for (s0, t), (sl, cs, slots) in zip(steps, args_):
+            t0 = time.perf_counter()
+            for l in range(L):
+                ops.kv_write(pools[l], kn[l], vn[l], dec_slots, stream=sh)
+                ops.kv_write(pools[l], k_pr[l][s0:s0 + t], v_pr[l][s0:s0 + t], slots, stream=sh)
+                if fused:
+                    ops.attn_mixed_batch(pools[l], q_dec[l], o_dec[l], dec_bt, ctx_t, ctx, q_pr[l][s0:s0 + t],
+                                         o_pr[l][s0:s0 + t], pr_bt, sl, cs, t, hq, workspace=ws, stream=sh)
+                else:
+                    ops.attn_decode(pools[l], q_dec[l], o_dec[l], dec_bt, ctx_t, ctx, hq, workspace=ws, stream=sh)
+                    ops.attn_prefill_chunk(pools[l], q_pr[l][s0:s0 + t], o_pr[l][s0:s0 + t], pr_bt, sl, cs, t, hq,
+                                           stream=sh)
+            stream.synchronize()
+            ts.append((time.perf_counter() - t0) * 1e3)
+        return ts, (time.perf_counter() - t_start) * 1e3
+
     def prefill_alone(key):
         n = prompts[key]
         torch.cuda.synchronize()
@@ -639,6 +676,13 @@ def bench_pdmux(args):
         for c in w.chunk_sizes:
             ts, tot = chunked(key, c)
             C[f"{key}_c{c}"] = {**stats(ts), "prefill_ms": round(tot, 2)}
+    E = {}
+    for key in ("16k", "32k"):
+        for budget in w.extra["stall_free_budgets"]:
+            for fused in (True, False):
+                ts, tot = stall_free(key, budget, fused)
+                E[f"{key}_b{budget}_{'fused' if fused else 'two_launches'}"] = {
+                    **stats(ts), "chunk": ops.stall_free_chunk(budget, B, prompts[key]), "prefill_ms": round(tot, 2)}
     D = {key: round(prefill_alone(key), 2) for key in prompts}
     mux.close()
     solo_med = float(np.median(A))
@@ -668,6 +712,7 @@ def bench_pdmux(args):
             "mux_over_solo_32k": round(float(np.median(B32)) / solo_med, 3),
             "level_sweep_16k": sweep,
             "chunked_whole_gpu": C,
+            "stall_free_whole_gpu": E,
             "prefill_alone_ms": D,
             "decode_bytes_per_step": decode_bytes([ctx] * B, hkv, d, hq) * L,
         },

@@ -7,15 +7,17 @@
 // decode step's idle compute is filled with prefill work) and section 2.3
 // (a chunk attends to everything before it plus the causal part of itself).
 //
-// One grid holds both kinds of workgroup.  The decode workgroups take the
-// low block ids, so the dispatcher starts them first (decode first); the
-// prefill workgroups fill the compute units as decode workgroups finish,
-// and on the whole device the bandwidth-bound decode work runs beside the
-// matrix-core-bound prefill work instead of after it.  Each workgroup runs
-// the same per-workgroup code as the separate decode and prefill kernels
+// One grid holds both kinds of workgroup, so on the whole device the
+// bandwidth-bound decode work runs beside the matrix-core-bound prefill work
+// instead of after it.  Decode first is the rule for what enters the batch;
+// inside the launch the step ends when its last workgroup does, so the
+// prefill workgroups (the long ones: a query tile walks every earlier key)
+// take the low block ids and are dispatched first, and the decode
+// workgroups fill the compute units around them.  Each workgroup runs the
+// same per-workgroup code as the separate decode and prefill kernels
 // (equal-splits decode plan; prefill with one key-tile group), so results
-// are those of the two kernels.  The decode block count is rounded up to a
-// multiple of the XCD count so the prefill blocks keep their XCD mapping.
+// are those of the two kernels.  The prefill block count is a multiple of
+// the XCD count, so the prefill blocks keep their XCD mapping.
 #include "decode_bf16.h"
 #include "prefill_bf16.h"
 
@@ -25,7 +27,8 @@ namespace {
 template <int D, int G>
 __global__ void __launch_bounds__(256, 2)
 attn_mixed_bf16_kernel(PoolDev pool,
-                       // decode part: equal splits, blocks (split, KV head, request) flattened split-fastest
+                       // decode part: equal splits, blocks (split, KV head, request) flattened split-fastest,
+                       // after the prefill blocks
                        const bf16_t* __restrict__ dq, bf16_t* __restrict__ dout, const int32_t* __restrict__ dbt,
                        int dbt_stride, const int32_t* __restrict__ ctx, int dbatch, int split_tokens,
                        int num_splits, float* __restrict__ part_o, float* __restrict__ part_ml, int dec_blocks,
@@ -33,20 +36,19 @@ attn_mixed_bf16_kernel(PoolDev pool,
                        const bf16_t* __restrict__ pq, bf16_t* __restrict__ pout, const int32_t* __restrict__ pbt,
                        int pbt_stride, const int32_t* __restrict__ start_loc, const int32_t* __restrict__ chunk_start,
                        int pbatch, int ntiles, int pf_items, int pf_blocks, int num_q_heads, float scale_log2) {
-  const int bid = blockIdx.x;
-  if (bid < dec_blocks) {
+  if ((int)blockIdx.x < pf_blocks) {
+    prefill_impl::prefill_bf16_block<D, 1>(pool, pq, pout, pbt, pbt_stride, start_loc, chunk_start, pbatch, ntiles,
+                                           num_q_heads, G, scale_log2, pf_items, blockIdx.x, pf_blocks);
+  } else {
+    const int bid = blockIdx.x - pf_blocks;
     const int hkv = num_q_heads / G;
     const int per_b = num_splits * hkv;
     const int b = bid / per_b;
-    if (b >= dbatch) return;                    // padding to a multiple of the XCD count
     const int rem = bid - b * per_b;
     const int kvh = rem / num_splits, split = rem - kvh * num_splits;
     decode_impl::decode_bf16_block<D, G, false>(pool, dq, dout, dbt, dbt_stride, ctx, dbatch, num_q_heads,
                                                 scale_log2, split_tokens, num_splits, part_o, part_ml, split, kvh, b,
                                                 0);
-  } else {
-    prefill_impl::prefill_bf16_block<D, 1>(pool, pq, pout, pbt, pbt_stride, start_loc, chunk_start, pbatch, ntiles,
-                                           num_q_heads, G, scale_log2, pf_items, bid - dec_blocks, pf_blocks);
   }
 }
 
@@ -57,8 +59,7 @@ template <int D, int G>
 hipError_t launch_mixed_dg(const PoolDev& pool, const MixedDecode& d, const MixedPrefill& p, int num_q_heads,
                            float scale, hipStream_t s) {
   const int hkv = num_q_heads / G;
-  int dec_blocks = d.batch > 0 ? d.plan.num_splits * hkv * d.batch : 0;
-  dec_blocks = (dec_blocks + kXcdCount - 1) / kXcdCount * kXcdCount;
+  const int dec_blocks = d.batch > 0 ? d.plan.num_splits * hkv * d.batch : 0;
   constexpr int BM = 128;
   const int ntiles = p.batch > 0 && p.max_chunk_len > 0 ? (p.max_chunk_len + BM - 1) / BM : 0;
   const int pf_items = hkv * ntiles * G * p.batch;

@@ -93,7 +93,9 @@ PDMUX_8B = Workload(
     block_size=16, dtype="bf16", input_scale=0.5, pool_blocks=32768,
     decode_batch=128, decode_context=(2048,) * 128, prompt_len=32768, chunk_sizes=(2048, 512),
     extra={"prompt_variant": 16384, "total_cus": 256, "cu_granularity": 8, "min_decode_cus": 32,
-           "group_num": 8, "decode_bs_divisor": 36, "token_budget": 65536},
+           "group_num": 8, "decode_bs_divisor": 36, "token_budget": 65536,
+           # stall-free token budgets: the pages' strict (512) and loose (2048) settings
+           "stall_free_budgets": (2048, 512)},
 )
 
 ALL = {w.config_id: w for w in (TINY, LLAMA3_8B, QWEN3_32B, RELAYOUT_70B, PDMUX_8B)}

@@ -210,9 +210,11 @@ int pkv_stall_free_chunk(int32_t token_budget, int32_t num_decode, int32_t promp
  * decode attention of num_decode requests (arguments as attn_decode) and
  * the prefill attention of num_prefill chunks (arguments as
  * attn_prefill_chunk), the two sharing the pool and num_q_heads.  Decode
- * workgroups are dispatched first and prefill workgroups fill the device as
- * they finish; the outputs equal those of attn_decode and
- * attn_prefill_chunk called one after the other.  Either part may be empty
+ * first is the rule for what enters the batch; inside the launch the
+ * prefill workgroups (the long ones) are dispatched first and the decode
+ * workgroups fill the device around them, since the step ends with its
+ * last workgroup.  The outputs equal those of attn_decode and
+ * attn_prefill_chunk called one after the other (to rounding order).  Either part may be empty
  * (num_decode = 0, or num_prefill = 0 / max_chunk_len = 0).  The decode part
  * always uses equal splits of the context (the workspace needed is at most
  * pkv_attn_decode_workspace_size(num_decode, ...)); when it needs more than
