@@ -48,6 +48,7 @@ struct pkv_mux {
   bool done_pending = false;     // event recorded, completion not yet seen
   bool prefill_finished = false; // completion seen; the level changes next round
   std::vector<int> used_levels;
+  std::vector<int> manual;       // decode-batch threshold of each split level (empty: the divisor rule)
 };
 
 namespace {
@@ -76,6 +77,31 @@ int choose(int n, int decode_bs, bool has_prefill, int divisor) {
   if (decode_bs > 0 && has_prefill) return std::min(n - 2, std::max(1, decode_bs * (n - 2) / divisor));
   if (decode_bs > 0) return n - 1;
   return 0;
+}
+
+// Manual divisions: split level i (1 .. n-2) is used from thresholds[i-1]
+// decode requests on (thresholds non-decreasing); below the first, level 1.
+int choose_manual(int n, int decode_bs, bool has_prefill, const int* thresholds) {
+  if (decode_bs > 0 && has_prefill) {
+    int level = 1;
+    for (int i = 1; i <= n - 2; ++i)
+      if (decode_bs >= thresholds[i - 1]) level = i;
+    return level;
+  }
+  if (decode_bs > 0) return n - 1;
+  return 0;
+}
+
+bool valid_thresholds(const int32_t* t, int n) {
+  for (int i = 0; i < n; ++i)
+    if (t[i] < 1 || (i && t[i] < t[i - 1])) return false;
+  return true;
+}
+
+int choose_m(const pkv_mux* m, int decode_bs, bool has_prefill) {
+  const int n = (int)m->groups.size();
+  if (!m->manual.empty()) return choose_manual(n, decode_bs, has_prefill, m->manual.data());
+  return choose(n, decode_bs, has_prefill, m->divisor);
 }
 
 // CU masks: decode takes the same number of CUs on every XCD.  Mask bit i of
@@ -276,7 +302,27 @@ int pkv_mux_groups(const pkv_mux* m, int32_t* prefill_cus, int32_t* decode_cus, 
 
 int pkv_mux_choose(const pkv_mux* m, int decode_bs, int has_prefill) {
   if (!m) return fail(PKV_EINVAL, "pkv_mux_choose: NULL mux");
-  return choose((int)m->groups.size(), decode_bs, has_prefill != 0, m->divisor);
+  return choose_m(m, decode_bs, has_prefill != 0);
+}
+
+int pkv_mux_policy_choose_manual(int num_groups, int decode_bs, int has_prefill, const int32_t* thresholds) {
+  if (num_groups < 3 || decode_bs < 0 || !thresholds || !valid_thresholds(thresholds, num_groups - 2))
+    return fail(PKV_EINVAL, "pkv_mux_policy_choose_manual");
+  std::vector<int> t(thresholds, thresholds + num_groups - 2);
+  return choose_manual(num_groups, decode_bs, has_prefill != 0, t.data());
+}
+
+int pkv_mux_set_manual_divisions(pkv_mux* m, const int32_t* thresholds, int32_t n) {
+  if (!m) return fail(PKV_EINVAL, "pkv_mux_set_manual_divisions: NULL mux");
+  if (n == 0) {
+    m->manual.clear();
+    return PKV_OK;
+  }
+  const int levels = (int)m->groups.size() - 2;
+  if (n != levels || !thresholds || !valid_thresholds(thresholds, n))
+    return fail(PKV_EINVAL, "pkv_mux_set_manual_divisions: need %d non-decreasing thresholds >= 1", levels);
+  m->manual.assign(thresholds, thresholds + n);
+  return PKV_OK;
 }
 
 int pkv_mux_set_level_override(pkv_mux* m, int level) {
@@ -332,7 +378,7 @@ int run_mux_round(pkv_mux* m, const pkv_decode_step* d, pkv_prefill_job* p, int3
   if (m->prefill_finished && !want_prefill) rechoose = true;
   if (!want_prefill && !m->level_with_prefill) rechoose = true;
   if (rechoose) {
-    int next = choose(ng, decode_bs, want_prefill, m->divisor);
+    int next = choose_m(m, decode_bs, want_prefill);
     if (want_prefill && decode_bs > 0 && m->override_level > 0) next = m->override_level;
     if (next != m->level)
       if (int rc = sync_level(m, m->level)) return rc;    // both streams of the old level drain first

@@ -253,6 +253,12 @@ class Mux:
     def set_level_override(self, level: int) -> None:
         _lib.check(_lib.load().pkv_mux_set_level_override(self._h, level), "pkv_mux_set_level_override")
 
+    def set_manual_divisions(self, thresholds) -> None:
+        """Decode batch size from which each split level is used (None or [] restores the divisor rule)."""
+        t = list(thresholds or [])
+        arr = (C.c_int32 * max(1, len(t)))(*t)
+        _lib.check(_lib.load().pkv_mux_set_manual_divisions(self._h, arr, len(t)), "pkv_mux_set_manual_divisions")
+
     def stream(self, level: int, which: int) -> int:
         return int(_lib.load().pkv_mux_stream(self._h, level, which) or 0)
 

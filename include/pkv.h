@@ -269,10 +269,17 @@ int pkv_mux_choose(const pkv_mux* mux, int decode_bs, int has_prefill);
 /* Layers per round for a prompt of prefill_tokens tokens. */
 int pkv_mux_layers_per_round(const pkv_mux* mux, int prefill_tokens, int num_layers);
 /* Fixes the level used while a prefill runs (1 .. group count - 2), in
- * place of the batch-size rule; -1 restores the rule.  The analogue of
- * spelling out the level per decode load by hand ([MUX] "SGLang's PD
- * multiplexing", manual divisions), used for level sweeps. */
+ * place of the batch-size rule; -1 restores the rule.  For level sweeps. */
 int pkv_mux_set_level_override(pkv_mux* mux, int level);
+/* Manual divisions ([MUX] "SGLang's PD multiplexing", level choice and its
+ * exercise): thresholds[i-1] is the decode batch size from which split
+ * level i is used (n = group count - 2 values, non-decreasing, >= 1); below
+ * the first threshold level 1.  It replaces the decode_bs_divisor rule while
+ * set; n = 0 restores the rule.  Decode only and prefill only still use the
+ * whole device.  pkv_mux_policy_choose_manual is the same rule without a
+ * mux (num_groups - 2 thresholds).  -1 (EINVAL) on a bad argument. */
+int pkv_mux_set_manual_divisions(pkv_mux* mux, const int32_t* thresholds, int32_t n);
+int pkv_mux_policy_choose_manual(int num_groups, int decode_bs, int has_prefill, const int32_t* thresholds);
 /* Stream of a group: which = 0 prefill, 1 decode (a hipStream_t). */
 void* pkv_mux_stream(const pkv_mux* mux, int level, int which);
 /* The 32-bit words of a group's CU mask (which = 0 prefill, 1 decode). */

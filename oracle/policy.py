@@ -98,3 +98,22 @@ def stall_free_batch(token_budget: int, num_decode: int, prompts_remaining: list
         chunks.append(take)
         left -= take
     return num_decode, chunks
+
+
+def choose_level_manual(num_groups: int, decode_bs: int, has_prefill: bool, thresholds: list[int]) -> int:
+    """Level choice with manual divisions ([MUX] "SGLang's PD multiplexing", level choice and its exercise).
+
+    ``thresholds[i-1]`` is the decode batch size from which split level ``i``
+    is used (one per split level, non-decreasing); below the first threshold
+    the first split level.  Decode only and prefill only keep the whole device.
+    """
+    assert len(thresholds) == num_groups - 2
+    if decode_bs > 0 and has_prefill:
+        level = 1
+        for i, t in enumerate(thresholds, start=1):
+            if decode_bs >= t:
+                level = i
+        return level
+    if decode_bs > 0:
+        return num_groups - 1
+    return 0

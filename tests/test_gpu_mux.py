@@ -160,3 +160,32 @@ def test_mux_prefill_only_and_decode_only():
         case.check_prefill()
     finally:
         mux.close()
+
+
+def test_mux_manual_divisions_pick_the_level():
+    # 4 decode requests: the divisor rule would pick level 1; thresholds
+    # that start level 5 at 4 requests move the round there
+    case = _MuxCase()
+    mux = ops.Mux(0, cu_granularity=8, min_decode_cus=32, sm_group_num=8, decode_bs_divisor=36, token_budget=1000)
+    try:
+        t = [1, 2, 3, 3, 4, 50]
+        mux.set_manual_divisions(t)
+        want = policy.choose_level_manual(len(mux.groups()), 4, True, t)
+        assert want == 5 and mux.choose(4, True) == want
+        levels, done = [], False
+        for _ in range(10):
+            lvl, done = mux.run_round(case.decode, case.prefill)
+            levels.append(lvl)
+            if done:
+                break
+        assert done and all(x == want for x in levels)
+        mux.wait_prefill()
+        torch.cuda.synchronize()
+        case.check_decode()
+        case.check_prefill()
+        mux.set_manual_divisions(None)
+        assert mux.choose(4, True) == policy.choose_level(len(mux.groups()), 4, True)
+        with pytest.raises(Exception):
+            mux.set_manual_divisions([1, 2, 3])      # one per split level
+    finally:
+        mux.close()

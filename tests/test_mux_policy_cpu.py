@@ -84,3 +84,30 @@ def test_policy_rejects_bad_arguments():
     assert lib.pkv_mux_policy_groups_grid(0, 8, 8, 32, 8, None, None, 0, C.byref(n)) == -1
     assert lib.pkv_mux_policy_choose(2, 1, 1, 36) == -1
     assert lib.pkv_mux_policy_layers_per_round(0, 32, 65536) == -1
+
+
+def test_manual_divisions_pins_and_library():
+    lib = _lib()
+    arr = lambda t: (C.c_int32 * len(t))(*t)  # noqa: E731
+    # the page's exercise: thresholds that make 24 decode requests pick the
+    # last of 6 split levels, as decode_bs_divisor = 24 does
+    t24 = [4, 8, 12, 16, 20, 24]
+    assert policy.choose_level_manual(8, 24, True, t24) == 6
+    assert policy.choose_level(8, 24, True, 24) == 6
+    # thresholds ceil(i * divisor / levels) reproduce the divisor rule at every batch size
+    for div in (24, 36, 100):
+        t = [-(-i * div // 6) for i in range(1, 7)]
+        for bs in range(0, 300):
+            for hp in (False, True):
+                assert policy.choose_level_manual(8, bs, hp, t) == policy.choose_level(8, bs, hp, div)
+    # below the first threshold: the first split level; decode only / prefill only: the whole device
+    assert policy.choose_level_manual(8, 1, True, [10, 20, 30, 40, 50, 60]) == 1
+    assert policy.choose_level_manual(8, 5, False, t24) == 7
+    assert policy.choose_level_manual(8, 0, True, t24) == 0
+    # library against the oracle, on uneven thresholds too
+    for t in (t24, [1, 1, 5, 9, 9, 200], [3, 6, 64, 65, 128, 129]):
+        for bs in range(0, 260, 3):
+            for hp in (0, 1):
+                assert lib.pkv_mux_policy_choose_manual(8, bs, hp, arr(t)) == policy.choose_level_manual(8, bs, bool(hp), t)
+    assert lib.pkv_mux_policy_choose_manual(8, 5, 1, arr([4, 3, 5, 6, 7, 8])) == -1     # decreasing
+    assert lib.pkv_mux_policy_choose_manual(8, 5, 1, arr([0, 3, 5, 6, 7, 8])) == -1     # below 1
