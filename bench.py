@@ -520,6 +520,8 @@ def bench_pdmux(args):
          and then one chunk (2048 or 512 tokens) through all layers, on one
          stream;
       D  prefill alone on the whole device (one stream);
+      A, B with the decode step captured as one HIP graph per level and
+         replayed (metrics "decode_graphs");
       E  stall-free batches on the whole device: each step takes every decode
          request and the prompt's share of a token budget (2048 and 512, the
          pages' loose and strict settings), per layer one attn_mixed_batch
@@ -666,6 +668,11 @@ def bench_pdmux(args):
     A = solo(max(10, args.steps))
     B16, pf16, lv16 = muxed("16k")
     B32, pf32, lv32 = muxed("32k")
+    # the same with the decode step as a per-level HIP graph
+    mux.set_decode_graphs(True)
+    Ag = solo(max(10, args.steps))
+    B16g, pf16g, _ = muxed("16k")
+    mux.set_decode_graphs(False)
     sweep = {}
     for lvl in range(1, len(groups) - 1):
         ts, pf, _ = muxed("16k", lvl)
@@ -710,6 +717,9 @@ def bench_pdmux(args):
             "mux_32k_decode": stats(B32), "mux_32k_prefill_ms": round(pf32, 2),
             "mux_over_solo_16k": round(mux_med / solo_med, 3),
             "mux_over_solo_32k": round(float(np.median(B32)) / solo_med, 3),
+            "decode_graphs": {"solo_decode": stats(Ag), "mux_16k_decode": stats(B16g),
+                              "mux_16k_prefill_ms": round(pf16g, 2),
+                              "mux_over_solo_16k": round(float(np.median(B16g)) / float(np.median(Ag)), 3)},
             "level_sweep_16k": sweep,
             "chunked_whole_gpu": C,
             "stall_free_whole_gpu": E,

@@ -14,6 +14,7 @@
 #include <algorithm>
 #include <array>
 #include <cmath>
+#include <cstring>
 #include <mutex>
 #include <vector>
 
@@ -49,6 +50,11 @@ struct pkv_mux {
   bool prefill_finished = false; // completion seen; the level changes next round
   std::vector<int> used_levels;
   std::vector<int> manual;       // decode-batch threshold of each split level (empty: the divisor rule)
+  // decode step as one HIP graph per level (opt-in): the captured launches
+  // and the arguments they were captured with
+  bool use_graphs = false;
+  std::vector<std::vector<uint64_t>> graph_sig;
+  std::vector<hipGraphExec_t> graph_exec;
 };
 
 namespace {
@@ -267,6 +273,8 @@ int pkv_mux_create(int device, int cu_granularity, int min_decode_cus, int sm_gr
   m->pmask.resize(n);
   m->dmask.resize(n);
   m->pstream.assign(n, nullptr);
+  m->graph_sig.assign(n, {});
+  m->graph_exec.assign(n, nullptr);
   m->dstream.assign(n, nullptr);
   for (size_t i = 0; i < n; ++i) build_masks(cus, m->groups[i].second, m->pmask[i], m->dmask[i]);
   e = hipStreamCreateWithFlags(&m->whole, hipStreamNonBlocking);
@@ -281,6 +289,8 @@ int pkv_mux_create(int device, int cu_granularity, int min_decode_cus, int sm_gr
 
 void pkv_mux_destroy(pkv_mux* m) {
   if (!m) return;
+  for (hipGraphExec_t g : m->graph_exec)
+    if (g) (void)hipGraphExecDestroy(g);
   for (size_t i = 0; i < m->pstream.size(); ++i) {
     if (m->pstream[i]) { (void)hipStreamSynchronize(m->pstream[i]); (void)hipStreamDestroy(m->pstream[i]); }
     if (m->dstream[i]) { (void)hipStreamSynchronize(m->dstream[i]); (void)hipStreamDestroy(m->dstream[i]); }
@@ -354,6 +364,98 @@ int pkv_mux_cu_mask(const pkv_mux* m, int level, int which, uint32_t* words, int
   return PKV_OK;
 }
 
+namespace {
+
+// Every argument a captured decode step depends on.
+std::vector<uint64_t> decode_signature(const pkv_decode_step* d) {
+  std::vector<uint64_t> v;
+  auto put = [&](uint64_t x) { v.push_back(x); };
+  auto ptr = [&](const void* x) { put((uint64_t)(uintptr_t)x); };
+  put((uint64_t)d->num_layers);
+  for (int l = 0; l < d->num_layers; ++l) {
+    const pkv_pool_layer& pl = d->pools[l];
+    for (int s = 0; s < PKV_MAX_SHARDS; ++s) {
+      ptr(pl.k[s]);
+      ptr(pl.v[s]);
+    }
+    put((uint64_t)pl.num_blocks);
+    put((uint64_t)pl.block_size);
+    put((uint64_t)pl.num_kv_heads);
+    put((uint64_t)pl.num_shards);
+    put((uint64_t)pl.head_dim);
+    put((uint64_t)pl.dtype);
+    ptr(d->q[l]);
+    ptr(d->k_new[l]);
+    ptr(d->v_new[l]);
+    ptr(d->out[l]);
+  }
+  ptr(d->slots);
+  ptr(d->block_tables);
+  ptr(d->context_lens);
+  ptr(d->workspace);
+  put((uint64_t)d->workspace_bytes);
+  put((uint64_t)d->bt_stride);
+  put((uint64_t)d->batch);
+  put((uint64_t)d->max_context_len);
+  put((uint64_t)d->num_q_heads);
+  uint32_t sb;
+  std::memcpy(&sb, &d->scale, sizeof(sb));
+  put(sb);
+  return v;
+}
+
+hipError_t launch_decode_step(const pkv_decode_step* d, const std::vector<PoolDev>& dpools, const DecodePlan& plan,
+                              hipStream_t ds) {
+  const float sc = scale_or_default(d->scale, dpools[0].head_dim);
+  for (int l = 0; l < d->num_layers; ++l) {
+    hipError_t e = launch_kv_write(dpools[l], d->pools[l].dtype, d->k_new[l], d->v_new[l], d->slots, d->batch, ds);
+    if (e == hipSuccess)
+      e = launch_attn_decode(dpools[l], d->pools[l].dtype, d->q[l], d->out[l], d->block_tables, d->bt_stride,
+                             d->context_lens, d->batch, d->num_q_heads, sc, plan, d->workspace, ds);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+// Runs the decode step on `ds` as the level's graph, capturing it first when
+// there is none or the arguments changed.
+hipError_t run_decode_graph(pkv_mux* m, int level, const pkv_decode_step* d, const std::vector<PoolDev>& dpools,
+                            const DecodePlan& plan, hipStream_t ds) {
+  std::vector<uint64_t> sig = decode_signature(d);
+  hipGraphExec_t& exec = m->graph_exec[level];
+  if (!exec || m->graph_sig[level] != sig) {
+    if (exec) {
+      (void)hipGraphExecDestroy(exec);
+      exec = nullptr;
+    }
+    hipError_t e = hipStreamBeginCapture(ds, hipStreamCaptureModeRelaxed);
+    if (e != hipSuccess) return e;
+    const hipError_t el = launch_decode_step(d, dpools, plan, ds);
+    hipGraph_t graph = nullptr;
+    e = hipStreamEndCapture(ds, &graph);
+    if (el != hipSuccess || e != hipSuccess) {
+      if (graph) (void)hipGraphDestroy(graph);
+      return el != hipSuccess ? el : e;
+    }
+    e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+    (void)hipGraphDestroy(graph);
+    if (e != hipSuccess) {
+      exec = nullptr;
+      return e;
+    }
+    m->graph_sig[level] = std::move(sig);
+  }
+  return hipGraphLaunch(exec, ds);
+}
+
+}  // namespace
+
+int pkv_mux_set_decode_graphs(pkv_mux* m, int enable) {
+  if (!m) return fail(PKV_EINVAL, "pkv_mux_set_decode_graphs: NULL mux");
+  m->use_graphs = enable != 0;
+  return PKV_OK;
+}
+
 int run_mux_round(pkv_mux* m, const pkv_decode_step* d, pkv_prefill_job* p, int32_t* level_out,
                   int32_t* prefill_done_out) {
   clear_error();
@@ -390,16 +492,10 @@ int run_mux_round(pkv_mux* m, const pkv_decode_step* d, pkv_prefill_job* p, int3
   if (int rc = ensure_streams(m, level)) return rc;
   hipStream_t ds = stream_of(m, level, 1), ps = stream_of(m, level, 0);
 
-  // ---- decode step on the decode stream ----
+  // ---- decode step on the decode stream (as the level's graph when on) ----
   if (d) {
-    const float sc = scale_or_default(d->scale, dpools[0].head_dim);
-    for (int l = 0; l < d->num_layers; ++l) {
-      e = launch_kv_write(dpools[l], d->pools[l].dtype, d->k_new[l], d->v_new[l], d->slots, d->batch, ds);
-      if (e == hipSuccess)
-        e = launch_attn_decode(dpools[l], d->pools[l].dtype, d->q[l], d->out[l], d->block_tables, d->bt_stride,
-                               d->context_lens, d->batch, d->num_q_heads, sc, plan, d->workspace, ds);
-      if (e != hipSuccess) return hip_fail(e, "run_mux_round(decode)");
-    }
+    e = m->use_graphs ? run_decode_graph(m, level, d, dpools, plan, ds) : launch_decode_step(d, dpools, plan, ds);
+    if (e != hipSuccess) return hip_fail(e, "run_mux_round(decode)");
   }
   // ---- next layers of the prefill on the prefill stream ----
   if (want_prefill) {

@@ -253,6 +253,10 @@ class Mux:
     def set_level_override(self, level: int) -> None:
         _lib.check(_lib.load().pkv_mux_set_level_override(self._h, level), "pkv_mux_set_level_override")
 
+    def set_decode_graphs(self, enable: bool) -> None:
+        """Capture each level's decode step as one HIP graph and replay it while its arguments stay the same."""
+        _lib.check(_lib.load().pkv_mux_set_decode_graphs(self._h, int(bool(enable))), "pkv_mux_set_decode_graphs")
+
     def set_manual_divisions(self, thresholds) -> None:
         """Decode batch size from which each split level is used (None or [] restores the divisor rule)."""
         t = list(thresholds or [])

@@ -279,6 +279,15 @@ int pkv_mux_set_level_override(pkv_mux* mux, int level);
  * whole device.  pkv_mux_policy_choose_manual is the same rule without a
  * mux (num_groups - 2 thresholds).  -1 (EINVAL) on a bad argument. */
 int pkv_mux_set_manual_divisions(pkv_mux* mux, const int32_t* thresholds, int32_t n);
+/* Per-level decode graphs ([MUX] "SGLang's PD multiplexing": a CUDA-graph
+ * state for each level): with enable != 0, run_mux_round captures the
+ * decode step (every layer's kv_write and attn_decode) as one HIP graph on
+ * the level's decode stream the first time it runs there, and replays it
+ * while the decode step's arguments (every pointer and size of
+ * pkv_decode_step and its pools) stay the same; a change recaptures.
+ * Results are those of the plain launches.  Off by default; the graphs are
+ * released by pkv_mux_destroy. */
+int pkv_mux_set_decode_graphs(pkv_mux* mux, int enable);
 int pkv_mux_policy_choose_manual(int num_groups, int decode_bs, int has_prefill, const int32_t* thresholds);
 /* Stream of a group: which = 0 prefill, 1 decode (a hipStream_t). */
 void* pkv_mux_stream(const pkv_mux* mux, int level, int which);

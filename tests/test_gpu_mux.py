@@ -189,3 +189,44 @@ def test_mux_manual_divisions_pick_the_level():
             mux.set_manual_divisions([1, 2, 3])      # one per split level
     finally:
         mux.close()
+
+
+def test_mux_decode_graphs_replay_the_eager_step():
+    # the decode step as a per-level HIP graph: every replay (with eager work
+    # and synchronizations in between) gives the bits of the plain launches,
+    # with and without a prefill on the complementary stream
+    case = _MuxCase(layers=2, ctx=(100, 37, 300, 64), prompt=500)
+    mux = ops.Mux(0, cu_granularity=8, min_decode_cus=32, sm_group_num=8, decode_bs_divisor=36, token_budget=1000)
+    try:
+        mux.run_round(case.decode, None)
+        torch.cuda.synchronize()
+        eager = [o.clone() for o in case.o_dec]
+        case.check_decode()
+        mux.set_decode_graphs(True)
+        scratch = torch.ones(1 << 20, device="cuda")
+        for i in range(4):
+            for o in case.o_dec:
+                o.zero_()
+            torch.cuda.synchronize()
+            mux.run_round(case.decode, None)
+            scratch.mul_(1.0001)                 # eager work between replays
+            torch.cuda.synchronize()
+            for got, want in zip(case.o_dec, eager):
+                assert torch.equal(got.view(torch.int16), want.view(torch.int16)), f"replay {i}"
+        # on a split level while a prefill runs
+        done = False
+        for _ in range(10):
+            for o in case.o_dec:
+                o.zero_()
+            _, done = mux.run_round(case.decode, case.prefill)
+            torch.cuda.synchronize()
+            for got, want in zip(case.o_dec, eager):
+                assert torch.equal(got.view(torch.int16), want.view(torch.int16))
+            if done:
+                break
+        assert done
+        mux.wait_prefill()
+        torch.cuda.synchronize()
+        case.check_prefill()
+    finally:
+        mux.close()
