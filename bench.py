@@ -17,7 +17,9 @@ Workloads (all synthetic, seeded, resident in HBM before timing):
   at chunk 512.  ``value`` is prefill-attention TFLOP/s.
 * ``relayout-70b``: 80 layers of a 4096-token request moved from block size
   16 / 4 shards to block size 32 / 8 shards, 80 calls back to back.
-  ``value`` is relayout HBM GB/s (read + write).
+  ``value`` is relayout HBM GB/s (read + write).  ``metrics`` adds the
+  converting relayout of the same layers into FP8 E4M3 token-major rows and
+  into a fused bf16 K/V tensor (kv_relayout_convert, timed separately).
 * ``pdmux``: the PD-multiplexing round (see ``bench_pdmux``).  ``value`` is
   the multiplexed decode step in ms.
 * ``copy-1gib``: a plain 1 GiB device copy, the known-size kernel that
@@ -456,8 +458,25 @@ def bench_relayout_70b(args):
 
     pg = PhaseGraphs(stream)
     pg.capture("relayout", relayout_all)
+    # the converting variant ([DISAGG] "布局转换"): into FP8 slot-major rows, and into a fused bf16 K/V tensor
+    conv = {"fp8_token_major": ("fp8", "token_major"), "bf16_kv_fused": ("bf16", "kv_fused")}
+    for name, (ddt, lay) in conv.items():
+        cdst = [ops.ConvertedPool(w.dst_pool_blocks, w.dst_block_size, hkv, w.dst_shards, d, ddt, lay, 0.02)
+                for _ in range(L)]
+
+        def convert_all(cdst=cdst):
+            for l in range(L):
+                ops.kv_relayout_convert(srcs[l], src_bt, cdst[l], dst_bt, N, stream=sh)
+        pg.capture(name, convert_all)
     step_ms = time_replays(pg, ["relayout"], args.steps, args.warmup)["relayout"]
+    t = time_replays(pg, list(conv), args.steps, args.warmup)
     per_layer = relayout_bytes(N, hkv, d)
+    conv_metrics = {}
+    for name, (ddt, _) in conv.items():
+        nbytes = per_layer // 2 * (1 + (0.5 if ddt == "fp8" else 1))   # bf16 read + destination write
+        ms = t[name] / L
+        conv_metrics[f"convert_{name}_gbps"] = round(nbytes / (ms * 1e-3) / 1e9, 1)
+        conv_metrics[f"convert_{name}_launch_ms"] = round(ms, 5)
     launch_ms = step_ms / L
     gbps = per_layer / (launch_ms * 1e-3) / 1e9
     result = {
@@ -474,7 +493,7 @@ def bench_relayout_70b(args):
                      "traffic": traffic_bytes("kv_relayout"), "bytes_per_launch": per_layer,
                      "launch_ms": round(launch_ms, 5)},
         "metrics": {"relayout_gbps": round(gbps, 1), "relayout_frac_hbm": round(gbps / HBM_PEAK_GBPS, 4),
-                    "relayout_launch_ms": round(launch_ms, 5)},
+                    "relayout_launch_ms": round(launch_ms, 5), **conv_metrics},
     }
     if args.cpu_baseline:
         result["cpu_baseline"] = cpu_baseline_relayout(w)

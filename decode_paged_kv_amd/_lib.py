@@ -9,7 +9,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libpkv.so")
 
 MAX_SHARDS = 16
-F32, BF16 = 0, 1
+F32, BF16, FP8_E4M3 = 0, 1, 2
+LAYOUT_POOL, LAYOUT_TOKEN_MAJOR, LAYOUT_KV_FUSED = 0, 1, 2
 OK, EINVAL, EUNSUPPORTED, EHIP, ERANGE = 0, -1, -2, -3, -4
 ERRBIT_BLOCK_ID, ERRBIT_SLOT, ERRBIT_TABLE = 1, 2, 4
 
@@ -35,6 +36,21 @@ class PoolLayer(C.Structure):
         ("head_dim", C.c_int32),
         ("dtype", C.c_int32),
         ("err_word", C.c_void_p),
+    ]
+
+
+class KvDest(C.Structure):
+    _fields_ = [
+        ("k", C.c_void_p * MAX_SHARDS),
+        ("v", C.c_void_p * MAX_SHARDS),
+        ("num_blocks", C.c_int32),
+        ("block_size", C.c_int32),
+        ("num_kv_heads", C.c_int32),
+        ("num_shards", C.c_int32),
+        ("head_dim", C.c_int32),
+        ("dtype", C.c_int32),
+        ("layout", C.c_int32),
+        ("scale", C.c_float),
     ]
 
 
@@ -88,6 +104,7 @@ _SIGS = {
     "pkv_slot_mapping": (C.c_int, [_P, _I, _P, _P, _I, _I, _I, _I, _P, _P, _P]),
     "kv_write": (C.c_int, [C.POINTER(PoolLayer), _P, _P, _P, _I, _P]),
     "kv_relayout": (C.c_int, [C.POINTER(PoolLayer), _P, C.POINTER(PoolLayer), _P, _I, _P]),
+    "kv_relayout_convert": (C.c_int, [C.POINTER(PoolLayer), _P, C.POINTER(KvDest), _P, _I, _P]),
     "attn_prefill_chunk": (C.c_int, [C.POINTER(PoolLayer), _P, _P, _P, _I, _P, _P, _I, _I, _I, C.c_float, _P]),
     "pkv_attn_decode_workspace_size": (C.c_size_t, [_I, _I, _I, _I]),
     "attn_decode": (C.c_int, [C.POINTER(PoolLayer), _P, _P, _P, _I, _P, _I, _I, _I, C.c_float, _P, C.c_size_t, _P]),

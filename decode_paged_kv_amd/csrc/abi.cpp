@@ -151,6 +151,53 @@ int kv_relayout(const pkv_pool_layer* src, const int32_t* src_bt, const pkv_pool
   return e == hipSuccess ? PKV_OK : hip_fail(e, "kv_relayout");
 }
 
+int kv_relayout_convert(const pkv_pool_layer* src, const int32_t* src_bt, const pkv_kv_dest* dst,
+                        const int32_t* dst_bt, int32_t n_tokens, hipStream_t stream) {
+  g_last_error.clear();
+  PoolDev ps;
+  if (int rc = check_pool(src, "kv_relayout_convert(src)", &ps)) return rc;
+  if (!dst) return fail(PKV_EINVAL, "kv_relayout_convert: dst is NULL");
+  if (dst->num_kv_heads != src->num_kv_heads || dst->head_dim != src->head_dim)
+    return fail(PKV_EINVAL, "kv_relayout_convert: heads/head_dim differ (%d/%d vs %d/%d)", src->num_kv_heads,
+                src->head_dim, dst->num_kv_heads, dst->head_dim);
+  if (dst->num_blocks <= 0) return fail(PKV_EINVAL, "kv_relayout_convert: dst num_blocks %d", dst->num_blocks);
+  if (log2_exact(dst->block_size) < 4 || dst->block_size > 128)
+    return fail(PKV_EUNSUPPORTED, "kv_relayout_convert: dst block_size %d (supported: 16, 32, 64, 128)",
+                dst->block_size);
+  if (dst->num_shards <= 0 || dst->num_shards > PKV_MAX_SHARDS || dst->num_kv_heads % dst->num_shards)
+    return fail(PKV_EUNSUPPORTED, "kv_relayout_convert: %d dst shards for %d kv heads", dst->num_shards,
+                dst->num_kv_heads);
+  if (dst->layout != PKV_LAYOUT_POOL && dst->layout != PKV_LAYOUT_TOKEN_MAJOR && dst->layout != PKV_LAYOUT_KV_FUSED)
+    return fail(PKV_EINVAL, "kv_relayout_convert: layout %d", dst->layout);
+  const bool fp8 = dst->dtype == PKV_FP8_E4M3;
+  if (!(dst->dtype == src->dtype || (fp8 && src->dtype == PKV_BF16)))
+    return fail(PKV_EUNSUPPORTED, "kv_relayout_convert: dtype %d -> %d", src->dtype, dst->dtype);
+  if (fp8 && !(dst->scale > 0.f && std::isfinite(dst->scale)))
+    return fail(PKV_EINVAL, "kv_relayout_convert: FP8 scale must be finite and > 0");
+  const size_t esize = fp8 ? 1 : (src->dtype == PKV_BF16 ? 2 : 4);
+  const size_t per_shard = (size_t)dst->num_blocks * (dst->num_kv_heads / dst->num_shards) * dst->block_size *
+                           dst->head_dim * esize * (dst->layout == PKV_LAYOUT_KV_FUSED ? 2 : 1);
+  if (per_shard > ((size_t)1 << 42)) return fail(PKV_ERANGE, "kv_relayout_convert: dst shard too large");
+  for (int t = 0; t < dst->num_shards; ++t) {
+    const bool need_v = dst->layout != PKV_LAYOUT_KV_FUSED;
+    if (!dst->k[t] || (need_v && !dst->v[t]))
+      return fail(PKV_EINVAL, "kv_relayout_convert: dst shard %d has a NULL buffer", t);
+    if (!aligned16(dst->k[t]) || (need_v && !aligned16(dst->v[t])))
+      return fail(PKV_EINVAL, "kv_relayout_convert: dst shard %d buffers must be 16-byte aligned", t);
+    for (int s = 0; s < src->num_shards; ++s)
+      if (dst->k[t] == src->k[s] || dst->k[t] == src->v[s] || (need_v && (dst->v[t] == src->k[s] || dst->v[t] == src->v[s])))
+        return fail(PKV_EINVAL, "kv_relayout_convert: source and destination share a buffer");
+  }
+  if (n_tokens < 0) return fail(PKV_EINVAL, "kv_relayout_convert: n_tokens %d", n_tokens);
+  if (n_tokens == 0) return PKV_OK;
+  if (!src_bt || !dst_bt) return fail(PKV_EINVAL, "kv_relayout_convert: NULL block table");
+  if ((int64_t)src->num_blocks * src->block_size < n_tokens || (int64_t)dst->num_blocks * dst->block_size < n_tokens)
+    return fail(PKV_EINVAL, "kv_relayout_convert: %d tokens do not fit a pool", n_tokens);
+  hipError_t e = launch_kv_relayout_convert(ps, src_bt, *dst, dst->num_kv_heads / dst->num_shards, dst_bt,
+                                            src->dtype, n_tokens, ps.err, stream);
+  return e == hipSuccess ? PKV_OK : hip_fail(e, "kv_relayout_convert");
+}
+
 int attn_prefill_chunk(const pkv_pool_layer* pool, const void* q, void* out, const int32_t* block_tables,
                        int32_t bt_stride, const int32_t* start_loc, const int32_t* chunk_start, int32_t batch,
                        int32_t max_chunk_len, int32_t num_q_heads, float scale, hipStream_t stream) {

@@ -187,7 +187,267 @@ kv_relayout_kernel(PoolDev src, const int32_t* __restrict__ src_bt, PoolDev dst,
   }
 }
 
+// ------------------------------------------------------ relayout + convert ----
+// One workgroup per (destination block j of the request, head), as
+// kv_relayout, for a destination that may differ in element type (bf16 ->
+// OCP E4M3 with a per-tensor scale) and layout (pool, token-major, K/V
+// fused).  Every global load is a 16-byte run of the source: K runs are
+// VEC dims of one token row, V runs are VEC tokens of one dim row (V is
+// dim-major in the source pool).  K runs map to token rows on every
+// destination, and so do V runs on the pool layout (dim rows there too).
+// For the token-major layouts, V is turned round in LDS: the dim-row runs
+// of up to 32 tokens are written into a token-major LDS tile, then read
+// back as VEC-dim runs of one token and stored, so both the loads and the
+// stores stay 16-byte runs (8-byte for E4M3).  Each thread issues its loads
+// of a round before converting and storing.
+struct ConvDest {
+  char* k[PKV_MAX_SHARDS];
+  char* v[PKV_MAX_SHARDS];
+  int num_blocks, block_size, heads_per_shard, head_dim, layout, esize;
+  float inv_scale;
+  int32_t* err;
+};
+
+// x * inv clamped to the largest finite E4M3 magnitude; NaN stays NaN (tested
+// on the bits: the library is built without NaN semantics for comparisons)
+__device__ __forceinline__ float fp8_sat(float x, float inv) {
+  const float f = x * inv;
+  const bool nan = (__float_as_uint(f) & 0x7fffffffu) > 0x7f800000u;
+  return nan ? f : fminf(fmaxf(f, -448.f), 448.f);
+}
+
+__device__ __forceinline__ uint8_t fp8_byte(float x, float inv) {
+  return (uint8_t)(__builtin_amdgcn_cvt_pk_fp8_f32(fp8_sat(x, inv), 0.f, 0, false) & 0xff);
+}
+
+// VEC source values -> destination bytes at dst (E4M3 when FP8); streamed stores
+template <typename T, bool FP8>
+__device__ __forceinline__ void store_run(char* dst, const T (&x)[16 / sizeof(T)], float inv) {
+  constexpr int VEC = 16 / sizeof(T);
+  if constexpr (FP8) {
+    static_assert(VEC == 8, "E4M3 from bf16 only");
+    uint32_t w[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      float f[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) f[j] = fp8_sat(bf16_to_f32(x[4 * i + j]), inv);
+      const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], 0, false);
+      w[i] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], lo, true);
+    }
+    typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+    typedef __attribute__((address_space(1))) u32x2_t global_u32x2_t;
+    const u32x2_t v = {w[0], w[1]};
+    __builtin_nontemporal_store(v, (global_u32x2_t*)dst);
+  } else {
+    uint4 v;
+    __builtin_memcpy(&v, x, 16);
+    store_nt16(dst, v);
+  }
+}
+
+// one element (ragged tails)
+template <typename T, bool FP8>
+__device__ __forceinline__ void store_one(char* dst, T x, float inv) {
+  if constexpr (FP8) *reinterpret_cast<uint8_t*>(dst) = fp8_byte(bf16_to_f32(x), inv);
+  else *reinterpret_cast<T*>(dst) = x;
+}
+
+constexpr int kConvTc = 32;         // tokens per chunk (and rows of the LDS transpose tile)
+
+template <typename T, bool FP8, int LAYOUT>
+__global__ void __launch_bounds__(kThreads)
+kv_relayout_convert_kernel(PoolDev src, const int32_t* __restrict__ src_bt, ConvDest dst,
+                           const int32_t* __restrict__ dst_bt, int n_tokens) {
+  constexpr int VEC = 16 / sizeof(T);
+  constexpr int ES = FP8 ? 1 : sizeof(T);           // destination element bytes
+  constexpr int LPAD = 8 / sizeof(T);              // 8-byte row pad of the LDS tile
+  constexpr bool kPoolV = LAYOUT == PKV_LAYOUT_POOL;
+  // 16-byte runs per thread per chunk, K and V each, at the largest head dim
+  constexpr int kConvNpt = kConvTc * 128 * (int)sizeof(T) / 16 / kThreads;
+  __shared__ int sblk[128 / 16];
+  __shared__ __align__(16) T vt[kPoolV ? 1 : kConvTc * (128 + LPAD)];
+  const int j = blockIdx.x, h = blockIdx.y;
+  const int D = dst.head_dim;
+  const int bsd = dst.block_size, bss = src.block_size;
+  const int p0 = j * bsd;
+  const int valid = min(bsd, n_tokens - p0);
+  const int dblk = dst_bt[j];
+  if (dblk < 0 || dblk >= dst.num_blocks) {
+    if (threadIdx.x == 0) flag_error(dst.err, PKV_ERRBIT_BLOCK_ID);
+    return;
+  }
+  const int first = p0 >> src.bs_shift;
+  const int nsrc = ((p0 + valid - 1) >> src.bs_shift) - first + 1;
+  if ((int)threadIdx.x < nsrc) {
+    int b = src_bt[first + threadIdx.x];
+    if (b < 0 || b >= src.num_blocks) {
+      flag_error(src.err, PKV_ERRBIT_BLOCK_ID);
+      b = -1;
+    }
+    sblk[threadIdx.x] = b;
+  }
+  __syncthreads();
+  const int hsd = dst.heads_per_shard;
+  const int dsh = h / hsd, dlh = h - dsh * hsd;
+  const int ssh = h / src.heads_per_shard, slh = h - ssh * src.heads_per_shard;
+  const T* sk = reinterpret_cast<const T*>(src.k[ssh]);
+  const T* sv = reinterpret_cast<const T*>(src.v[ssh]);
+  const size_t stile = (size_t)bss * D;
+  const int off0 = p0 & (bss - 1);
+  const float inv = dst.inv_scale;
+  // destination byte offset of element (token o, dim d) of K (kv = 0) or V (kv = 1)
+  auto dst_off = [&](int kv, int o, int d) -> size_t {
+    if constexpr (LAYOUT == PKV_LAYOUT_POOL) {
+      const size_t tile = ((size_t)dblk * hsd + dlh) * ((size_t)bsd * D);
+      return (tile + (kv ? (size_t)d * bsd + o : (size_t)o * D + d)) * ES;
+    } else {
+      const size_t row = LAYOUT == PKV_LAYOUT_KV_FUSED ? ((size_t)dblk * 2 + kv) * bsd + o : (size_t)dblk * bsd + o;
+      return ((row * hsd + dlh) * D + d) * ES;
+    }
+  };
+  // source element offsets of (span token r, dim d): K rows, V dim rows
+  auto src_k = [&](int b, int r, int d) {
+    return ((size_t)b * src.heads_per_shard + slh) * stile + (size_t)(r & (bss - 1)) * D + d;
+  };
+  auto src_v = [&](int b, int r, int d) {
+    return ((size_t)b * src.heads_per_shard + slh) * stile + (size_t)d * bss + (r & (bss - 1));
+  };
+  char* dk = dst.k[dsh];
+  char* dv = LAYOUT == PKV_LAYOUT_KV_FUSED ? dst.k[dsh] : dst.v[dsh];
+  const int rpt_shift = __builtin_ctz(D / VEC);    // runs per token row (K)
+  const int tc = min(bsd, kConvTc);                // tokens per chunk
+  const int vpk_shift = __builtin_ctz(tc / VEC);   // runs per dim row of a chunk (V)
+  const int ldsr = D + LPAD;
+  // Chunks of tc tokens.  Every load of a chunk (K rows, V dim rows, ragged
+  // tail elements) is issued and consumed before its first store, and the
+  // stores come last: a wait for a load issued after a store would also wait
+  // for the store.
+  for (int t0 = 0; t0 < valid; t0 += tc) {
+    const int nt = min(tc, valid - t0);
+    const int nk = nt << rpt_shift, nvr = D << vpk_shift;
+    uint4 kw[kConvNpt], vw[kConvNpt];
+    int kb[kConvNpt], vn[kConvNpt];                // K: source block (-1: none); V: elements present
+#pragma unroll
+    for (int u = 0; u < kConvNpt; ++u) {
+      const int e = threadIdx.x + u * kThreads;
+      {
+        const int o = e >> rpt_shift, d = (e & ((1 << rpt_shift) - 1)) * VEC;
+        const int b = e < nk ? sblk[(off0 + t0 + o) >> src.bs_shift] : -1;
+        kb[u] = b;
+        kw[u] = b >= 0 ? load_nt16(sk + src_k(b, off0 + t0 + o, d)) : make_uint4(0, 0, 0, 0);
+      }
+      {
+        const int d = e >> vpk_shift, o = (e & ((1 << vpk_shift) - 1)) * VEC;
+        const int b = (e < nvr && o < nt) ? sblk[(off0 + t0 + o) >> src.bs_shift] : -1;
+        vn[u] = b >= 0 ? min(VEC, nt - o) : 0;
+        vw[u] = vn[u] == VEC ? load_nt16(sv + src_v(b, off0 + t0 + o, d)) : make_uint4(0, 0, 0, 0);
+        if (vn[u] > 0 && vn[u] < VEC) {            // ragged tail of the request: element loads
+          const T* sp = sv + src_v(b, off0 + t0 + o, d);
+          T x[VEC];
+#pragma unroll
+          for (int i = 0; i < VEC; ++i) x[i] = i < vn[u] ? sp[i] : T(0);
+          __builtin_memcpy(&vw[u], x, 16);
+        }
+      }
+    }
+    if constexpr (!kPoolV) {
+      // V dim-row runs -> the LDS tile vt[token][dim] -> token-row runs
+#pragma unroll
+      for (int u = 0; u < kConvNpt; ++u) {
+        if (vn[u] == 0) continue;
+        const int e = threadIdx.x + u * kThreads;
+        const int d = e >> vpk_shift, o = (e & ((1 << vpk_shift) - 1)) * VEC;
+        T x[VEC];
+        __builtin_memcpy(x, &vw[u], 16);
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) vt[(o + i) * ldsr + d] = x[i];   // rows past nt are never read
+      }
+      __syncthreads();
+      for (int e = threadIdx.x; e < nk; e += kThreads) {
+        const int o = e >> rpt_shift, d = (e & ((1 << rpt_shift) - 1)) * VEC;
+        if (sblk[(off0 + t0 + o) >> src.bs_shift] < 0) continue;
+        T x[VEC];
+        const uint2* lp = reinterpret_cast<const uint2*>(&vt[o * ldsr + d]);
+        const uint2 a = lp[0], c = lp[1];
+        __builtin_memcpy(x, &a, 8);
+        __builtin_memcpy(reinterpret_cast<char*>(x) + 8, &c, 8);
+        store_run<T, FP8>(dv + dst_off(1, t0 + o, d), x, inv);
+      }
+    } else {
+      // V dim-row runs -> the pool layout's dim rows
+#pragma unroll
+      for (int u = 0; u < kConvNpt; ++u) {
+        if (vn[u] == 0) continue;
+        const int e = threadIdx.x + u * kThreads;
+        const int d = e >> vpk_shift, o = (e & ((1 << vpk_shift) - 1)) * VEC;
+        T x[VEC];
+        __builtin_memcpy(x, &vw[u], 16);
+        if (vn[u] == VEC) {
+          store_run<T, FP8>(dv + dst_off(1, t0 + o, d), x, inv);
+        } else {
+#pragma unroll
+          for (int i = 0; i < VEC; ++i)
+            if (i < vn[u]) store_one<T, FP8>(dv + dst_off(1, t0 + o + i, d), x[i], inv);
+        }
+      }
+    }
+    // K: token rows -> token rows
+#pragma unroll
+    for (int u = 0; u < kConvNpt; ++u) {
+      if (kb[u] < 0) continue;
+      const int e = threadIdx.x + u * kThreads;
+      const int o = e >> rpt_shift, d = (e & ((1 << rpt_shift) - 1)) * VEC;
+      T x[VEC];
+      __builtin_memcpy(x, &kw[u], 16);
+      store_run<T, FP8>(dk + dst_off(0, t0 + o, d), x, inv);
+    }
+    if (!kPoolV && t0 + tc < valid) __syncthreads();   // the tile is rewritten by the next chunk
+  }
+}
+
+template <typename T, bool FP8>
+void launch_convert_layout(int layout, dim3 grid, hipStream_t s, const PoolDev& src, const int32_t* src_bt,
+                           const ConvDest& cd, const int32_t* dst_bt, int n_tokens) {
+  if (layout == PKV_LAYOUT_POOL)
+    hipLaunchKernelGGL((kv_relayout_convert_kernel<T, FP8, PKV_LAYOUT_POOL>), grid, dim3(kThreads), 0, s, src,
+                       src_bt, cd, dst_bt, n_tokens);
+  else if (layout == PKV_LAYOUT_TOKEN_MAJOR)
+    hipLaunchKernelGGL((kv_relayout_convert_kernel<T, FP8, PKV_LAYOUT_TOKEN_MAJOR>), grid, dim3(kThreads), 0, s, src,
+                       src_bt, cd, dst_bt, n_tokens);
+  else
+    hipLaunchKernelGGL((kv_relayout_convert_kernel<T, FP8, PKV_LAYOUT_KV_FUSED>), grid, dim3(kThreads), 0, s, src,
+                       src_bt, cd, dst_bt, n_tokens);
+}
+
 }  // namespace
+
+hipError_t launch_kv_relayout_convert(const PoolDev& src, const int32_t* src_bt, const pkv_kv_dest& dst,
+                                      int heads_per_shard, const int32_t* dst_bt, int src_dtype, int n_tokens,
+                                      int32_t* err, hipStream_t s) {
+  if (n_tokens == 0) return hipSuccess;
+  ConvDest cd{};
+  for (int i = 0; i < PKV_MAX_SHARDS; ++i) {
+    cd.k[i] = static_cast<char*>(dst.k[i]);
+    cd.v[i] = static_cast<char*>(dst.v[i]);
+  }
+  cd.num_blocks = dst.num_blocks;
+  cd.block_size = dst.block_size;
+  cd.heads_per_shard = heads_per_shard;
+  cd.head_dim = dst.head_dim;
+  cd.layout = dst.layout;
+  cd.esize = dst.dtype == PKV_FP8_E4M3 ? 1 : (src_dtype == PKV_BF16 ? 2 : 4);
+  cd.inv_scale = dst.dtype == PKV_FP8_E4M3 ? 1.0f / dst.scale : 1.0f;
+  cd.err = err;
+  const dim3 grid((n_tokens + dst.block_size - 1) / dst.block_size, dst.num_kv_heads);
+  if (dst.dtype == PKV_FP8_E4M3)
+    launch_convert_layout<bf16_t, true>(dst.layout, grid, s, src, src_bt, cd, dst_bt, n_tokens);
+  else if (src_dtype == PKV_BF16)
+    launch_convert_layout<bf16_t, false>(dst.layout, grid, s, src, src_bt, cd, dst_bt, n_tokens);
+  else
+    launch_convert_layout<float, false>(dst.layout, grid, s, src, src_bt, cd, dst_bt, n_tokens);
+  return hipGetLastError();
+}
 
 hipError_t launch_slot_mapping(const int32_t* bt, int bt_stride, const int32_t* start_loc, const int32_t* pos_start,
                                int batch, int num_tokens, int block_size, int num_blocks, int32_t* slots,

@@ -101,6 +101,9 @@ hipError_t launch_kv_write(const PoolDev& pool, int dtype, const void* k, const 
                            int n_tokens, hipStream_t s);
 hipError_t launch_kv_relayout(const PoolDev& src, const int32_t* src_bt, const PoolDev& dst, const int32_t* dst_bt,
                               int dtype, int n_tokens, hipStream_t s);
+hipError_t launch_kv_relayout_convert(const PoolDev& src, const int32_t* src_bt, const pkv_kv_dest& dst,
+                                      int heads_per_shard, const int32_t* dst_bt, int src_dtype, int n_tokens,
+                                      int32_t* err, hipStream_t s);
 
 struct DecodePlan {
   int split_tokens;   // keys per split (multiple of 32); split plan only

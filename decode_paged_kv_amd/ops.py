@@ -13,7 +13,8 @@ import ctypes as C
 import torch
 
 from . import _lib
-from ._lib import BF16, F32, DecodeStep, PkvError, PkvLibraryMissing, PoolLayer, PrefillJob  # noqa: F401
+from ._lib import BF16, F32, FP8_E4M3, DecodeStep, KvDest, PkvError, PkvLibraryMissing, PoolLayer, PrefillJob  # noqa: F401
+from ._lib import LAYOUT_KV_FUSED, LAYOUT_POOL, LAYOUT_TOKEN_MAJOR  # noqa: F401
 
 _TORCH_DTYPE = {"bf16": torch.bfloat16, "f32": torch.float32}
 _CODE = {"bf16": BF16, "f32": F32}
@@ -106,6 +107,56 @@ def kv_relayout(src: PagedPool, src_bt, dst: PagedPool, dst_bt, n_tokens: int, s
     lib = _lib.load()
     _lib.check(lib.kv_relayout(C.byref(src.c()), _ptr(src_bt), C.byref(dst.c()), _ptr(dst_bt), n_tokens,
                                _stream(stream)), "kv_relayout")
+
+
+class ConvertedPool:
+    """Destination of kv_relayout_convert: one layer in another element type and/or physical layout.
+
+    ``dtype`` is "bf16", "f32" or "fp8" (E4M3 bits, stored as uint8; values are bits x ``scale``).  Per shard:
+    layout "pool" ``k[s]`` [blocks, H/S, bs, D] and ``v[s]`` [blocks, H/S, D, bs]; "token_major" ``k[s]`` and
+    ``v[s]`` [blocks, bs, H/S, D]; "kv_fused" ``k[s]`` [blocks, 2, bs, H/S, D] (K then V) and no ``v``.
+    """
+
+    _LAYOUT = {"pool": LAYOUT_POOL, "token_major": LAYOUT_TOKEN_MAJOR, "kv_fused": LAYOUT_KV_FUSED}
+    _TD = {"bf16": torch.bfloat16, "f32": torch.float32, "fp8": torch.uint8}
+    _DT = {"bf16": BF16, "f32": F32, "fp8": FP8_E4M3}
+
+    def __init__(self, num_blocks, block_size, num_kv_heads, num_shards, head_dim, dtype="bf16", layout="pool",
+                 scale=1.0, device="cuda"):
+        self.num_blocks, self.block_size = num_blocks, block_size
+        self.num_kv_heads, self.num_shards, self.head_dim = num_kv_heads, num_shards, head_dim
+        self.dtype, self.layout, self.scale = dtype, layout, float(scale)
+        hl, td = num_kv_heads // num_shards, self._TD[dtype]
+        if layout == "pool":
+            ks, vs = (num_blocks, hl, block_size, head_dim), (num_blocks, hl, head_dim, block_size)
+        elif layout == "token_major":
+            ks = vs = (num_blocks, block_size, hl, head_dim)
+        else:
+            ks, vs = (num_blocks, 2, block_size, hl, head_dim), None
+        self.k = [torch.empty(ks, dtype=td, device=device) for _ in range(num_shards)]
+        self.v = [torch.empty(vs, dtype=td, device=device) for _ in range(num_shards)] if vs else []
+
+    def fill_bits(self, pattern: int) -> "ConvertedPool":
+        view = {"bf16": torch.int16, "f32": torch.int32, "fp8": torch.uint8}[self.dtype]
+        for t in self.k + self.v:
+            t.view(view).fill_(pattern)
+        return self
+
+    def c(self) -> KvDest:
+        s = KvDest()
+        for i in range(self.num_shards):
+            s.k[i] = self.k[i].data_ptr()
+            s.v[i] = self.v[i].data_ptr() if self.v else None
+        s.num_blocks, s.block_size = self.num_blocks, self.block_size
+        s.num_kv_heads, s.num_shards, s.head_dim = self.num_kv_heads, self.num_shards, self.head_dim
+        s.dtype, s.layout, s.scale = self._DT[self.dtype], self._LAYOUT[self.layout], self.scale
+        return s
+
+
+def kv_relayout_convert(src: PagedPool, src_bt, dst: ConvertedPool, dst_bt, n_tokens: int, stream=None):
+    lib = _lib.load()
+    _lib.check(lib.kv_relayout_convert(C.byref(src.c()), _ptr(src_bt), C.byref(dst.c()), _ptr(dst_bt), n_tokens,
+                                       _stream(stream)), "kv_relayout_convert")
 
 
 def attn_prefill_chunk(pool: PagedPool, q, out, block_tables, start_loc, chunk_start, max_chunk_len: int,

@@ -58,7 +58,7 @@ extern "C" {
 #define PKV_MAX_SHARDS 16
 #define PKV_VERSION 1
 
-enum { PKV_F32 = 0, PKV_BF16 = 1 };
+enum { PKV_F32 = 0, PKV_BF16 = 1, PKV_FP8_E4M3 = 2 /* kv_relayout_convert destinations only */ };
 
 enum {
   PKV_OK = 0,
@@ -137,6 +137,49 @@ int kv_write(const pkv_pool_layer* pool, const void* k, const void* v, const int
  */
 int kv_relayout(const pkv_pool_layer* src, const int32_t* src_bt, const pkv_pool_layer* dst,
                 const int32_t* dst_bt, int32_t n_tokens, hipStream_t stream);
+
+/*
+ * kv_relayout_convert - kv_relayout into a destination that also differs in
+ * element type and/or physical layout.  [DISAGG] "布局转换" lists, besides
+ * block size and head split, the attention backend's layout (K and V fused
+ * or not, the order of the head and token dimensions) and the KV dtype (BF16
+ * on one side, FP8 on the other), all best converted on the GPU around the
+ * transfer.
+ * Destination layouts (per shard s, local head lh, block b, offset o, dim d):
+ *   PKV_LAYOUT_POOL        this library's pool: k[s][b][lh][o][d],
+ *                          v[s][b][lh][d][o] (readable by the attention calls
+ *                          when the dtype is PKV_BF16 or PKV_F32)
+ *   PKV_LAYOUT_TOKEN_MAJOR k[s][b][o][lh][d] and v[s][b][o][lh][d] (slot-major
+ *                          rows, the pages' [slot, kv_heads, head_dim] view)
+ *   PKV_LAYOUT_KV_FUSED    k[s][b][0][o][lh][d] for K and k[s][b][1][o][lh][d]
+ *                          for V in one tensor per shard (v[] unused)
+ * Element types: the source's dtype, or PKV_FP8_E4M3 from a PKV_BF16 source:
+ * OCP E4M3 ("fn": bias 7, no infinities, largest finite 448), stored value =
+ * round-to-nearest-even of clamp(x * fp32(1 / scale), -448, 448), the
+ * fp32 reciprocal and product being IEEE fp32 operations; the reader
+ * multiplies by scale; a NaN input stays a NaN code (0x7F or 0xFF).  scale
+ * must be finite and > 0 (ignored without a dtype change).  Tokens at or
+ * past n_tokens are not written.  Everything else as kv_relayout (tables,
+ * shards, the source's error word, no overlap).
+ * Errors: PKV_EINVAL for NULL/misaligned (16 B) buffers, shape mismatch,
+ * bad layout or scale; PKV_EUNSUPPORTED for block sizes, shard counts or
+ * dtype pairs outside the lists above.
+ */
+enum { PKV_LAYOUT_POOL = 0, PKV_LAYOUT_TOKEN_MAJOR = 1, PKV_LAYOUT_KV_FUSED = 2 };
+typedef struct pkv_kv_dest {
+  void* k[PKV_MAX_SHARDS];
+  void* v[PKV_MAX_SHARDS];
+  int32_t num_blocks;
+  int32_t block_size;        /* 16, 32, 64 or 128 */
+  int32_t num_kv_heads;
+  int32_t num_shards;
+  int32_t head_dim;
+  int32_t dtype;             /* the source's dtype, or PKV_FP8_E4M3 */
+  int32_t layout;            /* PKV_LAYOUT_* */
+  float scale;               /* PKV_FP8_E4M3 only */
+} pkv_kv_dest;
+int kv_relayout_convert(const pkv_pool_layer* src, const int32_t* src_bt, const pkv_kv_dest* dst,
+                        const int32_t* dst_bt, int32_t n_tokens, hipStream_t stream);
 
 /*
  * attn_prefill_chunk - causal GQA attention for one chunk of each request.

@@ -40,6 +40,8 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
+from . import fp8
+
 
 @dataclass
 class PoolModel:
@@ -151,3 +153,95 @@ def allocated_untouched(pool: PoolModel, fill, used_slots) -> bool:
         if not (np.all(k_rows[~used] == fill_arr) and np.all(v_rows[~used] == fill_arr)):
             return False
     return True
+
+
+# ---------------------------------------------------------------------------
+# Relayout with a change of element type and/or physical layout
+# ---------------------------------------------------------------------------
+#
+# [DISAGG] "布局转换": besides the block size and the head split, the
+# attention backend's layout (K and V fused or separate, the order of the
+# head and token dimensions) and the KV element type (BF16 on one side, FP8
+# on the other) may differ between the two instances.  Three destination
+# layouts are modelled (per shard s, block b, offset o, local head lh, dim d):
+#
+# * POOL:         k[s][b, lh, o, d],  v[s][b, lh, d, o]   (the layout above)
+# * TOKEN_MAJOR:  k[s][b, o, lh, d],  v[s][b, o, lh, d]   (slot-major rows:
+#   a shard's tensor viewed as [slot, heads, dim] is the pages' pool view)
+# * KV_FUSED:     kv[s][b, 0, o, lh, d] for K and kv[s][b, 1, o, lh, d] for V
+#
+# The FP8 element type is the E4M3 encoding of ``oracle.fp8`` (one scale per
+# tensor); a BF16 source value x is stored as encode(fp32(x) * fp32(1/scale)).
+
+LAYOUT_POOL, LAYOUT_TOKEN_MAJOR, LAYOUT_KV_FUSED = 0, 1, 2
+
+
+@dataclass
+class DestModel:
+    """One layer in a destination layout; ``elem`` np.uint8 means FP8 E4M3 bits."""
+
+    num_blocks: int
+    block_size: int
+    num_kv_heads: int
+    num_shards: int
+    head_dim: int
+    elem: type
+    layout: int
+    fill: int | float = 0
+    scale: float = 1.0
+    k: list = field(default_factory=list)
+    v: list = field(default_factory=list)
+
+    def __post_init__(self):
+        hl = self.num_kv_heads // self.num_shards
+        nb, bs, d = self.num_blocks, self.block_size, self.head_dim
+        if self.layout == LAYOUT_POOL:
+            ks, vs = (nb, hl, bs, d), (nb, hl, d, bs)
+        elif self.layout == LAYOUT_TOKEN_MAJOR:
+            ks = vs = (nb, bs, hl, d)
+        else:
+            ks, vs = (nb, 2, bs, hl, d), None
+        self.k = [np.full(ks, self.fill, dtype=self.elem) for _ in range(self.num_shards)]
+        self.v = [np.full(vs, self.fill, dtype=self.elem) for _ in range(self.num_shards)] if vs else []
+
+    def put(self, slot: int, head: int, krow, vrow) -> None:
+        hl = self.num_kv_heads // self.num_shards
+        s, b, o, lh = head // hl, slot // self.block_size, slot % self.block_size, head % hl
+        if self.layout == LAYOUT_POOL:
+            self.k[s][b, lh, o, :] = krow
+            self.v[s][b, lh, :, o] = vrow
+        elif self.layout == LAYOUT_TOKEN_MAJOR:
+            self.k[s][b, o, lh, :] = krow
+            self.v[s][b, o, lh, :] = vrow
+        else:
+            self.k[s][b, 0, o, lh, :] = krow
+            self.k[s][b, 1, o, lh, :] = vrow
+
+
+def convert_row(row, src_elem, dst_elem, scale: float):
+    """One row in the destination element type: unchanged, or BF16 bits -> E4M3 bits."""
+    if dst_elem == src_elem:
+        return row
+    if src_elem == np.uint16 and dst_elem == np.uint8:
+        return fp8.quantize_bf16(row, scale)
+    raise ValueError("only BF16 -> FP8 changes the element type")
+
+
+def relayout_convert(src: PoolModel, src_bt, dst: DestModel, dst_bt, n: int) -> int:
+    """Naive per-(token, head) copy of one layer into ``dst``'s layout and element type.
+
+    Returns the bytes written into the destination (K and V rows).
+    """
+    if (src.num_kv_heads, src.head_dim) != (dst.num_kv_heads, dst.head_dim):
+        raise ValueError("relayout keeps heads and head_dim")
+    src_slots = slots_for(src_bt, src.block_size, range(n))
+    dst_slots = slots_for(dst_bt, dst.block_size, range(n))
+    written = 0
+    for p in range(n):
+        for h in range(src.num_kv_heads):
+            krow, vrow = read_row(src, src_slots[p], h)
+            krow = convert_row(krow, src.elem, dst.elem, dst.scale)
+            vrow = convert_row(vrow, src.elem, dst.elem, dst.scale)
+            dst.put(dst_slots[p], h, krow, vrow)
+            written += krow.nbytes + vrow.nbytes
+    return written

@@ -35,7 +35,7 @@ def _declared_functions():
 def test_every_declared_symbol_is_exported():
     _lib()
     declared = _declared_functions()
-    assert "kv_write" in declared and "run_mux_round" in declared and len(declared) == 26
+    assert "kv_write" in declared and "run_mux_round" in declared and len(declared) == 27
     out = subprocess.run(["nm", "-D", "--defined-only", lib_mod.LIB_PATH], capture_output=True, text=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
     missing = [n for n in declared if n not in exported]
@@ -103,6 +103,50 @@ def test_relayout_validation():
     same = _pool(block_size=32)
     assert lib.kv_relayout(C.byref(src), 0x10, C.byref(same), 0x20, 16, None) == -1           # shared buffers
     assert lib.kv_relayout(C.byref(src), 0x10, C.byref(dst), 0x20, 0, None) == 0
+
+
+def _dest(**kw):
+    d = lib_mod.KvDest()
+    d.num_blocks, d.block_size, d.num_kv_heads, d.num_shards, d.head_dim = 8, 32, 8, 8, 128
+    d.dtype, d.layout, d.scale = lib_mod.FP8_E4M3, lib_mod.LAYOUT_TOKEN_MAJOR, 0.25
+    for s in range(8):
+        d.k[s] = 0x100000 * (s + 1)
+        d.v[s] = 0x100000 * (s + 20)
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return d
+
+
+def test_relayout_convert_validation():
+    lib = _lib()
+    src = _pool()
+    ok = lambda d, n=16, sbt=0x10: lib.kv_relayout_convert(C.byref(src), sbt, C.byref(d), 0x20, n, None)  # noqa
+    assert ok(_dest(), 0) == 0                                   # zero tokens: a no-op
+    assert lib.kv_relayout_convert(C.byref(src), 0x10, None, 0x20, 16, None) == -1
+    assert ok(_dest(head_dim=64)) == -1
+    assert ok(_dest(num_kv_heads=4)) == -1
+    assert ok(_dest(block_size=8)) == -2 and ok(_dest(block_size=48)) == -2 and ok(_dest(block_size=256)) == -2
+    assert ok(_dest(num_shards=3)) == -2 and ok(_dest(num_shards=0)) == -2
+    assert ok(_dest(layout=3)) == -1
+    assert ok(_dest(dtype=lib_mod.F32)) == -2                    # bf16 -> f32 is not a supported conversion
+    assert ok(_dest(scale=0.0)) == -1 and ok(_dest(scale=float("inf"))) == -1 and ok(_dest(scale=float("nan"))) == -1
+    assert ok(_dest(num_blocks=0)) == -1
+    assert ok(_dest(), -1) == -1
+    assert ok(_dest(), 16, 0) == -1                              # NULL source table
+    assert ok(_dest(), 8 * 32 + 1) == -1                         # does not fit
+    d = _dest()
+    d.v[3] = 0
+    assert ok(d) == -1                                           # NULL V buffer ...
+    d.layout = lib_mod.LAYOUT_KV_FUSED
+    assert ok(d, 0) == 0                                         # ... is fine when K and V are fused
+    d = _dest()
+    d.k[2] = 0x100008
+    assert ok(d) == -1                                           # misaligned
+    d = _dest()
+    d.k[5] = src.v[1]
+    assert ok(d) == -1                                           # shares a source buffer
+    fp32src = _pool(dtype=lib_mod.F32)
+    assert lib.kv_relayout_convert(C.byref(fp32src), 0x10, C.byref(_dest()), 0x20, 16, None) == -2   # fp8 from f32
 
 
 def test_attention_validation():

@@ -125,3 +125,77 @@ def test_relayout_70b_layers_back_to_back():
         pm.v = [from_dev(t, "bf16") for t in dst.v]
         gk, gv = opool.gather(pm, dst_bt[0], w.prompt_len)
         assert np.array_equal(gk, sc.k[0]) and np.array_equal(gv, sc.v[0])
+
+
+# --- relayout with a change of layout / element type ([DISAGG] "布局转换") ---
+
+_DEST_ELEM = {"bf16": np.uint16, "f32": np.float32, "fp8": np.uint8}
+_DEST_FILL = {"bf16": SENTINEL["bf16"], "f32": _fill_value("f32"), "fp8": 0x7F}
+_LAYOUT = {"pool": opool.LAYOUT_POOL, "token_major": opool.LAYOUT_TOKEN_MAJOR, "kv_fused": opool.LAYOUT_KV_FUSED}
+
+
+def _convert_case(dtype, ddtype, layout, n, sbs, ssh, sblk, dbs, dsh, dblk, hkv, d, seed, scale=1.0, plant=None):
+    sc = Scenario(num_q_heads=hkv, num_kv_heads=hkv, head_dim=d, block_size=sbs, dtype=dtype, lengths=[n],
+                  pool_blocks=sblk, num_shards=ssh, seed=seed)
+    if plant is not None:
+        plant(sc)
+    sc.write_all()
+    g = inputs.stream(seed, 0, 0, inputs.T_DST_PERM)
+    dst_bt, _ = inputs.assign_blocks(dblk, [n], dbs, g)
+    dst = ops.ConvertedPool(dblk, dbs, hkv, dsh, d, ddtype, layout, scale)
+    fill = {"bf16": SENTINEL["bf16"], "f32": SENTINEL["f32"], "fp8": 0x7F}[ddtype]
+    dst.fill_bits(fill)
+    print(f"kv_relayout_convert {dtype}->{ddtype} {layout} n={n} bs {sbs}->{dbs} shards {ssh}->{dsh}", flush=True)
+    ops.kv_relayout_convert(sc.pool, sc.bt_dev[0], dst, i32(dst_bt[0]), n)
+    torch.cuda.synchronize()
+    pm_src = _oracle_pool_from(sc)
+    ref = opool.DestModel(dblk, dbs, hkv, dsh, d, _DEST_ELEM[ddtype], _LAYOUT[layout], fill=_DEST_FILL[ddtype],
+                          scale=scale)
+    opool.relayout_convert(pm_src, sc.tables[0], ref, dst_bt[0], n)
+    got = [t.cpu().numpy() if ddtype == "fp8" else from_dev(t, ddtype) for t in dst.k + dst.v]
+    return sc, dst, dst_bt, got, ref.k + ref.v
+
+
+@pytest.mark.parametrize("dtype,ddtype,layout,n,sbs,ssh,sblk,dbs,dsh,dblk,hkv,d,scale", [
+    # the 70B layer at full size: bs16 / 4 shards -> bs32 / 8 shards, into FP8 slot-major rows
+    ("bf16", "fp8", "token_major", 4096, 16, 4, 256, 32, 8, 128, 8, 128, 0.02),
+    ("bf16", "fp8", "pool", 1003, 32, 8, 40, 16, 4, 70, 8, 128, 0.05),        # ragged tail: element copies of V
+    ("bf16", "fp8", "kv_fused", 517, 16, 2, 40, 128, 1, 8, 4, 64, 0.01),      # 8 source blocks per destination block
+    ("bf16", "bf16", "kv_fused", 77, 16, 2, 8, 64, 1, 4, 4, 64, 1.0),
+    ("bf16", "bf16", "token_major", 333, 128, 1, 4, 16, 2, 30, 2, 128, 1.0),
+    ("bf16", "bf16", "pool", 250, 16, 1, 20, 128, 2, 4, 2, 64, 1.0),
+    ("f32", "f32", "token_major", 300, 128, 1, 4, 16, 2, 30, 2, 128, 1.0),
+    ("f32", "f32", "pool", 95, 16, 2, 8, 32, 1, 4, 2, 64, 1.0),
+])
+def test_relayout_convert_bit_exact(dtype, ddtype, layout, n, sbs, ssh, sblk, dbs, dsh, dblk, hkv, d, scale):
+    sc, dst, dst_bt, got, ref = _convert_case(dtype, ddtype, layout, n, sbs, ssh, sblk, dbs, dsh, dblk, hkv, d,
+                                              seed=41, scale=scale)
+    for i, (a, b) in enumerate(zip(got, ref)):
+        assert np.array_equal(a.view(np.uint8), b.view(np.uint8)), f"destination tensor {i}"
+    if ddtype == dtype and layout == "pool":
+        # the same bytes as kv_relayout into a pool of that shape
+        same = ops.PagedPool(dblk, dbs, hkv, dsh, d, dtype).fill_bits(SENTINEL[dtype])
+        ops.kv_relayout(sc.pool, sc.bt_dev[0], same, i32(dst_bt[0]), n)
+        torch.cuda.synchronize()
+        for a, b in zip(dst.k + dst.v, same.k + same.v):
+            assert torch.equal(a.view(torch.uint8), b.view(torch.uint8))
+
+
+def test_relayout_convert_fp8_special_values():
+    """Overflow clamps to +-448, NaN stays NaN, tiny values become subnormal codes or zero."""
+    special = np.array([0x7FC0, 0xFFC0, 0x7F80, 0xFF80, 0x4400, 0xC400, 0x43E0, 0x3A80, 0x3A00, 0x0001, 0x8000,
+                        0x4380], np.uint16)   # NaN, -NaN, +-inf, +-512, 448, 2^-10 x 1.0, 2^-11, tiny, -0, 256
+
+    def plant(sc):
+        flat_k, flat_v = sc.k[0].reshape(-1), sc.v[0].reshape(-1)
+        idx = np.arange(special.size) * 97
+        flat_k[idx] = special
+        flat_v[idx + 5] = special
+
+    sc, dst, dst_bt, got, ref = _convert_case("bf16", "fp8", "token_major", 300, 16, 2, 24, 32, 2, 12, 4, 128,
+                                              seed=42, scale=1.0, plant=plant)
+    for a, b in zip(got, ref):
+        nan_a = (a & 0x7F) == 0x7F
+        nan_b = (b & 0x7F) == 0x7F
+        bad = np.flatnonzero((nan_a != nan_b) | (~nan_a & (a != b)))
+        assert bad.size == 0, [(int(i), hex(a.flat[i]), hex(b.flat[i])) for i in bad[:16]]

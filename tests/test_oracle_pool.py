@@ -13,7 +13,7 @@ import numpy as np
 
 from conftest import kv_fields, read_golden
 from decode_paged_kv_amd import inputs
-from oracle import accounting, pool
+from oracle import accounting, fp8, pool
 
 
 def test_slot_rule_hand_values():
@@ -92,3 +92,86 @@ def test_relayout_bytes_match_pages_closed_form():
     assert round(total / float(t["link"]) * 1e3) == int(t["ms"])
     # the relayout oracle moves exactly one layer's share per call
     assert accounting.relayout_payload_bytes(4096, 8, 128, 2) * 80 == total
+
+
+# --- relayout with a change of layout / element type ([DISAGG] "布局转换") ---
+
+def _logical_rows(dst, slots):
+    """Per layout, the destination's K and V as [n, heads, dim] through a plain reshape of the shard tensors
+    (heads of shard s are the s-th run of H/S heads); independent of DestModel.put's indexing."""
+    if dst.layout == pool.LAYOUT_KV_FUSED:
+        kk = np.concatenate([t[:, 0] for t in dst.k], axis=2)      # [blocks, bs, H, D]
+        vv = np.concatenate([t[:, 1] for t in dst.k], axis=2)
+    else:
+        kk = np.concatenate(dst.k, axis=2)
+        vv = np.concatenate(dst.v, axis=2)
+    flat = lambda t: t.reshape(dst.num_blocks * dst.block_size, dst.num_kv_heads, dst.head_dim)  # noqa: E731
+    return flat(kk)[slots], flat(vv)[slots]
+
+
+def test_convert_hand_placed_elements():
+    src = pool.PoolModel(2, 16, 4, 1, 8, np.float32)
+    k = np.arange(4 * 8, dtype=np.float32).reshape(1, 4, 8) + 1
+    pool.write(src, k, -k, [5])                          # position 5 of a request whose table is [0]
+    for layout in (pool.LAYOUT_POOL, pool.LAYOUT_TOKEN_MAJOR, pool.LAYOUT_KV_FUSED):
+        dst = pool.DestModel(4, 32, 4, 2, 8, np.float32, layout)
+        pool.relayout_convert(src, [0], dst, [3], 6)     # position 5 -> block 3, offset 5; head 3 = shard 1, local 1
+        if layout == pool.LAYOUT_POOL:
+            got_k, got_v = dst.k[1][3, 1, 5, :], dst.v[1][3, 1, :, 5]
+        elif layout == pool.LAYOUT_TOKEN_MAJOR:
+            got_k, got_v = dst.k[1][3, 5, 1, :], dst.v[1][3, 5, 1, :]
+        else:
+            got_k, got_v = dst.k[1][3, 0, 5, 1, :], dst.k[1][3, 1, 5, 1, :]
+        assert np.array_equal(got_k, k[0, 3]) and np.array_equal(got_v, -k[0, 3])
+        assert sum(np.count_nonzero(t) for t in dst.k + dst.v) == 2 * 4 * 8
+
+
+def test_convert_pool_layout_same_dtype_equals_relayout():
+    n = 150
+    src, src_bt, _, _ = _filled_pool(n, 16, 4, 16, seed=5)
+    g = inputs.stream(5, 99, 0, inputs.T_DST_PERM)
+    dst_bt, _ = inputs.assign_blocks(8, [n + 1], 32, g)
+    ref = pool.PoolModel(8, 32, 8, 8, 16, np.uint16, fill=0xBEEF)
+    pool.relayout(src, src_bt, ref, dst_bt[0], n)
+    got = pool.DestModel(8, 32, 8, 8, 16, np.uint16, pool.LAYOUT_POOL, fill=0xBEEF)
+    assert pool.relayout_convert(src, src_bt, got, dst_bt[0], n) == accounting.relayout_payload_bytes(n, 8, 16, 2)
+    for a, b in zip(ref.k + ref.v, got.k + got.v):
+        assert np.array_equal(a, b)
+
+
+def test_convert_token_major_and_fused_are_the_slot_view():
+    n = 137
+    src, src_bt, k, v = _filled_pool(n, 16, 4, 16, seed=6)
+    g = inputs.stream(6, 99, 0, inputs.T_DST_PERM)
+    dst_bt, _ = inputs.assign_blocks(6, [n], 32, g)
+    slots = np.array(pool.slots_for(dst_bt[0], 32, range(n)))
+    for layout in (pool.LAYOUT_TOKEN_MAJOR, pool.LAYOUT_KV_FUSED):
+        dst = pool.DestModel(6, 32, 8, 2, 16, np.uint16, layout, fill=0xBEEF)
+        pool.relayout_convert(src, src_bt, dst, dst_bt[0], n)
+        gk, gv = _logical_rows(dst, slots)
+        assert np.array_equal(gk, k) and np.array_equal(gv, v)
+        # every other slot keeps the fill
+        rest = np.setdiff1d(np.arange(6 * 32), slots)
+        rk, rv = _logical_rows(dst, rest)
+        assert np.all(rk == 0xBEEF) and np.all(rv == 0xBEEF)
+
+
+def test_convert_to_fp8_matches_torch_cast_and_scale():
+    import torch
+    n, scale = 70, 0.02
+    src, src_bt, k, v = _filled_pool(n, 16, 2, 8, seed=7)
+    dst_bt = np.array([1, 0, 2], np.int32)
+    dst = pool.DestModel(3, 32, 8, 4, 16, np.uint8, pool.LAYOUT_TOKEN_MAJOR, fill=0x7F, scale=scale)
+    assert pool.relayout_convert(src, src_bt, dst, dst_bt, n) == n * 8 * 16 * 2
+    gk, gv = _logical_rows(dst, np.array(pool.slots_for(dst_bt, 32, range(n))))
+    inv = np.float32(1.0) / np.float32(scale)
+    for got, x in ((gk, k), (gv, v)):
+        xf = (x.astype(np.uint32) << 16).view(np.float32)
+        # torch's E4M3 cast rounds to nearest even but does not saturate: clamp first
+        ref = torch.from_numpy(np.clip(xf * inv, -448, 448)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        assert np.array_equal(got, ref)
+        # decoded x scale is within half a code step of x (3 mantissa bits: relative 2^-4, or 2^-10 absolute
+        # below the smallest normal 2^-6, times the scale)
+        dec = fp8.dequantize(got, scale)
+        step = np.maximum(np.abs(xf) * 2.0 ** -4, 2.0 ** -10 * scale)
+        assert np.all(np.abs(dec - xf) <= step * (1 + 1e-6))
