@@ -79,15 +79,17 @@ def relayout_bytes(n, hkv, d, esize=2):
 # profiles/ summaries named for each kernel and workload.
 PMC_SCALE = {"fetch": 2.0, "write": 1.0}
 TRAFFIC = {
-    "attn_decode": {"sources": ['decode_paged_kv_amd/csrc/attn_decode.hip', 'decode_paged_kv_amd/csrc/pkv_internal.h'],
-                    "sha256": "20daf4a4721e752004cfc8a59b47b3637018cd2577604b4736c42b0af77ea956",
-                    "fetch_kib": 65949.26, "write_kib": 512.0},
-    "attn_prefill_chunk": {"sources": ['decode_paged_kv_amd/csrc/attn_prefill.hip', 'decode_paged_kv_amd/csrc/pkv_internal.h'],
-                           "sha256": "53c0fa6e78cb56acbfb1f2b3e40a3379a2c4dcdef1f5dd2981c3607478d65e90",
-                           "fetch_kib": 27173.41, "write_kib": 13107.73},
+    "attn_decode": {"sources": ['decode_paged_kv_amd/csrc/attn_decode.hip', 'decode_paged_kv_amd/csrc/decode_bf16.h',
+                                'decode_paged_kv_amd/csrc/pkv_internal.h'],
+                    "sha256": "111bac674e1312721e168f1b83c19f775055ba93603bee75df179630c5ed4d15",
+                    "fetch_kib": 65944.15, "write_kib": 512.00},
+    "attn_prefill_chunk": {"sources": ['decode_paged_kv_amd/csrc/attn_prefill.hip', 'decode_paged_kv_amd/csrc/prefill_bf16.h',
+                                       'decode_paged_kv_amd/csrc/pkv_internal.h'],
+                           "sha256": "ad3dcbcd8dd707e36cfec09cecc787b92428ef15bca8f26cee1573494f92eee3",
+                           "fetch_kib": 27174.25, "write_kib": 13107.74},
     "kv_relayout": {"sources": ['decode_paged_kv_amd/csrc/kv_ops.hip', 'decode_paged_kv_amd/csrc/pkv_internal.h'],
-                    "sha256": "ad28fef6862dad8395b483ee1c69cb6a6afb7de3af697948e61af46bc73b9a62",
-                    "fetch_kib": 8234.90, "write_kib": 16388.02},
+                    "sha256": "111df31fc6dcdcd7c6ba81b33f5ea739a3dde3193b71c819f47660b1061021ce",
+                    "fetch_kib": 8234.60, "write_kib": 16389.25},
 }
 
 
