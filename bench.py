@@ -19,7 +19,9 @@ Workloads (all synthetic, seeded, resident in HBM before timing):
   16 / 4 shards to block size 32 / 8 shards, 80 calls back to back.
   ``value`` is relayout HBM GB/s (read + write).  ``metrics`` adds the
   converting relayout of the same layers into FP8 E4M3 token-major rows and
-  into a fused bf16 K/V tensor (kv_relayout_convert, timed separately).
+  into a fused bf16 K/V tensor (kv_relayout_convert, timed separately), and
+  the layer-wise overlap of the moves with the prompt's prefill (each
+  layer's relayout released by an event as soon as that layer is computed).
 * ``pdmux``: the PD-multiplexing round (see ``bench_pdmux``).  ``value`` is
   the multiplexed decode step in ms.
 * ``copy-1gib``: a plain 1 GiB device copy, the known-size kernel that
@@ -497,9 +499,62 @@ def bench_relayout_70b(args):
         "metrics": {"relayout_gbps": round(gbps, 1), "relayout_frac_hbm": round(gbps / HBM_PEAK_GBPS, 4),
                     "relayout_launch_ms": round(launch_ms, 5), **conv_metrics},
     }
+    result["metrics"]["layerwise_overlap"] = layerwise_overlap(w, srcs, dsts, src_bt, dst_bt, args.steps, args.warmup)
     if args.cpu_baseline:
         result["cpu_baseline"] = cpu_baseline_relayout(w)
     return result
+
+
+def layerwise_overlap(w, srcs, dsts, src_bt, dst_bt, steps, warmup):
+    """[DISAGG] "流程": a layer's KV moves as soon as that layer is computed.  The prompt's prefill (per layer:
+    kv_write of its 4096 tokens + attn_prefill_chunk from position 0) runs on a compute stream; after each layer
+    an event releases that layer's kv_relayout on a second stream, so the move overlaps the next layers'
+    prefill.  Compared with the prefill alone and with prefill + relayout in one stream."""
+    L, hq, hkv, d, N = w.layers, w.num_q_heads, w.num_kv_heads, w.head_dim, w.prompt_len
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(w.seed + 1)
+    q = rand_bf16((N, hq, d), gen)
+    out = torch.empty_like(q)
+    k, v = rand_bf16((N, hkv, d), gen), rand_bf16((N, hkv, d), gen)
+    start, pos0 = i32([0, N]), i32([0])
+    slots = ops.slot_mapping(src_bt, start, pos0, N, w.block_size, w.pool_blocks)
+    torch.cuda.synchronize()
+    comp, xfer = torch.cuda.Stream(), torch.cuda.Stream()
+    cs, xs = comp.cuda_stream, xfer.cuda_stream
+
+    def prefill_layer(l):
+        ops.kv_write(srcs[l], k, v, slots, stream=cs)
+        ops.attn_prefill_chunk(srcs[l], q, out, src_bt, start, pos0, N, hq, stream=cs)
+
+    def run(mode):
+        for l in range(L):
+            prefill_layer(l)
+            if mode == "serial":
+                ops.kv_relayout(srcs[l], src_bt, dsts[l], dst_bt, N, stream=cs)
+            elif mode == "overlap":
+                ev = torch.cuda.Event()
+                ev.record(comp)
+                xfer.wait_event(ev)
+                ops.kv_relayout(srcs[l], src_bt, dsts[l], dst_bt, N, stream=xs)
+        comp.wait_stream(xfer)
+
+    def timed(mode):
+        for _ in range(warmup):
+            run(mode)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(comp)
+        for _ in range(steps):
+            run(mode)
+        e1.record(comp)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    t = {m: timed(m) for m in ("prefill", "serial", "overlap")}
+    added_serial = t["serial"] - t["prefill"]
+    return {"prefill_ms": round(t["prefill"], 3), "prefill_then_relayout_ms": round(t["serial"], 3),
+            "overlapped_ms": round(t["overlap"], 3),
+            "relayout_hidden_frac": round((t["serial"] - t["overlap"]) / added_serial, 3) if added_serial > 0 else None}
 
 
 def cpu_baseline_relayout(w):

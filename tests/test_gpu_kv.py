@@ -199,3 +199,49 @@ def test_relayout_convert_fp8_special_values():
         nan_b = (b & 0x7F) == 0x7F
         bad = np.flatnonzero((nan_a != nan_b) | (~nan_a & (a != b)))
         assert bad.size == 0, [(int(i), hex(a.flat[i]), hex(b.flat[i])) for i in bad[:16]]
+
+
+@pytest.mark.parametrize("convert", [False, True])
+def test_relayout_bad_block_ids_are_skipped_and_flagged(convert):
+    """A source or destination table entry outside its pool is never dereferenced: the tokens it covers are
+    not written (their destination slots keep the sentinel), every other token is, and the error word gets the
+    block-id bit."""
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    n, sbs, dbs, hkv, d, dblk = 200, 16, 32, 4, 128, 8
+    sc = Scenario(num_q_heads=hkv, num_kv_heads=hkv, head_dim=d, block_size=sbs, dtype="bf16", lengths=[n],
+                  pool_blocks=16, num_shards=2, seed=51, err_word=err)
+    sc.write_all()
+    torch.cuda.synchronize()
+    err.zero_()
+    dst_bt, _ = inputs.assign_blocks(dblk, [n], dbs, inputs.stream(51, 0, 0, inputs.T_DST_PERM))
+    src_tab, dst_tab = sc.tables[0].copy(), dst_bt[0].copy()
+    src_tab[3] = 16 + 5                    # source tokens 48..63: block id past the pool
+    dst_tab[5] = -2                        # destination tokens 160..191: negative block id
+    skipped = list(range(48, 64)) + list(range(160, 192))
+    print(f"relayout with bad block ids, convert={convert}", flush=True)
+    pm_src = _oracle_pool_from(sc)
+    if convert:
+        dst = ops.ConvertedPool(dblk, dbs, hkv, 1, d, "fp8", "token_major", 0.05).fill_bits(0x7F)
+        ops.kv_relayout_convert(sc.pool, i32(src_tab), dst, i32(dst_tab), n)
+        ref = opool.DestModel(dblk, dbs, hkv, 1, d, np.uint8, opool.LAYOUT_TOKEN_MAJOR, fill=0x7F, scale=0.05)
+        opool.relayout_convert(pm_src, sc.tables[0], ref, dst_bt[0], n)
+        fill_row = np.full(d, 0x7F, np.uint8)
+        for p in skipped:                  # what the valid tables would have written there stays unwritten
+            for h in range(hkv):
+                ref.put(opool.slots_for(dst_bt[0], dbs, [p])[0], h, fill_row, fill_row)
+        got, want = [t.cpu().numpy() for t in dst.k + dst.v], ref.k + ref.v
+    else:
+        dst = ops.PagedPool(dblk, dbs, hkv, 1, d, "bf16", err_word=err).fill_bits(SENTINEL["bf16"])
+        ops.kv_relayout(sc.pool, i32(src_tab), dst, i32(dst_tab), n)
+        ref = opool.PoolModel(dblk, dbs, hkv, 1, d, np.uint16, fill=SENTINEL["bf16"])
+        opool.relayout(pm_src, sc.tables[0], ref, dst_bt[0], n)
+        for p in skipped:
+            for h in range(hkv):
+                s, blk, off, lh = ref.where(opool.slots_for(dst_bt[0], dbs, [p])[0], h)
+                ref.k[s][blk, lh, off, :] = SENTINEL["bf16"]
+                ref.v[s][blk, lh, :, off] = SENTINEL["bf16"]
+        got, want = [from_dev(t, "bf16") for t in dst.k + dst.v], ref.k + ref.v
+    torch.cuda.synchronize()
+    for a, b in zip(got, want):
+        assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
+    assert int(err.item()) & 1
