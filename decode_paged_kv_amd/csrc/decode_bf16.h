@@ -44,6 +44,11 @@ constexpr int kThreads = kWaves * 64;
 // registers of a wave's tile are refilled with its next tile as soon as
 // they are consumed: K right after S^T, V right after P V.  Three waves per
 // SIMD keep about 16 KB each in flight.
+// In the stream split a workgroup's range can span several (request, KV
+// head) segments; each wave issues the next segment's q, block ids and first
+// tile loads as soon as it is done with the current segment's tiles, before
+// the 4-wave merge of the current segment, so the merge and the next
+// segment's first load latency overlap (about 1% on uneven contexts).
 // A request whose context fits one split writes its output directly;
 // otherwise each split writes its partial (m, l, acc) and the merge kernel
 // combines them (a device-wide handoff inside the kernel would need L2
@@ -174,23 +179,35 @@ __device__ __forceinline__ void decode_bf16_block(PoolDev pool, const bf16_t* __
   const size_t block_stride = (size_t)hl * bs * D;
   const int tile_bytes = bs * D * 2;
 
-  // keys [start, end) of request b (context L) and KV head kvh; the result
-  // goes to out when final_out, else to the partial rows prow + g * pstride
-  auto segment = [&](int b, int kvh, int L, int start, int end, bool final_out, size_t prow, int pstride) {
-  const int sh = kvh / hl, lh = kvh - sh * hl;
-  const bf16_t* kpool = reinterpret_cast<const bf16_t*>(pool.k[sh]);
-  const bf16_t* vpool = reinterpret_cast<const bf16_t*>(pool.v[sh]);
-  const size_t head_off = (size_t)lh * bs * D;                  // elements
-  const int32_t* table = bt + (size_t)b * bt_stride;
-
+  // One segment: keys [start, end) of request b and KV head kvh; the result
+  // goes to out when final_out, else to the partial rows prow + g * pstride.
+  struct Seg {
+    int b, kvh, start, end;
+    bool final_out;
+    size_t prow;
+    int pstride;
+  };
+  // the segment whose loads are being issued: its KV head's pools, its
+  // table, its end (wave-uniform, in scalar registers)
+  const bf16_t* kpool = nullptr;
+  const bf16_t* vpool = nullptr;
+  size_t head_off = 0;                                          // elements
+  const int32_t* table = bt;
+  int end = 0;
   // q as the B operand of S^T: head l16 (zero columns past G), dims 32c + 8 j4
   uint4 qf[KC];
-  {
+  auto bind = [&](const Seg& sg) {
+    const int sh = sg.kvh / hl, lh = sg.kvh - sh * hl;
+    kpool = reinterpret_cast<const bf16_t*>(pool.k[sh]);
+    vpool = reinterpret_cast<const bf16_t*>(pool.v[sh]);
+    head_off = (size_t)lh * bs * D;
+    table = bt + (size_t)sg.b * bt_stride;
+    end = sg.end;
     const bool hv = l16 < G;
-    const bf16_t* qrow = q + ((size_t)b * num_q_heads + (size_t)kvh * G + (hv ? l16 : 0)) * D + 8 * j4;
+    const bf16_t* qrow = q + ((size_t)sg.b * num_q_heads + (size_t)sg.kvh * G + (hv ? l16 : 0)) * D + 8 * j4;
 #pragma unroll
     for (int c = 0; c < KC; ++c) qf[c] = hv ? *reinterpret_cast<const uint4*>(qrow + 32 * c) : make_uint4(0, 0, 0, 0);
-  }
+  };
 
   const int k_voff = (l16 * D + 8 * j4) * 2;                    // bytes within a half's 16 K rows
   const int v_voff = (l16 * bs + 4 * j4) * 2;                   // dim l16 of a 16-dim slab, 4 keys
@@ -233,8 +250,6 @@ __device__ __forceinline__ void decode_bf16_block(PoolDev pool, const bf16_t* __
   };
 
   f32x4_t o[DT];
-#pragma unroll
-  for (int mm = 0; mm < DT; ++mm) o[mm] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   // running max of head l16 (log2 units; finite start, so a tile whose keys
   // are all absent gives p = exp2(-inf) = 0) and this lane's share of the sum
   float m = -1e30f, lsum = 0.f;
@@ -315,65 +330,80 @@ __device__ __forceinline__ void decode_bf16_block(PoolDev pool, const bf16_t* __
     if (k0_next >= 0) issue_v(k0_next, r);
   };
 
-  const int ntiles = (end - start + TK - 1) / TK;
   // two tiles in flight per wave: ra holds tiles wave + 8i, rb tiles wave + 8i + 4
   DecodeTile<D> ra, rb;
   constexpr int W = kWaves;
-  if (wave < ntiles) {
-    fetch_ids(start + wave * TK, ra.blk);
-    issue_k(start + wave * TK, ra);
-    issue_v(start + wave * TK, ra);
-  }
-  if (wave + W < ntiles) {
-    fetch_ids(start + (wave + W) * TK, rb.blk);
-    issue_k(start + (wave + W) * TK, rb);
-    issue_v(start + (wave + W) * TK, rb);
-  }
-  if (wave + 2 * W < ntiles) fetch_ids(start + (wave + 2 * W) * TK, ids_next);
-  auto at = [&](int t) { return t < ntiles ? start + t * TK : -1; };
-  for (int t = wave; t < ntiles; t += 2 * W) {
-    process(start + t * TK, ra, at(t + 2 * W), at(t + 3 * W));
-    if (t + W < ntiles) process(start + (t + W) * TK, rb, at(t + 3 * W), at(t + 4 * W));
-  }
-
-  // ---- merge the 4 waves ----
-  lsum = col_sum(lsum);
-  if (l16 < G) {
-    if (j4 == 0) {
-      sm.m[wave][l16] = m;
-      sm.l[wave][l16] = lsum;
+  // q, the block ids and the loads of a segment's first tiles; issued for
+  // the next segment as soon as this wave is done with the current one's
+  // tiles, ahead of the current segment's merge
+  auto prologue = [&](const Seg& sg) {
+    bind(sg);
+    const int ntiles = (sg.end - sg.start + TK - 1) / TK;
+    if (wave < ntiles) {
+      fetch_ids(sg.start + wave * TK, ra.blk);
+      issue_k(sg.start + wave * TK, ra);
+      issue_v(sg.start + wave * TK, ra);
     }
-#pragma unroll
-    for (int mm = 0; mm < DT; ++mm)
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) sm.acc[wave][l16][16 * mm + 4 * j4 + rr] = o[mm][rr];
-  }
-  __syncthreads();
-  for (int i = threadIdx.x; i < G * D; i += kThreads) {
-    const int g = i / D, d = i - g * D;
-    float mx = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) mx = fmaxf(mx, sm.m[w][g]);
-    float l = 0.f, acc = 0.f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const float f = __builtin_amdgcn_exp2f(sm.m[w][g] - mx);
-      l += sm.l[w][g] * f;
-      acc += sm.acc[w][g][d] * f;
+    if (wave + W < ntiles) {
+      fetch_ids(sg.start + (wave + W) * TK, rb.blk);
+      issue_k(sg.start + (wave + W) * TK, rb);
+      issue_v(sg.start + (wave + W) * TK, rb);
     }
-    const int h = kvh * G + g;
-    if (final_out) {
-      out[((size_t)b * num_q_heads + h) * D + d] = f32_to_bf16(acc / l);
-    } else {
-      const size_t row = prow + (size_t)g * pstride;
-      part_o[row * D + d] = acc;
-      if (d == 0) {
-        part_ml[row * 2 + 0] = mx;
-        part_ml[row * 2 + 1] = l;
+    if (wave + 2 * W < ntiles) fetch_ids(sg.start + (wave + 2 * W) * TK, ids_next);
+  };
+  // the tiles of the bound segment (its prologue has run)
+  auto body = [&](const Seg& sg) {
+#pragma unroll
+    for (int mm = 0; mm < DT; ++mm) o[mm] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    m = -1e30f;
+    lsum = 0.f;
+    const int start = sg.start;
+    const int ntiles = (sg.end - start + TK - 1) / TK;
+    auto at = [&](int t) { return t < ntiles ? start + t * TK : -1; };
+    for (int t = wave; t < ntiles; t += 2 * W) {
+      process(start + t * TK, ra, at(t + 2 * W), at(t + 3 * W));
+      if (t + W < ntiles) process(start + (t + W) * TK, rb, at(t + 3 * W), at(t + 4 * W));
+    }
+  };
+  // the 4 waves' (m, l, acc) of a segment, combined and written
+  auto merge = [&](const Seg& sg) {
+    lsum = col_sum(lsum);
+    if (l16 < G) {
+      if (j4 == 0) {
+        sm.m[wave][l16] = m;
+        sm.l[wave][l16] = lsum;
+      }
+#pragma unroll
+      for (int mm = 0; mm < DT; ++mm)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) sm.acc[wave][l16][16 * mm + 4 * j4 + rr] = o[mm][rr];
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < G * D; i += kThreads) {
+      const int g = i / D, d = i - g * D;
+      float mx = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) mx = fmaxf(mx, sm.m[w][g]);
+      float l = 0.f, acc = 0.f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float f = __builtin_amdgcn_exp2f(sm.m[w][g] - mx);
+        l += sm.l[w][g] * f;
+        acc += sm.acc[w][g][d] * f;
+      }
+      const int h = sg.kvh * G + g;
+      if (sg.final_out) {
+        out[((size_t)sg.b * num_q_heads + h) * D + d] = f32_to_bf16(acc / l);
+      } else {
+        const size_t row = sg.prow + (size_t)g * sg.pstride;
+        part_o[row * D + d] = acc;
+        if (d == 0) {
+          part_ml[row * 2 + 0] = mx;
+          part_ml[row * 2 + 1] = l;
+        }
       }
     }
-  }
-  __syncthreads();                              // the merge buffers are free again
+    __syncthreads();                              // the merge buffers are free again
   };
 
   if constexpr (!STREAM) {
@@ -386,8 +416,11 @@ __device__ __forceinline__ void decode_bf16_block(PoolDev pool, const bf16_t* __
     }
     const int start = split * split_tokens;
     if (start >= L) return;
-    segment(b, kvh, L, start, min(L, start + split_tokens), L <= split_tokens,
-            ((size_t)b * num_q_heads + (size_t)kvh * G) * num_splits + split, num_splits);
+    const Seg sg{b, kvh, start, min(L, start + split_tokens), L <= split_tokens,
+                 ((size_t)b * num_q_heads + (size_t)kvh * G) * num_splits + split, num_splits};
+    prologue(sg);
+    body(sg);
+    merge(sg);
   } else {
     // stream split: workgroup w takes the pair-tiles [w W / NW, (w+1) W / NW)
     // of the W = Hkv * sum_b ceil(L_b / 32) tiles of the batch, ordered by
@@ -397,31 +430,51 @@ __device__ __forceinline__ void decode_bf16_block(PoolDev pool, const bf16_t* __
     const long long NW = nbx, w = bx;
     const TileScan tot = scan_tiles(ctx, batch, cap, hkv, -1, 0);
     if (tot.over && w == 0 && threadIdx.x == 0) flag_error(pool.err, PKV_ERRBIT_TABLE);
-    const long long W = tot.total;
-    long long t = w * W / NW;
-    const long long t1 = (w + 1) * W / NW;
+    const long long Wt = tot.total;
+    long long t = w * Wt / NW;
+    const long long t1 = (w + 1) * Wt / NW;
     if (t >= t1) return;
     const TileScan at = scan_tiles(ctx, batch, cap, hkv, t, 0);
     int b = at.b;
     long long base = at.base;
-    while (t < t1) {
-      const int L = min(ctx[b], cap);
-      const int ntb = (L + TK - 1) / TK;
-      if (ntb == 0) {                           // an empty request holds no tiles
-        ++b;
-        continue;
+    // the segments of this workgroup's range, in order
+    auto next_seg = [&](Seg& sg) -> bool {
+      while (t < t1) {
+        const int L = max(min(ctx[b], cap), 0);
+        const int ntb = (L + TK - 1) / TK;
+        if (ntb == 0) {                         // an empty request holds no tiles
+          ++b;
+          continue;
+        }
+        const int kvh = (int)((t - base) / ntb);
+        const long long pstart = base + (long long)kvh * ntb;
+        const long long seg_end = min(t1, pstart + ntb);
+        sg.b = b;
+        sg.kvh = kvh;
+        sg.start = (int)(t - pstart) * TK;
+        sg.end = min(L, (int)(seg_end - pstart) * TK);
+        sg.final_out = stream_owner(pstart, NW, Wt) == stream_owner(pstart + ntb - 1, NW, Wt);
+        sg.prow = (size_t)(w + (long long)b * hkv + kvh) * G;
+        sg.pstride = 1;
+        t = seg_end;
+        if (t == base + (long long)hkv * ntb) {
+          base = t;
+          ++b;
+        }
+        return true;
       }
-      const int kvh = (int)((t - base) / ntb);
-      const long long pstart = base + (long long)kvh * ntb;
-      const long long seg_end = min(t1, pstart + ntb);
-      const bool final_out = stream_owner(pstart, NW, W) == stream_owner(pstart + ntb - 1, NW, W);
-      segment(b, kvh, L, (int)(t - pstart) * TK, min(L, (int)(seg_end - pstart) * TK), final_out,
-              (size_t)(w + (long long)b * hkv + kvh) * G, 1);
-      t = seg_end;
-      if (t == base + (long long)hkv * ntb) {
-        base = t;
-        ++b;
-      }
+      return false;
+    };
+    Seg cur{}, nxt{};
+    if (!next_seg(cur)) return;
+    prologue(cur);
+    while (true) {
+      body(cur);
+      const bool more = next_seg(nxt);
+      if (more) prologue(nxt);
+      merge(cur);
+      if (!more) break;
+      cur = nxt;
     }
   }
 }
