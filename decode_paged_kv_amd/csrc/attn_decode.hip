@@ -11,16 +11,20 @@
 // The G = Hq/Hkv q-heads of the KV head share every K/V byte the workgroup
 // reads, so K and V are each read from HBM once per step.
 //
-// Inside a workgroup each wave walks 64-key tiles (tile i of the split goes
-// to wave i % 4):
+// bf16 (the measured path): the MFMA kernel of decode_bf16.h, with the
+// equal-splits plan or, for batches with fewer (request, KV head) pairs
+// than resident workgroups, the stream split (plans below).
+//
+// fp32 (small checks): the kernel in this file.  Inside a workgroup each
+// wave walks 64-key tiles (tile i of the split goes to wave i % 4):
 //   q.k   lane l owns key l of the tile and reads its K row (16-byte loads
 //         of a block's contiguous rows); the G query rows are broadcast
-//         from LDS; bf16 pairs use v_dot2_f32_bf16 with fp32 accumulation.
+//         from LDS; fp32 fma accumulation.
 //   soft  online softmax per wave in the exp2 domain (scores pre-scaled by
 //         scale*log2 e): running max m, per-lane partial sums.
 //   p.v   p goes through the wave's own LDS slice; lane l owns head-dim
 //         columns and reads the dim-major V tile (16 keys of one dim are
-//         32 contiguous bytes), multiplying bf16 key pairs with v_dot2.
+//         contiguous).
 // The 4 waves' (m, l, acc) are merged in LDS.  A request whose context
 // fits one split writes its output there; otherwise the split partials go
 // to the workspace and a second kernel merges them.
@@ -449,7 +453,8 @@ DecodePlan plan_decode(int batch, int num_q_heads, int num_kv_heads, int max_con
   // one split per pair and needs no merge.  Below that a pair is cut into
   // splits of at most 512 keys (short workgroups balance uneven contexts as
   // they finish), shorter still until there are about three workgroups per
-  // CU (the bf16 kernel's occupancy), but no shorter than 128 keys.  Splits
+  // CU (more than are resident at once at head dim 128, so short and long
+  // splits even out), but no shorter than 128 keys.  Splits
   // are whole 32-key tiles.
   const long pairs = (long)batch * num_kv_heads;
   long split = max_context_len;

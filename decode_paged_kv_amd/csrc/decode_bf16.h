@@ -42,8 +42,9 @@ constexpr int kThreads = kWaves * 64;
 //                  whole 32-byte dim rows, 512 contiguous bytes).
 // Nothing goes through LDS until the final 4-wave merge.  The operand
 // registers of a wave's tile are refilled with its next tile as soon as
-// they are consumed: K right after S^T, V right after P V.  Three waves per
-// SIMD keep about 16 KB each in flight.
+// they are consumed: K right after S^T, V right after P V.  At head dim
+// 128 the kernel holds about 250 registers per lane, two waves per SIMD,
+// each with two 16 KB tiles in flight.
 // In the stream split a workgroup's range can span several (request, KV
 // head) segments; each wave issues the next segment's q, block ids and first
 // tile loads as soon as it is done with the current segment's tiles, before
