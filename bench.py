@@ -846,8 +846,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: the path runs on one MI355X's share of the work and has no multi-GPU "
-              "mode (how it would shard is described in DESIGN.md).", file=sys.stderr)
+        print("bench.py measures one GPU: the path runs on one MI355X's share of the work (decode and prefill "
+              "attention shard by request or KV head with no exchange; relayout sends each head to the "
+              "destination shard that owns it) and has no multi-GPU mode.", file=sys.stderr)
         sys.exit(2)
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
