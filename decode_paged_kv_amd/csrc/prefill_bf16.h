@@ -455,7 +455,7 @@ __device__ __forceinline__ void prefill_bf16_block(PoolDev pool, const bf16_t* _
 #pragma unroll
     for (int s = 0; s < R; ++s) fr[s] = frag(s);
     uint32_t pw[4][4];                                          // P in bf16 pairs, by quarter
-    float psum[2] = {0.f, 0.f};
+    float psum[2] = {-0.f, -0.f};                               // x + -0 folds to x
     float mh[2] = {-INFINITY, -INFINITY};
     __builtin_amdgcn_s_setprio(1);
     __builtin_amdgcn_sched_barrier(0);
@@ -490,7 +490,7 @@ __device__ __forceinline__ void prefill_bf16_block(PoolDev pool, const bf16_t* _
       for (int h = 0; h < 2; ++h)
 #pragma unroll
         for (int k = 0; k < 8; ++k)
-          if (BP::max_slot(h, k) == s) mh[h] = fmaxf(mh[h], fmaxf(stn.v[h][2 * k], stn.v[h][2 * k + 1]));
+          if (BP::max_slot(h, k) == s) mh[h] = fmaxf(fmaxf(mh[h], stn.v[h][2 * k]), stn.v[h][2 * k + 1]);
       __builtin_amdgcn_sched_barrier(0);
     }
     __builtin_amdgcn_s_setprio(0);
