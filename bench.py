@@ -83,12 +83,12 @@ PMC_SCALE = {"fetch": 2.0, "write": 1.0}
 TRAFFIC = {
     "attn_decode": {"sources": ['decode_paged_kv_amd/csrc/attn_decode.hip', 'decode_paged_kv_amd/csrc/decode_bf16.h',
                                 'decode_paged_kv_amd/csrc/pkv_internal.h'],
-                    "sha256": "111bac674e1312721e168f1b83c19f775055ba93603bee75df179630c5ed4d15",
-                    "fetch_kib": 65944.15, "write_kib": 512.00},
+                    "sha256": "828d34ff33bbe55e9695c8f3bbd5eb6651e6be0923f5d8494953e4b46842da85",
+                    "fetch_kib": 65952.85, "write_kib": 512.00},
     "attn_prefill_chunk": {"sources": ['decode_paged_kv_amd/csrc/attn_prefill.hip', 'decode_paged_kv_amd/csrc/prefill_bf16.h',
                                        'decode_paged_kv_amd/csrc/pkv_internal.h'],
-                           "sha256": "ad3dcbcd8dd707e36cfec09cecc787b92428ef15bca8f26cee1573494f92eee3",
-                           "fetch_kib": 27174.25, "write_kib": 13107.74},
+                           "sha256": "5e377b1bdca7eae6694ccdaa0cc783b2178151af6f55738a95baa83e0d02dcb2",
+                           "fetch_kib": 27183.66, "write_kib": 13107.55},
     "kv_relayout": {"sources": ['decode_paged_kv_amd/csrc/kv_ops.hip', 'decode_paged_kv_amd/csrc/pkv_internal.h'],
                     "sha256": "111df31fc6dcdcd7c6ba81b33f5ea739a3dde3193b71c819f47660b1061021ce",
                     "fetch_kib": 8234.60, "write_kib": 16389.25},
