@@ -47,6 +47,7 @@ def oracle_decode(sc: Scenario, q_np):
     ("bf16", 32, 8, 128, 16, 1, [1, 2, 15, 16, 17, 63, 64, 65, 300, 511, 1000, 1537]),
     ("bf16", 64, 8, 128, 16, 1, [2048, 8192, 3001, 4097]),
     ("bf16", 16, 16, 128, 32, 4, [129, 700]),              # G = 1, several shards
+    ("bf16", 32, 16, 64, 16, 16, [1, 47, 300]),            # the most shards (16 x 1 head)
     ("bf16", 32, 2, 64, 64, 2, [1, 333, 2000]),            # G = 16, head dim 64
     ("bf16", 8, 4, 128, 128, 1, [5, 256, 1025]),
     ("f32", 8, 2, 128, 32, 2, [1, 90, 513]),

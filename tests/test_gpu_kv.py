@@ -100,6 +100,7 @@ def _relayout_case(dtype, n, src_bs, src_shards, src_blocks, dst_bs, dst_shards,
     ("bf16", 1000, 32, 8, 40, 16, 4, 70, 8, 128),       # the inverse direction, ragged tail
     ("bf16", 77, 16, 2, 8, 64, 1, 4, 4, 64),
     ("f32", 300, 128, 1, 4, 16, 2, 30, 2, 128),
+    ("bf16", 333, 16, 4, 24, 64, 16, 8, 16, 64),        # the most shards (16 x 1 head), block size 64
 ])
 def test_relayout_bit_exact(dtype, n, sbs, ssh, sblk, dbs, dsh, dblk, hkv, d):
     (sc, dst, dst_bt), = _relayout_case(dtype, n, sbs, ssh, sblk, dbs, dsh, dblk, hkv, d, seed=21)
