@@ -2,6 +2,7 @@
 // kernel launchers.  Every check here runs before any HIP call, so a
 // rejected call enqueues nothing.  See include/pkv.h for the contracts.
 #include <cmath>
+#include <cstring>
 #include <cstdarg>
 #include <cstdio>
 #include <string>
@@ -81,7 +82,22 @@ static int check_heads(const PoolDev& pool, int num_q_heads) {
   return PKV_OK;
 }
 
-static float resolve_scale(float scale, int head_dim) {
+static // Finite and >= 0 (0 selects the default scale), tested on the bits: the
+// library is built without NaN semantics for comparisons, so a NaN compare
+// would be folded away.
+bool scale_ok(float x) {
+  uint32_t u;
+  std::memcpy(&u, &x, 4);
+  return (u & 0x7f800000u) != 0x7f800000u && !(u >> 31 && (u & 0x7fffffffu));
+}
+// finite and > 0
+bool positive_finite(float x) {
+  uint32_t u;
+  std::memcpy(&u, &x, 4);
+  return (u & 0x7f800000u) != 0x7f800000u && !(u >> 31) && (u & 0x7fffffffu);
+}
+
+float resolve_scale(float scale, int head_dim) {
   return scale > 0.f ? scale : 1.0f / std::sqrt((float)head_dim);
 }
 
@@ -172,7 +188,7 @@ int kv_relayout_convert(const pkv_pool_layer* src, const int32_t* src_bt, const 
   const bool fp8 = dst->dtype == PKV_FP8_E4M3;
   if (!(dst->dtype == src->dtype || (fp8 && src->dtype == PKV_BF16)))
     return fail(PKV_EUNSUPPORTED, "kv_relayout_convert: dtype %d -> %d", src->dtype, dst->dtype);
-  if (fp8 && !(dst->scale > 0.f && std::isfinite(dst->scale)))
+  if (fp8 && !positive_finite(dst->scale))
     return fail(PKV_EINVAL, "kv_relayout_convert: FP8 scale must be finite and > 0");
   const size_t esize = fp8 ? 1 : (src->dtype == PKV_BF16 ? 2 : 4);
   const size_t per_shard = (size_t)dst->num_blocks * (dst->num_kv_heads / dst->num_shards) * dst->block_size *
@@ -211,7 +227,7 @@ int attn_prefill_chunk(const pkv_pool_layer* pool, const void* q, void* out, con
     return fail(PKV_EINVAL, "attn_prefill_chunk: NULL device array");
   if (!aligned16(q) || !aligned16(out)) return fail(PKV_EINVAL, "attn_prefill_chunk: q/out must be 16-byte aligned");
   if (bt_stride <= 0) return fail(PKV_EINVAL, "attn_prefill_chunk: bt_stride %d", bt_stride);
-  if (!(scale >= 0.f) || std::isinf(scale)) return fail(PKV_EINVAL, "attn_prefill_chunk: scale must be finite");
+  if (!scale_ok(scale)) return fail(PKV_EINVAL, "attn_prefill_chunk: scale must be finite and >= 0");
   if ((int64_t)max_chunk_len * 2 > INT32_MAX / 64) return fail(PKV_ERANGE, "attn_prefill_chunk: chunk too long");
   hipError_t e = launch_attn_prefill(pd, pool->dtype, q, out, block_tables, bt_stride, start_loc, chunk_start, batch,
                                      max_chunk_len, num_q_heads, resolve_scale(scale, pd.head_dim), stream);
@@ -248,7 +264,7 @@ int attn_decode(const pkv_pool_layer* pool, const void* q, void* out, const int3
   if (!aligned16(q) || !aligned16(out)) return fail(PKV_EINVAL, "attn_decode: q/out must be 16-byte aligned");
   if (bt_stride <= 0 || (int64_t)bt_stride * pd.block_size < max_context_len)
     return fail(PKV_EINVAL, "attn_decode: bt_stride %d blocks cannot hold %d tokens", bt_stride, max_context_len);
-  if (!(scale >= 0.f) || std::isinf(scale)) return fail(PKV_EINVAL, "attn_decode: scale must be finite");
+  if (!scale_ok(scale)) return fail(PKV_EINVAL, "attn_decode: scale must be finite and >= 0");
   const DecodePlan plan = plan_decode(batch, num_q_heads, pd.num_kv_heads, max_context_len, pd.head_dim, pool->dtype);
   if (plan.workspace > 0) {
     if (!workspace || workspace_bytes < plan.workspace)
@@ -259,6 +275,37 @@ int attn_decode(const pkv_pool_layer* pool, const void* q, void* out, const int3
   hipError_t e = launch_attn_decode(pd, pool->dtype, q, out, block_tables, bt_stride, context_lens, batch, num_q_heads,
                                     resolve_scale(scale, pd.head_dim), plan, workspace, stream);
   return e == hipSuccess ? PKV_OK : hip_fail(e, "attn_decode");
+}
+
+int attn_decode_append(const pkv_pool_layer* pool, const void* q, const void* k_new, const void* v_new, void* out,
+                       const int32_t* block_tables, int32_t bt_stride, const int32_t* context_lens, int32_t batch,
+                       int32_t max_context_len, int32_t num_q_heads, float scale, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream) {
+  g_last_error.clear();
+  PoolDev pd;
+  if (int rc = check_pool(pool, "attn_decode_append", &pd)) return rc;
+  if (int rc = check_heads(pd, num_q_heads)) return rc;
+  if (batch < 0) return fail(PKV_EINVAL, "attn_decode_append: batch %d", batch);
+  if (batch == 0) return PKV_OK;
+  if (max_context_len <= 0) return fail(PKV_EINVAL, "attn_decode_append: max_context_len %d", max_context_len);
+  if (!q || !out || !block_tables || !context_lens || !k_new || !v_new)
+    return fail(PKV_EINVAL, "attn_decode_append: NULL device array");
+  if (!aligned16(q) || !aligned16(out) || !aligned16(k_new) || !aligned16(v_new))
+    return fail(PKV_EINVAL, "attn_decode_append: q/k_new/v_new/out must be 16-byte aligned");
+  if (bt_stride <= 0 || (int64_t)bt_stride * pd.block_size < max_context_len)
+    return fail(PKV_EINVAL, "attn_decode_append: bt_stride %d blocks cannot hold %d tokens", bt_stride,
+                max_context_len);
+  if (!scale_ok(scale)) return fail(PKV_EINVAL, "attn_decode_append: scale must be finite and >= 0");
+  const DecodePlan plan = plan_decode(batch, num_q_heads, pd.num_kv_heads, max_context_len, pd.head_dim, pool->dtype);
+  if (plan.workspace > 0) {
+    if (!workspace || workspace_bytes < plan.workspace)
+      return fail(PKV_EINVAL, "attn_decode_append: workspace of %zu bytes needed, %zu given", plan.workspace,
+                  workspace ? workspace_bytes : (size_t)0);
+    if (!aligned16(workspace)) return fail(PKV_EINVAL, "attn_decode_append: workspace must be 16-byte aligned");
+  }
+  hipError_t e = launch_attn_decode(pd, pool->dtype, q, out, block_tables, bt_stride, context_lens, batch, num_q_heads,
+                                    resolve_scale(scale, pd.head_dim), plan, workspace, stream, k_new, v_new);
+  return e == hipSuccess ? PKV_OK : hip_fail(e, "attn_decode_append");
 }
 
 int pkv_stall_free_chunk(int32_t token_budget, int32_t num_decode, int32_t prompt_remaining) {
@@ -281,7 +328,7 @@ int attn_mixed_batch(const pkv_pool_layer* pool, const void* q_dec, void* out_de
   if (int rc = check_heads(pd, num_q_heads)) return rc;
   if (num_decode < 0 || num_prefill < 0 || max_chunk_len < 0)
     return fail(PKV_EINVAL, "attn_mixed_batch: negative batch or chunk length");
-  if (!(scale >= 0.f) || std::isinf(scale)) return fail(PKV_EINVAL, "attn_mixed_batch: scale must be finite");
+  if (!scale_ok(scale)) return fail(PKV_EINVAL, "attn_mixed_batch: scale must be finite and >= 0");
   MixedDecode d{};
   MixedPrefill p{};
   if (num_decode > 0) {

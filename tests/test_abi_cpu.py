@@ -35,7 +35,7 @@ def _declared_functions():
 def test_every_declared_symbol_is_exported():
     _lib()
     declared = _declared_functions()
-    assert "kv_write" in declared and "run_mux_round" in declared and len(declared) == 27
+    assert "kv_write" in declared and "run_mux_round" in declared and len(declared) == 28
     out = subprocess.run(["nm", "-D", "--defined-only", lib_mod.LIB_PATH], capture_output=True, text=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
     missing = [n for n in declared if n not in exported]
@@ -164,6 +164,19 @@ def test_attention_validation():
     assert lib.attn_decode(C.byref(p), 0x100, 0x200, 0x300, 512, 0x400, 4, 8192, 32, float("inf"), 0x500,
                            need, None) == -1
     assert lib.attn_decode(C.byref(p), 0x100, 0x200, 0x300, 8, 0x400, 0, 64, 32, 0.0, 0, 0, None) == 0
+    # append: the new rows must be there and aligned; otherwise as attn_decode
+    ap = lambda kn, vn, bt_stride=8, scale=0.0: lib.attn_decode_append(  # noqa: E731
+        C.byref(p), 0x100, kn, vn, 0x200, 0x300, bt_stride, 0x400, 2, 64, 32, scale, 0x500, 1 << 20, None)
+    assert ap(0, 0x700) == -1 and ap(0x600, 0) == -1 and ap(0x608, 0x700) == -1
+    assert ap(0x600, 0x700, bt_stride=2) == -1 and ap(0x600, 0x700, scale=float("nan")) == -1
+    assert lib.attn_decode_append(C.byref(p), 0x100, 0x600, 0x700, 0x200, 0x300, 8, 0x400, 0, 64, 32, 0.0, 0, 0,
+                                  None) == 0
+    # a NaN or negative scale is rejected on the host (tested on the bits)
+    for bad_scale in (float("nan"), -float("nan"), -0.5, float("-inf")):
+        assert lib.attn_decode(C.byref(p), 0x100, 0x200, 0x300, 8, 0x400, 2, 64, 32, bad_scale, 0x500, 1 << 20,
+                               None) == -1
+        assert lib.attn_prefill_chunk(C.byref(p), 0x100, 0x200, 0x300, 8, 0x400, 0x500, 1, 64, 32, bad_scale,
+                                      None) == -1
     assert lib.attn_prefill_chunk(C.byref(p), 0x100, 0x200, 0x300, 8, 0x400, 0x500, 1, 64, 30, 0.0, None) == -1
     assert lib.attn_prefill_chunk(C.byref(p), 0x108, 0x200, 0x300, 8, 0x400, 0x500, 1, 64, 32, 0.0, None) == -1
     assert lib.attn_prefill_chunk(C.byref(p), 0x100, 0x200, 0x300, 8, 0x400, 0x500, 0, 64, 32, 0.0, None) == 0
