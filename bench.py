@@ -226,6 +226,12 @@ def bench_llama3_8b(args):
             ops.kv_write(pools[l], kn[l], vn[l], dec_slots, stream=sh)
             ops.attn_decode(pools[l], q_dec[l], o_dec[l], dec_bt, ctx_t, ctx, hq, workspace=ws, stream=sh)
 
+    def decode_step_append():
+        # the same step with each layer's write and attention in one attn_decode_append launch
+        for l in range(L):
+            ops.attn_decode_append(pools[l], q_dec[l], kn[l], vn[l], o_dec[l], dec_bt, ctx_t, ctx, hq, workspace=ws,
+                                   stream=sh)
+
     def prefill_attn():
         for (s, t), (sl, cs, _) in zip(chunks, ch_args):
             for l in range(L):
@@ -249,10 +255,11 @@ def bench_llama3_8b(args):
 
     pg = PhaseGraphs(stream)
     for name, fn in (("step", step), ("decode_attn", decode_attn), ("prefill_attn", prefill_attn),
-                     ("relayout", relayout), ("decode_step", decode_step)):
+                     ("relayout", relayout), ("decode_step", decode_step), ("decode_step_append", decode_step_append)):
         pg.capture(name, fn)
     t_step = time_replays(pg, ["step"], args.steps, args.warmup)["step"]
-    t = time_replays(pg, ["decode_attn", "prefill_attn", "relayout", "decode_step"], args.steps, args.warmup)
+    t = time_replays(pg, ["decode_attn", "prefill_attn", "relayout", "decode_step", "decode_step_append"], args.steps,
+                     args.warmup)
 
     dec_launch_ms = t["decode_attn"] / L
     dbytes = decode_bytes([ctx] * B, hkv, d, hq)
@@ -278,6 +285,7 @@ def bench_llama3_8b(args):
         "metrics": {
             "decode_attn_gbps": round(dec_gbps, 1),
             "decode_step_ms": round(t["decode_step"], 4),
+            "decode_step_append_ms": round(t["decode_step_append"], 4),
             "prefill_attn_tflops": round(pf_tflops, 2),
             "prefill_attn_frac_bf16_peak": round(pf_tflops / BF16_PEAK_TFLOPS, 4),
             "prefill_attn_ms_per_layer": round(t["prefill_attn"] / L, 5),

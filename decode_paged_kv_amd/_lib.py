@@ -108,6 +108,8 @@ _SIGS = {
     "attn_prefill_chunk": (C.c_int, [C.POINTER(PoolLayer), _P, _P, _P, _I, _P, _P, _I, _I, _I, C.c_float, _P]),
     "pkv_attn_decode_workspace_size": (C.c_size_t, [_I, _I, _I, _I]),
     "attn_decode": (C.c_int, [C.POINTER(PoolLayer), _P, _P, _P, _I, _P, _I, _I, _I, C.c_float, _P, C.c_size_t, _P]),
+    "attn_decode_append": (C.c_int, [C.POINTER(PoolLayer), _P, _P, _P, _P, _P, _I, _P, _I, _I, _I, C.c_float, _P,
+                                     C.c_size_t, _P]),
     "pkv_stall_free_chunk": (C.c_int, [_I, _I, _I]),
     "attn_mixed_batch": (C.c_int, [C.POINTER(PoolLayer), _P, _P, _P, _I, _P, _I, _I, _P, _P, _P, _I, _P, _P, _I, _I,
                                    _I, C.c_float, _P, C.c_size_t, _P]),

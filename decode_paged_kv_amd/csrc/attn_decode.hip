@@ -276,9 +276,43 @@ __global__ void __launch_bounds__(kThreads, 2)
 attn_decode_bf16_kernel(PoolDev pool, const bf16_t* __restrict__ q, bf16_t* __restrict__ out,
                         const int32_t* __restrict__ bt, int bt_stride, const int32_t* __restrict__ ctx, int batch,
                         int num_q_heads, float scale_log2, int split_tokens, int num_splits,
-                        float* __restrict__ part_o, float* __restrict__ part_ml) {
+                        float* __restrict__ part_o, float* __restrict__ part_ml, const bf16_t* __restrict__ k_new,
+                        const bf16_t* __restrict__ v_new) {
   decode_bf16_block<D, G, STREAM>(pool, q, out, bt, bt_stride, ctx, batch, num_q_heads, scale_log2, split_tokens,
-                                  num_splits, part_o, part_ml, blockIdx.x, blockIdx.y, blockIdx.z, gridDim.x);
+                                  num_splits, part_o, part_ml, k_new, v_new, blockIdx.x, blockIdx.y, blockIdx.z,
+                                  gridDim.x);
+}
+
+// The new token's K/V row of each (request, KV head) written at position
+// L-1 of the request (the fp32 path of attn_decode_append; the bf16 kernel
+// writes it itself).  One workgroup per (KV head, request), a thread per dim.
+template <typename T>
+__global__ void __launch_bounds__(128)
+kv_append_kernel(PoolDev pool, const T* __restrict__ k_new, const T* __restrict__ v_new,
+                 const int32_t* __restrict__ bt, int bt_stride, const int32_t* __restrict__ ctx) {
+  const int kvh = blockIdx.x, b = blockIdx.y, D = pool.head_dim;
+  const int L = ctx[b];
+  if (L <= 0) return;
+  if (L > (bt_stride << pool.bs_shift)) {
+    if (threadIdx.x == 0 && kvh == 0) flag_error(pool.err, PKV_ERRBIT_TABLE);
+    return;
+  }
+  const int blk = bt[(size_t)b * bt_stride + ((L - 1) >> pool.bs_shift)];
+  if (blk < 0 || blk >= pool.num_blocks) {
+    if (threadIdx.x == 0) flag_error(pool.err, PKV_ERRBIT_BLOCK_ID);
+    return;
+  }
+  const int hl = pool.heads_per_shard, sh = kvh / hl, lh = kvh - sh * hl;
+  const size_t tile = tile_elems(pool, blk, lh);
+  const int off = (L - 1) & (pool.block_size - 1);
+  const T* kn = k_new + ((size_t)b * pool.num_kv_heads + kvh) * D;
+  const T* vn = v_new + ((size_t)b * pool.num_kv_heads + kvh) * D;
+  T* kp = reinterpret_cast<T*>(pool.k[sh]) + tile + (size_t)off * D;
+  T* vp = reinterpret_cast<T*>(pool.v[sh]) + tile + off;
+  for (int d = threadIdx.x; d < D; d += 128) {
+    kp[d] = kn[d];
+    vp[(size_t)d * pool.block_size] = vn[d];
+  }
 }
 
 // Merge the split partials of each (request, q-head): rescale each split's
@@ -375,7 +409,7 @@ attn_decode_stream_merge_kernel(const float* __restrict__ part_o, const float* _
 template <typename T, int D, int G>
 hipError_t launch_typed(const PoolDev& pool, const void* q, void* out, const int32_t* bt, int bt_stride,
                         const int32_t* ctx, int batch, int num_q_heads, float scale_log2, const DecodePlan& plan,
-                        void* ws, hipStream_t s) {
+                        void* ws, hipStream_t s, const void* k_new, const void* v_new) {
   float* part_o = static_cast<float*>(ws);
   float* part_ml = part_o ? part_o + (size_t)batch * num_q_heads * plan.num_splits * D : nullptr;
   if constexpr (sizeof(T) == 2) {
@@ -383,7 +417,8 @@ hipError_t launch_typed(const PoolDev& pool, const void* q, void* out, const int
       float* ml = static_cast<float*>(ws) + (size_t)(plan.stream_wgs + batch * (num_q_heads / G)) * G * D;
       hipLaunchKernelGGL((attn_decode_bf16_kernel<D, G, true>), dim3(plan.stream_wgs), dim3(kThreads), 0, s, pool,
                          static_cast<const bf16_t*>(q), static_cast<bf16_t*>(out), bt, bt_stride, ctx, batch,
-                         num_q_heads, scale_log2, 0, 0, part_o, ml);
+                         num_q_heads, scale_log2, 0, 0, part_o, ml, static_cast<const bf16_t*>(k_new),
+                         static_cast<const bf16_t*>(v_new));
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
       hipLaunchKernelGGL((attn_decode_stream_merge_kernel<D>), dim3(num_q_heads, batch), dim3(D), 0, s, part_o, ml,
@@ -393,10 +428,19 @@ hipError_t launch_typed(const PoolDev& pool, const void* q, void* out, const int
     }
   }
   const dim3 grid(plan.num_splits, num_q_heads / G, batch);
+  if constexpr (sizeof(T) == 4) {
+    if (k_new) {
+      hipLaunchKernelGGL(kv_append_kernel<T>, dim3(pool.num_kv_heads, batch), dim3(128), 0, s, pool,
+                         static_cast<const T*>(k_new), static_cast<const T*>(v_new), bt, bt_stride, ctx);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+  }
   if constexpr (sizeof(T) == 2)
     hipLaunchKernelGGL((attn_decode_bf16_kernel<D, G, false>), grid, dim3(kThreads), 0, s, pool,
                        static_cast<const bf16_t*>(q), static_cast<bf16_t*>(out), bt, bt_stride, ctx, batch,
-                       num_q_heads, scale_log2, plan.split_tokens, plan.num_splits, part_o, part_ml);
+                       num_q_heads, scale_log2, plan.split_tokens, plan.num_splits, part_o, part_ml,
+                       static_cast<const bf16_t*>(k_new), static_cast<const bf16_t*>(v_new));
   else
     hipLaunchKernelGGL((attn_decode_kernel<T, D, G>), grid, dim3(kThreads), 0, s, pool, static_cast<const T*>(q),
                        static_cast<T*>(out), bt, bt_stride, ctx, num_q_heads, scale_log2, plan.split_tokens,
@@ -412,13 +456,13 @@ hipError_t launch_typed(const PoolDev& pool, const void* q, void* out, const int
 template <typename T, int D>
 hipError_t launch_d(int group, const PoolDev& pool, const void* q, void* out, const int32_t* bt, int bt_stride,
                     const int32_t* ctx, int batch, int num_q_heads, float scale_log2, const DecodePlan& plan,
-                    void* ws, hipStream_t s) {
+                    void* ws, hipStream_t s, const void* k_new, const void* v_new) {
   switch (group) {
-    case 1: return launch_typed<T, D, 1>(pool, q, out, bt, bt_stride, ctx, batch, num_q_heads, scale_log2, plan, ws, s);
-    case 2: return launch_typed<T, D, 2>(pool, q, out, bt, bt_stride, ctx, batch, num_q_heads, scale_log2, plan, ws, s);
-    case 4: return launch_typed<T, D, 4>(pool, q, out, bt, bt_stride, ctx, batch, num_q_heads, scale_log2, plan, ws, s);
-    case 8: return launch_typed<T, D, 8>(pool, q, out, bt, bt_stride, ctx, batch, num_q_heads, scale_log2, plan, ws, s);
-    case 16: return launch_typed<T, D, 16>(pool, q, out, bt, bt_stride, ctx, batch, num_q_heads, scale_log2, plan, ws, s);
+    case 1: return launch_typed<T, D, 1>(pool, q, out, bt, bt_stride, ctx, batch, num_q_heads, scale_log2, plan, ws, s, k_new, v_new);
+    case 2: return launch_typed<T, D, 2>(pool, q, out, bt, bt_stride, ctx, batch, num_q_heads, scale_log2, plan, ws, s, k_new, v_new);
+    case 4: return launch_typed<T, D, 4>(pool, q, out, bt, bt_stride, ctx, batch, num_q_heads, scale_log2, plan, ws, s, k_new, v_new);
+    case 8: return launch_typed<T, D, 8>(pool, q, out, bt, bt_stride, ctx, batch, num_q_heads, scale_log2, plan, ws, s, k_new, v_new);
+    case 16: return launch_typed<T, D, 16>(pool, q, out, bt, bt_stride, ctx, batch, num_q_heads, scale_log2, plan, ws, s, k_new, v_new);
     default: return hipErrorInvalidValue;
   }
 }
@@ -497,16 +541,17 @@ DecodePlan plan_decode(int batch, int num_q_heads, int num_kv_heads, int max_con
 
 hipError_t launch_attn_decode(const PoolDev& pool, int dtype, const void* q, void* out, const int32_t* bt,
                               int bt_stride, const int32_t* ctx, int batch, int num_q_heads, float scale,
-                              const DecodePlan& plan, void* workspace, hipStream_t s) {
+                              const DecodePlan& plan, void* workspace, hipStream_t s, const void* k_new,
+                              const void* v_new) {
   if (batch == 0) return hipSuccess;
   const int group = num_q_heads / pool.num_kv_heads;
   const float sl2 = scale * kLog2e;
   if (dtype == PKV_BF16) {
-    if (pool.head_dim == 128) return launch_d<bf16_t, 128>(group, pool, q, out, bt, bt_stride, ctx, batch, num_q_heads, sl2, plan, workspace, s);
-    return launch_d<bf16_t, 64>(group, pool, q, out, bt, bt_stride, ctx, batch, num_q_heads, sl2, plan, workspace, s);
+    if (pool.head_dim == 128) return launch_d<bf16_t, 128>(group, pool, q, out, bt, bt_stride, ctx, batch, num_q_heads, sl2, plan, workspace, s, k_new, v_new);
+    return launch_d<bf16_t, 64>(group, pool, q, out, bt, bt_stride, ctx, batch, num_q_heads, sl2, plan, workspace, s, k_new, v_new);
   }
-  if (pool.head_dim == 128) return launch_d<float, 128>(group, pool, q, out, bt, bt_stride, ctx, batch, num_q_heads, sl2, plan, workspace, s);
-  return launch_d<float, 64>(group, pool, q, out, bt, bt_stride, ctx, batch, num_q_heads, sl2, plan, workspace, s);
+  if (pool.head_dim == 128) return launch_d<float, 128>(group, pool, q, out, bt, bt_stride, ctx, batch, num_q_heads, sl2, plan, workspace, s, k_new, v_new);
+  return launch_d<float, 64>(group, pool, q, out, bt, bt_stride, ctx, batch, num_q_heads, sl2, plan, workspace, s, k_new, v_new);
 }
 
 }  // namespace pkv

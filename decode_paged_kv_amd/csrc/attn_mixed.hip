@@ -47,8 +47,8 @@ attn_mixed_bf16_kernel(PoolDev pool,
     const int rem = bid - b * per_b;
     const int kvh = rem / num_splits, split = rem - kvh * num_splits;
     decode_impl::decode_bf16_block<D, G, false>(pool, dq, dout, dbt, dbt_stride, ctx, dbatch, num_q_heads,
-                                                scale_log2, split_tokens, num_splits, part_o, part_ml, split, kvh, b,
-                                                0);
+                                                scale_log2, split_tokens, num_splits, part_o, part_ml, nullptr,
+                                                nullptr, split, kvh, b, 0);
   }
 }
 

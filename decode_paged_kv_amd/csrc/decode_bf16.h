@@ -95,6 +95,7 @@ struct DecodeBf16Smem {
   float acc[kWaves][G][D];
   float m[kWaves][G];
   float l[kWaves][G];
+  float snew[G];            // score of the appended key, per q-head (log2 units)
 };
 
 // Running max update rule (log2 units): the max used for exp2 moves only
@@ -166,7 +167,9 @@ __device__ __forceinline__ void decode_bf16_block(PoolDev pool, const bf16_t* __
                                                   int bt_stride, const int32_t* __restrict__ ctx, int batch,
                                                   int num_q_heads, float scale_log2, int split_tokens,
                                                   int num_splits, float* __restrict__ part_o,
-                                                  float* __restrict__ part_ml, int bx, int by, int bz, int nbx) {
+                                                  float* __restrict__ part_ml, const bf16_t* __restrict__ k_new,
+                                                  const bf16_t* __restrict__ v_new, int bx, int by, int bz,
+                                                  int nbx) {
   static_assert(G >= 1 && G <= 16, "the q-heads of a KV head are the 16 MFMA columns");
   constexpr int KC = D / 32, DT = D / 16, TK = 32;
   __shared__ DecodeBf16Smem<D, G> sm;
@@ -182,11 +185,15 @@ __device__ __forceinline__ void decode_bf16_block(PoolDev pool, const bf16_t* __
 
   // One segment: keys [start, end) of request b and KV head kvh; the result
   // goes to out when final_out, else to the partial rows prow + g * pstride.
+  // With `last` (append mode) the request's new key L-1 follows the segment:
+  // its K/V come from k_new / v_new, are added to the softmax in the merge,
+  // and are written to the pool there; the tiles stop at L-1.
   struct Seg {
     int b, kvh, start, end;
     bool final_out;
     size_t prow;
     int pstride;
+    bool last;
   };
   // the segment whose loads are being issued: its KV head's pools, its
   // table, its end (wave-uniform, in scalar registers)
@@ -368,6 +375,37 @@ __device__ __forceinline__ void decode_bf16_block(PoolDev pool, const bf16_t* __
   };
   // the 4 waves' (m, l, acc) of a segment, combined and written
   auto merge = [&](const Seg& sg) {
+    if (sg.last) {
+      // the appended key: its score for each q-head (wave w takes heads
+      // w, w+4, ...; a lane 1 or 2 dims), and its row written to the pool
+      // at position L-1 (the tiles never read that slot)
+      const int L = sg.end + 1;
+      const bf16_t* kn = k_new + ((size_t)sg.b * (num_q_heads / G) + sg.kvh) * D;
+      const bf16_t* vn = v_new + ((size_t)sg.b * (num_q_heads / G) + sg.kvh) * D;
+      for (int g = wave; g < G; g += kWaves) {
+        const bf16_t* qr = q + ((size_t)sg.b * num_q_heads + (size_t)sg.kvh * G + g) * D;
+        float part = 0.f;
+        for (int d = lane; d < D; d += 64) part = fmaf(bf16_to_f32(qr[d]), bf16_to_f32(kn[d]), part);
+#pragma unroll
+        for (int o2 = 32; o2 >= 1; o2 >>= 1) part += __shfl_xor(part, o2);
+        if (lane == 0) sm.snew[g] = part * scale_log2;
+      }
+      const int32_t* tb = bt + (size_t)sg.b * bt_stride;
+      const int blk = tb[(L - 1) >> pool.bs_shift];
+      if (blk >= 0 && blk < pool.num_blocks) {
+        const int sh = sg.kvh / hl, lh = sg.kvh - sh * hl;
+        const size_t tile = ((size_t)blk * hl + lh) * ((size_t)bs * D);
+        const int off = (L - 1) & (bs - 1);
+        bf16_t* kp = const_cast<bf16_t*>(reinterpret_cast<const bf16_t*>(pool.k[sh])) + tile + (size_t)off * D;
+        bf16_t* vp = const_cast<bf16_t*>(reinterpret_cast<const bf16_t*>(pool.v[sh])) + tile + off;
+        for (int d = threadIdx.x; d < D; d += kThreads) {
+          kp[d] = kn[d];
+          vp[(size_t)d * bs] = vn[d];
+        }
+      } else if (threadIdx.x == 0) {
+        flag_error(pool.err, PKV_ERRBIT_BLOCK_ID);
+      }
+    }
     lsum = col_sum(lsum);
     if (l16 < G) {
       if (j4 == 0) {
@@ -391,6 +429,15 @@ __device__ __forceinline__ void decode_bf16_block(PoolDev pool, const bf16_t* __
         const float f = __builtin_amdgcn_exp2f(sm.m[w][g] - mx);
         l += sm.l[w][g] * f;
         acc += sm.acc[w][g][d] * f;
+      }
+      if (sg.last) {
+        const float sn = sm.snew[g];
+        const float mf = fmaxf(mx, sn);
+        const float fo = __builtin_amdgcn_exp2f(mx - mf), fn = __builtin_amdgcn_exp2f(sn - mf);
+        const bf16_t* vn = v_new + ((size_t)sg.b * (num_q_heads / G) + sg.kvh) * D;
+        l = l * fo + fn;
+        acc = acc * fo + fn * bf16_to_f32(vn[d]);
+        mx = mf;
       }
       const int h = sg.kvh * G + g;
       if (sg.final_out) {
@@ -417,8 +464,10 @@ __device__ __forceinline__ void decode_bf16_block(PoolDev pool, const bf16_t* __
     }
     const int start = split * split_tokens;
     if (start >= L) return;
-    const Seg sg{b, kvh, start, min(L, start + split_tokens), L <= split_tokens,
-                 ((size_t)b * num_q_heads + (size_t)kvh * G) * num_splits + split, num_splits};
+    const int end = min(L, start + split_tokens);
+    const bool last = k_new != nullptr && ctx[b] <= cap && end == L;
+    const Seg sg{b, kvh, start, last ? end - 1 : end, L <= split_tokens,
+                 ((size_t)b * num_q_heads + (size_t)kvh * G) * num_splits + split, num_splits, last};
     prologue(sg);
     body(sg);
     merge(sg);
@@ -441,7 +490,8 @@ __device__ __forceinline__ void decode_bf16_block(PoolDev pool, const bf16_t* __
     // the segments of this workgroup's range, in order
     auto next_seg = [&](Seg& sg) -> bool {
       while (t < t1) {
-        const int L = max(min(ctx[b], cap), 0);
+        const int raw = ctx[b];
+        const int L = max(min(raw, cap), 0);
         const int ntb = (L + TK - 1) / TK;
         if (ntb == 0) {                         // an empty request holds no tiles
           ++b;
@@ -457,6 +507,8 @@ __device__ __forceinline__ void decode_bf16_block(PoolDev pool, const bf16_t* __
         sg.final_out = stream_owner(pstart, NW, Wt) == stream_owner(pstart + ntb - 1, NW, Wt);
         sg.prow = (size_t)(w + (long long)b * hkv + kvh) * G;
         sg.pstride = 1;
+        sg.last = k_new != nullptr && raw <= cap && sg.end == L;
+        if (sg.last) sg.end = L - 1;
         t = seg_end;
         if (t == base + (long long)hkv * ntb) {
           base = t;

@@ -118,9 +118,12 @@ DecodePlan plan_decode(int batch, int num_q_heads, int num_kv_heads, int max_con
 hipError_t launch_decode_split_merge(const PoolDev& pool, int dtype, void* out, const int32_t* ctx, int bt_stride,
                                      int batch, int num_q_heads, const DecodePlan& plan, void* workspace,
                                      hipStream_t s);
+// k_new / v_new non-null: append mode (each request's new K/V row written
+// at position L-1 and used for that key; see attn_decode_append)
 hipError_t launch_attn_decode(const PoolDev& pool, int dtype, const void* q, void* out, const int32_t* bt,
                               int bt_stride, const int32_t* ctx, int batch, int num_q_heads, float scale,
-                              const DecodePlan& plan, void* workspace, hipStream_t s);
+                              const DecodePlan& plan, void* workspace, hipStream_t s, const void* k_new = nullptr,
+                              const void* v_new = nullptr);
 hipError_t launch_attn_prefill(const PoolDev& pool, int dtype, const void* q, void* out, const int32_t* bt,
                                int bt_stride, const int32_t* start_loc, const int32_t* chunk_start, int batch,
                                int max_chunk_len, int num_q_heads, float scale, hipStream_t s);

@@ -188,6 +188,22 @@ def attn_decode(pool: PagedPool, q, out, block_tables, context_lens, max_context
     _lib.check(rc, "attn_decode")
 
 
+def attn_decode_append(pool: PagedPool, q, k_new, v_new, out, block_tables, context_lens, max_context_len: int,
+                       num_q_heads: int, scale: float = 0.0, workspace=None, stream=None):
+    """kv_write of each request's new row at position L-1 and attn_decode over [0, L), in one launch."""
+    lib = _lib.load()
+    c = pool.c()
+    batch = context_lens.numel()
+    if workspace is None:
+        nbytes = attn_decode_workspace_size(batch, num_q_heads, max_context_len, pool.head_dim)
+        workspace = torch.zeros(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    rc = lib.attn_decode_append(C.byref(c), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(out), _ptr(block_tables),
+                                block_tables.shape[-1], _ptr(context_lens), batch, max_context_len, num_q_heads,
+                                scale, _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                _stream(stream))
+    _lib.check(rc, "attn_decode_append")
+
+
 def stall_free_chunk(token_budget: int, num_decode: int, prompt_remaining: int) -> int:
     """Tokens of a prompt that fit a stall-free step: what the decode requests leave of the budget."""
     rc = int(_lib.load().pkv_stall_free_chunk(token_budget, num_decode, prompt_remaining))

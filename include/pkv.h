@@ -237,6 +237,27 @@ int attn_decode(const pkv_pool_layer* pool, const void* q, void* out, const int3
                 hipStream_t stream);
 
 /*
+ * attn_decode_append - one decode step's K/V append and attention in one
+ * launch.  [DISAGG] "实现" (a decode step writes the new token's K/V at the
+ * request's next slot, then attends over all its cached keys) and [L7]
+ * section 1.1.  For request b with context L = context_lens[b] (the new
+ * token included): the rows k_new[b], v_new[b] ([B, Hkv, D], device,
+ * 16-byte aligned) are written at position L-1, slot
+ * block_tables[b][(L-1)/bs] * bs + (L-1) % bs, with the same result in the
+ * pool as kv_write; and out[b] is attn_decode over keys [0, L), key L-1
+ * taken from k_new/v_new (not read back from the pool).  Other arguments,
+ * workspace size (pkv_attn_decode_workspace_size) and errors as
+ * attn_decode.  A request whose context exceeds its table, or whose slot
+ * L-1 lies in a block id outside the pool, has nothing written and sets
+ * the error word (PKV_ERRBIT_TABLE / PKV_ERRBIT_BLOCK_ID).  The request's
+ * slot L-1 must not be read by any other call on another stream meanwhile.
+ */
+int attn_decode_append(const pkv_pool_layer* pool, const void* q, const void* k_new, const void* v_new, void* out,
+                       const int32_t* block_tables, int32_t bt_stride, const int32_t* context_lens, int32_t batch,
+                       int32_t max_context_len, int32_t num_q_heads, float scale, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Stall-free mixed batch ([L7] section 2.4): each step takes
  * every decoding request first, one token each, and fills what is left of a
  * per-step token budget with prefill chunks, so the step time is bounded and

@@ -13,7 +13,7 @@ import pytest
 import torch
 
 from decode_paged_kv_amd import inputs, ops, workloads
-from gpu_common import Scenario, assert_close, from_dev, i32, to_dev
+from gpu_common import SENTINEL, Scenario, assert_close, from_dev, i32, to_dev
 from oracle import attention as oa
 
 pytestmark = pytest.mark.gpu
@@ -237,3 +237,40 @@ def test_bad_block_id_makes_its_keys_absent():
     ref = np.stack([oa.decode(f(qp)[i], *present(0, s0 + i + 1)) for i in range(t)])
     assert_close(got, ref, "bf16", "prefill with absent keys")
     assert int(err.item()) & 1
+
+
+@pytest.mark.parametrize("dtype,hq,hkv,d,bs,shards,lengths", [
+    # 512 (request, KV head) pairs: one workgroup per pair, the new key in its merge
+    ("bf16", 32, 8, 128, 16, 1, [int(x) for x in np.random.default_rng(13).integers(1, 600, 64)]),
+    # few pairs, long contexts: the stream split (the new key in the last piece of each pair)
+    ("bf16", 64, 8, 128, 16, 1, [2048, 8192, 3001, 4097, 33]),
+    ("bf16", 32, 2, 64, 64, 2, [1, 333, 2000, 32, 33]),    # G = 16, head dim 64, tile-edge contexts
+    ("bf16", 8, 4, 128, 128, 1, [5, 256, 1025]),
+    ("f32", 8, 2, 128, 32, 2, [1, 90, 513]),               # fp32: the append kernel, then decode
+])
+def test_decode_append_writes_the_row_and_attends(dtype, hq, hkv, d, bs, shards, lengths):
+    """attn_decode_append over contexts L whose first L-1 tokens are in the pool: out equals the oracle over all
+    L keys, and the pool equals, byte for byte, the oracle's pool with all L tokens written."""
+    from oracle import pool as opool
+    nblk = sum(-(-n // bs) for n in lengths) + 3
+    sc = Scenario(num_q_heads=hq, num_kv_heads=hkv, head_dim=d, block_size=bs, dtype=dtype, lengths=lengths,
+                  pool_blocks=nblk, num_shards=shards, scale=0.5 if dtype == "bf16" else 1.0, seed=15)
+    sc.write_all(upto=[n - 1 for n in lengths])
+    kn = np.stack([sc.k[r][n - 1] for r, n in enumerate(lengths)])
+    vn = np.stack([sc.v[r][n - 1] for r, n in enumerate(lengths)])
+    q = _q(sc, (len(lengths), hq, d), scale=0.5 if dtype == "bf16" else 1.0)
+    out = torch.empty((len(lengths), hq, d), dtype=_tdtype(dtype), device="cuda")
+    print(f"attn_decode_append {dtype} hq={hq} hkv={hkv} d={d} bs={bs} lengths={lengths[:6]}", flush=True)
+    ops.attn_decode_append(sc.pool, to_dev(q, dtype), to_dev(kn, dtype), to_dev(vn, dtype), out, sc.bt_dev,
+                           i32(lengths), max(lengths), hq)
+    torch.cuda.synchronize()
+    got = inputs.as_float(from_dev(out, dtype), dtype)
+    assert_close(got, oracle_decode(sc, q), dtype, "decode append")
+    elem = np.uint16 if dtype == "bf16" else np.float32
+    fill = SENTINEL[dtype] if dtype == "bf16" else np.array([SENTINEL[dtype]], np.uint32).view(np.float32)[0]
+    pm = opool.PoolModel(nblk, bs, hkv, shards, d, elem, fill=fill)
+    for r, n in enumerate(lengths):
+        opool.write(pm, sc.k[r], sc.v[r], opool.slots_for(sc.tables[r], bs, range(n)))
+    for s in range(shards):
+        assert np.array_equal(from_dev(sc.pool.k[s], dtype).view(np.uint8), pm.k[s].view(np.uint8)), f"K shard {s}"
+        assert np.array_equal(from_dev(sc.pool.v[s], dtype).view(np.uint8), pm.v[s].view(np.uint8)), f"V shard {s}"
