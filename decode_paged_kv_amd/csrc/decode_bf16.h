@@ -375,24 +375,28 @@ __device__ __forceinline__ void decode_bf16_block(PoolDev pool, const bf16_t* __
   };
   // the 4 waves' (m, l, acc) of a segment, combined and written
   auto merge = [&](const Seg& sg) {
+    // the appended key (append mode, last piece of the request): its row is
+    // written to the pool at position L-1 (the tiles never read that slot)
+    // and its score for each q-head computed (wave w takes heads w, w+4,
+    // ...; a lane 1 or 2 dims); a block id outside the pool makes it absent,
+    // as for any key
+    bool add_new = false;
     if (sg.last) {
-      // the appended key: its score for each q-head (wave w takes heads
-      // w, w+4, ...; a lane 1 or 2 dims), and its row written to the pool
-      // at position L-1 (the tiles never read that slot)
       const int L = sg.end + 1;
       const bf16_t* kn = k_new + ((size_t)sg.b * (num_q_heads / G) + sg.kvh) * D;
       const bf16_t* vn = v_new + ((size_t)sg.b * (num_q_heads / G) + sg.kvh) * D;
-      for (int g = wave; g < G; g += kWaves) {
-        const bf16_t* qr = q + ((size_t)sg.b * num_q_heads + (size_t)sg.kvh * G + g) * D;
-        float part = 0.f;
-        for (int d = lane; d < D; d += 64) part = fmaf(bf16_to_f32(qr[d]), bf16_to_f32(kn[d]), part);
-#pragma unroll
-        for (int o2 = 32; o2 >= 1; o2 >>= 1) part += __shfl_xor(part, o2);
-        if (lane == 0) sm.snew[g] = part * scale_log2;
-      }
       const int32_t* tb = bt + (size_t)sg.b * bt_stride;
       const int blk = tb[(L - 1) >> pool.bs_shift];
-      if (blk >= 0 && blk < pool.num_blocks) {
+      add_new = blk >= 0 && blk < pool.num_blocks;
+      if (add_new) {
+        for (int g = wave; g < G; g += kWaves) {
+          const bf16_t* qr = q + ((size_t)sg.b * num_q_heads + (size_t)sg.kvh * G + g) * D;
+          float part = 0.f;
+          for (int d = lane; d < D; d += 64) part = fmaf(bf16_to_f32(qr[d]), bf16_to_f32(kn[d]), part);
+#pragma unroll
+          for (int o2 = 32; o2 >= 1; o2 >>= 1) part += __shfl_xor(part, o2);
+          if (lane == 0) sm.snew[g] = part * scale_log2;
+        }
         const int sh = sg.kvh / hl, lh = sg.kvh - sh * hl;
         const size_t tile = ((size_t)blk * hl + lh) * ((size_t)bs * D);
         const int off = (L - 1) & (bs - 1);
@@ -430,7 +434,7 @@ __device__ __forceinline__ void decode_bf16_block(PoolDev pool, const bf16_t* __
         l += sm.l[w][g] * f;
         acc += sm.acc[w][g][d] * f;
       }
-      if (sg.last) {
+      if (add_new) {
         const float sn = sm.snew[g];
         const float mf = fmaxf(mx, sn);
         const float fo = __builtin_amdgcn_exp2f(mx - mf), fn = __builtin_amdgcn_exp2f(sn - mf);

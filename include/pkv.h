@@ -249,7 +249,8 @@ int attn_decode(const pkv_pool_layer* pool, const void* q, void* out, const int3
  * workspace size (pkv_attn_decode_workspace_size) and errors as
  * attn_decode.  A request whose context exceeds its table, or whose slot
  * L-1 lies in a block id outside the pool, has nothing written and sets
- * the error word (PKV_ERRBIT_TABLE / PKV_ERRBIT_BLOCK_ID).  The request's
+ * the error word (PKV_ERRBIT_TABLE / PKV_ERRBIT_BLOCK_ID); its output is
+ * then attn_decode's (a key in a bad block is absent).  The request's
  * slot L-1 must not be read by any other call on another stream meanwhile.
  */
 int attn_decode_append(const pkv_pool_layer* pool, const void* q, const void* k_new, const void* v_new, void* out,

@@ -274,3 +274,37 @@ def test_decode_append_writes_the_row_and_attends(dtype, hq, hkv, d, bs, shards,
     for s in range(shards):
         assert np.array_equal(from_dev(sc.pool.k[s], dtype).view(np.uint8), pm.k[s].view(np.uint8)), f"K shard {s}"
         assert np.array_equal(from_dev(sc.pool.v[s], dtype).view(np.uint8), pm.v[s].view(np.uint8)), f"V shard {s}"
+
+
+def test_decode_append_with_a_bad_last_block():
+    """The block holding a request's new key is outside the pool: nothing is written, the whole block's keys
+    (the new one included) are absent, the error word gets the block-id bit; other requests are unaffected."""
+    bs, hq, hkv, d = 16, 16, 4, 128
+    lengths = [300, 77]
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    sc = Scenario(num_q_heads=hq, num_kv_heads=hkv, head_dim=d, block_size=bs, dtype="bf16", lengths=lengths,
+                  pool_blocks=40, scale=0.5, seed=16, err_word=err)
+    sc.write_all(upto=[n - 1 for n in lengths])
+    torch.cuda.synchronize()
+    err.zero_()
+    tables = sc.tables.copy()
+    tables[0, 299 // bs] = 40 + 3                          # request 0's last block: past the pool
+    sc.bt_dev = i32(tables)
+    before = [from_dev(t, "bf16").copy() for t in sc.pool.k + sc.pool.v]
+    kn = np.stack([sc.k[r][n - 1] for r, n in enumerate(lengths)])
+    vn = np.stack([sc.v[r][n - 1] for r, n in enumerate(lengths)])
+    q = _q(sc, (2, hq, d), scale=0.5)
+    out = torch.empty((2, hq, d), dtype=torch.bfloat16, device="cuda")
+    ops.attn_decode_append(sc.pool, to_dev(q, "bf16"), to_dev(kn, "bf16"), to_dev(vn, "bf16"), out, sc.bt_dev,
+                           i32(lengths), max(lengths), hq)
+    torch.cuda.synchronize()
+    got = inputs.as_float(from_dev(out, "bf16"), "bf16")
+    qf = inputs.as_float(q, "bf16")
+    keep = [p for p in range(300) if p // bs != 299 // bs]
+    assert_close(got[0], oa.decode(qf[0], sc.kf(0)[keep], sc.vf(0)[keep]), "bf16", "request with a bad last block")
+    assert_close(got[1], oa.decode(qf[1], sc.kf(1), sc.vf(1)), "bf16", "request 1")
+    assert int(err.item()) & 1
+    after = [from_dev(t, "bf16") for t in sc.pool.k + sc.pool.v]
+    # only request 1's new row changed the pool
+    changed = sum(int(np.count_nonzero(a != b)) for a, b in zip(after, before))
+    assert 0 < changed <= 2 * hkv * d
