@@ -605,7 +605,8 @@ def bench_pdmux(args):
          stream;
       D  prefill alone on the whole device (one stream);
       A, B with the decode step captured as one HIP graph per level and
-         replayed (metrics "decode_graphs");
+         replayed (metrics "decode_graphs"), and with each decode layer as
+         one attn_decode_append launch (metrics "decode_append");
       E  stall-free batches on the whole device: each step takes every decode
          request and the prompt's share of a token budget (2048 and 512, the
          pages' loose and strict settings), per layer one attn_mixed_batch
@@ -757,6 +758,11 @@ def bench_pdmux(args):
     Ag = solo(max(10, args.steps))
     B16g, pf16g, _ = muxed("16k")
     mux.set_decode_graphs(False)
+    # the same with each decode layer as one attn_decode_append (write + attention)
+    mux.set_decode_append(True)
+    Aa = solo(max(10, args.steps))
+    B16a, pf16a, _ = muxed("16k")
+    mux.set_decode_append(False)
     sweep = {}
     for lvl in range(1, len(groups) - 1):
         ts, pf, _ = muxed("16k", lvl)
@@ -804,6 +810,9 @@ def bench_pdmux(args):
             "decode_graphs": {"solo_decode": stats(Ag), "mux_16k_decode": stats(B16g),
                               "mux_16k_prefill_ms": round(pf16g, 2),
                               "mux_over_solo_16k": round(float(np.median(B16g)) / float(np.median(Ag)), 3)},
+            "decode_append": {"solo_decode": stats(Aa), "mux_16k_decode": stats(B16a),
+                              "mux_16k_prefill_ms": round(pf16a, 2),
+                              "mux_over_solo_16k": round(float(np.median(B16a)) / float(np.median(Aa)), 3)},
             "level_sweep_16k": sweep,
             "chunked_whole_gpu": C,
             "stall_free_whole_gpu": E,

@@ -124,6 +124,7 @@ _SIGS = {
     "pkv_mux_set_level_override": (C.c_int, [_P, C.c_int]),
     "pkv_mux_set_manual_divisions": (C.c_int, [_P, C.POINTER(_I), _I]),
     "pkv_mux_set_decode_graphs": (C.c_int, [_P, C.c_int]),
+    "pkv_mux_set_decode_append": (C.c_int, [_P, C.c_int]),
     "pkv_mux_policy_choose_manual": (C.c_int, [C.c_int, C.c_int, C.c_int, C.POINTER(_I)]),
     "pkv_mux_stream": (_P, [_P, C.c_int, C.c_int]),
     "pkv_mux_cu_mask": (C.c_int, [_P, C.c_int, C.c_int, C.POINTER(C.c_uint32), _I, C.POINTER(_I)]),

@@ -53,6 +53,7 @@ struct pkv_mux {
   // decode step as one HIP graph per level (opt-in): the captured launches
   // and the arguments they were captured with
   bool use_graphs = false;
+  bool decode_append = false;
   std::vector<std::vector<uint64_t>> graph_sig;
   std::vector<hipGraphExec_t> graph_exec;
 };
@@ -405,9 +406,17 @@ std::vector<uint64_t> decode_signature(const pkv_decode_step* d) {
 }
 
 hipError_t launch_decode_step(const pkv_decode_step* d, const std::vector<PoolDev>& dpools, const DecodePlan& plan,
-                              hipStream_t ds) {
+                              hipStream_t ds, bool append) {
   const float sc = scale_or_default(d->scale, dpools[0].head_dim);
   for (int l = 0; l < d->num_layers; ++l) {
+    if (append) {
+      // the write and the attention of each layer in one launch (slots unused)
+      const hipError_t e = launch_attn_decode(dpools[l], d->pools[l].dtype, d->q[l], d->out[l], d->block_tables,
+                                              d->bt_stride, d->context_lens, d->batch, d->num_q_heads, sc, plan,
+                                              d->workspace, ds, d->k_new[l], d->v_new[l]);
+      if (e != hipSuccess) return e;
+      continue;
+    }
     hipError_t e = launch_kv_write(dpools[l], d->pools[l].dtype, d->k_new[l], d->v_new[l], d->slots, d->batch, ds);
     if (e == hipSuccess)
       e = launch_attn_decode(dpools[l], d->pools[l].dtype, d->q[l], d->out[l], d->block_tables, d->bt_stride,
@@ -430,7 +439,7 @@ hipError_t run_decode_graph(pkv_mux* m, int level, const pkv_decode_step* d, con
     }
     hipError_t e = hipStreamBeginCapture(ds, hipStreamCaptureModeRelaxed);
     if (e != hipSuccess) return e;
-    const hipError_t el = launch_decode_step(d, dpools, plan, ds);
+    const hipError_t el = launch_decode_step(d, dpools, plan, ds, m->decode_append);
     hipGraph_t graph = nullptr;
     e = hipStreamEndCapture(ds, &graph);
     if (el != hipSuccess || e != hipSuccess) {
@@ -453,6 +462,13 @@ hipError_t run_decode_graph(pkv_mux* m, int level, const pkv_decode_step* d, con
 int pkv_mux_set_decode_graphs(pkv_mux* m, int enable) {
   if (!m) return fail(PKV_EINVAL, "pkv_mux_set_decode_graphs: NULL mux");
   m->use_graphs = enable != 0;
+  return PKV_OK;
+}
+
+int pkv_mux_set_decode_append(pkv_mux* m, int enable) {
+  if (!m) return fail(PKV_EINVAL, "pkv_mux_set_decode_append: NULL mux");
+  m->decode_append = enable != 0;
+  for (auto& sig : m->graph_sig) sig.clear();   // captured steps hold the other form: capture again
   return PKV_OK;
 }
 
@@ -494,7 +510,8 @@ int run_mux_round(pkv_mux* m, const pkv_decode_step* d, pkv_prefill_job* p, int3
 
   // ---- decode step on the decode stream (as the level's graph when on) ----
   if (d) {
-    e = m->use_graphs ? run_decode_graph(m, level, d, dpools, plan, ds) : launch_decode_step(d, dpools, plan, ds);
+    e = m->use_graphs ? run_decode_graph(m, level, d, dpools, plan, ds)
+                      : launch_decode_step(d, dpools, plan, ds, m->decode_append);
     if (e != hipSuccess) return hip_fail(e, "run_mux_round(decode)");
   }
   // ---- next layers of the prefill on the prefill stream ----

@@ -324,6 +324,10 @@ class Mux:
         """Capture each level's decode step as one HIP graph and replay it while its arguments stay the same."""
         _lib.check(_lib.load().pkv_mux_set_decode_graphs(self._h, int(bool(enable))), "pkv_mux_set_decode_graphs")
 
+    def set_decode_append(self, enable: bool) -> None:
+        """Run each decode layer as one attn_decode_append (write + attention) instead of kv_write + attn_decode."""
+        _lib.check(_lib.load().pkv_mux_set_decode_append(self._h, int(bool(enable))), "pkv_mux_set_decode_append")
+
     def set_manual_divisions(self, thresholds) -> None:
         """Decode batch size from which each split level is used (None or [] restores the divisor rule)."""
         t = list(thresholds or [])

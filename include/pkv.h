@@ -353,6 +353,12 @@ int pkv_mux_set_manual_divisions(pkv_mux* mux, const int32_t* thresholds, int32_
  * Results are those of the plain launches.  Off by default; the graphs are
  * released by pkv_mux_destroy. */
 int pkv_mux_set_decode_graphs(pkv_mux* mux, int enable);
+/* Decode step in append form: with enable != 0, each layer of the decode
+ * step is one attn_decode_append launch (the new rows go to position L-1
+ * of each request through its block table; pkv_decode_step.slots is not
+ * used) instead of kv_write + attn_decode.  Off by default.  Captured
+ * decode graphs are captured again.  -1 (EINVAL) on a NULL mux. */
+int pkv_mux_set_decode_append(pkv_mux* mux, int enable);
 int pkv_mux_policy_choose_manual(int num_groups, int decode_bs, int has_prefill, const int32_t* thresholds);
 /* Stream of a group: which = 0 prefill, 1 decode (a hipStream_t). */
 void* pkv_mux_stream(const pkv_mux* mux, int level, int which);

@@ -35,7 +35,7 @@ def _declared_functions():
 def test_every_declared_symbol_is_exported():
     _lib()
     declared = _declared_functions()
-    assert "kv_write" in declared and "run_mux_round" in declared and len(declared) == 28
+    assert "kv_write" in declared and "run_mux_round" in declared and len(declared) == 29
     out = subprocess.run(["nm", "-D", "--defined-only", lib_mod.LIB_PATH], capture_output=True, text=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
     missing = [n for n in declared if n not in exported]

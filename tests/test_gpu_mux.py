@@ -230,3 +230,37 @@ def test_mux_decode_graphs_replay_the_eager_step():
         case.check_prefill()
     finally:
         mux.close()
+
+
+def test_mux_decode_append_matches_the_oracle():
+    # the decode step as one attn_decode_append per layer: outputs against the
+    # oracle, eager and as a per-level graph, alone and beside a prefill
+    case = _MuxCase(layers=2, ctx=(100, 37, 300, 64), prompt=500)
+    mux = ops.Mux(0, cu_granularity=8, min_decode_cus=32, sm_group_num=8, decode_bs_divisor=36, token_budget=1000)
+    try:
+        mux.set_decode_append(True)
+        mux.run_round(case.decode, None)
+        torch.cuda.synchronize()
+        case.check_decode()
+        mux.set_decode_graphs(True)
+        for _ in range(3):
+            for o in case.o_dec:
+                o.zero_()
+            mux.run_round(case.decode, None)
+            torch.cuda.synchronize()
+            case.check_decode()
+        done = False
+        for _ in range(10):
+            for o in case.o_dec:
+                o.zero_()
+            _, done = mux.run_round(case.decode, case.prefill)
+            torch.cuda.synchronize()
+            case.check_decode()
+            if done:
+                break
+        assert done
+        mux.wait_prefill()
+        torch.cuda.synchronize()
+        case.check_prefill()
+    finally:
+        mux.close()
