@@ -83,15 +83,15 @@ PMC_SCALE = {"fetch": 2.0, "write": 1.0}
 TRAFFIC = {
     "attn_decode": {"sources": ['decode_paged_kv_amd/csrc/attn_decode.hip', 'decode_paged_kv_amd/csrc/decode_bf16.h',
                                 'decode_paged_kv_amd/csrc/pkv_internal.h'],
-                    "sha256": "828d34ff33bbe55e9695c8f3bbd5eb6651e6be0923f5d8494953e4b46842da85",
-                    "fetch_kib": 65952.85, "write_kib": 512.00},
+                    "sha256": "4dcec43414a12bde837e36c7330a42173d2ba0442145f6b3777b70bb3dd5fad0",
+                    "fetch_kib": 65949.64, "write_kib": 512.00},
     "attn_prefill_chunk": {"sources": ['decode_paged_kv_amd/csrc/attn_prefill.hip', 'decode_paged_kv_amd/csrc/prefill_bf16.h',
                                        'decode_paged_kv_amd/csrc/pkv_internal.h'],
-                           "sha256": "5e377b1bdca7eae6694ccdaa0cc783b2178151af6f55738a95baa83e0d02dcb2",
-                           "fetch_kib": 27183.66, "write_kib": 13107.55},
+                           "sha256": "00668a9501a32c3151cfe4d74c5d455a596e0a36c3cdd58a4eeb6b8854c4fda5",
+                           "fetch_kib": 27183.54, "write_kib": 13107.55},
     "kv_relayout": {"sources": ['decode_paged_kv_amd/csrc/kv_ops.hip', 'decode_paged_kv_amd/csrc/pkv_internal.h'],
-                    "sha256": "111df31fc6dcdcd7c6ba81b33f5ea739a3dde3193b71c819f47660b1061021ce",
-                    "fetch_kib": 8234.60, "write_kib": 16389.25},
+                    "sha256": "cc536ff9f8cbf3ab2dbde48e081d02e1ebd8200669e82b0ee4e66cb6d1940da6",
+                    "fetch_kib": 8234.20, "write_kib": 16390.35},
 }
 
 

@@ -271,14 +271,14 @@ attn_decode_kernel(PoolDev pool, const T* __restrict__ q, T* __restrict__ out, c
   }
 }
 
-template <int D, int G, bool STREAM>
+template <int D, int G, bool STREAM, bool APPEND>
 __global__ void __launch_bounds__(kThreads, 2)
 attn_decode_bf16_kernel(PoolDev pool, const bf16_t* __restrict__ q, bf16_t* __restrict__ out,
                         const int32_t* __restrict__ bt, int bt_stride, const int32_t* __restrict__ ctx, int batch,
                         int num_q_heads, float scale_log2, int split_tokens, int num_splits,
                         float* __restrict__ part_o, float* __restrict__ part_ml, const bf16_t* __restrict__ k_new,
                         const bf16_t* __restrict__ v_new) {
-  decode_bf16_block<D, G, STREAM>(pool, q, out, bt, bt_stride, ctx, batch, num_q_heads, scale_log2, split_tokens,
+  decode_bf16_block<D, G, STREAM, APPEND>(pool, q, out, bt, bt_stride, ctx, batch, num_q_heads, scale_log2, split_tokens,
                                   num_splits, part_o, part_ml, k_new, v_new, blockIdx.x, blockIdx.y, blockIdx.z,
                                   gridDim.x);
 }
@@ -415,10 +415,14 @@ hipError_t launch_typed(const PoolDev& pool, const void* q, void* out, const int
   if constexpr (sizeof(T) == 2) {
     if (plan.stream_wgs > 0) {
       float* ml = static_cast<float*>(ws) + (size_t)(plan.stream_wgs + batch * (num_q_heads / G)) * G * D;
-      hipLaunchKernelGGL((attn_decode_bf16_kernel<D, G, true>), dim3(plan.stream_wgs), dim3(kThreads), 0, s, pool,
-                         static_cast<const bf16_t*>(q), static_cast<bf16_t*>(out), bt, bt_stride, ctx, batch,
-                         num_q_heads, scale_log2, 0, 0, part_o, ml, static_cast<const bf16_t*>(k_new),
-                         static_cast<const bf16_t*>(v_new));
+#define PKV_STREAM_LAUNCH(AP)                                                                                      \
+      hipLaunchKernelGGL((attn_decode_bf16_kernel<D, G, true, AP>), dim3(plan.stream_wgs), dim3(kThreads), 0, s,    \
+                         pool, static_cast<const bf16_t*>(q), static_cast<bf16_t*>(out), bt, bt_stride, ctx, batch, \
+                         num_q_heads, scale_log2, 0, 0, part_o, ml, static_cast<const bf16_t*>(k_new),            \
+                         static_cast<const bf16_t*>(v_new))
+      if (k_new) PKV_STREAM_LAUNCH(true);
+      else PKV_STREAM_LAUNCH(false);
+#undef PKV_STREAM_LAUNCH
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
       hipLaunchKernelGGL((attn_decode_stream_merge_kernel<D>), dim3(num_q_heads, batch), dim3(D), 0, s, part_o, ml,
@@ -437,10 +441,16 @@ hipError_t launch_typed(const PoolDev& pool, const void* q, void* out, const int
     }
   }
   if constexpr (sizeof(T) == 2)
-    hipLaunchKernelGGL((attn_decode_bf16_kernel<D, G, false>), grid, dim3(kThreads), 0, s, pool,
-                       static_cast<const bf16_t*>(q), static_cast<bf16_t*>(out), bt, bt_stride, ctx, batch,
-                       num_q_heads, scale_log2, plan.split_tokens, plan.num_splits, part_o, part_ml,
-                       static_cast<const bf16_t*>(k_new), static_cast<const bf16_t*>(v_new));
+  {
+#define PKV_SPLIT_LAUNCH(AP)                                                                                       \
+    hipLaunchKernelGGL((attn_decode_bf16_kernel<D, G, false, AP>), grid, dim3(kThreads), 0, s, pool,               \
+                       static_cast<const bf16_t*>(q), static_cast<bf16_t*>(out), bt, bt_stride, ctx, batch,       \
+                       num_q_heads, scale_log2, plan.split_tokens, plan.num_splits, part_o, part_ml,              \
+                       static_cast<const bf16_t*>(k_new), static_cast<const bf16_t*>(v_new))
+    if (k_new) PKV_SPLIT_LAUNCH(true);
+    else PKV_SPLIT_LAUNCH(false);
+#undef PKV_SPLIT_LAUNCH
+  }
   else
     hipLaunchKernelGGL((attn_decode_kernel<T, D, G>), grid, dim3(kThreads), 0, s, pool, static_cast<const T*>(q),
                        static_cast<T*>(out), bt, bt_stride, ctx, num_q_heads, scale_log2, plan.split_tokens,

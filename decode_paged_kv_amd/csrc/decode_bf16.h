@@ -161,7 +161,7 @@ __device__ __forceinline__ long long stream_owner(long long x, long long NW, lon
 
 // One workgroup's work.  Equal splits (STREAM false): block (bx, by, bz) =
 // (split, KV head, request).  Stream split: block bx of nbx.
-template <int D, int G, bool STREAM>
+template <int D, int G, bool STREAM, bool APPEND = false>
 __device__ __forceinline__ void decode_bf16_block(PoolDev pool, const bf16_t* __restrict__ q,
                                                   bf16_t* __restrict__ out, const int32_t* __restrict__ bt,
                                                   int bt_stride, const int32_t* __restrict__ ctx, int batch,
@@ -381,7 +381,7 @@ __device__ __forceinline__ void decode_bf16_block(PoolDev pool, const bf16_t* __
     // ...; a lane 1 or 2 dims); a block id outside the pool makes it absent,
     // as for any key
     bool add_new = false;
-    if (sg.last) {
+    if (APPEND && sg.last) {
       const int L = sg.end + 1;
       const bf16_t* kn = k_new + ((size_t)sg.b * (num_q_heads / G) + sg.kvh) * D;
       const bf16_t* vn = v_new + ((size_t)sg.b * (num_q_heads / G) + sg.kvh) * D;
@@ -469,7 +469,7 @@ __device__ __forceinline__ void decode_bf16_block(PoolDev pool, const bf16_t* __
     const int start = split * split_tokens;
     if (start >= L) return;
     const int end = min(L, start + split_tokens);
-    const bool last = k_new != nullptr && ctx[b] <= cap && end == L;
+    const bool last = APPEND && ctx[b] <= cap && end == L;
     const Seg sg{b, kvh, start, last ? end - 1 : end, L <= split_tokens,
                  ((size_t)b * num_q_heads + (size_t)kvh * G) * num_splits + split, num_splits, last};
     prologue(sg);
@@ -511,7 +511,7 @@ __device__ __forceinline__ void decode_bf16_block(PoolDev pool, const bf16_t* __
         sg.final_out = stream_owner(pstart, NW, Wt) == stream_owner(pstart + ntb - 1, NW, Wt);
         sg.prow = (size_t)(w + (long long)b * hkv + kvh) * G;
         sg.pstride = 1;
-        sg.last = k_new != nullptr && raw <= cap && sg.end == L;
+        sg.last = APPEND && raw <= cap && sg.end == L;
         if (sg.last) sg.end = L - 1;
         t = seg_end;
         if (t == base + (long long)hkv * ntb) {
