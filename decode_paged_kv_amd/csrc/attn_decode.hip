@@ -418,10 +418,16 @@ hipError_t launch_typed(const PoolDev& pool, const void* q, void* out, const int
 #define PKV_STREAM_LAUNCH(AP)                                                                                      \
       hipLaunchKernelGGL((attn_decode_bf16_kernel<D, G, true, AP>), dim3(plan.stream_wgs), dim3(kThreads), 0, s,    \
                          pool, static_cast<const bf16_t*>(q), static_cast<bf16_t*>(out), bt, bt_stride, ctx, batch, \
-                         num_q_heads, scale_log2, 0, 0, part_o, ml, static_cast<const bf16_t*>(k_new),            \
-                         static_cast<const bf16_t*>(v_new))
-      if (k_new) PKV_STREAM_LAUNCH(true);
-      else PKV_STREAM_LAUNCH(false);
+                         num_q_heads, scale_log2, 0, 0, part_o, ml, nullptr, nullptr)
+      // append with the stream split: the row is written by a small kernel
+      // first (the fused form would push this kernel past its registers)
+      if (k_new) {
+        hipLaunchKernelGGL(kv_append_kernel<T>, dim3(pool.num_kv_heads, batch), dim3(128), 0, s, pool,
+                           static_cast<const T*>(k_new), static_cast<const T*>(v_new), bt, bt_stride, ctx);
+        hipError_t ea = hipGetLastError();
+        if (ea != hipSuccess) return ea;
+      }
+      PKV_STREAM_LAUNCH(false);
 #undef PKV_STREAM_LAUNCH
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;

@@ -373,13 +373,14 @@ __device__ __forceinline__ void decode_bf16_block(PoolDev pool, const bf16_t* __
       if (t + W < ntiles) process(start + (t + W) * TK, rb, at(t + 3 * W), at(t + 4 * W));
     }
   };
-  // the 4 waves' (m, l, acc) of a segment, combined and written
-  auto merge = [&](const Seg& sg) {
-    // the appended key (append mode, last piece of the request): its row is
-    // written to the pool at position L-1 (the tiles never read that slot)
-    // and its score for each q-head computed (wave w takes heads w, w+4,
-    // ...; a lane 1 or 2 dims); a block id outside the pool makes it absent,
-    // as for any key
+  // The appended key of a segment (append mode, last piece of the request):
+  // its row is written to the pool at position L-1 (the tiles never read
+  // that slot) and its score for each q-head computed into LDS (wave w takes
+  // heads w, w+4, ...; a lane 1 or 2 dims); a block id outside the pool
+  // makes it absent, as for any key.  Run by every wave right after its
+  // tiles, before the next segment's loads are issued (fewer live
+  // registers); the merge's first barrier publishes the scores.
+  auto append_key = [&](const Seg& sg) -> bool {
     bool add_new = false;
     if (APPEND && sg.last) {
       const int L = sg.end + 1;
@@ -410,6 +411,10 @@ __device__ __forceinline__ void decode_bf16_block(PoolDev pool, const bf16_t* __
         flag_error(pool.err, PKV_ERRBIT_BLOCK_ID);
       }
     }
+    return add_new;
+  };
+  // the 4 waves' (m, l, acc) of a segment, combined and written
+  auto merge = [&](const Seg& sg, bool add_new) {
     lsum = col_sum(lsum);
     if (l16 < G) {
       if (j4 == 0) {
@@ -474,7 +479,8 @@ __device__ __forceinline__ void decode_bf16_block(PoolDev pool, const bf16_t* __
                  ((size_t)b * num_q_heads + (size_t)kvh * G) * num_splits + split, num_splits, last};
     prologue(sg);
     body(sg);
-    merge(sg);
+    const bool add_new = append_key(sg);
+    merge(sg, add_new);
   } else {
     // stream split: workgroup w takes the pair-tiles [w W / NW, (w+1) W / NW)
     // of the W = Hkv * sum_b ceil(L_b / 32) tiles of the batch, ordered by
@@ -527,9 +533,10 @@ __device__ __forceinline__ void decode_bf16_block(PoolDev pool, const bf16_t* __
     prologue(cur);
     while (true) {
       body(cur);
+      const bool add_new = append_key(cur);
       const bool more = next_seg(nxt);
       if (more) prologue(nxt);
-      merge(cur);
+      merge(cur, add_new);
       if (!more) break;
       cur = nxt;
     }

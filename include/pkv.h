@@ -237,8 +237,9 @@ int attn_decode(const pkv_pool_layer* pool, const void* q, void* out, const int3
                 hipStream_t stream);
 
 /*
- * attn_decode_append - one decode step's K/V append and attention in one
- * launch.  [DISAGG] "实现" (a decode step writes the new token's K/V at the
+ * attn_decode_append - one decode step's K/V append and attention, in one
+ * launch for batches with a workgroup per (request, KV head) pair (with the
+ * stream split used for fewer pairs, a small kernel writes the rows first).  [DISAGG] "实现" (a decode step writes the new token's K/V at the
  * request's next slot, then attends over all its cached keys) and [L7]
  * section 1.1.  For request b with context L = context_lens[b] (the new
  * token included): the rows k_new[b], v_new[b] ([B, Hkv, D], device,
