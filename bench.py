@@ -83,8 +83,8 @@ PMC_SCALE = {"fetch": 2.0, "write": 1.0}
 TRAFFIC = {
     "attn_decode": {"sources": ['decode_paged_kv_amd/csrc/attn_decode.hip', 'decode_paged_kv_amd/csrc/decode_bf16.h',
                                 'decode_paged_kv_amd/csrc/pkv_internal.h'],
-                    "sha256": "7a375aa543607eb615d9f5e7cdde77d8fd25a3c53bc637ab00ebb395154e7b6a",
-                    "fetch_kib": 65950.19, "write_kib": 512.00},
+                    "sha256": "4afa4231b115841ce0dcf336c45d405e17699366f0c46e94e77096b308556496",
+                    "fetch_kib": 65952.84, "write_kib": 512.00},
     "attn_prefill_chunk": {"sources": ['decode_paged_kv_amd/csrc/attn_prefill.hip', 'decode_paged_kv_amd/csrc/prefill_bf16.h',
                                        'decode_paged_kv_amd/csrc/pkv_internal.h'],
                            "sha256": "00668a9501a32c3151cfe4d74c5d455a596e0a36c3cdd58a4eeb6b8854c4fda5",
