@@ -470,12 +470,9 @@ __device__ __forceinline__ void prefill_bf16_block(PoolDev pool, const bf16_t* _
       }
       if (s + R < BP::NS) fr[s % R] = frag(s + R);
       // the pairs of P placed in this slot: p = 2^(s*scale - m), in bf16
-      // for the MFMA.  The row sum: with one key-tile group, v_dot2 of the
-      // rounded pairs with (1, 1) (the values the MFMA uses, one
-      // instruction per pair; 2.7% faster on the chunk of 2048); with two
-      // groups, fp32 adds of p (there the v_dot2 form measured 2% slower),
-      // which differ from the sum of the rounded values by unbiased
-      // rounding noise only
+      // for the MFMA; the row sum adds p in fp32 (plain adds: a v_dot2 of
+      // the rounded pairs stalls next to the MFMAs), which differs from the
+      // sum of the rounded values by unbiased rounding noise only
 #pragma unroll
       for (int pj = 0; pj < 16; ++pj) {
         if (BP::pair_slot(pj) != s) continue;
@@ -484,12 +481,8 @@ __device__ __forceinline__ void prefill_bf16_block(PoolDev pool, const bf16_t* _
         const float p0 = __builtin_amdgcn_exp2f(fmaf(st.v[i][r], scale_log2, -m));
         const float p1 = __builtin_amdgcn_exp2f(fmaf(st.v[i][r + 1], scale_log2, -m));
         pw[pc][w] = pack_bf16x2(p0, p1);
-        if constexpr (NG == 1) {
-          psum[w & 1] = dot2_bf16(pw[pc][w], 0x3F803F80u, psum[w & 1]);   // bf16 (1, 1)
-        } else {
-          psum[0] += p0;
-          psum[1] += p1;
-        }
+        psum[0] += p0;
+        psum[1] += p1;
       }
       // the row max of S(kt+NG), a few registers per slot once each half
       // is complete
