@@ -167,6 +167,8 @@ def _convert_case(dtype, ddtype, layout, n, sbs, ssh, sblk, dbs, dsh, dblk, hkv,
     ("bf16", "bf16", "pool", 250, 16, 1, 20, 128, 2, 4, 2, 64, 1.0),
     ("f32", "f32", "token_major", 300, 128, 1, 4, 16, 2, 30, 2, 128, 1.0),
     ("f32", "f32", "pool", 95, 16, 2, 8, 32, 1, 4, 2, 64, 1.0),
+    ("f32", "f32", "kv_fused", 130, 32, 1, 8, 128, 2, 3, 2, 64, 1.0),
+    ("bf16", "fp8", "token_major", 700, 128, 2, 8, 16, 16, 50, 16, 64, 0.125),   # 16 shards, bs 128 -> 16
 ])
 def test_relayout_convert_bit_exact(dtype, ddtype, layout, n, sbs, ssh, sblk, dbs, dsh, dblk, hkv, d, scale):
     sc, dst, dst_bt, got, ref = _convert_case(dtype, ddtype, layout, n, sbs, ssh, sblk, dbs, dsh, dblk, hkv, d,
