@@ -12,7 +12,7 @@ MAX_SHARDS = 16
 F32, BF16, FP8_E4M3 = 0, 1, 2
 LAYOUT_POOL, LAYOUT_TOKEN_MAJOR, LAYOUT_KV_FUSED = 0, 1, 2
 OK, EINVAL, EUNSUPPORTED, EHIP, ERANGE = 0, -1, -2, -3, -4
-ERRBIT_BLOCK_ID, ERRBIT_SLOT, ERRBIT_TABLE = 1, 2, 4
+ERRBIT_BLOCK_ID, ERRBIT_SLOT, ERRBIT_TABLE, ERRBIT_CONTEXT = 1, 2, 4, 8
 
 
 class PkvLibraryMissing(RuntimeError):
@@ -105,14 +105,15 @@ _SIGS = {
     "kv_write": (C.c_int, [C.POINTER(PoolLayer), _P, _P, _P, _I, _P]),
     "kv_relayout": (C.c_int, [C.POINTER(PoolLayer), _P, C.POINTER(PoolLayer), _P, _I, _P]),
     "kv_relayout_convert": (C.c_int, [C.POINTER(PoolLayer), _P, C.POINTER(KvDest), _P, _I, _P]),
-    "attn_prefill_chunk": (C.c_int, [C.POINTER(PoolLayer), _P, _P, _P, _I, _P, _P, _I, _I, _I, C.c_float, _P]),
+    "attn_prefill_chunk": (C.c_int, [C.POINTER(PoolLayer), _P, _P, _P, _I, _P, _P, _I, _I, _I, _I, C.c_float, _P]),
     "pkv_attn_decode_workspace_size": (C.c_size_t, [_I, _I, _I, _I]),
+    "pkv_attn_decode_workspace_size_for": (C.c_size_t, [C.POINTER(PoolLayer), _I, _I, _I]),
     "attn_decode": (C.c_int, [C.POINTER(PoolLayer), _P, _P, _P, _I, _P, _I, _I, _I, C.c_float, _P, C.c_size_t, _P]),
     "attn_decode_append": (C.c_int, [C.POINTER(PoolLayer), _P, _P, _P, _P, _P, _I, _P, _I, _I, _I, C.c_float, _P,
                                      C.c_size_t, _P]),
     "pkv_stall_free_chunk": (C.c_int, [_I, _I, _I]),
     "attn_mixed_batch": (C.c_int, [C.POINTER(PoolLayer), _P, _P, _P, _I, _P, _I, _I, _P, _P, _P, _I, _P, _P, _I, _I,
-                                   _I, C.c_float, _P, C.c_size_t, _P]),
+                                   _I, _I, C.c_float, _P, C.c_size_t, _P]),
     "pkv_mux_policy_groups_grid": (C.c_int, [C.c_int] * 5 + [C.POINTER(_I), C.POINTER(_I), _I, C.POINTER(_I)]),
     "pkv_mux_policy_choose": (C.c_int, [C.c_int] * 4),
     "pkv_mux_policy_layers_per_round": (C.c_int, [C.c_int] * 3),
@@ -130,6 +131,11 @@ _SIGS = {
     "pkv_mux_cu_mask": (C.c_int, [_P, C.c_int, C.c_int, C.POINTER(C.c_uint32), _I, C.POINTER(_I)]),
     "run_mux_round": (C.c_int, [_P, C.POINTER(DecodeStep), C.POINTER(PrefillJob), C.POINTER(_I), C.POINTER(_I)]),
     "pkv_mux_wait_prefill": (C.c_int, [_P]),
+    "pkv_stall_free_batch": (C.c_int, [_I, _I, C.POINTER(_I), _I, C.POINTER(_I)]),
+    "pkv_mux_check_decode_step": (C.c_int, [C.POINTER(DecodeStep)]),
+    "pkv_mux_check_prefill_job": (C.c_int, [C.POINTER(PrefillJob)]),
+    "pkv_mux_policy_cu_masks": (C.c_int, [C.c_int, C.c_int, C.POINTER(C.c_uint32), C.POINTER(C.c_uint32), _I]),
+    "pkv_mux_policy_mask_ok": (C.c_int, [C.POINTER(C.c_uint32), _I, C.c_int]),
 }
 EXPORTED = tuple(_SIGS)
 

@@ -29,7 +29,7 @@ int hip_fail(hipError_t e, const char* where) {
   return fail(PKV_EHIP, "%s: HIP error %d (%s)", where, (int)e, hipGetErrorString(e));
 }
 
-static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 static int log2_exact(int x) {
   int s = 0;
@@ -72,7 +72,7 @@ int check_pool(const pkv_pool_layer* p, const char* name, PoolDev* out) {
   return PKV_OK;
 }
 
-static int check_heads(const PoolDev& pool, int num_q_heads) {
+int check_heads(const PoolDev& pool, int num_q_heads) {
   if (num_q_heads <= 0 || num_q_heads % pool.num_kv_heads)
     return fail(PKV_EINVAL, "num_q_heads %d is not a positive multiple of %d kv heads", num_q_heads,
                 pool.num_kv_heads);
@@ -82,7 +82,7 @@ static int check_heads(const PoolDev& pool, int num_q_heads) {
   return PKV_OK;
 }
 
-static // Finite and >= 0 (0 selects the default scale), tested on the bits: the
+// Finite and >= 0 (0 selects the default scale), tested on the bits: the
 // library is built without NaN semantics for comparisons, so a NaN compare
 // would be folded away.
 bool scale_ok(float x) {
@@ -216,7 +216,8 @@ int kv_relayout_convert(const pkv_pool_layer* src, const int32_t* src_bt, const 
 
 int attn_prefill_chunk(const pkv_pool_layer* pool, const void* q, void* out, const int32_t* block_tables,
                        int32_t bt_stride, const int32_t* start_loc, const int32_t* chunk_start, int32_t batch,
-                       int32_t max_chunk_len, int32_t num_q_heads, float scale, hipStream_t stream) {
+                       int32_t max_chunk_len, int32_t max_total_len, int32_t num_q_heads, float scale,
+                       hipStream_t stream) {
   g_last_error.clear();
   PoolDev pd;
   if (int rc = check_pool(pool, "attn_prefill_chunk", &pd)) return rc;
@@ -227,11 +228,28 @@ int attn_prefill_chunk(const pkv_pool_layer* pool, const void* q, void* out, con
     return fail(PKV_EINVAL, "attn_prefill_chunk: NULL device array");
   if (!aligned16(q) || !aligned16(out)) return fail(PKV_EINVAL, "attn_prefill_chunk: q/out must be 16-byte aligned");
   if (bt_stride <= 0) return fail(PKV_EINVAL, "attn_prefill_chunk: bt_stride %d", bt_stride);
+  if (max_total_len < max_chunk_len)
+    return fail(PKV_EINVAL, "attn_prefill_chunk: max_total_len %d is below max_chunk_len %d", max_total_len,
+                max_chunk_len);
+  if ((int64_t)bt_stride * pd.block_size < max_total_len)
+    return fail(PKV_EINVAL, "attn_prefill_chunk: bt_stride %d blocks cannot hold %d tokens", bt_stride,
+                max_total_len);
   if (!scale_ok(scale)) return fail(PKV_EINVAL, "attn_prefill_chunk: scale must be finite and >= 0");
   if ((int64_t)max_chunk_len * 2 > INT32_MAX / 64) return fail(PKV_ERANGE, "attn_prefill_chunk: chunk too long");
   hipError_t e = launch_attn_prefill(pd, pool->dtype, q, out, block_tables, bt_stride, start_loc, chunk_start, batch,
-                                     max_chunk_len, num_q_heads, resolve_scale(scale, pd.head_dim), stream);
+                                     max_chunk_len, max_total_len, num_q_heads, resolve_scale(scale, pd.head_dim),
+                                     stream);
   return e == hipSuccess ? PKV_OK : hip_fail(e, "attn_prefill_chunk");
+}
+
+size_t pkv_attn_decode_workspace_size_for(const pkv_pool_layer* pool, int32_t batch, int32_t num_q_heads,
+                                          int32_t max_context_len) {
+  // the plan attn_decode, attn_decode_append and run_mux_round make for this
+  // pool (KV heads, head dim, dtype); 0 for arguments those calls reject
+  if (!pool || batch <= 0 || num_q_heads <= 0 || max_context_len <= 0) return 0;
+  if (pool->num_kv_heads <= 0 || num_q_heads % pool->num_kv_heads) return 0;
+  if (pool->dtype != PKV_F32 && pool->dtype != PKV_BF16) return 0;
+  return plan_decode(batch, num_q_heads, pool->num_kv_heads, max_context_len, pool->head_dim, pool->dtype).workspace;
 }
 
 size_t pkv_attn_decode_workspace_size(int32_t batch, int32_t num_q_heads, int32_t max_context_len,
@@ -316,12 +334,35 @@ int pkv_stall_free_chunk(int32_t token_budget, int32_t num_decode, int32_t promp
   return prompt_remaining < left ? prompt_remaining : left;
 }
 
+int pkv_stall_free_batch(int32_t token_budget, int32_t num_decode, const int32_t* prompt_remaining,
+                         int32_t num_prompts, int32_t* chunks_out) {
+  g_last_error.clear();
+  if (token_budget < 0 || num_decode < 0 || num_prompts < 0)
+    return fail(PKV_EINVAL, "pkv_stall_free_batch: negative argument");
+  if (num_prompts > 0 && (!prompt_remaining || !chunks_out))
+    return fail(PKV_EINVAL, "pkv_stall_free_batch: NULL prompt or chunk array");
+  for (int i = 0; i < num_prompts; ++i)
+    if (prompt_remaining[i] < 0) return fail(PKV_EINVAL, "pkv_stall_free_batch: prompt %d has %d tokens left", i,
+                                             prompt_remaining[i]);
+  // decode first (one token each, never dropped); then each prompt in the
+  // caller's order, the ongoing ones before the new, takes what is left
+  int64_t left = token_budget > num_decode ? (int64_t)token_budget - num_decode : 0;
+  int64_t total = 0;
+  for (int i = 0; i < num_prompts; ++i) {
+    const int64_t take = prompt_remaining[i] < left ? prompt_remaining[i] : left;
+    chunks_out[i] = (int32_t)take;
+    left -= take;
+    total += take;
+  }
+  return (int)total;
+}
+
 int attn_mixed_batch(const pkv_pool_layer* pool, const void* q_dec, void* out_dec, const int32_t* dec_block_tables,
                      int32_t dec_bt_stride, const int32_t* context_lens, int32_t num_decode, int32_t max_context_len,
                      const void* q_pf, void* out_pf, const int32_t* pf_block_tables, int32_t pf_bt_stride,
                      const int32_t* start_loc, const int32_t* chunk_start, int32_t num_prefill,
-                     int32_t max_chunk_len, int32_t num_q_heads, float scale, void* workspace,
-                     size_t workspace_bytes, hipStream_t stream) {
+                     int32_t max_chunk_len, int32_t max_total_len, int32_t num_q_heads, float scale,
+                     void* workspace, size_t workspace_bytes, hipStream_t stream) {
   g_last_error.clear();
   PoolDev pd;
   if (int rc = check_pool(pool, "attn_mixed_batch", &pd)) return rc;
@@ -356,8 +397,15 @@ int attn_mixed_batch(const pkv_pool_layer* pool, const void* q_dec, void* out_de
     if (!aligned16(q_pf) || !aligned16(out_pf))
       return fail(PKV_EINVAL, "attn_mixed_batch: prefill q/out must be 16-byte aligned");
     if (pf_bt_stride <= 0) return fail(PKV_EINVAL, "attn_mixed_batch: pf_bt_stride %d", pf_bt_stride);
+    if (max_total_len < max_chunk_len)
+      return fail(PKV_EINVAL, "attn_mixed_batch: max_total_len %d is below max_chunk_len %d", max_total_len,
+                  max_chunk_len);
+    if ((int64_t)pf_bt_stride * pd.block_size < max_total_len)
+      return fail(PKV_EINVAL, "attn_mixed_batch: pf_bt_stride %d blocks cannot hold %d tokens", pf_bt_stride,
+                  max_total_len);
     if ((int64_t)max_chunk_len * 2 > INT32_MAX / 64) return fail(PKV_ERANGE, "attn_mixed_batch: chunk too long");
-    p = MixedPrefill{q_pf, out_pf, pf_block_tables, pf_bt_stride, start_loc, chunk_start, num_prefill, max_chunk_len};
+    p = MixedPrefill{q_pf,        out_pf,      pf_block_tables, pf_bt_stride, start_loc,
+                     chunk_start, num_prefill, max_chunk_len,   max_total_len};
   }
   if (d.batch == 0 && p.batch == 0) return PKV_OK;
   hipError_t e = launch_attn_mixed(pd, pool->dtype, d, p, num_q_heads, resolve_scale(scale, pd.head_dim), stream);

@@ -57,34 +57,32 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-template <typename T, int D, int G>
+template <int D, int G>
 struct DecodeSmem {
-  static constexpr int QW = (sizeof(T) == 2) ? D / 2 : D;            // q words per head
-  uint32_t q[G][QW];                                                  // bf16 pairs or fp32 bits
-  // p of the current tile per wave: bf16 (packed pairs) or fp32
-  uint32_t p[kWaves][G][(sizeof(T) == 2) ? kTile / 2 : kTile];
+  float q[G][D];
+  float p[kWaves][G][kTile];     // p of the current tile, per wave
   float red_acc[kWaves][G][D];
   float red_m[kWaves][G];
   float red_l[kWaves][G];
 };
 
-template <typename T, int D, int G>
+// fp32 kernel (bf16 runs the MFMA kernel of decode_bf16.h).
+template <int D, int G>
 __global__ void __launch_bounds__(kThreads)
-attn_decode_kernel(PoolDev pool, const T* __restrict__ q, T* __restrict__ out, const int32_t* __restrict__ bt,
-                   int bt_stride, const int32_t* __restrict__ ctx, int num_q_heads, float scale_log2,
-                   int split_tokens, int num_splits, float* __restrict__ part_o, float* __restrict__ part_ml) {
-  constexpr bool kBf16 = sizeof(T) == 2;
+attn_decode_f32_kernel(PoolDev pool, const float* __restrict__ q, float* __restrict__ out,
+                       const int32_t* __restrict__ bt, int bt_stride, const int32_t* __restrict__ ctx,
+                       int num_q_heads, float scale_log2, int split_tokens, int num_splits, int max_len,
+                       float* __restrict__ part_o, float* __restrict__ part_ml) {
   constexpr int DPL = D / 64;                  // head-dim columns per lane in p.v
-  constexpr int VEC = 16 / sizeof(T);          // elements per 16-byte load
-  using Smem = DecodeSmem<T, D, G>;
+  using Smem = DecodeSmem<D, G>;
   __shared__ Smem sm;
 
   const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int L = ctx[b];
-  if (L > (bt_stride << pool.bs_shift)) {        // never index past the request's table
-    if (threadIdx.x == 0 && split == 0 && kvh == 0) flag_error(pool.err, PKV_ERRBIT_TABLE);
-    L = bt_stride << pool.bs_shift;
+  if (L > max_len) {                             // past max_context_len: cut, flagged
+    if (threadIdx.x == 0 && split == 0 && kvh == 0) flag_error(pool.err, PKV_ERRBIT_CONTEXT);
+    L = max_len;
   }
   const int start = split * split_tokens;
   if (start >= L) return;
@@ -92,16 +90,16 @@ attn_decode_kernel(PoolDev pool, const T* __restrict__ q, T* __restrict__ out, c
 
   const int hl = pool.heads_per_shard;
   const int sh = kvh / hl, lh = kvh - sh * hl;
-  const T* kpool = reinterpret_cast<const T*>(pool.k[sh]);
-  const T* vpool = reinterpret_cast<const T*>(pool.v[sh]);
+  const float* kpool = reinterpret_cast<const float*>(pool.k[sh]);
+  const float* vpool = reinterpret_cast<const float*>(pool.v[sh]);
   const int bs = pool.block_size;
   const int32_t* table = bt + (size_t)b * bt_stride;
 
   // q rows of this KV head's group -> LDS
   {
-    const uint32_t* qsrc = reinterpret_cast<const uint32_t*>(q + ((size_t)b * num_q_heads + (size_t)kvh * G) * D);
-    uint32_t* qdst = &sm.q[0][0];
-    for (int i = threadIdx.x; i < G * Smem::QW; i += kThreads) qdst[i] = qsrc[i];
+    const float* qsrc = q + ((size_t)b * num_q_heads + (size_t)kvh * G) * D;
+    float* qdst = &sm.q[0][0];
+    for (int i = threadIdx.x; i < G * D; i += kThreads) qdst[i] = qsrc[i];
   }
   __syncthreads();
 
@@ -120,7 +118,7 @@ attn_decode_kernel(PoolDev pool, const T* __restrict__ q, T* __restrict__ out, c
     // ---- q.k: lane owns key k0 + lane ----
     const int key = k0 + lane;
     bool valid = key < end;
-    const T* krow = nullptr;
+    const float* krow = nullptr;
     if (valid) {
       const int blk = table[key >> pool.bs_shift];
       if (blk < 0 || blk >= pool.num_blocks) {
@@ -135,22 +133,15 @@ attn_decode_kernel(PoolDev pool, const T* __restrict__ q, T* __restrict__ out, c
     for (int g = 0; g < G; ++g) s[g] = 0.f;
     if (valid) {
 #pragma unroll 4
-      for (int c = 0; c < D / VEC; ++c) {
-        const uint4 kv = *reinterpret_cast<const uint4*>(krow + c * VEC);
+      for (int c = 0; c < D / 4; ++c) {
+        const float4 kv = *reinterpret_cast<const float4*>(krow + c * 4);
 #pragma unroll
         for (int g = 0; g < G; ++g) {
-          const uint4 qv = *reinterpret_cast<const uint4*>(&sm.q[g][c * 4]);
-          if constexpr (kBf16) {
-            s[g] = dot2_bf16(kv.x, qv.x, s[g]);
-            s[g] = dot2_bf16(kv.y, qv.y, s[g]);
-            s[g] = dot2_bf16(kv.z, qv.z, s[g]);
-            s[g] = dot2_bf16(kv.w, qv.w, s[g]);
-          } else {
-            s[g] = fmaf(__uint_as_float(kv.x), __uint_as_float(qv.x), s[g]);
-            s[g] = fmaf(__uint_as_float(kv.y), __uint_as_float(qv.y), s[g]);
-            s[g] = fmaf(__uint_as_float(kv.z), __uint_as_float(qv.z), s[g]);
-            s[g] = fmaf(__uint_as_float(kv.w), __uint_as_float(qv.w), s[g]);
-          }
+          const float4 qv = *reinterpret_cast<const float4*>(&sm.q[g][c * 4]);
+          s[g] = fmaf(kv.x, qv.x, s[g]);
+          s[g] = fmaf(kv.y, qv.y, s[g]);
+          s[g] = fmaf(kv.z, qv.z, s[g]);
+          s[g] = fmaf(kv.w, qv.w, s[g]);
         }
       }
     }
@@ -165,11 +156,7 @@ attn_decode_kernel(PoolDev pool, const T* __restrict__ q, T* __restrict__ out, c
       lsum[g] = lsum[g] * alpha + p;
 #pragma unroll
       for (int j = 0; j < DPL; ++j) acc[g][j] *= alpha;
-      if constexpr (kBf16) {
-        reinterpret_cast<bf16_t*>(&sm.p[wave][g][0])[lane] = f32_to_bf16(p);
-      } else {
-        sm.p[wave][g][lane] = __float_as_uint(p);
-      }
+      sm.p[wave][g][lane] = p;
     }
     wave_lds_sync();
     // ---- p.v: lane owns head-dim columns lane*DPL .. +DPL ----
@@ -180,51 +167,24 @@ attn_decode_kernel(PoolDev pool, const T* __restrict__ q, T* __restrict__ out, c
       const int blk = table[key16 >> pool.bs_shift];
       if (blk < 0 || blk >= pool.num_blocks) continue;     // its keys already have p = 0
       const int nvalid = min(16, end - key16);
-      const T* vtile = vpool + tile_elems(pool, blk, lh) + (key16 & (bs - 1));
+      const float* vtile = vpool + tile_elems(pool, blk, lh) + (key16 & (bs - 1));
 #pragma unroll
       for (int j = 0; j < DPL; ++j) {
         const int d = lane * DPL + j;
-        const T* vrow = vtile + (size_t)d * bs;          // 16 keys of dim d
-        uint4 vv[16 / VEC];
+        const float* vrow = vtile + (size_t)d * bs;      // 16 keys of dim d
+        float vv[16];
 #pragma unroll
-        for (int u = 0; u < 16 / VEC; ++u) vv[u] = *reinterpret_cast<const uint4*>(vrow + u * VEC);
-        uint32_t* vw = reinterpret_cast<uint32_t*>(vv);
-        if (nvalid < 16) {            // keys past the context hold arbitrary bits: zero them
+        for (int u = 0; u < 4; ++u) *reinterpret_cast<float4*>(&vv[4 * u]) = *reinterpret_cast<const float4*>(vrow + 4 * u);
+        // keys past the context hold arbitrary bits: zero them (0 * NaN is NaN)
 #pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            if (e >= nvalid) {
-              if constexpr (kBf16) vw[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
-              else vw[e] = 0u;
-            }
-          }
-        }
+        for (int e = 0; e < 16; ++e)
+          if (e >= nvalid) vv[e] = 0.f;
 #pragma unroll
         for (int g = 0; g < G; ++g) {
-          if constexpr (kBf16) {
-            const uint4 p0 = *reinterpret_cast<const uint4*>(&sm.p[wave][g][kk / 2]);
-            const uint4 p1 = *reinterpret_cast<const uint4*>(&sm.p[wave][g][kk / 2 + 4]);
-            float a = acc[g][j];
-            a = dot2_bf16(p0.x, vw[0], a);
-            a = dot2_bf16(p0.y, vw[1], a);
-            a = dot2_bf16(p0.z, vw[2], a);
-            a = dot2_bf16(p0.w, vw[3], a);
-            a = dot2_bf16(p1.x, vw[4], a);
-            a = dot2_bf16(p1.y, vw[5], a);
-            a = dot2_bf16(p1.z, vw[6], a);
-            a = dot2_bf16(p1.w, vw[7], a);
-            acc[g][j] = a;
-          } else {
-            float a = acc[g][j];
+          float a = acc[g][j];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-              const uint4 pp = *reinterpret_cast<const uint4*>(&sm.p[wave][g][kk + u * 4]);
-              a = fmaf(__uint_as_float(pp.x), __uint_as_float(vw[u * 4 + 0]), a);
-              a = fmaf(__uint_as_float(pp.y), __uint_as_float(vw[u * 4 + 1]), a);
-              a = fmaf(__uint_as_float(pp.z), __uint_as_float(vw[u * 4 + 2]), a);
-              a = fmaf(__uint_as_float(pp.w), __uint_as_float(vw[u * 4 + 3]), a);
-            }
-            acc[g][j] = a;
-          }
+          for (int e = 0; e < 16; ++e) a = fmaf(sm.p[wave][g][kk + e], vv[e], a);
+          acc[g][j] = a;
         }
       }
     }
@@ -257,9 +217,7 @@ attn_decode_kernel(PoolDev pool, const T* __restrict__ q, T* __restrict__ out, c
     }
     const int h = kvh * G + g;
     if (L <= split_tokens) {                   // the request's only split: final output
-      const float r = o / l;
-      if constexpr (kBf16) out[((size_t)b * num_q_heads + h) * D + d] = f32_to_bf16(r);
-      else out[((size_t)b * num_q_heads + h) * D + d] = r;
+      out[((size_t)b * num_q_heads + h) * D + d] = o / l;
     } else {
       const size_t row = ((size_t)b * num_q_heads + h) * num_splits + split;
       part_o[row * D + d] = o;
@@ -275,12 +233,12 @@ template <int D, int G, bool STREAM, bool APPEND>
 __global__ void __launch_bounds__(kThreads, 2)
 attn_decode_bf16_kernel(PoolDev pool, const bf16_t* __restrict__ q, bf16_t* __restrict__ out,
                         const int32_t* __restrict__ bt, int bt_stride, const int32_t* __restrict__ ctx, int batch,
-                        int num_q_heads, float scale_log2, int split_tokens, int num_splits,
+                        int num_q_heads, float scale_log2, int split_tokens, int num_splits, int max_len,
                         float* __restrict__ part_o, float* __restrict__ part_ml, const bf16_t* __restrict__ k_new,
                         const bf16_t* __restrict__ v_new) {
-  decode_bf16_block<D, G, STREAM, APPEND>(pool, q, out, bt, bt_stride, ctx, batch, num_q_heads, scale_log2, split_tokens,
-                                  num_splits, part_o, part_ml, k_new, v_new, blockIdx.x, blockIdx.y, blockIdx.z,
-                                  gridDim.x);
+  decode_bf16_block<D, G, STREAM, APPEND>(pool, q, out, bt, bt_stride, ctx, batch, num_q_heads, scale_log2,
+                                          split_tokens, num_splits, max_len, part_o, part_ml, k_new, v_new,
+                                          blockIdx.x, blockIdx.y, blockIdx.z, gridDim.x);
 }
 
 // The new token's K/V row of each (request, KV head) written at position
@@ -289,12 +247,12 @@ attn_decode_bf16_kernel(PoolDev pool, const bf16_t* __restrict__ q, bf16_t* __re
 template <typename T>
 __global__ void __launch_bounds__(128)
 kv_append_kernel(PoolDev pool, const T* __restrict__ k_new, const T* __restrict__ v_new,
-                 const int32_t* __restrict__ bt, int bt_stride, const int32_t* __restrict__ ctx) {
+                 const int32_t* __restrict__ bt, int bt_stride, const int32_t* __restrict__ ctx, int max_len) {
   const int kvh = blockIdx.x, b = blockIdx.y, D = pool.head_dim;
   const int L = ctx[b];
   if (L <= 0) return;
-  if (L > (bt_stride << pool.bs_shift)) {
-    if (threadIdx.x == 0 && kvh == 0) flag_error(pool.err, PKV_ERRBIT_TABLE);
+  if (L > max_len) {                              // past max_context_len: nothing written, flagged
+    if (threadIdx.x == 0 && kvh == 0) flag_error(pool.err, PKV_ERRBIT_CONTEXT);
     return;
   }
   const int blk = bt[(size_t)b * bt_stride + ((L - 1) >> pool.bs_shift)];
@@ -362,6 +320,9 @@ attn_decode_merge_kernel(const float* __restrict__ part_o, const float* __restri
 // Merge of the stream split: pair (b, h / G) has one partial per workgroup
 // that met it, rows (w + pair index) * G + g for w in [owner of its first
 // tile, owner of its last]; a pair met by one workgroup is already final.
+// The owners are computed over the same NW = min(grid, tiles) workgroups as
+// in the attention kernel, every one of which has tiles, so each row read
+// here was written by this launch (never a stale row of a reused workspace).
 template <int D>
 __global__ void __launch_bounds__(D)
 attn_decode_stream_merge_kernel(const float* __restrict__ part_o, const float* __restrict__ part_ml,
@@ -373,8 +334,9 @@ attn_decode_stream_merge_kernel(const float* __restrict__ part_o, const float* _
   const int L = min(ctx[b], cap);
   const int ntb = (max(L, 0) + 31) >> 5;
   if (ntb == 0) return;
+  const long long nw = min((long long)nwg, sc.total);
   const long long pstart = sc.base_rb + (long long)kvh * ntb;
-  const long long wlo = stream_owner(pstart, nwg, sc.total), whi = stream_owner(pstart + ntb - 1, nwg, sc.total);
+  const long long wlo = stream_owner(pstart, nw, sc.total), whi = stream_owner(pstart + ntb - 1, nw, sc.total);
   if (wlo == whi) return;
   const size_t row0 = (size_t)(wlo + (long long)b * hkv + kvh) * G + g;
   const int ns = (int)(whi - wlo + 1);
@@ -412,60 +374,49 @@ hipError_t launch_typed(const PoolDev& pool, const void* q, void* out, const int
                         void* ws, hipStream_t s, const void* k_new, const void* v_new) {
   float* part_o = static_cast<float*>(ws);
   float* part_ml = part_o ? part_o + (size_t)batch * num_q_heads * plan.num_splits * D : nullptr;
+  // append mode with the stream split or in fp32: the new rows are written
+  // by a small kernel first (in the stream-split bf16 kernel the fused form
+  // would push it past its registers)
+  const bool append_first = k_new && (sizeof(T) == 4 || plan.stream_wgs > 0);
+  if (append_first) {
+    hipLaunchKernelGGL(kv_append_kernel<T>, dim3(pool.num_kv_heads, batch), dim3(128), 0, s, pool,
+                       static_cast<const T*>(k_new), static_cast<const T*>(v_new), bt, bt_stride, ctx, plan.max_len);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   if constexpr (sizeof(T) == 2) {
     if (plan.stream_wgs > 0) {
       float* ml = static_cast<float*>(ws) + (size_t)(plan.stream_wgs + batch * (num_q_heads / G)) * G * D;
-#define PKV_STREAM_LAUNCH(AP)                                                                                      \
-      hipLaunchKernelGGL((attn_decode_bf16_kernel<D, G, true, AP>), dim3(plan.stream_wgs), dim3(kThreads), 0, s,    \
-                         pool, static_cast<const bf16_t*>(q), static_cast<bf16_t*>(out), bt, bt_stride, ctx, batch, \
-                         num_q_heads, scale_log2, 0, 0, part_o, ml, nullptr, nullptr)
-      // append with the stream split: the row is written by a small kernel
-      // first (the fused form would push this kernel past its registers)
-      if (k_new) {
-        hipLaunchKernelGGL(kv_append_kernel<T>, dim3(pool.num_kv_heads, batch), dim3(128), 0, s, pool,
-                           static_cast<const T*>(k_new), static_cast<const T*>(v_new), bt, bt_stride, ctx);
-        hipError_t ea = hipGetLastError();
-        if (ea != hipSuccess) return ea;
-      }
-      PKV_STREAM_LAUNCH(false);
-#undef PKV_STREAM_LAUNCH
+      hipLaunchKernelGGL((attn_decode_bf16_kernel<D, G, true, false>), dim3(plan.stream_wgs), dim3(kThreads), 0, s,
+                         pool, static_cast<const bf16_t*>(q), static_cast<bf16_t*>(out), bt, bt_stride, ctx, batch,
+                         num_q_heads, scale_log2, 0, 0, plan.max_len, part_o, ml, nullptr, nullptr);
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
       hipLaunchKernelGGL((attn_decode_stream_merge_kernel<D>), dim3(num_q_heads, batch), dim3(D), 0, s, part_o, ml,
-                         ctx, static_cast<bf16_t*>(out), batch, num_q_heads, num_q_heads / G,
-                         bt_stride << pool.bs_shift, plan.stream_wgs);
+                         ctx, static_cast<bf16_t*>(out), batch, num_q_heads, num_q_heads / G, plan.max_len,
+                         plan.stream_wgs);
       return hipGetLastError();
     }
   }
   const dim3 grid(plan.num_splits, num_q_heads / G, batch);
-  if constexpr (sizeof(T) == 4) {
-    if (k_new) {
-      hipLaunchKernelGGL(kv_append_kernel<T>, dim3(pool.num_kv_heads, batch), dim3(128), 0, s, pool,
-                         static_cast<const T*>(k_new), static_cast<const T*>(v_new), bt, bt_stride, ctx);
-      hipError_t e = hipGetLastError();
-      if (e != hipSuccess) return e;
-    }
-  }
-  if constexpr (sizeof(T) == 2)
-  {
+  if constexpr (sizeof(T) == 2) {
 #define PKV_SPLIT_LAUNCH(AP)                                                                                       \
     hipLaunchKernelGGL((attn_decode_bf16_kernel<D, G, false, AP>), grid, dim3(kThreads), 0, s, pool,               \
                        static_cast<const bf16_t*>(q), static_cast<bf16_t*>(out), bt, bt_stride, ctx, batch,       \
-                       num_q_heads, scale_log2, plan.split_tokens, plan.num_splits, part_o, part_ml,              \
+                       num_q_heads, scale_log2, plan.split_tokens, plan.num_splits, plan.max_len, part_o, part_ml, \
                        static_cast<const bf16_t*>(k_new), static_cast<const bf16_t*>(v_new))
     if (k_new) PKV_SPLIT_LAUNCH(true);
     else PKV_SPLIT_LAUNCH(false);
 #undef PKV_SPLIT_LAUNCH
+  } else {
+    hipLaunchKernelGGL((attn_decode_f32_kernel<D, G>), grid, dim3(kThreads), 0, s, pool, static_cast<const float*>(q),
+                       static_cast<float*>(out), bt, bt_stride, ctx, num_q_heads, scale_log2, plan.split_tokens,
+                       plan.num_splits, plan.max_len, part_o, part_ml);
   }
-  else
-    hipLaunchKernelGGL((attn_decode_kernel<T, D, G>), grid, dim3(kThreads), 0, s, pool, static_cast<const T*>(q),
-                       static_cast<T*>(out), bt, bt_stride, ctx, num_q_heads, scale_log2, plan.split_tokens,
-                       plan.num_splits, part_o, part_ml);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || plan.num_splits == 1) return e;
   hipLaunchKernelGGL((attn_decode_merge_kernel<T, D>), dim3(num_q_heads, batch), dim3(D), 0, s, part_o, part_ml,
-                     ctx, static_cast<T*>(out), num_q_heads, plan.split_tokens, plan.num_splits,
-                     bt_stride << pool.bs_shift);
+                     ctx, static_cast<T*>(out), num_q_heads, plan.split_tokens, plan.num_splits, plan.max_len);
   return hipGetLastError();
 }
 
@@ -491,10 +442,9 @@ hipError_t launch_decode_split_merge(const PoolDev& pool, int dtype, void* out, 
   if (batch == 0 || plan.stream_wgs > 0 || plan.num_splits <= 1) return hipSuccess;
   const float* part_o = static_cast<const float*>(workspace);
   const float* part_ml = part_o + (size_t)batch * num_q_heads * plan.num_splits * pool.head_dim;
-  const int max_len = bt_stride << pool.bs_shift;
 #define PKV_MERGE(T, DD)                                                                                           \
   hipLaunchKernelGGL((attn_decode_merge_kernel<T, DD>), dim3(num_q_heads, batch), dim3(DD), 0, s, part_o, part_ml, \
-                     ctx, static_cast<T*>(out), num_q_heads, plan.split_tokens, plan.num_splits, max_len)
+                     ctx, static_cast<T*>(out), num_q_heads, plan.split_tokens, plan.num_splits, plan.max_len)
   if (dtype == PKV_BF16) {
     if (pool.head_dim == 128) PKV_MERGE(bf16_t, 128);
     else PKV_MERGE(bf16_t, 64);
@@ -531,6 +481,7 @@ DecodePlan plan_decode(int batch, int num_q_heads, int num_kv_heads, int max_con
   }();
   if (forced) split = forced;
   DecodePlan p;
+  p.max_len = max_context_len;
   p.split_tokens = (int)split;
   p.num_splits = (int)((max_context_len + split - 1) / split);
   p.stream_wgs = 0;

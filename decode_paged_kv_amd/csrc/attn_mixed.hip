@@ -18,6 +18,8 @@
 // (equal-splits decode plan; prefill with one key-tile group), so results
 // are those of the two kernels.  The prefill block count is a multiple of
 // the XCD count, so the prefill blocks keep their XCD mapping.
+#include <algorithm>
+
 #include "decode_bf16.h"
 #include "prefill_bf16.h"
 
@@ -31,14 +33,17 @@ attn_mixed_bf16_kernel(PoolDev pool,
                        // after the prefill blocks
                        const bf16_t* __restrict__ dq, bf16_t* __restrict__ dout, const int32_t* __restrict__ dbt,
                        int dbt_stride, const int32_t* __restrict__ ctx, int dbatch, int split_tokens,
-                       int num_splits, float* __restrict__ part_o, float* __restrict__ part_ml, int dec_blocks,
+                       int num_splits, int max_len, float* __restrict__ part_o, float* __restrict__ part_ml,
+                       int dec_blocks,
                        // prefill part
                        const bf16_t* __restrict__ pq, bf16_t* __restrict__ pout, const int32_t* __restrict__ pbt,
                        int pbt_stride, const int32_t* __restrict__ start_loc, const int32_t* __restrict__ chunk_start,
-                       int pbatch, int ntiles, int pf_items, int pf_blocks, int num_q_heads, float scale_log2) {
+                       int pbatch, int ntiles, int pf_items, int pf_blocks, int pf_max_total, int num_q_heads,
+                       float scale_log2) {
   if ((int)blockIdx.x < pf_blocks) {
     prefill_impl::prefill_bf16_block<D, 1>(pool, pq, pout, pbt, pbt_stride, start_loc, chunk_start, pbatch, ntiles,
-                                           num_q_heads, G, scale_log2, pf_items, blockIdx.x, pf_blocks);
+                                           num_q_heads, G, scale_log2, pf_items, pf_max_total, blockIdx.x,
+                                           pf_blocks);
   } else {
     const int bid = blockIdx.x - pf_blocks;
     const int hkv = num_q_heads / G;
@@ -47,7 +52,7 @@ attn_mixed_bf16_kernel(PoolDev pool,
     const int rem = bid - b * per_b;
     const int kvh = rem / num_splits, split = rem - kvh * num_splits;
     decode_impl::decode_bf16_block<D, G, false>(pool, dq, dout, dbt, dbt_stride, ctx, dbatch, num_q_heads,
-                                                scale_log2, split_tokens, num_splits, part_o, part_ml, nullptr,
+                                                scale_log2, split_tokens, num_splits, max_len, part_o, part_ml, nullptr,
                                                 nullptr, split, kvh, b, 0);
   }
 }
@@ -64,14 +69,17 @@ hipError_t launch_mixed_dg(const PoolDev& pool, const MixedDecode& d, const Mixe
   const int ntiles = p.batch > 0 && p.max_chunk_len > 0 ? (p.max_chunk_len + BM - 1) / BM : 0;
   const int pf_items = hkv * ntiles * G * p.batch;
   const int pf_blocks = (pf_items + kXcdCount - 1) / kXcdCount * kXcdCount;
+  const int pf_max_total =
+      p.batch > 0 ? (int)std::min<long long>(p.max_total_len, (long long)p.bt_stride << pool.bs_shift) : 0;
   if (dec_blocks + pf_blocks == 0) return hipSuccess;
   float* part_o = static_cast<float*>(d.workspace);
   float* part_ml = part_o ? part_o + (size_t)d.batch * num_q_heads * d.plan.num_splits * D : nullptr;
   hipLaunchKernelGGL((attn_mixed_bf16_kernel<D, G>), dim3(dec_blocks + pf_blocks), dim3(256), 0, s, pool,
                      static_cast<const bf16_t*>(d.q), static_cast<bf16_t*>(d.out), d.bt, d.bt_stride, d.ctx, d.batch,
-                     d.plan.split_tokens, d.plan.num_splits, part_o, part_ml, dec_blocks,
+                     d.plan.split_tokens, d.plan.num_splits, d.plan.max_len, part_o, part_ml, dec_blocks,
                      static_cast<const bf16_t*>(p.q), static_cast<bf16_t*>(p.out), p.bt, p.bt_stride, p.start_loc,
-                     p.chunk_start, p.batch, ntiles, pf_items, pf_blocks, num_q_heads, scale * kLog2eMixed);
+                     p.chunk_start, p.batch, ntiles, pf_items, pf_blocks, pf_max_total, num_q_heads,
+                     scale * kLog2eMixed);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_decode_split_merge(pool, PKV_BF16, d.out, d.ctx, d.bt_stride, d.batch, num_q_heads, d.plan,
@@ -101,7 +109,7 @@ hipError_t launch_attn_mixed(const PoolDev& pool, int dtype, const MixedDecode& 
                                       d.plan, d.workspace, s);
     if (e != hipSuccess) return e;
     return launch_attn_prefill(pool, dtype, p.q, p.out, p.bt, p.bt_stride, p.start_loc, p.chunk_start, p.batch,
-                               p.max_chunk_len, num_q_heads, scale, s);
+                               p.max_chunk_len, p.max_total_len, num_q_heads, scale, s);
   }
   const int group = num_q_heads / pool.num_kv_heads;
   if (pool.head_dim == 128) return launch_mixed_d<128>(group, pool, d, p, num_q_heads, scale, s);

@@ -32,6 +32,8 @@
 //   one KV head then stream the same K/V through the same L2.
 //
 // fp32 path: a plain wave-per-(query, head) kernel for small checks.
+#include <algorithm>
+
 #include "prefill_bf16.h"
 
 namespace pkv {
@@ -44,9 +46,9 @@ __global__ void __launch_bounds__(256 * NG, 2 / NG)
 attn_prefill_bf16_kernel(PoolDev pool, const bf16_t* __restrict__ q, bf16_t* __restrict__ out,
                          const int32_t* __restrict__ bt, int bt_stride, const int32_t* __restrict__ start_loc,
                          const int32_t* __restrict__ chunk_start, int batch, int ntiles, int num_q_heads,
-                         int group, float scale_log2, int total_items) {
+                         int group, float scale_log2, int total_items, int max_total) {
   prefill_bf16_block<D, NG>(pool, q, out, bt, bt_stride, start_loc, chunk_start, batch, ntiles, num_q_heads, group,
-                            scale_log2, total_items, blockIdx.x, gridDim.x);
+                            scale_log2, total_items, max_total, blockIdx.x, gridDim.x);
 }
 
 // fp32: one wave per (query row, q-head); lane owns head-dim columns.
@@ -55,7 +57,7 @@ __global__ void __launch_bounds__(256)
 attn_prefill_f32_kernel(PoolDev pool, const float* __restrict__ q, float* __restrict__ out,
                         const int32_t* __restrict__ bt, int bt_stride, const int32_t* __restrict__ start_loc,
                         const int32_t* __restrict__ chunk_start, int max_chunk_len, int num_q_heads, int group,
-                        float scale_log2) {
+                        float scale_log2, int max_total) {
   constexpr int DPL = D / 64;
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);     // query row within the chunk
@@ -65,10 +67,10 @@ attn_prefill_f32_kernel(PoolDev pool, const float* __restrict__ q, float* __rest
   if (row >= T || row >= max_chunk_len) return;
   const int S = chunk_start[b];
   const int pos = S + row;
-  if (pos >= (bt_stride << pool.bs_shift)) {
-    if (lane == 0) flag_error(pool.err, PKV_ERRBIT_TABLE);
-    return;
-  }
+  // keys [0, pos], cut to max_total_len (checked against the table's
+  // capacity on the host) and flagged if the chunk reaches past it
+  if (row == 0 && lane == 0 && S + T > max_total) flag_error(pool.err, PKV_ERRBIT_CONTEXT);
+  const int kend = min(pos + 1, max_total);
   const int kvh = h / group;
   const int hl = pool.heads_per_shard;
   const int sh = kvh / hl, lh = kvh - sh * hl;
@@ -83,7 +85,7 @@ attn_prefill_f32_kernel(PoolDev pool, const float* __restrict__ q, float* __rest
     acc[j] = 0.f;
   }
   float m = -INFINITY, l = 0.f;
-  for (int key = 0; key <= pos; ++key) {
+  for (int key = 0; key < kend; ++key) {
     const int blk = table[key >> pool.bs_shift];
     if (blk < 0 || blk >= pool.num_blocks) {
       if (lane == 0) flag_error(pool.err, PKV_ERRBIT_BLOCK_ID);
@@ -113,8 +115,11 @@ attn_prefill_f32_kernel(PoolDev pool, const float* __restrict__ q, float* __rest
 
 hipError_t launch_attn_prefill(const PoolDev& pool, int dtype, const void* q, void* out, const int32_t* bt,
                                int bt_stride, const int32_t* start_loc, const int32_t* chunk_start, int batch,
-                               int max_chunk_len, int num_q_heads, float scale, hipStream_t s) {
+                               int max_chunk_len, int max_total_len, int num_q_heads, float scale, hipStream_t s) {
   if (batch == 0 || max_chunk_len == 0) return hipSuccess;
+  // never past what the table addresses (the ABI has checked max_total_len
+  // against it already)
+  const int max_total = (int)std::min<long long>(max_total_len, (long long)bt_stride << pool.bs_shift);
   const int group = num_q_heads / pool.num_kv_heads;
   const float sl2 = scale * kLog2e;
   if (dtype == PKV_BF16) {
@@ -128,7 +133,7 @@ hipError_t launch_attn_prefill(const PoolDev& pool, int dtype, const void* q, vo
 #define PKV_PREFILL_LAUNCH(DD, NG)                                                                               \
     hipLaunchKernelGGL((attn_prefill_bf16_kernel<DD, NG>), dim3(grid), dim3(256 * NG), 0, s, pool,                \
                        static_cast<const bf16_t*>(q), static_cast<bf16_t*>(out), bt, bt_stride, start_loc,       \
-                       chunk_start, batch, ntiles, num_q_heads, group, sl2, items)
+                       chunk_start, batch, ntiles, num_q_heads, group, sl2, items, max_total)
     if (pool.head_dim == 128) {
       if (split) PKV_PREFILL_LAUNCH(128, 2);
       else PKV_PREFILL_LAUNCH(128, 1);
@@ -143,11 +148,11 @@ hipError_t launch_attn_prefill(const PoolDev& pool, int dtype, const void* q, vo
   if (pool.head_dim == 128)
     hipLaunchKernelGGL(attn_prefill_f32_kernel<128>, grid, dim3(256), 0, s, pool, static_cast<const float*>(q),
                        static_cast<float*>(out), bt, bt_stride, start_loc, chunk_start, max_chunk_len, num_q_heads,
-                       group, sl2);
+                       group, sl2, max_total);
   else
     hipLaunchKernelGGL(attn_prefill_f32_kernel<64>, grid, dim3(256), 0, s, pool, static_cast<const float*>(q),
                        static_cast<float*>(out), bt, bt_stride, start_loc, chunk_start, max_chunk_len, num_q_heads,
-                       group, sl2);
+                       group, sl2, max_total);
   return hipGetLastError();
 }
 

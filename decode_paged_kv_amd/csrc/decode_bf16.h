@@ -103,7 +103,7 @@ struct DecodeBf16Smem {
 constexpr float kDecodeSlack = 8.0f;
 
 // Stream split bookkeeping.  Request b holds Hkv * ceil(L_b / 32) pair-tiles
-// (L_b clamped to what its table addresses), laid out by request, then KV
+// (L_b clamped to max_context_len), laid out by request, then KV
 // head, then key.  scan_tiles returns the total, the request holding pair-
 // tile `target` (-1: none) with the index of its first pair-tile, and the
 // index of request rb's first pair-tile; every lane of the wave gets the
@@ -113,7 +113,7 @@ struct TileScan {
   int b;
   long long base;
   long long base_rb;
-  bool over;                                    // some context exceeds its table
+  bool over;                                    // some context exceeds the cap
 };
 __device__ __forceinline__ long long uniform64(long long x) {
   const int lo = __builtin_amdgcn_readfirstlane((int)(unsigned)(unsigned long long)x);
@@ -166,7 +166,7 @@ __device__ __forceinline__ void decode_bf16_block(PoolDev pool, const bf16_t* __
                                                   bf16_t* __restrict__ out, const int32_t* __restrict__ bt,
                                                   int bt_stride, const int32_t* __restrict__ ctx, int batch,
                                                   int num_q_heads, float scale_log2, int split_tokens,
-                                                  int num_splits, float* __restrict__ part_o,
+                                                  int num_splits, int max_len, float* __restrict__ part_o,
                                                   float* __restrict__ part_ml, const bf16_t* __restrict__ k_new,
                                                   const bf16_t* __restrict__ v_new, int bx, int by, int bz,
                                                   int nbx) {
@@ -177,7 +177,9 @@ __device__ __forceinline__ void decode_bf16_block(PoolDev pool, const bf16_t* __
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l16 = lane & 15, j4 = lane >> 4;
-  const int cap = bt_stride << pool.bs_shift;                   // keys the table can address
+  // keys a request may have: max_context_len, which the host has checked
+  // against the table's capacity; a longer context is cut to it and flagged
+  const int cap = max_len;
   const int hl = pool.heads_per_shard;
   const int bs = pool.block_size;
   const size_t block_stride = (size_t)hl * bs * D;
@@ -467,8 +469,8 @@ __device__ __forceinline__ void decode_bf16_block(PoolDev pool, const bf16_t* __
     // one segment: split bx of (request bz, KV head by)
     const int split = bx, kvh = by, b = bz;
     int L = ctx[b];
-    if (L > cap) {                              // never index past the request's table
-      if (threadIdx.x == 0 && split == 0 && kvh == 0) flag_error(pool.err, PKV_ERRBIT_TABLE);
+    if (L > cap) {                              // past max_context_len: cut, flagged
+      if (threadIdx.x == 0 && split == 0 && kvh == 0) flag_error(pool.err, PKV_ERRBIT_CONTEXT);
       L = cap;
     }
     const int start = split * split_tokens;
@@ -485,15 +487,18 @@ __device__ __forceinline__ void decode_bf16_block(PoolDev pool, const bf16_t* __
     // stream split: workgroup w takes the pair-tiles [w W / NW, (w+1) W / NW)
     // of the W = Hkv * sum_b ceil(L_b / 32) tiles of the batch, ordered by
     // request, KV head, key; a pair met by several workgroups leaves one
-    // partial per workgroup, in row (w + pair index) * G + g
+    // partial per workgroup, in row (w + pair index) * G + g.  NW is the grid
+    // size or W if smaller (the grid is sized from max_context_len, an upper
+    // bound): then every workgroup below NW has at least one tile and writes
+    // every partial row the merge kernel will read, and the rest exit.
     const int hkv = num_q_heads / G;
-    const long long NW = nbx, w = bx;
     const TileScan tot = scan_tiles(ctx, batch, cap, hkv, -1, 0);
-    if (tot.over && w == 0 && threadIdx.x == 0) flag_error(pool.err, PKV_ERRBIT_TABLE);
+    if (tot.over && bx == 0 && threadIdx.x == 0) flag_error(pool.err, PKV_ERRBIT_CONTEXT);
     const long long Wt = tot.total;
+    const long long NW = min((long long)nbx, Wt), w = bx;
+    if (w >= NW) return;
     long long t = w * Wt / NW;
     const long long t1 = (w + 1) * Wt / NW;
-    if (t >= t1) return;
     const TileScan at = scan_tiles(ctx, batch, cap, hkv, t, 0);
     int b = at.b;
     long long base = at.base;

@@ -24,6 +24,9 @@ namespace pkv {
 int fail(int code, const char* fmt, ...);
 int hip_fail(hipError_t e, const char* where);
 int check_pool(const pkv_pool_layer* p, const char* name, PoolDev* out);
+int check_heads(const PoolDev& pool, int num_q_heads);
+bool scale_ok(float x);
+bool aligned16(const void* p);
 void clear_error();
 }  // namespace pkv
 
@@ -118,19 +121,17 @@ int choose_m(const pkv_mux* m, int decode_bs, bool has_prefill) {
 void build_masks(int total, int decode_cus, std::array<uint32_t, kMaskWords>& pm, std::array<uint32_t, kMaskWords>& dm) {
   pm.fill(0);
   dm.fill(0);
-  const int per_xcd = total / kXcds;
   const int dec_per_xcd = decode_cus / kXcds;
   for (int i = 0; i < total; ++i) {
     const int cu_in_xcd = i / kXcds;
     auto& m = cu_in_xcd < dec_per_xcd ? dm : pm;
     m[i / 32] |= 1u << (i % 32);
   }
-  (void)per_xcd;
 }
 
 // A queue whose mask leaves some XCD without a CU can never run the share of
 // its workgroups dispatched there; every mask used must keep >= 1 CU per XCD.
-bool every_xcd_has_a_cu(const std::array<uint32_t, kMaskWords>& m, int total) {
+bool every_xcd_has_a_cu(const uint32_t* m, int total) {
   int per[kXcds] = {0};
   for (int i = 0; i < total; ++i)
     if ((m[i / 32] >> (i % 32)) & 1u) per[i % kXcds]++;
@@ -143,7 +144,8 @@ int ensure_streams(pkv_mux* m, int level) {
   const auto& g = m->groups[level];
   if (g.first == 0 || g.second == 0) return PKV_OK;      // whole-device groups use the ordinary stream
   if (m->pstream[level] && m->dstream[level]) return PKV_OK;
-  if (!every_xcd_has_a_cu(m->pmask[level], m->total_cus) || !every_xcd_has_a_cu(m->dmask[level], m->total_cus))
+  if (!every_xcd_has_a_cu(m->pmask[level].data(), m->total_cus) ||
+      !every_xcd_has_a_cu(m->dmask[level].data(), m->total_cus))
     return fail(PKV_EINVAL, "CU masks of level %d leave an XCD without a CU", level);
   hipError_t e = hipExtStreamCreateWithCUMask(&m->pstream[level], kMaskWords, m->pmask[level].data());
   if (e != hipSuccess) return hip_fail(e, "hipExtStreamCreateWithCUMask(prefill)");
@@ -170,44 +172,73 @@ int sync_level(pkv_mux* m, int level) {
   return PKV_OK;
 }
 
+// Every layer's pool must have layer 0's shape: the split plan, the
+// workspace size and the table checks are made once, from layer 0.
+int check_layer_pools(const pkv_pool_layer* pools, int n, std::vector<PoolDev>& out, const char* what) {
+  out.resize(n);
+  for (int l = 0; l < n; ++l) {
+    if (int rc = check_pool(&pools[l], what, &out[l])) return rc;
+    const pkv_pool_layer &a = pools[0], &b = pools[l];
+    if (b.dtype != a.dtype || b.num_kv_heads != a.num_kv_heads || b.head_dim != a.head_dim ||
+        b.block_size != a.block_size || b.num_shards != a.num_shards || b.num_blocks != a.num_blocks)
+      return fail(PKV_EINVAL, "%s: layer %d's pool differs from layer 0's (dtype, heads, head_dim, block size, "
+                  "shards or blocks)", what, l);
+  }
+  return PKV_OK;
+}
+
 int check_decode_step(const pkv_decode_step* d, std::vector<PoolDev>& pools, DecodePlan& plan) {
+  if (!d) return fail(PKV_EINVAL, "run_mux_round: decode step is NULL");
   if (d->num_layers <= 0 || !d->pools || !d->q || !d->k_new || !d->v_new || !d->out)
     return fail(PKV_EINVAL, "run_mux_round: decode step needs layers and per-layer arrays");
   if (d->batch <= 0 || d->max_context_len <= 0 || !d->slots || !d->block_tables || !d->context_lens)
     return fail(PKV_EINVAL, "run_mux_round: decode step batch/context/tables");
-  pools.resize(d->num_layers);
+  if (int rc = check_layer_pools(d->pools, d->num_layers, pools, "run_mux_round(decode pool)")) return rc;
   for (int l = 0; l < d->num_layers; ++l) {
-    if (int rc = check_pool(&d->pools[l], "run_mux_round(decode pool)", &pools[l])) return rc;
     if (!d->q[l] || !d->k_new[l] || !d->v_new[l] || !d->out[l])
       return fail(PKV_EINVAL, "run_mux_round: decode layer %d has a NULL tensor", l);
+    if (!aligned16(d->q[l]) || !aligned16(d->k_new[l]) || !aligned16(d->v_new[l]) || !aligned16(d->out[l]))
+      return fail(PKV_EINVAL, "run_mux_round: decode layer %d q/k_new/v_new/out must be 16-byte aligned", l);
   }
   const PoolDev& p0 = pools[0];
-  if (d->num_q_heads <= 0 || d->num_q_heads % p0.num_kv_heads)
-    return fail(PKV_EINVAL, "run_mux_round: num_q_heads %d", d->num_q_heads);
-  if ((int64_t)d->bt_stride * p0.block_size < d->max_context_len)
-    return fail(PKV_EINVAL, "run_mux_round: decode bt_stride too small");
+  if (int rc = check_heads(p0, d->num_q_heads)) return rc;
+  if (!scale_ok(d->scale)) return fail(PKV_EINVAL, "run_mux_round: decode scale must be finite and >= 0");
+  if (d->bt_stride <= 0 || (int64_t)d->bt_stride * p0.block_size < d->max_context_len)
+    return fail(PKV_EINVAL, "run_mux_round: decode bt_stride %d blocks cannot hold %d tokens", d->bt_stride,
+                d->max_context_len);
+  if ((int64_t)p0.num_blocks * p0.block_size > INT32_MAX) return fail(PKV_ERANGE, "run_mux_round: pool too large");
   plan = plan_decode(d->batch, d->num_q_heads, p0.num_kv_heads, d->max_context_len, p0.head_dim, d->pools[0].dtype);
-  if (plan.workspace > 0 && (!d->workspace || d->workspace_bytes < plan.workspace))
-    return fail(PKV_EINVAL, "run_mux_round: decode workspace of %zu bytes needed", plan.workspace);
+  if (plan.workspace > 0) {
+    if (!d->workspace || d->workspace_bytes < plan.workspace)
+      return fail(PKV_EINVAL, "run_mux_round: decode workspace of %zu bytes needed, %zu given", plan.workspace,
+                  d->workspace ? d->workspace_bytes : (size_t)0);
+    if (!aligned16(d->workspace)) return fail(PKV_EINVAL, "run_mux_round: decode workspace must be 16-byte aligned");
+  }
   return PKV_OK;
 }
 
 int check_prefill_job(const pkv_prefill_job* p, std::vector<PoolDev>& pools) {
+  if (!p) return fail(PKV_EINVAL, "run_mux_round: prefill job is NULL");
   if (p->num_layers <= 0 || !p->pools || !p->q || !p->k || !p->v || !p->out)
     return fail(PKV_EINVAL, "run_mux_round: prefill job needs layers and per-layer arrays");
   if (p->num_tokens <= 0 || !p->slots || !p->block_table || !p->start_loc || !p->chunk_start)
     return fail(PKV_EINVAL, "run_mux_round: prefill job tokens/tables");
   if (p->next_layer < 0 || p->next_layer > p->num_layers) return fail(PKV_EINVAL, "run_mux_round: next_layer");
-  pools.resize(p->num_layers);
+  if (int rc = check_layer_pools(p->pools, p->num_layers, pools, "run_mux_round(prefill pool)")) return rc;
   for (int l = 0; l < p->num_layers; ++l) {
-    if (int rc = check_pool(&p->pools[l], "run_mux_round(prefill pool)", &pools[l])) return rc;
     if (!p->q[l] || !p->k[l] || !p->v[l] || !p->out[l])
       return fail(PKV_EINVAL, "run_mux_round: prefill layer %d has a NULL tensor", l);
+    if (!aligned16(p->q[l]) || !aligned16(p->k[l]) || !aligned16(p->v[l]) || !aligned16(p->out[l]))
+      return fail(PKV_EINVAL, "run_mux_round: prefill layer %d q/k/v/out must be 16-byte aligned", l);
   }
-  if (p->num_q_heads <= 0 || p->num_q_heads % pools[0].num_kv_heads)
-    return fail(PKV_EINVAL, "run_mux_round: prefill num_q_heads %d", p->num_q_heads);
-  if ((int64_t)p->bt_stride * pools[0].block_size < p->num_tokens)
-    return fail(PKV_EINVAL, "run_mux_round: prefill bt_stride too small");
+  if (int rc = check_heads(pools[0], p->num_q_heads)) return rc;
+  if (!scale_ok(p->scale)) return fail(PKV_EINVAL, "run_mux_round: prefill scale must be finite and >= 0");
+  if (p->bt_stride <= 0 || (int64_t)p->bt_stride * pools[0].block_size < p->num_tokens)
+    return fail(PKV_EINVAL, "run_mux_round: prefill bt_stride %d blocks cannot hold %d tokens", p->bt_stride,
+                p->num_tokens);
+  if ((int64_t)p->num_tokens * 2 > INT32_MAX / 64) return fail(PKV_ERANGE, "run_mux_round: prompt too long");
+  if ((int64_t)pools[0].num_blocks * pools[0].block_size > INT32_MAX)
+    return fail(PKV_ERANGE, "run_mux_round: pool too large");
   return PKV_OK;
 }
 
@@ -235,6 +266,48 @@ int pkv_mux_policy_groups_grid(int total_units, int min_part, int granularity, i
 int pkv_mux_policy_choose(int num_groups, int decode_bs, int has_prefill, int decode_bs_divisor) {
   if (num_groups < 3 || decode_bs < 0 || decode_bs_divisor <= 0) return fail(PKV_EINVAL, "pkv_mux_policy_choose");
   return choose(num_groups, decode_bs, has_prefill != 0, decode_bs_divisor);
+}
+
+int pkv_mux_check_decode_step(const pkv_decode_step* d) {
+  clear_error();
+  std::vector<PoolDev> pools;
+  DecodePlan plan{};
+  return check_decode_step(d, pools, plan);
+}
+
+int pkv_mux_check_prefill_job(const pkv_prefill_job* p) {
+  clear_error();
+  std::vector<PoolDev> pools;
+  return check_prefill_job(p, pools);
+}
+
+int pkv_mux_policy_cu_masks(int total_cus, int decode_cus, uint32_t* prefill_words, uint32_t* decode_words,
+                            int32_t cap_words) {
+  clear_error();
+  if (total_cus <= 0 || total_cus > kMaskWords * 32 || total_cus % kXcds)
+    return fail(PKV_EUNSUPPORTED, "pkv_mux_policy_cu_masks: %d CUs (a multiple of %d, at most %d)", total_cus, kXcds,
+                kMaskWords * 32);
+  if (decode_cus <= 0 || decode_cus >= total_cus || decode_cus % kXcds)
+    return fail(PKV_EINVAL, "pkv_mux_policy_cu_masks: %d decode CUs (a multiple of %d, 0 < n < %d)", decode_cus,
+                kXcds, total_cus);
+  if (cap_words < (total_cus + 31) / 32 || !prefill_words || !decode_words)
+    return fail(PKV_EINVAL, "pkv_mux_policy_cu_masks: output arrays");
+  std::array<uint32_t, kMaskWords> pm, dm;
+  build_masks(total_cus, decode_cus, pm, dm);
+  for (int i = 0; i < (total_cus + 31) / 32; ++i) {
+    prefill_words[i] = pm[i];
+    decode_words[i] = dm[i];
+  }
+  return PKV_OK;
+}
+
+int pkv_mux_policy_mask_ok(const uint32_t* words, int32_t nwords, int total_cus) {
+  clear_error();
+  if (!words || total_cus <= 0 || total_cus > kMaskWords * 32 || total_cus % kXcds || nwords < (total_cus + 31) / 32)
+    return fail(PKV_EINVAL, "pkv_mux_policy_mask_ok: bad argument");
+  std::array<uint32_t, kMaskWords> m{};
+  for (int i = 0; i < (total_cus + 31) / 32; ++i) m[i] = words[i];
+  return every_xcd_has_a_cu(m.data(), total_cus) ? 1 : 0;
 }
 
 int pkv_mux_policy_layers_per_round(int prefill_tokens, int num_layers, int token_budget) {
@@ -523,7 +596,8 @@ int run_mux_round(pkv_mux* m, const pkv_decode_step* d, pkv_prefill_job* p, int3
       e = launch_kv_write(ppools[l], p->pools[l].dtype, p->k[l], p->v[l], p->slots, p->num_tokens, ps);
       if (e == hipSuccess)
         e = launch_attn_prefill(ppools[l], p->pools[l].dtype, p->q[l], p->out[l], p->block_table, p->bt_stride,
-                                p->start_loc, p->chunk_start, 1, p->num_tokens, p->num_q_heads, sc, ps);
+                                p->start_loc, p->chunk_start, 1, p->num_tokens, p->num_tokens, p->num_q_heads, sc,
+                                ps);
       if (e != hipSuccess) return hip_fail(e, "run_mux_round(prefill)");
     }
     p->next_layer = end;

@@ -106,6 +106,7 @@ hipError_t launch_kv_relayout_convert(const PoolDev& src, const int32_t* src_bt,
                                       int32_t* err, hipStream_t s);
 
 struct DecodePlan {
+  int max_len;        // max_context_len: longer contexts are cut to it and flagged
   int split_tokens;   // keys per split (multiple of 32); split plan only
   int num_splits;     // splits per (request, kv head) at max_context_len; split plan only
   int stream_wgs;     // > 0: stream split over this many workgroups instead
@@ -126,7 +127,7 @@ hipError_t launch_attn_decode(const PoolDev& pool, int dtype, const void* q, voi
                               const void* v_new = nullptr);
 hipError_t launch_attn_prefill(const PoolDev& pool, int dtype, const void* q, void* out, const int32_t* bt,
                                int bt_stride, const int32_t* start_loc, const int32_t* chunk_start, int batch,
-                               int max_chunk_len, int num_q_heads, float scale, hipStream_t s);
+                               int max_chunk_len, int max_total_len, int num_q_heads, float scale, hipStream_t s);
 // decode (plan made with stream_ok = false) and prefill chunks of one layer
 // in one launch (bf16), decode workgroups first; fp32 runs the two kernels
 struct MixedDecode {
@@ -148,6 +149,7 @@ struct MixedPrefill {
   const int32_t* chunk_start;
   int batch;
   int max_chunk_len;
+  int max_total_len;
 };
 hipError_t launch_attn_mixed(const PoolDev& pool, int dtype, const MixedDecode& d, const MixedPrefill& p,
                              int num_q_heads, float scale, hipStream_t s);

@@ -110,7 +110,7 @@ __device__ __forceinline__ void prefill_bf16_block(PoolDev pool, const bf16_t* _
                                                    int bt_stride, const int32_t* __restrict__ start_loc,
                                                    const int32_t* __restrict__ chunk_start, int batch, int ntiles,
                                                    int num_q_heads, int group, float scale_log2, int total_items,
-                                                   int bid, int nblocks) {
+                                                   int max_total, int bid, int nblocks) {
   using C = PrefillCfg<D>;
   // double-buffered K and V tiles; four separate arrays so the compiler
   // sees that a DMA into one buffer never overlaps reads of another
@@ -136,8 +136,10 @@ __device__ __forceinline__ void prefill_bf16_block(PoolDev pool, const bf16_t* _
   const int T = start_loc[b + 1] - q0;
   if (qt * C::BM >= T) return;
   const int S = chunk_start[b];
-  const int kv_len = min(S + T, bt_stride << pool.bs_shift);
-  if (S + T > (bt_stride << pool.bs_shift) && threadIdx.x == 0) flag_error(pool.err, PKV_ERRBIT_TABLE);
+  // keys [0, S+T), cut to max_total_len (which the host has checked against
+  // the table's capacity) and flagged if a chunk reaches past it
+  const int kv_len = min(S + T, max_total);
+  if (S + T > max_total && threadIdx.x == 0) flag_error(pool.err, PKV_ERRBIT_CONTEXT);
   const int kend = min(kv_len, S + min(T, (qt + 1) * C::BM));   // one past the last query's position
 
   const int tid = threadIdx.x;
@@ -157,7 +159,9 @@ __device__ __forceinline__ void prefill_bf16_block(PoolDev pool, const bf16_t* _
 
   // ---- this lane's query row and its Q fragments (B operand of S^T) ----
   const int qrel = qt * C::BM + wave * 32 + l32;
-  const int qpos = S + qrel;
+  // the causal limit of this lane's query: its position, or the last key
+  // when the chunk is cut at max_total_len (keys past it are never seen)
+  const int qpos = min(S + qrel, kv_len - 1);
   uint4 qf[C::KS];
   {
     const bool ok = qrel < T;
@@ -165,7 +169,7 @@ __device__ __forceinline__ void prefill_bf16_block(PoolDev pool, const bf16_t* _
 #pragma unroll
     for (int s = 0; s < C::KS; ++s) qf[s] = ok ? *reinterpret_cast<const uint4*>(qrow + 16 * s) : make_uint4(0, 0, 0, 0);
   }
-  const int wave_first_q = S + qt * C::BM + wave * 32;
+  const int wave_first_q = min(S + qt * C::BM + wave * 32, kv_len - 1);
 
   // ---- tile loads: LDS DMA, wave w moves 16-key group w of K and of V ----
   // K tile in LDS: row r holds key 32(r/32) + key_perm(r%32) (so that the

@@ -15,6 +15,7 @@ import torch
 from . import _lib
 from ._lib import BF16, F32, FP8_E4M3, DecodeStep, KvDest, PkvError, PkvLibraryMissing, PoolLayer, PrefillJob  # noqa: F401
 from ._lib import LAYOUT_KV_FUSED, LAYOUT_POOL, LAYOUT_TOKEN_MAJOR  # noqa: F401
+from ._lib import ERRBIT_BLOCK_ID, ERRBIT_CONTEXT, ERRBIT_SLOT, ERRBIT_TABLE  # noqa: F401
 
 _TORCH_DTYPE = {"bf16": torch.bfloat16, "f32": torch.float32}
 _CODE = {"bf16": BF16, "f32": F32}
@@ -160,18 +161,28 @@ def kv_relayout_convert(src: PagedPool, src_bt, dst: ConvertedPool, dst_bt, n_to
 
 
 def attn_prefill_chunk(pool: PagedPool, q, out, block_tables, start_loc, chunk_start, max_chunk_len: int,
-                       num_q_heads: int, scale: float = 0.0, stream=None):
+                       num_q_heads: int, scale: float = 0.0, stream=None, max_total_len: int | None = None):
+    """``max_total_len`` (an upper bound of every S+T) defaults to what the block table addresses."""
     lib = _lib.load()
     c = pool.c()
     batch = chunk_start.numel()
+    if max_total_len is None:
+        max_total_len = block_tables.shape[-1] * pool.block_size
     rc = lib.attn_prefill_chunk(C.byref(c), _ptr(q), _ptr(out), _ptr(block_tables), block_tables.shape[-1],
-                                _ptr(start_loc), _ptr(chunk_start), batch, max_chunk_len, num_q_heads, scale,
-                                _stream(stream))
+                                _ptr(start_loc), _ptr(chunk_start), batch, max_chunk_len, max_total_len, num_q_heads,
+                                scale, _stream(stream))
     _lib.check(rc, "attn_prefill_chunk")
 
 
 def attn_decode_workspace_size(batch: int, num_q_heads: int, max_context_len: int, head_dim: int) -> int:
+    """Worst case over group sizes and dtypes (the library is told neither)."""
     return int(_lib.load().pkv_attn_decode_workspace_size(batch, num_q_heads, max_context_len, head_dim))
+
+
+def attn_decode_workspace_size_for(pool: PagedPool, batch: int, num_q_heads: int, max_context_len: int) -> int:
+    """Exactly what attn_decode needs for this pool (KV heads, head dim, dtype)."""
+    return int(_lib.load().pkv_attn_decode_workspace_size_for(C.byref(pool.c()), batch, num_q_heads,
+                                                               max_context_len))
 
 
 def attn_decode(pool: PagedPool, q, out, block_tables, context_lens, max_context_len: int, num_q_heads: int,
@@ -211,9 +222,19 @@ def stall_free_chunk(token_budget: int, num_decode: int, prompt_remaining: int) 
     return rc
 
 
+def stall_free_batch(token_budget: int, num_decode: int, prompts_remaining) -> list[int]:
+    """Chunks of several prompts in one stall-free step (ongoing prefills listed before new requests)."""
+    n = len(prompts_remaining)
+    rem = (C.c_int32 * max(n, 1))(*[int(x) for x in prompts_remaining])
+    out = (C.c_int32 * max(n, 1))()
+    rc = int(_lib.load().pkv_stall_free_batch(token_budget, num_decode, rem, n, out))
+    _lib.check(rc if rc < 0 else 0, "pkv_stall_free_batch")
+    return [int(out[i]) for i in range(n)]
+
+
 def attn_mixed_batch(pool: PagedPool, q_dec, out_dec, dec_block_tables, context_lens, max_context_len: int,
                      q_pf, out_pf, pf_block_tables, start_loc, chunk_start, max_chunk_len: int, num_q_heads: int,
-                     scale: float = 0.0, workspace=None, stream=None):
+                     scale: float = 0.0, workspace=None, stream=None, max_total_len: int | None = None):
     """Decode attention for every request in context_lens and prefill attention for the chunks described by
     start_loc / chunk_start, one launch (bf16).  Pass None for the tensors of an empty part."""
     lib = _lib.load()
@@ -225,12 +246,15 @@ def attn_mixed_batch(pool: PagedPool, q_dec, out_dec, dec_block_tables, context_
         dev = q_dec.device
         workspace = torch.zeros(max(nbytes, 16), dtype=torch.uint8, device=dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if max_total_len is None:
+        max_total_len = 0 if pf_block_tables is None else pf_block_tables.shape[-1] * pool.block_size
     p = lambda t: None if t is None else _ptr(t)  # noqa: E731
     rc = lib.attn_mixed_batch(C.byref(c), p(q_dec), p(out_dec), p(dec_block_tables),
                               0 if dec_block_tables is None else dec_block_tables.shape[-1], p(context_lens), nd,
                               max_context_len, p(q_pf), p(out_pf), p(pf_block_tables),
                               0 if pf_block_tables is None else pf_block_tables.shape[-1], p(start_loc),
-                              p(chunk_start), npf, max_chunk_len, num_q_heads, scale, p(workspace), ws_bytes,
+                              p(chunk_start), npf, max_chunk_len, max_total_len, num_q_heads, scale, p(workspace),
+                              ws_bytes,
                               _stream(stream))
     _lib.check(rc, "attn_mixed_batch")
 

@@ -68,7 +68,7 @@ enum {
   PKV_ERANGE = -4         /* a size exceeds a documented limit                     */
 };
 
-enum { PKV_ERRBIT_BLOCK_ID = 1, PKV_ERRBIT_SLOT = 2, PKV_ERRBIT_TABLE = 4 };
+enum { PKV_ERRBIT_BLOCK_ID = 1, PKV_ERRBIT_SLOT = 2, PKV_ERRBIT_TABLE = 4, PKV_ERRBIT_CONTEXT = 8 };
 
 /* One layer of one instance's paged KV pool (see "Pool layout" above). */
 typedef struct pkv_pool_layer {
@@ -193,13 +193,18 @@ int kv_relayout_convert(const pkv_pool_layer* src, const int32_t* src_bt, const 
  *   start_loc     device int32 [batch + 1] offsets of each request's chunk
  *   chunk_start   device int32 [batch] S of each request
  *   max_chunk_len host upper bound of every T (sizes the grid)
+ *   max_total_len host upper bound of every S+T: at least max_chunk_len, and
+ *                 the table must address it (bt_stride * block_size >=
+ *                 max_total_len), else PKV_EINVAL before any launch.  A chunk
+ *                 reaching past it attends to keys [0, max_total_len) only
+ *                 and sets PKV_ERRBIT_CONTEXT.
  * The chunk's own K/V must already be in the pool (kv_write); keys
  * [0, S+T) are read from the pool only.  scale <= 0 selects 1/sqrt(head_dim).
  */
 int attn_prefill_chunk(const pkv_pool_layer* pool, const void* q, void* out, const int32_t* block_tables,
                        int32_t bt_stride, const int32_t* start_loc, const int32_t* chunk_start,
-                       int32_t batch, int32_t max_chunk_len, int32_t num_q_heads, float scale,
-                       hipStream_t stream);
+                       int32_t batch, int32_t max_chunk_len, int32_t max_total_len, int32_t num_q_heads,
+                       float scale, hipStream_t stream);
 
 /*
  * attn_decode - one query per request over its whole cached context.
@@ -208,8 +213,11 @@ int attn_prefill_chunk(const pkv_pool_layer* pool, const void* q, void* out, con
  * L = context_lens[b] (its own K/V already written at L-1).
  *   q, out          device [batch][num_q_heads][head_dim]
  *   block_tables    device int32 [batch][bt_stride]
- *   context_lens    device int32 [batch], each in [1, max_context_len]
- *   max_context_len host upper bound of every L (sizes the grid)
+ *   context_lens    device int32 [batch], each in [1, max_context_len]; a
+ *                   longer context is cut to its first max_context_len keys
+ *                   (every plan and dtype alike) and sets PKV_ERRBIT_CONTEXT
+ *   max_context_len host upper bound of every L (sizes the grid); the table
+ *                   must address it: bt_stride * block_size >= max_context_len
  *   workspace       device scratch of at least
  *                   pkv_attn_decode_workspace_size(...) bytes for the
  *                   split-KV partial results; caller-owned, may be NULL
@@ -224,13 +232,22 @@ int attn_prefill_chunk(const pkv_pool_layer* pool, const void* q, void* out, con
  * variable PKV_DECODE_STREAM_WGS, read once) each takes an equal run of
  * 32-key tiles over the whole batch, so uneven contexts leave no idle tail.
  * PKV_DECODE_SPLIT_TOKENS (a multiple of 32, read once) forces equal splits
- * of that many keys, for tuning.  pkv_attn_decode_workspace_size accounts
- * for all of these.  A pair handled by one workgroup is finished by the
- * attention kernel; the partial results of the others are merged by a
- * second kernel on the same stream.
+ * of that many keys, for tuning.  A pair handled by one workgroup is
+ * finished by the attention kernel; the partial results of the others are
+ * merged by a second kernel on the same stream.
+ *
+ * Workspace sizes.  pkv_attn_decode_workspace_size_for returns exactly what
+ * attn_decode (and attn_decode_append, run_mux_round) need for this pool's
+ * KV-head count, head dim and dtype (0 for arguments those calls reject).
+ * pkv_attn_decode_workspace_size is told neither the KV-head count nor the
+ * dtype, so it returns the largest need over every supported group size
+ * (1, 2, 4, 8, 16 q-heads per KV head) and both dtypes: always enough,
+ * often more than the call uses.
  */
 size_t pkv_attn_decode_workspace_size(int32_t batch, int32_t num_q_heads, int32_t max_context_len,
                                       int32_t head_dim);
+size_t pkv_attn_decode_workspace_size_for(const pkv_pool_layer* pool, int32_t batch, int32_t num_q_heads,
+                                          int32_t max_context_len);
 int attn_decode(const pkv_pool_layer* pool, const void* q, void* out, const int32_t* block_tables,
                 int32_t bt_stride, const int32_t* context_lens, int32_t batch, int32_t max_context_len,
                 int32_t num_q_heads, float scale, void* workspace, size_t workspace_bytes,
@@ -248,10 +265,11 @@ int attn_decode(const pkv_pool_layer* pool, const void* q, void* out, const int3
  * pool as kv_write; and out[b] is attn_decode over keys [0, L), key L-1
  * taken from k_new/v_new (not read back from the pool).  Other arguments,
  * workspace size (pkv_attn_decode_workspace_size) and errors as
- * attn_decode.  A request whose context exceeds its table, or whose slot
- * L-1 lies in a block id outside the pool, has nothing written and sets
- * the error word (PKV_ERRBIT_TABLE / PKV_ERRBIT_BLOCK_ID); its output is
- * then attn_decode's (a key in a bad block is absent).  The request's
+ * attn_decode.  A request whose context exceeds max_context_len, or whose
+ * slot L-1 lies in a block id outside the pool, has nothing written and
+ * sets the error word (PKV_ERRBIT_CONTEXT / PKV_ERRBIT_BLOCK_ID); its
+ * output is then attn_decode's (the context cut to max_context_len; a key
+ * in a bad block is absent).  The request's
  * slot L-1 must not be read by any other call on another stream meanwhile.
  */
 int attn_decode_append(const pkv_pool_layer* pool, const void* q, const void* k_new, const void* v_new, void* out,
@@ -271,6 +289,20 @@ int attn_decode_append(const pkv_pool_layer* pool, const void* q, const void* k_
  * argument.
  */
 int pkv_stall_free_chunk(int32_t token_budget, int32_t num_decode, int32_t prompt_remaining);
+/*
+ * pkv_stall_free_batch - the prefill chunks of one stall-free step for
+ * several prompts ([L7] section 2.4, steps 2-4): the num_decode decoding
+ * requests take one token each first (never dropped, even past the
+ * budget); then each prompt, in the order given (the caller lists the
+ * unfinished prefills before the newly admitted requests), takes
+ * min(its remaining tokens, what is left of token_budget).
+ *   prompt_remaining  host int32 [num_prompts], each >= 0
+ *   chunks_out        host int32 [num_prompts]: the chunk of each prompt
+ * Returns the prefill tokens of the step (sum of chunks_out), or PKV_EINVAL
+ * for a negative argument or NULL array.
+ */
+int pkv_stall_free_batch(int32_t token_budget, int32_t num_decode, const int32_t* prompt_remaining,
+                         int32_t num_prompts, int32_t* chunks_out);
 /*
  * attn_mixed_batch - one layer of such a batch in a single launch: the
  * decode attention of num_decode requests (arguments as attn_decode) and
@@ -292,8 +324,8 @@ int attn_mixed_batch(const pkv_pool_layer* pool, const void* q_dec, void* out_de
                      int32_t dec_bt_stride, const int32_t* context_lens, int32_t num_decode, int32_t max_context_len,
                      const void* q_pf, void* out_pf, const int32_t* pf_block_tables, int32_t pf_bt_stride,
                      const int32_t* start_loc, const int32_t* chunk_start, int32_t num_prefill,
-                     int32_t max_chunk_len, int32_t num_q_heads, float scale, void* workspace,
-                     size_t workspace_bytes, hipStream_t stream);
+                     int32_t max_chunk_len, int32_t max_total_len, int32_t num_q_heads, float scale,
+                     void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
  * PD multiplexing on one GPU ([MUX] "SGLang's PD multiplexing").
@@ -322,6 +354,20 @@ int pkv_mux_policy_groups_grid(int total_units, int min_part, int granularity, i
                                int32_t* prefill_units, int32_t* decode_units, int32_t cap, int32_t* n);
 int pkv_mux_policy_choose(int num_groups, int decode_bs, int has_prefill, int decode_bs_divisor);
 int pkv_mux_policy_layers_per_round(int prefill_tokens, int num_layers, int token_budget);
+/* The CU masks of a split, as pkv_mux_create builds them ("Green contexts:
+ * carving out SMs for a stream" in [MUX]: a stream bound to a subset of the
+ * compute units).  MI355X sends mask bit i to CU i / 8 of XCD i % 8, so
+ * decode takes the lowest decode_cus / 8 CUs of every XCD and prefill the
+ * rest: both queues keep CUs on every XCD.  decode_cus must be a multiple
+ * of 8 with 0 < decode_cus < total_cus; writes ceil(total_cus / 32) words
+ * each.  PKV_EINVAL / PKV_EUNSUPPORTED on a bad argument. */
+int pkv_mux_policy_cu_masks(int total_cus, int decode_cus, uint32_t* prefill_words, uint32_t* decode_words,
+                            int32_t cap_words);
+/* 1 if a CU mask (bit i = CU i / 8 of XCD i % 8) keeps at least one CU on
+ * every XCD, else 0 (such a mask can never run the workgroups dispatched to
+ * the XCD it leaves empty: pkv_mux_create and run_mux_round refuse it);
+ * PKV_EINVAL on a bad argument. */
+int pkv_mux_policy_mask_ok(const uint32_t* words, int32_t nwords, int total_cus);
 
 /* Builds the CU-masked stream pairs of every level on `device`.  The total
  * CU count is the device's; cu_granularity must divide it. */
@@ -425,6 +471,17 @@ int run_mux_round(pkv_mux* mux, const pkv_decode_step* d, pkv_prefill_job* p, in
                   int32_t* prefill_done_out);
 /* Blocks until every submitted prefill layer has finished. */
 int pkv_mux_wait_prefill(pkv_mux* mux);
+
+/* The host validation run_mux_round applies to a decode step / prefill job,
+ * alone (no device work, no mux): every layer's pool valid and equal in
+ * shape to layer 0's (dtype, KV heads, head dim, block size, shards,
+ * blocks), every per-layer tensor non-NULL and 16-byte aligned, q-heads a
+ * supported multiple of the KV heads, scale finite and >= 0, the block
+ * table wide enough for max_context_len (decode) or the prompt (prefill),
+ * and the decode workspace at least the plan's size.  PKV_OK or the code
+ * run_mux_round would return. */
+int pkv_mux_check_decode_step(const pkv_decode_step* d);
+int pkv_mux_check_prefill_job(const pkv_prefill_job* p);
 
 #ifdef __cplusplus
 }

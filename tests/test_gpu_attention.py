@@ -308,3 +308,102 @@ def test_decode_append_with_a_bad_last_block():
     # only request 1's new row changed the pool
     changed = sum(int(np.count_nonzero(a != b)) for a, b in zip(after, before))
     assert 0 < changed <= 2 * hkv * d
+
+
+def _decode_with(sc, q_np, ctx, max_ctx, workspace, err=None):
+    b = len(ctx)
+    out = torch.empty((b, sc.hq, sc.d), dtype=_tdtype(sc.dtype), device="cuda")
+    ops.attn_decode(sc.pool, to_dev(q_np, sc.dtype), out, sc.bt_dev, i32(ctx), max_ctx, sc.hq, workspace=workspace)
+    torch.cuda.synchronize()
+    return inputs.as_float(from_dev(out, sc.dtype), sc.dtype)
+
+
+def test_decode_stream_split_reads_only_rows_it_wrote():
+    """Stream split with max_context_len far above every context: the batch has fewer 32-key tiles than the
+    grid has workgroups.  The workspace starts as NaN bits and is then reused for another set of contexts, so a
+    partial row that no workgroup of the current launch wrote would poison the output."""
+    lengths = [2100, 700, 33]
+    sc = Scenario(num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=16, dtype="bf16", lengths=lengths,
+                  pool_blocks=200, scale=0.5, seed=17, table_pad=120)
+    sc.write_all()
+    q = _q(sc, (3, 32, 128), scale=0.5)
+    qf = inputs.as_float(q, "bf16")
+    max_ctx = 4000
+    nbytes = ops.attn_decode_workspace_size_for(sc.pool, 3, 32, max_ctx)
+    assert nbytes > 0                                   # the stream plan (24 pairs, splits needed)
+    ws = torch.full((nbytes // 4,), 0x7FC00000, dtype=torch.int32, device="cuda").view(torch.uint8)
+    for ctx in ([100, 700, 33], [2100, 650, 20], [40, 64, 33], [2100, 700, 33]):
+        print(f"stream split contexts {ctx} max_ctx {max_ctx}", flush=True)
+        got = _decode_with(sc, q, ctx, max_ctx, ws)
+        ref = np.stack([oa.decode(qf[r], sc.kf(r)[:L], sc.vf(r)[:L]) for r, L in enumerate(ctx)])
+        assert_close(got, ref, "bf16", f"stream split, contexts {ctx}")
+
+
+@pytest.mark.parametrize("dtype,hq,hkv,lengths,max_ctx", [
+    ("bf16", 32, 8, [300, 90, 250], 200),       # stream split (24 pairs, two splits at 200)
+    ("f32", 8, 2, [300, 90, 250], 200),         # fp32 equal splits
+    ("bf16", 32, 8, [40] * 70, 32),             # 560 pairs: one workgroup per pair
+])
+def test_decode_context_above_max_is_cut_and_flagged(dtype, hq, hkv, lengths, max_ctx):
+    """A context above max_context_len attends to its first max_context_len keys in every plan, and sets the
+    context bit of the error word."""
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    d = 128
+    sc = Scenario(num_q_heads=hq, num_kv_heads=hkv, head_dim=d, block_size=16, dtype=dtype, lengths=lengths,
+                  pool_blocks=sum(-(-n // 16) for n in lengths) + 2, scale=0.5 if dtype == "bf16" else 1.0, seed=18,
+                  err_word=err)
+    sc.write_all()
+    torch.cuda.synchronize()
+    err.zero_()
+    q = _q(sc, (len(lengths), hq, d), scale=0.5 if dtype == "bf16" else 1.0)
+    qf = inputs.as_float(q, dtype)
+    ws = torch.zeros(max(16, ops.attn_decode_workspace_size_for(sc.pool, len(lengths), hq, max_ctx)),
+                     dtype=torch.uint8, device="cuda")
+    got = _decode_with(sc, q, lengths, max_ctx, ws)
+    ref = np.stack([oa.decode(qf[r], sc.kf(r)[:min(L, max_ctx)], sc.vf(r)[:min(L, max_ctx)])
+                    for r, L in enumerate(lengths)])
+    assert_close(got, ref, dtype, "contexts cut to max_context_len")
+    assert int(err.item()) & ops.ERRBIT_CONTEXT
+
+
+def test_mixed_batch_decode_context_above_max_is_cut_and_flagged():
+    """The mixed batch's decode part (equal splits) cuts and flags like attn_decode."""
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    lengths = [300, 90, 250]
+    sc = Scenario(num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=16, dtype="bf16", lengths=lengths,
+                  pool_blocks=50, scale=0.5, seed=19, err_word=err)
+    sc.write_all()
+    torch.cuda.synchronize()
+    err.zero_()
+    q = _q(sc, (3, 32, 128), scale=0.5)
+    qf = inputs.as_float(q, "bf16")
+    out = torch.empty((3, 32, 128), dtype=torch.bfloat16, device="cuda")
+    ops.attn_mixed_batch(sc.pool, to_dev(q, "bf16"), out, sc.bt_dev, i32(lengths), 200, None, None, None, None, None,
+                         0, 32)
+    torch.cuda.synchronize()
+    got = inputs.as_float(from_dev(out, "bf16"), "bf16")
+    ref = np.stack([oa.decode(qf[r], sc.kf(r)[:min(L, 200)], sc.vf(r)[:min(L, 200)]) for r, L in enumerate(lengths)])
+    assert_close(got, ref, "bf16", "mixed batch, contexts cut")
+    assert int(err.item()) & ops.ERRBIT_CONTEXT
+
+
+def test_prefill_chunk_past_max_total_len_is_cut_and_flagged():
+    """A chunk reaching past max_total_len attends to keys [0, max_total_len) only and sets the context bit."""
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    n, s0, t, cap = 400, 200, 200, 330
+    sc = Scenario(num_q_heads=16, num_kv_heads=4, head_dim=128, block_size=16, dtype="bf16", lengths=[n],
+                  pool_blocks=30, scale=0.5, seed=20, err_word=err)
+    sc.write_all()
+    torch.cuda.synchronize()
+    err.zero_()
+    qp = _q(sc, (t, 16, 128), scale=0.5)
+    out = torch.empty((t, 16, 128), dtype=torch.bfloat16, device="cuda")
+    ops.attn_prefill_chunk(sc.pool, to_dev(qp, "bf16"), out, sc.bt_dev, i32([0, t]), i32([s0]), t, 16,
+                           max_total_len=cap)
+    torch.cuda.synchronize()
+    got = inputs.as_float(from_dev(out, "bf16"), "bf16")
+    qf = inputs.as_float(qp, "bf16")
+    ref = np.stack([oa.decode(qf[i], sc.kf(0)[:min(s0 + i + 1, cap)], sc.vf(0)[:min(s0 + i + 1, cap)])
+                    for i in range(t)])
+    assert_close(got, ref, "bf16", "prefill cut at max_total_len")
+    assert int(err.item()) & ops.ERRBIT_CONTEXT

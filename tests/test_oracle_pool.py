@@ -10,6 +10,7 @@
 """
 
 import numpy as np
+import pytest
 
 from conftest import kv_fields, read_golden
 from decode_paged_kv_amd import inputs
@@ -175,3 +176,36 @@ def test_convert_to_fp8_matches_torch_cast_and_scale():
         dec = fp8.dequantize(got, scale)
         step = np.maximum(np.abs(xf) * 2.0 ** -4, 2.0 ** -10 * scale)
         assert np.all(np.abs(dec - xf) <= step * (1 + 1e-6))
+
+
+@pytest.mark.parametrize("where", ["k_row", "v_row", "k_last_dim", "v_other_shard", "unused_block"])
+def test_allocated_untouched_catches_a_stray_write(where):
+    # negative pin: one element outside the written slots changed (in K or V, any shard, any block) must make
+    # allocated_untouched say so; a version that always answers True fails here
+    pm, bt, _, _ = _filled_pool(100, 16, 4, 16, seed=4)
+    used = pool.slots_for(bt, 16, range(100))
+    assert pool.allocated_untouched(pm, 0xDEAD, used)
+    free_slots = sorted(set(range(pm.num_blocks * 16)) - set(int(s) for s in used))
+    slot = free_slots[len(free_slots) // 2]
+    blk, off = slot // 16, slot % 16
+    if where == "k_row":
+        pm.k[0][blk, 0, off, 0] = 0x1234            # K: [block][head][offset][dim]
+    elif where == "v_row":
+        pm.v[0][blk, 1, 3, off] = 0x1234            # V: [block][head][dim][offset]
+    elif where == "k_last_dim":
+        pm.k[pm.num_shards - 1][blk, -1, off, -1] = 0x1234
+    elif where == "v_other_shard":
+        pm.v[pm.num_shards - 1][blk, 0, 0, off] = 0x1234
+    else:
+        unused = [b for b in range(pm.num_blocks) if b not in set(int(x) for x in bt[:7])]
+        pm.k[0][unused[0], 0, 0, 0] = 0x1234
+    assert not pool.allocated_untouched(pm, 0xDEAD, used)
+
+
+def test_allocated_untouched_ignores_the_written_slots():
+    # the complement: changing a written slot is not a stray write
+    pm, bt, _, _ = _filled_pool(100, 16, 4, 16, seed=4)
+    used = pool.slots_for(bt, 16, range(100))
+    s = int(used[37])
+    pm.k[1][s // 16, 0, s % 16, 5] ^= 0xFFFF
+    assert pool.allocated_untouched(pm, 0xDEAD, used)
