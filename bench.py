@@ -1,10 +1,13 @@
 """Benchmark of the paged-KV hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline] [--full]
 
 Workloads (all synthetic, seeded, resident in HBM before timing):
 
-* ``llama3-8b`` (default): 32 layers of a Llama-3-8B-shaped attention
+* ``all`` (default): ``qwen3-32b`` (its prefill TFLOP/s is ``value``), then
+  ``llama3-8b``, ``relayout-70b`` and ``pdmux``, each reported under
+  ``metrics["workloads"]`` with its own value, roofline and oracle baseline.
+* ``llama3-8b``: 32 layers of a Llama-3-8B-shaped attention
   (32 q-heads / 8 KV heads, head dim 128, bf16, block size 16, pool of 8192
   blocks cut into 4 head shards).  One step = the decode step of 64
   requests at context 512 (slot mapping, then per layer kv_write of the new
@@ -235,14 +238,16 @@ def bench_llama3_8b(args):
     def prefill_attn():
         for (s, t), (sl, cs, _) in zip(chunks, ch_args):
             for l in range(L):
-                ops.attn_prefill_chunk(pools[l], q_pr[l][s:s + t], o_pr[l][s:s + t], pr_bt, sl, cs, t, hq, stream=sh)
+                ops.attn_prefill_chunk(pools[l], q_pr[l][s:s + t], o_pr[l][s:s + t], pr_bt, sl, cs, t, hq, stream=sh,
+                                       max_total_len=N)
 
     def prefill():
         for (s, t), (sl, cs, slots) in zip(chunks, ch_args):
             ops.slot_mapping(pr_bt, sl, cs, t, bs, w.pool_blocks, out=slots, stream=sh)
             for l in range(L):
                 ops.kv_write(pools[l], k_pr[l][s:s + t], v_pr[l][s:s + t], slots, stream=sh)
-                ops.attn_prefill_chunk(pools[l], q_pr[l][s:s + t], o_pr[l][s:s + t], pr_bt, sl, cs, t, hq, stream=sh)
+                ops.attn_prefill_chunk(pools[l], q_pr[l][s:s + t], o_pr[l][s:s + t], pr_bt, sl, cs, t, hq, stream=sh,
+                                       max_total_len=N)
 
     def relayout():
         for l in range(L):
@@ -294,15 +299,14 @@ def bench_llama3_8b(args):
         },
     }
     if args.cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline_decode(w)
+        result["cpu_baseline"] = cpu_baseline_decode(w, seconds=args.cpu_seconds)
     return result
 
 
-def cpu_baseline_decode(w):
+def cpu_baseline_decode(w, nreq=16, seconds=10.0):
     """The oracle's decode on a bounded sample of the same workload, timed on the host."""
     from oracle import attention as oa
     hq, hkv, d, ctx = w.num_q_heads, w.num_kv_heads, w.head_dim, w.decode_context[0]
-    nreq = 16
     g = lambda t, i: inputs.stream(w.seed, w.config_id, 0, t, i)  # noqa: E731
     ks = [inputs.as_float(inputs.normal((ctx, hkv, d), 0.5, "bf16", g(inputs.T_K, r)), "bf16") for r in range(nreq)]
     vs = [inputs.as_float(inputs.normal((ctx, hkv, d), 0.5, "bf16", g(inputs.T_V, r)), "bf16") for r in range(nreq)]
@@ -312,7 +316,7 @@ def cpu_baseline_decode(w):
     while True:
         oa.decode_batch(q, ks, vs)
         reps += 1
-        if time.perf_counter() - t0 > 10.0:
+        if time.perf_counter() - t0 > seconds:
             break
     dt = time.perf_counter() - t0
     nbytes = decode_bytes([ctx] * nreq, hkv, d, hq) * reps
@@ -373,7 +377,7 @@ def bench_qwen3_32b(args):
                     if with_write:
                         ops.kv_write(pools[l], k_pr[l][s:s + t], v_pr[l][s:s + t], slots, stream=sh)
                     ops.attn_prefill_chunk(pools[l], q_pr[l][s:s + t], o_pr[l][s:s + t], pr_bt, sl, cs, t, hq,
-                                           stream=sh)
+                                           stream=sh, max_total_len=N)
         return run
 
     pg = PhaseGraphs(stream)
@@ -423,11 +427,11 @@ def bench_qwen3_32b(args):
         },
     }
     if args.cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline_prefill(w)
+        result["cpu_baseline"] = cpu_baseline_prefill(w, seconds=max(args.cpu_seconds, 10.0))
     return result
 
 
-def cpu_baseline_prefill(w):
+def cpu_baseline_prefill(w, seconds=10.0):
     from oracle import attention as oa
     hq, hkv, d, N = w.num_q_heads, w.num_kv_heads, w.head_dim, w.prompt_len
     t, s = 512, N - 512
@@ -440,7 +444,7 @@ def cpu_baseline_prefill(w):
     while True:
         oa.prefill_chunk(q, k, v, s)
         reps += 1
-        if time.perf_counter() - t0 > 10.0:
+        if time.perf_counter() - t0 > seconds:
             break
     dt = time.perf_counter() - t0
     fl = prefill_flops(hq, d, t, s) * reps
@@ -509,7 +513,7 @@ def bench_relayout_70b(args):
     }
     result["metrics"]["layerwise_overlap"] = layerwise_overlap(w, srcs, dsts, src_bt, dst_bt, args.steps, args.warmup)
     if args.cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline_relayout(w)
+        result["cpu_baseline"] = cpu_baseline_relayout(w, seconds=args.cpu_seconds)
     return result
 
 
@@ -565,7 +569,7 @@ def layerwise_overlap(w, srcs, dsts, src_bt, dst_bt, steps, warmup):
             "relayout_hidden_frac": round((t["serial"] - t["overlap"]) / added_serial, 3) if added_serial > 0 else None}
 
 
-def cpu_baseline_relayout(w):
+def cpu_baseline_relayout(w, seconds=10.0):
     from oracle import pool as opool
     hkv, d, N = w.num_kv_heads, w.head_dim, w.prompt_len
     g = lambda tid: inputs.stream(w.seed, w.config_id, 0, tid)  # noqa: E731
@@ -580,7 +584,7 @@ def cpu_baseline_relayout(w):
         dst = opool.PoolModel(w.dst_pool_blocks, w.dst_block_size, hkv, w.dst_shards, d, np.uint16)
         opool.relayout(src, src_bt[0], dst, dst_bt[0], N)
         reps += 1
-        if time.perf_counter() - t0 > 10.0:
+        if time.perf_counter() - t0 > seconds:
             break
     dt = time.perf_counter() - t0
     return {"value": round(relayout_bytes(N, hkv, d) * reps / dt / 1e9, 4), "unit": "GB/s", "cores": 1,
@@ -748,26 +752,49 @@ def bench_pdmux(args):
         return {"median_ms": round(float(np.median(a)), 3), "p99_ms": round(float(np.percentile(a, 99)), 3),
                 "max_ms": round(float(a.max()), 3), "n": int(a.size)}
 
-    solo(max(2, args.warmup))                    # warm-up (also creates the level's streams)
+    def muxed_reps(key, min_rounds=30):
+        """Multiplexed runs of the prompt back to back until at least min_rounds decode steps are timed."""
+        ts, pfs, lv = [], [], set()
+        while len(ts) < min_rounds:
+            t, pf, levels = muxed(key)
+            ts += t
+            pfs.append(pf)
+            lv |= set(levels)
+        return ts, float(np.median(pfs)), sorted(lv)
+
+    # warm-up: code objects, the whole-device stream, and the CU-masked
+    # streams of the level the rule picks (created by one untimed
+    # multiplexed run, so no timed round pays for their creation)
+    solo(max(2, args.warmup))
     prefill_alone("16k")
-    A = solo(max(10, args.steps))
-    B16, pf16, lv16 = muxed("16k")
-    B32, pf32, lv32 = muxed("32k")
-    # the same with the decode step as a per-level HIP graph
-    mux.set_decode_graphs(True)
-    Ag = solo(max(10, args.steps))
-    B16g, pf16g, _ = muxed("16k")
-    mux.set_decode_graphs(False)
-    # the same with each decode layer as one attn_decode_append (write + attention)
-    mux.set_decode_append(True)
-    Aa = solo(max(10, args.steps))
-    B16a, pf16a, _ = muxed("16k")
-    mux.set_decode_append(False)
-    sweep = {}
-    for lvl in range(1, len(groups) - 1):
-        ts, pf, _ = muxed("16k", lvl)
-        sweep[f"{groups[lvl][0]}:{groups[lvl][1]}"] = {"decode_median_ms": round(float(np.median(ts)), 3),
-                                                        "prefill_ms": round(pf, 2)}
+    muxed("16k")
+    A = solo(max(30, args.steps))
+    B16, pf16, lv16 = muxed_reps("16k")
+    B32, pf32, lv32 = muxed_reps("32k")
+    extra = {}
+    if args.full:
+        # the same with the decode step as a per-level HIP graph
+        mux.set_decode_graphs(True)
+        Ag = solo(max(30, args.steps))
+        B16g, pf16g, _ = muxed_reps("16k")
+        mux.set_decode_graphs(False)
+        # the same with each decode layer as one attn_decode_append (write + attention)
+        mux.set_decode_append(True)
+        Aa = solo(max(30, args.steps))
+        B16a, pf16a, _ = muxed_reps("16k")
+        mux.set_decode_append(False)
+        sweep = {}
+        for lvl in range(1, len(groups) - 1):
+            ts, pf, _ = muxed("16k", lvl)
+            sweep[f"{groups[lvl][0]}:{groups[lvl][1]}"] = {"decode_median_ms": round(float(np.median(ts)), 3),
+                                                            "prefill_ms": round(pf, 2)}
+        extra = {"decode_graphs": {"solo_decode": stats(Ag), "mux_16k_decode": stats(B16g),
+                                   "mux_16k_prefill_ms": round(pf16g, 2),
+                                   "mux_over_solo_16k": round(float(np.median(B16g)) / float(np.median(Ag)), 3)},
+                 "decode_append": {"solo_decode": stats(Aa), "mux_16k_decode": stats(B16a),
+                                   "mux_16k_prefill_ms": round(pf16a, 2),
+                                   "mux_over_solo_16k": round(float(np.median(B16a)) / float(np.median(Aa)), 3)},
+                 "level_sweep_16k": sweep}
     C = {}
     for key in ("16k", "32k"):
         for c in w.chunk_sizes:
@@ -776,7 +803,7 @@ def bench_pdmux(args):
     E = {}
     for key in ("16k", "32k"):
         for budget in w.extra["stall_free_budgets"]:
-            for fused in (True, False):
+            for fused in ((True, False) if args.full else (True,)):
                 ts, tot = stall_free(key, budget, fused)
                 E[f"{key}_b{budget}_{'fused' if fused else 'two_launches'}"] = {
                     **stats(ts), "chunk": ops.stall_free_chunk(budget, B, prompts[key]), "prefill_ms": round(tot, 2)}
@@ -807,19 +834,17 @@ def bench_pdmux(args):
             "mux_32k_decode": stats(B32), "mux_32k_prefill_ms": round(pf32, 2),
             "mux_over_solo_16k": round(mux_med / solo_med, 3),
             "mux_over_solo_32k": round(float(np.median(B32)) / solo_med, 3),
-            "decode_graphs": {"solo_decode": stats(Ag), "mux_16k_decode": stats(B16g),
-                              "mux_16k_prefill_ms": round(pf16g, 2),
-                              "mux_over_solo_16k": round(float(np.median(B16g)) / float(np.median(Ag)), 3)},
-            "decode_append": {"solo_decode": stats(Aa), "mux_16k_decode": stats(B16a),
-                              "mux_16k_prefill_ms": round(pf16a, 2),
-                              "mux_over_solo_16k": round(float(np.median(B16a)) / float(np.median(Aa)), 3)},
-            "level_sweep_16k": sweep,
+            "mux_p99_over_solo_median_16k": round(float(np.percentile(B16, 99)) / solo_med, 3),
+            "mux_p99_over_solo_median_32k": round(float(np.percentile(B32, 99)) / solo_med, 3),
+            **extra,
             "chunked_whole_gpu": C,
             "stall_free_whole_gpu": E,
             "prefill_alone_ms": D,
             "decode_bytes_per_step": decode_bytes([ctx] * B, hkv, d, hq) * L,
         },
     }
+    if args.cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline_decode(w, nreq=8, seconds=args.cpu_seconds)
     return result
 
 
@@ -849,9 +874,38 @@ def bench_copy_1gib(args):
                          "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": 2 * n}}
 
 
+# ---------------------------------------------------------------- all ----
+def _free_device():
+    import gc
+    gc.collect()
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def bench_all(args):
+    """The headline workload (Qwen3-32B-like 16K prompt at chunks 2048 and 512: prefill TFLOP/s is ``value``)
+    and, under ``metrics["workloads"]``, the Llama-3-8B-shaped step (decode GB/s), the 70B relayout (GB/s) and the
+    PD-multiplexing round (decode step ms), each with its own roofline, traffic and oracle baseline.  The
+    workloads run one after the other; each frees its device memory before the next."""
+    t0 = time.perf_counter()
+    res = bench_qwen3_32b(args)
+    _free_device()
+    sub = {}
+    for name, fn in (("llama3_8b", bench_llama3_8b), ("relayout_70b", bench_relayout_70b), ("pdmux", bench_pdmux)):
+        t1 = time.perf_counter()
+        r = fn(args)
+        _free_device()
+        sub[name] = {k: r[k] for k in ("metric", "value", "unit", "higher_is_better", "ms_per_step", "config",
+                                       "roofline", "metrics", "cpu_baseline") if k in r}
+        sub[name]["wall_s"] = round(time.perf_counter() - t1, 1)
+    res["metrics"]["workloads"] = sub
+    res["metrics"]["wall_s"] = round(time.perf_counter() - t0, 1)
+    return res
+
+
 # --------------------------------------------------------------- main ----
-BENCHES = {"llama3-8b": bench_llama3_8b, "qwen3-32b": bench_qwen3_32b, "relayout-70b": bench_relayout_70b,
-           "pdmux": bench_pdmux, "copy-1gib": bench_copy_1gib}
+BENCHES = {"all": bench_all, "llama3-8b": bench_llama3_8b, "qwen3-32b": bench_qwen3_32b,
+           "relayout-70b": bench_relayout_70b, "pdmux": bench_pdmux, "copy-1gib": bench_copy_1gib}
 
 
 def main():
@@ -859,8 +913,13 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--workload", default="llama3-8b", choices=sorted(BENCHES))
+    ap.add_argument("--workload", default="all", choices=sorted(BENCHES))
     ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false")
+    ap.add_argument("--cpu-seconds", type=float, default=5.0,
+                    help="host time per oracle baseline of the secondary workloads (the headline's takes >= 10 s)")
+    ap.add_argument("--full", action="store_true",
+                    help="pdmux: also the per-level graph and append arms, the level sweep, the two-launch "
+                         "stall-free arm")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the path runs on one MI355X's share of the work (decode and prefill "
