@@ -132,6 +132,7 @@ _SIGS = {
     "run_mux_round": (C.c_int, [_P, C.POINTER(DecodeStep), C.POINTER(PrefillJob), C.POINTER(_I), C.POINTER(_I)]),
     "pkv_mux_wait_prefill": (C.c_int, [_P]),
     "pkv_stall_free_batch": (C.c_int, [_I, _I, C.POINTER(_I), _I, C.POINTER(_I)]),
+    "attn_decode_noalloc": (C.c_int, [C.POINTER(PoolLayer), _P, _P, _P, _I, _P, _I, _I, _I, C.c_float, _P]),
     "pkv_mux_check_decode_step": (C.c_int, [C.POINTER(DecodeStep)]),
     "pkv_mux_check_prefill_job": (C.c_int, [C.POINTER(PrefillJob)]),
     "pkv_mux_policy_cu_masks": (C.c_int, [C.c_int, C.c_int, C.POINTER(C.c_uint32), C.POINTER(C.c_uint32), _I]),

@@ -199,6 +199,16 @@ def attn_decode(pool: PagedPool, q, out, block_tables, context_lens, max_context
     _lib.check(rc, "attn_decode")
 
 
+def attn_decode_noalloc(pool: PagedPool, q, out, block_tables, context_lens, max_context_len: int, num_q_heads: int,
+                        scale: float = 0.0, stream=None):
+    """attn_decode with the split partials in the library's fixed device scratch (no workspace, no allocation)."""
+    lib = _lib.load()
+    rc = lib.attn_decode_noalloc(C.byref(pool.c()), _ptr(q), _ptr(out), _ptr(block_tables), block_tables.shape[-1],
+                                 _ptr(context_lens), context_lens.numel(), max_context_len, num_q_heads, scale,
+                                 _stream(stream))
+    _lib.check(rc, "attn_decode_noalloc")
+
+
 def attn_decode_append(pool: PagedPool, q, k_new, v_new, out, block_tables, context_lens, max_context_len: int,
                        num_q_heads: int, scale: float = 0.0, workspace=None, stream=None):
     """kv_write of each request's new row at position L-1 and attn_decode over [0, L), in one launch."""

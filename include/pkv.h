@@ -254,6 +254,26 @@ int attn_decode(const pkv_pool_layer* pool, const void* q, void* out, const int3
                 hipStream_t stream);
 
 /*
+ * attn_decode_noalloc - attn_decode for callers that cannot allocate memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same kernels and results as attn_decode, with the
+ * split-KV partial results in a fixed device array of the library instead
+ * of a caller workspace.  It calls no allocating routine.
+ * Arguments, layouts and errors as attn_decode, without the workspace.  The
+ * array holds PKV_DECODE_NOALLOC_SCRATCH_BYTES (16 MiB); a call whose split
+ * plan needs more (pkv_attn_decode_workspace_size_for) returns PKV_ERANGE
+ * before any HIP call.  Each GPU holds its own copy of the array from the
+ * first call on it until the process ends.  Every call on one GPU uses that
+ * same array: calls that can overlap on one GPU (on other streams, or graph
+ * replays beside other work) race and must not be issued; calls ordered on
+ * one stream are safe (no state is kept from one call to the next).
+ */
+#define PKV_DECODE_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+int attn_decode_noalloc(const pkv_pool_layer* pool, const void* q, void* out, const int32_t* block_tables,
+                        int32_t bt_stride, const int32_t* context_lens, int32_t batch, int32_t max_context_len,
+                        int32_t num_q_heads, float scale, hipStream_t stream);
+
+/*
  * attn_decode_append - one decode step's K/V append and attention, in one
  * launch for batches with a workgroup per (request, KV head) pair (with the
  * stream split used for fewer pairs, a small kernel writes the rows first).  [DISAGG] "实现" (a decode step writes the new token's K/V at the
