@@ -115,11 +115,9 @@ kv_relayout_kernel(PoolDev src, const int32_t* __restrict__ src_bt, PoolDev dst,
   const int bsd = dst.block_size, bss = src.block_size;
   const int p0 = j * bsd;
   const int valid = min(bsd, n_tokens - p0);     // tokens of this block that exist
+  // the destination and source block ids are read together (the source
+  // ids do not wait for the destination id's check)
   const int dblk = dst_bt[j];
-  if (dblk < 0 || dblk >= dst.num_blocks) {
-    if (threadIdx.x == 0) flag_error(dst.err, PKV_ERRBIT_BLOCK_ID);
-    return;
-  }
   const int first = p0 >> src.bs_shift;
   const int nsrc = ((p0 + valid - 1) >> src.bs_shift) - first + 1;
   if ((int)threadIdx.x < nsrc) {
@@ -129,6 +127,10 @@ kv_relayout_kernel(PoolDev src, const int32_t* __restrict__ src_bt, PoolDev dst,
       b = -1;
     }
     sblk[threadIdx.x] = b;
+  }
+  if (dblk < 0 || dblk >= dst.num_blocks) {
+    if (threadIdx.x == 0) flag_error(dst.err, PKV_ERRBIT_BLOCK_ID);
+    return;
   }
   __syncthreads();
   const int dsh = h / dst.heads_per_shard, dlh = h - dsh * dst.heads_per_shard;
@@ -272,11 +274,9 @@ kv_relayout_convert_kernel(PoolDev src, const int32_t* __restrict__ src_bt, Conv
   const int bsd = dst.block_size, bss = src.block_size;
   const int p0 = j * bsd;
   const int valid = min(bsd, n_tokens - p0);
+  // the destination and source block ids are read together (the source
+  // ids do not wait for the destination id's check)
   const int dblk = dst_bt[j];
-  if (dblk < 0 || dblk >= dst.num_blocks) {
-    if (threadIdx.x == 0) flag_error(dst.err, PKV_ERRBIT_BLOCK_ID);
-    return;
-  }
   const int first = p0 >> src.bs_shift;
   const int nsrc = ((p0 + valid - 1) >> src.bs_shift) - first + 1;
   if ((int)threadIdx.x < nsrc) {
@@ -286,6 +286,10 @@ kv_relayout_convert_kernel(PoolDev src, const int32_t* __restrict__ src_bt, Conv
       b = -1;
     }
     sblk[threadIdx.x] = b;
+  }
+  if (dblk < 0 || dblk >= dst.num_blocks) {
+    if (threadIdx.x == 0) flag_error(dst.err, PKV_ERRBIT_BLOCK_ID);
+    return;
   }
   __syncthreads();
   const int hsd = dst.heads_per_shard;

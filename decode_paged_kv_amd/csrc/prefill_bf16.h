@@ -3,6 +3,8 @@
 // top of attn_prefill.hip.
 #pragma once
 
+#include <type_traits>
+
 #include "pkv_internal.h"
 
 namespace pkv {
@@ -21,6 +23,20 @@ __device__ __forceinline__ f32x16_t mfma32(const uint4& a, const uint4& b, f32x1
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
                                                  0, 0, 0);
 }
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ f32x4_t mfma16x32(const uint4& a, const uint4& b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
+                                                 0, 0, 0);
+}
+
+// Q scaled by scale * log2(e) once, at load: bf16 products rounded to bf16.
+__device__ __forceinline__ uint4 scale_bf16x8(uint4 v, float c) {
+  uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) w[i] = pack_bf16x2(bf16_lo(w[i]) * c, bf16_hi(w[i]) * c);
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+__device__ __forceinline__ float round_bf16(float x) { return bf16_to_f32(f32_to_bf16(x)); }
 
 // Row of the 32-key half tile that lane row m of the S^T MFMA's A operand
 // holds: chosen so that accumulator registers 8s..8s+7 of a lane in half
@@ -167,7 +183,10 @@ __device__ __forceinline__ void prefill_bf16_block(PoolDev pool, const bf16_t* _
     const bool ok = qrel < T;
     const bf16_t* qrow = q + ((size_t)(q0 + (ok ? qrel : 0)) * num_q_heads + h) * D + 8 * half;
 #pragma unroll
-    for (int s = 0; s < C::KS; ++s) qf[s] = ok ? *reinterpret_cast<const uint4*>(qrow + 16 * s) : make_uint4(0, 0, 0, 0);
+    for (int s = 0; s < C::KS; ++s) {
+      qf[s] = ok ? *reinterpret_cast<const uint4*>(qrow + 16 * s) : make_uint4(0, 0, 0, 0);
+      qf[s] = scale_bf16x8(qf[s], scale_log2);
+    }
   }
   const int wave_first_q = min(S + qt * C::BM + wave * 32, kv_len - 1);
 
@@ -301,11 +320,29 @@ __device__ __forceinline__ void prefill_bf16_block(PoolDev pool, const bf16_t* _
   f32x16_t o[C::DT];
 #pragma unroll
   for (int t = 0; t < C::DT; ++t) o[t] = f32x16_t{};
-  // running max (log2 units): finite start, so a tile whose keys are all
-  // masked or absent gives p = exp2(-inf) = 0 rather than exp2(-inf + inf)
-  float m = -1e30f, lsum = 0.f;
+  // Softmax state, in log2 units.  Q carries scale * log2(e), and the S
+  // MFMA chain subtracts the running max m itself: its first MFMA per
+  // 32-key half multiplies a constant A (1.0 in head-dim slot 0 of every
+  // key row: aones) by B = -m (bf16, slot 0 of the lane's query: mq), so
+  // the accumulator starts at -m and p = exp2(S) needs no multiply-add.  m
+  // is kept bf16-representable, so the MFMA subtracts exactly the m used
+  // in every rescale.  It is 0 until the first tile with a valid key sets
+  // it (mset).
+  float m = 0.f;
+  bool mset = false;
+  const uint4 aones = make_uint4(half == 0 ? 0x3F80u : 0u, 0u, 0u, 0u);
+  uint4 mq = make_uint4(0u, 0u, 0u, 0u);
+  // Row sums of P on the matrix cores: one 16x16x32 MFMA per 16 keys whose
+  // B operand is the P register quad as laid out for the 32x32x16 product
+  // (lane l: query l%32, keys 8(l/32)..+7) and whose constant A has row 0
+  // selecting the lanes of queries 0..15 (lanes 0, 32: K groups 0, 2) and
+  // row 1 those of queries 16..31 (lanes 17, 49: K groups 1, 3); so lanes
+  // 0..15 accumulate the sums of queries lane (rs[0]) and lane + 16 (rs[1]).
+  f32x4_t rs = f32x4_t{};
+  const uint32_t ones_row = (lane == 0 || lane == 32 || lane == 17 || lane == 49) ? 0x3F803F80u : 0u;
+  const uint4 arow = make_uint4(ones_row, ones_row, ones_row, ones_row);
 
-  // row max of a score tile over both lane halves, in log2 units
+  // row max of a score tile over both lane halves
   auto rowmax = [&](const f32x16x2& st) -> float {
     float mx = -INFINITY;
 #pragma unroll
@@ -313,8 +350,9 @@ __device__ __forceinline__ void prefill_bf16_block(PoolDev pool, const bf16_t* _
 #pragma unroll
       for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(st.v[i][r], st.v[i][r + 1]));
     auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-    return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * scale_log2;
+    return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
   };
+  // the first tile's S (m = 0 then, so no -m term)
   auto qk = [&](const char* kbuf) -> f32x16x2 {
     f32x16x2 st;
     uint4 kf[2][C::KS];
@@ -365,25 +403,35 @@ __device__ __forceinline__ void prefill_bf16_block(PoolDev pool, const bf16_t* _
   // A step of this group on key tile kt has three phases:
   //  * stats(kt): softmax statistics of S(kt) in registers: masks for
   //    causality (tiles reaching past this wave's first query) and for
-  //    absent groups, the row max, the rare rescale of O;
+  //    absent groups, the row max, the rare move of m with the rescale of O
+  //    and the row sums (the tile's scores then shifted by the same amount);
   //  * sync(kt): K(kt+NG) and V(kt) have arrived (this wave's loads, one
   //    step old); after the workgroup barrier every wave is past step
   //    kt-NG, so K(kt)'s buffer (kcur) and the buffer of V(kt-NG) (vnext)
   //    take the loads of K(kt+2NG) and V(kt+NG);
-  //  * block(kt): S(kt+NG) = K Q^T into stn with the exponentials of P(kt)
-  //    between its MFMAs, each quarter of P followed by its O^T += V^T P^T
-  //    MFMAs, in an order fixed by scheduling fences, every LDS fragment read
-  //    a few MFMAs before its use, at raised wave priority so that the
-  //    matrix cores go to the wave that has work for them.
+  //  * block(kt): S(kt+NG) = K Q^T - m into stn with the exponentials of
+  //    P(kt) between its MFMAs, each quarter of P followed by its
+  //    O^T += V^T P^T and row-sum MFMAs, in an order fixed by scheduling
+  //    fences, every LDS fragment read a few MFMAs before its use, at raised
+  //    wave priority so that the matrix cores go to the wave that has work
+  //    for them.
   // Group 0 runs sync, block, stats of the next tile; group 1 (NG = 2) runs
   // sync, stats, block, so that between two barriers one group's softmax
   // work overlaps the other's MFMAs.  A step past the group's last tile only
   // keeps the barrier count equal across the groups.
+  // O and the row sums times alpha (this lane's query)
+  auto rescale = [&](float alpha) {
+    const float a0 = __shfl(alpha, lane & 15), a1 = __shfl(alpha, (lane & 15) + 16);
+    rs[0] *= a0;
+    rs[1] *= a1;
+#pragma unroll
+    for (int t = 0; t < C::DT; ++t) o[t] *= alpha;
+  };
   auto stats = [&](int kt, f32x16x2& st, uint32_t absent, float mx_block) {
     if (kt >= nkt) return;
     bool masked = false;
     const int kbase = kt * C::BN;
-    if (kbase + C::BN - 1 > wave_first_q) {
+    if (kbase + C::BN - 1 > wave_first_q) {                    // wave-uniform
       // an opaque copy keeps the compares inside this branch (hoisted, they
       // would run on every tile)
       int d;
@@ -395,7 +443,7 @@ __device__ __forceinline__ void prefill_bf16_block(PoolDev pool, const bf16_t* _
           if (32 * i + 16 * (r >> 3) + (r & 7) > d) st.v[i][r] = -INFINITY;
       masked = true;
     }
-    if (absent) {
+    if (absent) {                                               // wave-uniform, rare
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -405,15 +453,19 @@ __device__ __forceinline__ void prefill_bf16_block(PoolDev pool, const bf16_t* _
     }
     // the block that computed S took its max; a masked tile takes it again
     const float mx = masked ? rowmax(st) : mx_block;
-    // move the running max only when this tile exceeds it by the slack
-    const bool grow = mx > m + kRescaleSlack;
+    // S already has m subtracted: move m when this tile exceeds it by the
+    // slack, or to the first finite tile max of the row
+    const bool grow = mset ? mx > kRescaleSlack : mx > -INFINITY;
     if (__builtin_amdgcn_ballot_w64(grow)) {                    // wave-uniform, rare
-      const float mnew = grow ? mx : m;
-      const float alpha = __builtin_amdgcn_exp2f(m - mnew);    // 0 on the first growth
-      m = mnew;
-      lsum *= alpha;
+      const float delta = grow ? round_bf16(m + mx) - m : 0.f;
+      m += delta;
+      mset = mset || grow;
+      mq.x = half == 0 ? (uint32_t)f32_to_bf16(-m) : 0u;
 #pragma unroll
-      for (int t = 0; t < C::DT; ++t) o[t] *= alpha;
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) st.v[i][r] -= delta;
+      rescale(__builtin_amdgcn_exp2f(-delta));
     }
   };
   uint32_t absent_after = 0;
@@ -459,7 +511,6 @@ __device__ __forceinline__ void prefill_bf16_block(PoolDev pool, const bf16_t* _
 #pragma unroll
     for (int s = 0; s < R; ++s) fr[s] = frag(s);
     uint32_t pw[4][4];                                          // P in bf16 pairs, by quarter
-    float psum[2] = {-0.f, -0.f};                               // x + -0 folds to x
     float mh[2] = {-INFINITY, -INFINITY};
     __builtin_amdgcn_s_setprio(1);
     __builtin_amdgcn_sched_barrier(0);
@@ -468,25 +519,23 @@ __device__ __forceinline__ void prefill_bf16_block(PoolDev pool, const bf16_t* _
       const int g = BP::group_of(s), j = s - BP::gstart(g), c = BP::gq(g);
       if (BP::gtype(g) == 0) {
         const int qi = c * BP::QPG + j, hs = qi / C::KS, ks = qi % C::KS;
-        stn.v[hs] = mfma32(fr[s % R], qf[ks], ks == 0 ? f32x16_t{} : stn.v[hs]);
+        if (ks == 0) stn.v[hs] = mfma32(aones, mq, f32x16_t{});   // the -m term
+        stn.v[hs] = mfma32(fr[s % R], qf[ks], stn.v[hs]);
       } else {
-        o[j] = mfma32(fr[s % R], make_uint4(pw[c][0], pw[c][1], pw[c][2], pw[c][3]), o[j]);
+        const uint4 pc = make_uint4(pw[c][0], pw[c][1], pw[c][2], pw[c][3]);
+        o[j] = mfma32(fr[s % R], pc, o[j]);
+        if (j == 0) rs = mfma16x32(arow, pc, rs);                 // row sums of this quarter
       }
       if (s + R < BP::NS) fr[s % R] = frag(s + R);
-      // the pairs of P placed in this slot: p = 2^(s*scale - m), in bf16
-      // for the MFMA; the row sum adds p in fp32 (plain adds: a v_dot2 of
-      // the rounded pairs stalls next to the MFMAs), which differs from the
-      // sum of the rounded values by unbiased rounding noise only
+      // the pairs of P placed in this slot: p = 2^S in bf16 for the MFMAs
 #pragma unroll
       for (int pj = 0; pj < 16; ++pj) {
         if (BP::pair_slot(pj) != s) continue;
         const int pc = pj >> 2, w = pj & 3;
         const int i = pc >> 1, r = 8 * (pc & 1) + 2 * w;
-        const float p0 = __builtin_amdgcn_exp2f(fmaf(st.v[i][r], scale_log2, -m));
-        const float p1 = __builtin_amdgcn_exp2f(fmaf(st.v[i][r + 1], scale_log2, -m));
+        const float p0 = __builtin_amdgcn_exp2f(st.v[i][r]);
+        const float p1 = __builtin_amdgcn_exp2f(st.v[i][r + 1]);
         pw[pc][w] = pack_bf16x2(p0, p1);
-        psum[0] += p0;
-        psum[1] += p1;
       }
       // the row max of S(kt+NG), a few registers per slot once each half
       // is complete
@@ -498,10 +547,9 @@ __device__ __forceinline__ void prefill_bf16_block(PoolDev pool, const bf16_t* _
       __builtin_amdgcn_sched_barrier(0);
     }
     __builtin_amdgcn_s_setprio(0);
-    lsum += psum[0] + psum[1];
     float mx = fmaxf(mh[0], mh[1]);
     auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-    mx_stn = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * scale_log2;
+    mx_stn = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
   };
 
   // every group takes the same number of steps (one barrier each); st is
@@ -524,6 +572,15 @@ __device__ __forceinline__ void prefill_bf16_block(PoolDev pool, const bf16_t* _
     if (u + 1 < nsteps) step(grp + NG * (u + 1), k1b, k0b, v1b, v0b, sb, sa, mxb, mxa);
   }
 
+  // the row sum of this lane's query over all keys of this group
+  float ltot;
+  {
+    const int qq = lane & 31;
+    const float t0 = __shfl(rs[0], qq & 15), t1 = __shfl(rs[1], qq & 15);
+    ltot = qq < 16 ? t0 : t1;
+  }
+  // a row that never saw a valid key contributes nothing to the merge
+  if (!mset) m = -1e30f;
   if constexpr (NG == 2) {
     // ---- merge group 1's (m, l, O) into group 0's, lane by lane (both
     // groups hold the same queries in the same layout) ----
@@ -536,14 +593,14 @@ __device__ __forceinline__ void prefill_bf16_block(PoolDev pool, const bf16_t* _
 #pragma unroll
         for (int r = 0; r < 16; ++r) ox[(16 * t + r) * 64 + lane] = o[t][r];
       mlx[lane] = m;
-      mlx[64 + lane] = lsum;
+      mlx[64 + lane] = ltot;
     }
     __syncthreads();
     if (grp == 1) return;
     const float m1 = mlx[lane], l1 = mlx[64 + lane];
     const float mn = fmaxf(m, m1);
     const float a0 = __builtin_amdgcn_exp2f(m - mn), a1 = __builtin_amdgcn_exp2f(m1 - mn);
-    lsum = lsum * a0 + l1 * a1;
+    ltot = ltot * a0 + l1 * a1;
 #pragma unroll
     for (int t = 0; t < C::DT; ++t)
 #pragma unroll
@@ -551,7 +608,6 @@ __device__ __forceinline__ void prefill_bf16_block(PoolDev pool, const bf16_t* _
   }
 
   // ---- normalise and store: lane holds dims 32t + 8a + 4*half + 0..3 of its query ----
-  const float ltot = lsum + __shfl_xor(lsum, 32);
   if (qrel < T) {
     const float inv = 1.f / ltot;
     bf16_t* orow = out + ((size_t)(q0 + qrel) * num_q_heads + h) * D;
