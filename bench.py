@@ -29,6 +29,9 @@ Workloads (all synthetic, seeded, resident in HBM before timing):
   the multiplexed decode step in ms.
 * ``copy-1gib``: a plain 1 GiB device copy, the known-size kernel that
   calibrates the FETCH_SIZE / WRITE_SIZE counters behind ``traffic``.
+* ``mfma-peak``: the device's dense bf16 matrix-core rate (four independent
+  MFMA chains per wave, two waves per SIMD) and the shader clock the waves
+  ran at, measured on the box the other workloads run on.
 
 One JSON line is printed.  Kernel times come from HIP events recorded on
 the stream the kernels are launched on.
@@ -86,15 +89,15 @@ PMC_SCALE = {"fetch": 2.0, "write": 1.0}
 TRAFFIC = {
     "attn_decode": {"sources": ['decode_paged_kv_amd/csrc/attn_decode.hip', 'decode_paged_kv_amd/csrc/decode_bf16.h',
                                 'decode_paged_kv_amd/csrc/pkv_internal.h'],
-                    "sha256": "4afa4231b115841ce0dcf336c45d405e17699366f0c46e94e77096b308556496",
-                    "fetch_kib": 65952.84, "write_kib": 512.00},
+                    "sha256": "9b697f3e299766e4b28f331019815c0dc4c129536f6980b37a5d7ba24efc99f0",
+                    "fetch_kib": 65955.01, "write_kib": 512.00},
     "attn_prefill_chunk": {"sources": ['decode_paged_kv_amd/csrc/attn_prefill.hip', 'decode_paged_kv_amd/csrc/prefill_bf16.h',
                                        'decode_paged_kv_amd/csrc/pkv_internal.h'],
-                           "sha256": "00668a9501a32c3151cfe4d74c5d455a596e0a36c3cdd58a4eeb6b8854c4fda5",
-                           "fetch_kib": 27183.54, "write_kib": 13107.55},
+                           "sha256": "1d5796c6b9bc8b16893ea75fed87cf42d222b90e74a0165f1d68d3eb2c42a756",
+                           "fetch_kib": 28005.16, "write_kib": 15974.11},
     "kv_relayout": {"sources": ['decode_paged_kv_amd/csrc/kv_ops.hip', 'decode_paged_kv_amd/csrc/pkv_internal.h'],
-                    "sha256": "cc536ff9f8cbf3ab2dbde48e081d02e1ebd8200669e82b0ee4e66cb6d1940da6",
-                    "fetch_kib": 8234.20, "write_kib": 16390.35},
+                    "sha256": "5545d74d4886e161295a0ab8da04d5c32eec5610e2dc05e0bbbf64e4726c0377",
+                    "fetch_kib": 8233.78, "write_kib": 16386.02},
 }
 
 
@@ -874,6 +877,62 @@ def bench_copy_1gib(args):
                          "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": 2 * n}}
 
 
+# ------------------------------------------------------- mfma-peak ----
+def bench_mfma_peak(args):
+    """The device's dense bf16 matrix-core rate and its shader clock while the matrix cores are busy: 512
+    workgroups of 4 waves (two per CU, two waves per SIMD), each wave running four independent chains of
+    32x32x16 bf16 MFMAs, timed with HIP events on the launching stream; every wave also reads the shader clock
+    counter and the 100 MHz reference counter around its loop (kernel in decode_paged_kv_amd/calib)."""
+    import ctypes as C
+    from decode_paged_kv_amd import build as b
+    if not os.path.exists(b.CALIB_LIB):
+        raise RuntimeError(f"{b.CALIB_LIB} is not built (python -m decode_paged_kv_amd.build)")
+    lib = C.CDLL(b.CALIB_LIB)
+    lib.pkv_calib_mfma.restype = C.c_int
+    lib.pkv_calib_mfma.argtypes = [C.c_int, C.c_int, C.c_void_p, C.c_void_p, C.c_void_p]
+    blocks, iters = 512, 4096
+    sink = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    clocks = torch.zeros(blocks * 4 * 2, dtype=torch.int64, device="cuda")
+    stream = torch.cuda.Stream()
+
+    def launch():
+        rc = lib.pkv_calib_mfma(iters, blocks, sink.data_ptr(), clocks.data_ptr(), stream.cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"pkv_calib_mfma: HIP error {rc}")
+
+    for _ in range(max(1, args.warmup)):
+        launch()
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(max(3, args.steps)):
+        a, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        launch()
+        e.record(stream)
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(e))
+    ms = float(np.median(times))
+    flops = blocks * 4 * iters * 4 * 32 * 32 * 16 * 2
+    tflops = flops / (ms * 1e-3) / 1e12
+    ck = clocks.view(-1, 2).cpu().numpy().astype(np.float64)
+    ghz = ck[:, 0] / (ck[:, 1] / 100e6) / 1e9
+    clk = float(np.median(ghz))
+    # the rate the same MFMA stream would reach at the nominal 2.4 GHz, and the peak at the measured clock
+    peak_at_clock = BF16_PEAK_TFLOPS * clk / 2.4
+    return {"metric": "dense bf16 MFMA TFLOP/s (calibration)", "value": round(tflops, 1), "unit": "TFLOP/s",
+            "n_gpus": 1, "steps": len(times), "warmup": args.warmup, "ms_per_step": round(ms, 4),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": "mfma-peak: 512 workgroups x 4 waves, 4 independent chains of "
+                                   "v_mfma_f32_32x32x16_bf16 per wave, 4096 rounds"},
+            "roofline": {"kernel": "mfma_chain_kernel", "bound": "mfma", "achieved": round(tflops, 1),
+                         "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tflops / BF16_PEAK_TFLOPS, 4),
+                         "traffic": None},
+            "metrics": {"shader_clock_ghz_median": round(clk, 3), "shader_clock_ghz_min": round(float(ghz.min()), 3),
+                        "shader_clock_ghz_max": round(float(ghz.max()), 3),
+                        "peak_at_measured_clock_tflops": round(peak_at_clock, 1),
+                        "frac_of_peak_at_measured_clock": round(tflops / peak_at_clock, 4)}}
+
+
 # ---------------------------------------------------------------- all ----
 def _free_device():
     import gc
@@ -905,7 +964,8 @@ def bench_all(args):
 
 # --------------------------------------------------------------- main ----
 BENCHES = {"all": bench_all, "llama3-8b": bench_llama3_8b, "qwen3-32b": bench_qwen3_32b,
-           "relayout-70b": bench_relayout_70b, "pdmux": bench_pdmux, "copy-1gib": bench_copy_1gib}
+           "relayout-70b": bench_relayout_70b, "pdmux": bench_pdmux, "copy-1gib": bench_copy_1gib,
+           "mfma-peak": bench_mfma_peak}
 
 
 def main():

@@ -15,8 +15,11 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
+CALIB = os.path.join(HERE, "calib")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libpkv.so")
+# the benchmark's calibration kernels (matrix-core rate and shader clock); not part of libpkv
+CALIB_LIB = os.path.join(HERE, "libpkv_calib.so")
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
@@ -66,7 +69,22 @@ def build(verbose: bool = False, extra_flags: list[str] | None = None) -> str:
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB} from {len(srcs)} sources")
+    build_calib(extra)
     return LIB
+
+
+def build_calib(extra: list[str] | None = None) -> str:
+    """Compile the calibration kernels into libpkv_calib.so."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    srcs = sorted(os.path.join(CALIB, f) for f in os.listdir(CALIB) if f.endswith(".hip"))
+    objs = [_compile(src, list(extra or [])) for src in srcs]
+    tmp = CALIB_LIB + ".tmp"
+    res = subprocess.run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp],
+                         capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"link failed:\n{res.stderr}")
+    os.replace(tmp, CALIB_LIB)
+    return CALIB_LIB
 
 
 if __name__ == "__main__":
