@@ -32,6 +32,9 @@ Workloads (all synthetic, seeded, resident in HBM before timing):
 * ``mfma-peak``: the device's dense bf16 matrix-core rate (four independent
   MFMA chains per wave, two waves per SIMD) and the shader clock the waves
   ran at, measured on the box the other workloads run on.
+* ``hbm-ceiling``: what HBM delivers to decode's permuted 4 KiB tile reads
+  and to the relayout's permuted tile copies at those kernels' launch sizes
+  (see ``bench_hbm_ceiling``).
 
 One JSON line is printed.  Kernel times come from HIP events recorded on
 the stream the kernels are launched on.
@@ -883,13 +886,7 @@ def bench_mfma_peak(args):
     workgroups of 4 waves (two per CU, two waves per SIMD), each wave running four independent chains of
     32x32x16 bf16 MFMAs, timed with HIP events on the launching stream; every wave also reads the shader clock
     counter and the 100 MHz reference counter around its loop (kernel in decode_paged_kv_amd/calib)."""
-    import ctypes as C
-    from decode_paged_kv_amd import build as b
-    if not os.path.exists(b.CALIB_LIB):
-        raise RuntimeError(f"{b.CALIB_LIB} is not built (python -m decode_paged_kv_amd.build)")
-    lib = C.CDLL(b.CALIB_LIB)
-    lib.pkv_calib_mfma.restype = C.c_int
-    lib.pkv_calib_mfma.argtypes = [C.c_int, C.c_int, C.c_void_p, C.c_void_p, C.c_void_p]
+    lib = _calib_lib()
     blocks, iters = 512, 4096
     sink = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
     clocks = torch.zeros(blocks * 4 * 2, dtype=torch.int64, device="cuda")
@@ -933,6 +930,121 @@ def bench_mfma_peak(args):
                         "frac_of_peak_at_measured_clock": round(tflops / peak_at_clock, 4)}}
 
 
+# ----------------------------------------------------- hbm-ceiling ----
+def _calib_lib():
+    import ctypes as C
+    from decode_paged_kv_amd import build as b
+    if not os.path.exists(b.CALIB_LIB):
+        raise RuntimeError(f"{b.CALIB_LIB} is not built (python -m decode_paged_kv_amd.build)")
+    lib = C.CDLL(b.CALIB_LIB)
+    lib.pkv_calib_mfma.restype = C.c_int
+    lib.pkv_calib_mfma.argtypes = [C.c_int, C.c_int, C.c_void_p, C.c_void_p, C.c_void_p]
+    lib.pkv_calib_tiled_read.restype = C.c_int
+    lib.pkv_calib_tiled_read.argtypes = [C.c_void_p, C.c_void_p, C.c_int, C.c_int, C.c_int, C.c_void_p, C.c_void_p]
+    lib.pkv_calib_tiled_copy.restype = C.c_int
+    lib.pkv_calib_tiled_copy.argtypes = [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_int, C.c_int, C.c_int,
+                                         C.c_void_p]
+    lib.pkv_calib_copy.restype = C.c_int
+    lib.pkv_calib_copy.argtypes = [C.c_void_p, C.c_void_p, C.c_size_t, C.c_int, C.c_void_p]
+    return lib
+
+
+def bench_hbm_ceiling(args):
+    """What HBM delivers to the library's own access patterns, measured like the kernels they bound (HIP graph
+    of back-to-back launches, HIP events on the replaying stream; kernels in decode_paged_kv_amd/calib):
+
+    * decode's reads: 512 workgroups, each reading the 64 permuted 4 KiB tiles of one (request, KV head) pair
+      (the Llama-3-8B-shaped decode launch: 134,217,728 B), 32 launches over 32 pools; and 150 tiles per
+      workgroup (314,572,800 B, the size of the Qwen3-32B-like decode launch), 16 launches over 16 pools;
+    * the relayout's copies: 80 layers of 4096 permuted 4 KiB source tiles (16.8 MB) to permuted destination
+      tiles, 1024 workgroups of 4 tiles (all loads before the stores, as kv_relayout), and a contiguous copy of
+      the same bytes.
+
+    ``value`` is the decode-shaped read rate (best of the unroll depths tried)."""
+    lib = _calib_lib()
+    stream = torch.cuda.Stream()
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(0)
+    res = {}
+
+    def timed(name, launch, n_launch, nbytes, reps):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(stream):
+            launch()
+        stream.synchronize()
+        with torch.cuda.graph(g, stream=stream):
+            launch()
+        for _ in range(max(1, args.warmup)):
+            with torch.cuda.stream(stream):
+                g.replay()
+        stream.synchronize()
+        ts = []
+        for _ in range(reps):
+            a, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            with torch.cuda.stream(stream):
+                a.record(stream)
+                g.replay()
+                e.record(stream)
+            stream.synchronize()
+            ts.append(a.elapsed_time(e))
+        us = float(np.median(ts)) * 1e3 / n_launch
+        res[name] = {"us_per_launch": round(us, 3), "gbps": round(nbytes / (us * 1e-6) / 1e9, 1)}
+        del g
+
+    def check(rc, what):
+        if rc != 0:
+            raise RuntimeError(f"{what}: HIP error {rc}")
+
+    reps = max(3, args.steps)
+    # decode-shaped reads
+    for label, tpw, nl in (("read_134mb", 64, 32), ("read_315mb", 150, 16)):
+        wgs = 512
+        ntile = wgs * tpw
+        pools = [torch.empty(ntile * 4096, dtype=torch.uint8, device="cuda") for _ in range(nl)]
+        ids = [torch.randperm(ntile, generator=gen, device="cuda").to(torch.int32) for _ in range(nl)]
+        sink = torch.empty(wgs * 256, dtype=torch.int32, device="cuda")
+        for u in (4, 8, 16):
+            def launch(u=u):
+                for l in range(nl):
+                    check(lib.pkv_calib_tiled_read(pools[l].data_ptr(), ids[l].data_ptr(), wgs, tpw, u,
+                                                   sink.data_ptr(), stream.cuda_stream), "pkv_calib_tiled_read")
+            timed(f"{label}_unroll{u}", launch, nl, ntile * 4096, reps)
+        del pools, ids, sink
+        _free_device()
+    # relayout-shaped copies: 80 layers of 16.8 MB read + 16.8 MB written
+    L, ntile = 80, 4096
+    src = [torch.empty(ntile * 4096, dtype=torch.uint8, device="cuda") for _ in range(L)]
+    dst = [torch.empty(ntile * 4096, dtype=torch.uint8, device="cuda") for _ in range(L)]
+    sids = [torch.randperm(ntile, generator=gen, device="cuda").to(torch.int32) for _ in range(L)]
+    dids = [torch.randperm(ntile, generator=gen, device="cuda").to(torch.int32) for _ in range(L)]
+    for u in (2, 4):
+        def launch(u=u):
+            for l in range(L):
+                check(lib.pkv_calib_tiled_copy(src[l].data_ptr(), sids[l].data_ptr(), dst[l].data_ptr(),
+                                               dids[l].data_ptr(), 1024, 4, u, stream.cuda_stream),
+                      "pkv_calib_tiled_copy")
+        timed(f"copy_tiled_16.8mb_unroll{u}", launch, L, 2 * ntile * 4096, reps)
+    for wgs in (1024, 2048):
+        def launch(wgs=wgs):
+            for l in range(L):
+                check(lib.pkv_calib_copy(src[l].data_ptr(), dst[l].data_ptr(), ntile * 4096, wgs, stream.cuda_stream),
+                      "pkv_calib_copy")
+        timed(f"copy_contiguous_16.8mb_wgs{wgs}", launch, L, 2 * ntile * 4096, reps)
+    del src, dst, sids, dids
+    _free_device()
+    best_read = max(v["gbps"] for k, v in res.items() if k.startswith("read_134mb"))
+    return {"metric": "HBM GB/s at the library's access patterns (calibration)", "value": best_read, "unit": "GB/s",
+            "n_gpus": 1, "steps": reps, "warmup": args.warmup,
+            "ms_per_step": min(v["us_per_launch"] for k, v in res.items() if k.startswith("read_134mb")) / 1e3,
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "u8", "data": "synthetic",
+            "config": {"workload": "hbm-ceiling: permuted 4 KiB tile reads of decode's launch sizes (134 MB, "
+                                   "315 MB) and permuted tile copies / contiguous copies of the 70B relayout's "
+                                   "layer (16.8 MB read + 16.8 MB written)"},
+            "roofline": {"kernel": "tiled_read_kernel", "bound": "hbm", "achieved": best_read, "peak": HBM_PEAK_GBPS,
+                         "unit": "GB/s", "frac": round(best_read / HBM_PEAK_GBPS, 4), "traffic": None},
+            "metrics": res}
+
+
 # ---------------------------------------------------------------- all ----
 def _free_device():
     import gc
@@ -965,7 +1077,7 @@ def bench_all(args):
 # --------------------------------------------------------------- main ----
 BENCHES = {"all": bench_all, "llama3-8b": bench_llama3_8b, "qwen3-32b": bench_qwen3_32b,
            "relayout-70b": bench_relayout_70b, "pdmux": bench_pdmux, "copy-1gib": bench_copy_1gib,
-           "mfma-peak": bench_mfma_peak}
+           "mfma-peak": bench_mfma_peak, "hbm-ceiling": bench_hbm_ceiling}
 
 
 def main():

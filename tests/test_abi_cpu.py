@@ -47,6 +47,31 @@ def test_every_declared_symbol_is_exported():
     assert sorted(lib_mod.EXPORTED) == declared
 
 
+def test_calibration_library_exports_and_rejects_bad_arguments():
+    """The benchmark's calibration kernels (libpkv_calib.so): exported, and argument errors come back from the
+    host side as hipErrorInvalidValue (1) before any launch."""
+    from decode_paged_kv_amd import build as b
+    if not os.path.exists(b.CALIB_LIB):
+        pytest.skip("libpkv_calib.so not built")
+    out = subprocess.run(["nm", "-D", "--defined-only", b.CALIB_LIB], capture_output=True, text=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    assert {"pkv_calib_mfma", "pkv_calib_tiled_read", "pkv_calib_tiled_copy", "pkv_calib_copy"} <= exported
+    cl = C.CDLL(b.CALIB_LIB)
+    cl.pkv_calib_tiled_read.argtypes = [C.c_void_p, C.c_void_p, C.c_int, C.c_int, C.c_int, C.c_void_p, C.c_void_p]
+    cl.pkv_calib_tiled_copy.argtypes = [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_int, C.c_int, C.c_int,
+                                        C.c_void_p]
+    cl.pkv_calib_copy.argtypes = [C.c_void_p, C.c_void_p, C.c_size_t, C.c_int, C.c_void_p]
+    cl.pkv_calib_mfma.argtypes = [C.c_int, C.c_int, C.c_void_p, C.c_void_p, C.c_void_p]
+    fake = 0x100000
+    assert cl.pkv_calib_tiled_read(None, fake, 1, 1, 8, fake, None) == 1
+    assert cl.pkv_calib_tiled_read(fake, fake, 1, 1, 5, fake, None) == 1       # unroll not built
+    assert cl.pkv_calib_tiled_copy(fake, fake, fake, fake, 1, 0, 4, None) == 1
+    assert cl.pkv_calib_tiled_copy(fake, fake, fake, fake, 1, 1, 3, None) == 1
+    assert cl.pkv_calib_copy(fake, fake, 24, 1, None) == 1                      # not a multiple of 16
+    assert cl.pkv_calib_copy(fake + 8, fake, 32, 1, None) == 1                  # misaligned
+    assert cl.pkv_calib_mfma(0, 1, fake, fake, None) == 1
+
+
 def _pool(**kw):
     p = lib_mod.PoolLayer()
     p.num_blocks, p.block_size, p.num_kv_heads, p.num_shards, p.head_dim = 8, 16, 8, 4, 128
