@@ -8,6 +8,10 @@
   stream ("PD multiplexing" page, "SGLang's PD multiplexing": the main
   loop).  Every decode and prefill output is checked against the oracle,
   and the level changes only when the prefill starts and after it finishes.
+* Decode on the CU-masked stream of a split level with the equal-splits
+  plan (the whole-line K kernel): head dims 64 and 128, GQA groups 1 to 16,
+  ragged contexts from 1 key, plain and append steps, eager and as graphs,
+  against the oracle.
 """
 
 import numpy as np
@@ -259,6 +263,51 @@ def test_mux_decode_append_matches_the_oracle():
             if done:
                 break
         assert done
+        mux.wait_prefill()
+        torch.cuda.synchronize()
+        case.check_prefill()
+    finally:
+        mux.close()
+
+
+def _ragged_contexts(n, hi, seed):
+    # every tile-edge case of a 32-key tile and a 16-key block, then random
+    fixed = [1, 2, 15, 16, 17, 31, 32, 33, 63, 64, 65, 127, 128]
+    rng = np.random.default_rng(seed)
+    return tuple(int(c) for c in ([c for c in fixed if c <= hi] + list(rng.integers(1, hi + 1, n)))[:n])
+
+
+# (q-heads, KV heads, head dim, contexts): 64 x 8 pairs take one split each;
+# the smaller batches have contexts of at most 128 keys, also one split
+_LINE_CASES = [
+    (32, 8, 128, _ragged_contexts(64, 700, 1)),
+    (8, 8, 128, _ragged_contexts(9, 128, 2)),
+    (16, 1, 128, _ragged_contexts(13, 128, 3)),
+    (16, 2, 64, _ragged_contexts(13, 128, 4)),
+    (4, 2, 64, _ragged_contexts(7, 128, 5)),
+]
+
+
+@pytest.mark.parametrize("append", [False, True])
+@pytest.mark.parametrize("hq,hkv,d,ctx", _LINE_CASES)
+def test_mux_split_level_decode_matches_the_oracle(hq, hkv, d, ctx, append):
+    print(f"split-level decode hq={hq} hkv={hkv} d={d} batch={len(ctx)} append={append}", flush=True)
+    case = _MuxCase(layers=3, hq=hq, hkv=hkv, d=d, ctx=ctx, prompt=400, seed=40 + hq + d)
+    # budget 400 with a 400-token prompt: 1 layer per round, 3 rounds
+    mux = ops.Mux(0, cu_granularity=8, min_decode_cus=32, sm_group_num=8, decode_bs_divisor=36, token_budget=400)
+    try:
+        groups = mux.groups()
+        mux.set_decode_append(append)
+        for i in range(3):
+            mux.set_decode_graphs(i > 0)        # eager first, then the level's graph (captured, replayed)
+            for o in case.o_dec:
+                o.zero_()
+            lvl, _ = mux.run_round(case.decode, case.prefill)
+            torch.cuda.synchronize()
+            pcu, dcu = groups[lvl]
+            assert pcu > 0 and dcu > 0, "a split level"
+            case.check_decode()
+        assert case.prefill.done_submitting    # finished or not: waited for below
         mux.wait_prefill()
         torch.cuda.synchronize()
         case.check_prefill()
