@@ -90,17 +90,18 @@ def relayout_bytes(n, hkv, d, esize=2):
 # profiles/ summaries named for each kernel and workload.
 PMC_SCALE = {"fetch": 2.0, "write": 1.0}
 TRAFFIC = {
-    "attn_decode": {"sources": ['decode_paged_kv_amd/csrc/attn_decode.hip', 'decode_paged_kv_amd/csrc/decode_bf16.h',
-                                'decode_paged_kv_amd/csrc/pkv_internal.h'],
-                    "sha256": "9b697f3e299766e4b28f331019815c0dc4c129536f6980b37a5d7ba24efc99f0",
-                    "fetch_kib": 65955.01, "write_kib": 512.00},
-    "attn_prefill_chunk": {"sources": ['decode_paged_kv_amd/csrc/attn_prefill.hip', 'decode_paged_kv_amd/csrc/prefill_bf16.h',
-                                       'decode_paged_kv_amd/csrc/pkv_internal.h'],
-                           "sha256": "1d5796c6b9bc8b16893ea75fed87cf42d222b90e74a0165f1d68d3eb2c42a756",
-                           "fetch_kib": 28005.16, "write_kib": 15974.11},
+    "attn_decode": {"sources": ['decode_paged_kv_amd/csrc/attn_decode.hip', 'decode_paged_kv_amd/csrc/decode_bf16.h', 'decode_paged_kv_amd/csrc/pkv_internal.h'],
+                    "sha256": "d6878f76e0665bc0e6abfc2b0d84f9a50303b24b30f5922736b361e6e1f1ea99",
+                    "fetch_kib": 65946.74, "write_kib": 512.00},
+    "attn_prefill_chunk": {"sources": ['decode_paged_kv_amd/csrc/attn_prefill.hip', 'decode_paged_kv_amd/csrc/prefill_bf16.h', 'decode_paged_kv_amd/csrc/pkv_internal.h'],
+                           "sha256": "0442718885b929d101243ff1f859a07477bbb8122c3c141c8cf19dbac3738a65",
+                           "fetch_kib": 28005.08, "write_kib": 15974.18},
     "kv_relayout": {"sources": ['decode_paged_kv_amd/csrc/kv_ops.hip', 'decode_paged_kv_amd/csrc/pkv_internal.h'],
-                    "sha256": "5545d74d4886e161295a0ab8da04d5c32eec5610e2dc05e0bbbf64e4726c0377",
-                    "fetch_kib": 8233.78, "write_kib": 16386.02},
+                    "sha256": "b4fc2c35595665667f6ee1c43d0035272138904c17b236794f6195797b4aee74",
+                    "fetch_kib": 8233.69, "write_kib": 16388.01},
+    "attn_decode_line": {"sources": ['decode_paged_kv_amd/csrc/attn_decode.hip', 'decode_paged_kv_amd/csrc/decode_line.h', 'decode_paged_kv_amd/csrc/decode_bf16.h', 'decode_paged_kv_amd/csrc/pkv_internal.h'],
+                         "sha256": "71a915a977d69f7a7fb1b2f33546e6cc418d7e130a9998a705496b47545c63e5",
+                         "fetch_kib": 525394.48, "write_kib": 1024.00},
 }
 
 
@@ -818,6 +819,7 @@ def bench_pdmux(args):
     solo_med = float(np.median(A))
     mux_med = float(np.median(B16))
     dstep_bytes = decode_bytes([ctx] * B, hkv, d, hq) * L
+    line_traffic = traffic_bytes("attn_decode_line")
     result = {
         "metric": METRIC, "value": round(mux_med, 3), "unit": "ms", "n_gpus": 1, "steps": len(B16),
         "warmup": args.warmup, "ms_per_step": round(mux_med, 3), "higher_is_better": False, "scaling": "weak",
@@ -828,12 +830,15 @@ def bench_pdmux(args):
                    "level_32k": [f"{groups[x][0]}:{groups[x][1]}" for x in lv32],
                    "value_is": "median decode step (32 layers: kv_write + attn_decode) wall time per round while the "
                                "16K prefill runs"},
-        "roofline": {"kernel": "attn_decode (decode step under multiplexing)", "bound": "hbm",
+        "roofline": {"kernel": "attn_decode (decode step under multiplexing: the whole-line K kernel on the "
+                               "CU-masked stream)", "bound": "hbm",
                      "achieved": round(dstep_bytes / (mux_med * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(dstep_bytes / (mux_med * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "frac": round(dstep_bytes / (mux_med * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                     "traffic": L * line_traffic if line_traffic else None,
                      "bytes_per_step": dstep_bytes,
                      "note": "decode K/V + q/out bytes of the 32-layer step over its median wall time (host "
-                             "clock around each round, kv_write launches included)"},
+                             "clock around each round, kv_write launches included); traffic: the counters' bytes "
+                             "of the step's 32 decode launches"},
         "metrics": {
             "solo_decode": stats(A),
             "mux_16k_decode": stats(B16), "mux_16k_prefill_ms": round(pf16, 2),
