@@ -15,8 +15,8 @@
 // equal-splits plan or, for batches with fewer (request, KV head) pairs
 // than resident workgroups, the stream split (plans below).  A plan made
 // for a launch on part of the device's CUs (the decode stream of a PD
-// multiplexing level) with equal splits runs the whole-line K form of
-// decode_line.h instead.
+// multiplexing level) with one split per (request, KV head) runs the
+// whole-line K form of decode_line.h instead.
 //
 // fp32 (small checks): the kernel in this file.  Inside a workgroup each
 // wave walks 64-key tiles (tile i of the split goes to wave i % 4):
@@ -245,18 +245,17 @@ attn_decode_bf16_kernel(PoolDev pool, const bf16_t* __restrict__ q, bf16_t* __re
                                           blockIdx.x, blockIdx.y, blockIdx.z, gridDim.x);
 }
 
+// grid (1, KV heads, requests): one workgroup per (request, KV head)
 template <int D, int G, bool APPEND>
 __global__ void __launch_bounds__(kThreads, 2)
 attn_decode_line_kernel(PoolDev pool, const bf16_t* __restrict__ q, bf16_t* __restrict__ out,
                         const int32_t* __restrict__ bt, int bt_stride, const int32_t* __restrict__ ctx,
-                        int num_q_heads, float scale_log2, int split_tokens, int num_splits, int max_len,
-                        float* __restrict__ part_o, float* __restrict__ part_ml, const bf16_t* __restrict__ k_new,
+                        int num_q_heads, float scale_log2, int max_len, const bf16_t* __restrict__ k_new,
                         const bf16_t* __restrict__ v_new) {
   __shared__ __attribute__((aligned(1024))) char ktiles[decode_line::LineKCfg<D>::REGION];
   __shared__ decode_line::LineSmem<D, G> sm;
-  decode_line::decode_line_block<D, G, APPEND>(pool, q, out, bt, bt_stride, ctx, num_q_heads, scale_log2,
-                                               split_tokens, num_splits, max_len, part_o, part_ml, k_new, v_new,
-                                               blockIdx.x, blockIdx.y, blockIdx.z, ktiles, sm);
+  decode_line::decode_line_block<D, G, APPEND>(pool, q, out, bt, bt_stride, ctx, num_q_heads, scale_log2, max_len,
+                                               k_new, v_new, blockIdx.y, blockIdx.z, ktiles, sm);
 }
 
 // The new token's K/V row of each (request, KV head) written at position
@@ -426,9 +425,9 @@ hipError_t launch_typed(const PoolDev& pool, const void* q, void* out, const int
 #define PKV_LINE_LAUNCH(AP)                                                                                        \
     hipLaunchKernelGGL((attn_decode_line_kernel<D, G, AP>), grid, dim3(kThreads), 0, s, pool,                      \
                        static_cast<const bf16_t*>(q), static_cast<bf16_t*>(out), bt, bt_stride, ctx, num_q_heads, \
-                       scale_log2, plan.split_tokens, plan.num_splits, plan.max_len, part_o, part_ml,             \
-                       static_cast<const bf16_t*>(k_new), static_cast<const bf16_t*>(v_new))
-    if (plan.line_k) {
+                       scale_log2, plan.max_len, static_cast<const bf16_t*>(k_new),                               \
+                       static_cast<const bf16_t*>(v_new))
+    if (plan.line_k && plan.num_splits == 1) {
       if (k_new) PKV_LINE_LAUNCH(true);
       else PKV_LINE_LAUNCH(false);
     } else {

@@ -1,8 +1,8 @@
 // bf16 paged GQA decode attention for one workgroup, the whole-line K form,
 // used where the decode runs on part of the device's CUs (a CU-masked
-// stream beside a prefill).  Equal splits only: block (split, KV head,
-// request), as in decode_bf16.h, whose work decomposition, MFMA contraction,
-// softmax and merge this form shares.  What differs is how a tile's K
+// stream beside a prefill).  One workgroup per (KV head, request), all of
+// the request's keys, as decode_bf16.h does for such batches, whose work
+// decomposition, MFMA contraction, softmax and merge this form shares.  What differs is how a tile's K
 // reaches the matrix cores.
 //
 // decode_bf16.h loads K straight in the S^T operand layout: one instruction
@@ -183,17 +183,16 @@ struct LineSmem {
   float snew[G];            // score of the appended key, per q-head (log2 units)
 };
 
-// One workgroup's work: split `split` of (request b, KV head kvh).  kregion:
+// One workgroup's work: every key of (request b, KV head kvh), one split
+// per pair, so the workgroup writes the output rows itself.  kregion:
 // LineKCfg<D>::REGION bytes of LDS (1 KB aligned), the K tile of every wave.
 template <int D, int G, bool APPEND>
 __device__ __forceinline__ void decode_line_block(PoolDev pool, const bf16_t* __restrict__ q,
                                                   bf16_t* __restrict__ out, const int32_t* __restrict__ bt,
                                                   int bt_stride, const int32_t* __restrict__ ctx, int num_q_heads,
-                                                  float scale_log2, int split_tokens, int num_splits, int max_len,
-                                                  float* __restrict__ part_o, float* __restrict__ part_ml,
-                                                  const bf16_t* __restrict__ k_new, const bf16_t* __restrict__ v_new,
-                                                  int split, int kvh, int b, char* const kregion,
-                                                  LineSmem<D, G>& sm) {
+                                                  float scale_log2, int max_len, const bf16_t* __restrict__ k_new,
+                                                  const bf16_t* __restrict__ v_new, int kvh, int b,
+                                                  char* const kregion, LineSmem<D, G>& sm) {
   static_assert(G >= 1 && G <= 16, "the q-heads of a KV head are the 16 MFMA columns");
   constexpr int KC = D / 32, DT = D / 16, TK = 32;
   using KCF = LineKCfg<D>;
@@ -210,17 +209,12 @@ __device__ __forceinline__ void decode_line_block(PoolDev pool, const bf16_t* __
   const size_t block_stride = (size_t)hl * bs * D;
   const int tile_bytes = bs * D * 2;
 
-  // The workgroup's keys [start, end) of request b and KV head kvh; the
-  // result goes to out when final_out, else to the partial rows
-  // prow + g * pstride.
-  // With `last` (append mode) the request's new key L-1 follows the segment:
-  // its K/V come from k_new / v_new, are added to the softmax in the merge,
-  // and are written to the pool there; the tiles stop at L-1.
+  // The workgroup's keys [start, end) of request b and KV head kvh.  With
+  // `last` (append mode) the request's new key L-1 follows them: its K/V
+  // come from k_new / v_new, are added to the softmax in the merge, and are
+  // written to the pool there; the tiles stop at L-1.
   struct Seg {
     int b, kvh, start, end;
-    bool final_out;
-    size_t prow;
-    int pstride;
     bool last;
   };
   // its KV head's pools, its table, its end (wave-uniform, in scalar
@@ -263,7 +257,7 @@ __device__ __forceinline__ void decode_line_block(PoolDev pool, const bf16_t* __
   // position (4c + j4) ^ swz(l16) = byte offset kx ^ 64c
   const int ksw = (l16 >> KCF::SWS) & (KCF::NCH - 1);
   const int kx = l16 * KCF::ROWB + 16 * (j4 ^ (ksw & 3)) + 64 * (ksw >> 2);
-  // block ids of the tile at k0 (-1: past the split or out of range)
+  // block ids of the tile at k0 (-1: past the context or out of range)
   auto fetch_ids = [&](int k0, int (&ids)[2]) {
     bool bad = false;
 #pragma unroll
@@ -464,12 +458,12 @@ __device__ __forceinline__ void decode_line_block(PoolDev pool, const bf16_t* __
     wait_vm_v<0>(ra.v);
     wait_vm_v<0>(rb.v);
   };
-  // The appended key (append mode, the request's last split): its row is
-  // written to the pool at position L-1 (the tiles never read that slot) and
-  // its score for each q-head computed into LDS (wave w takes heads w, w+4,
-  // ...; a lane 1 or 2 dims); a block id outside the pool makes it absent,
-  // as for any key.  Run by every wave right after its tiles; the merge's
-  // first barrier publishes the scores.
+  // The appended key (append mode): its row is written to the pool at
+  // position L-1 (the tiles never read that slot) and its score for each
+  // q-head computed into LDS (wave w takes heads w, w+4, ...; a lane 1 or 2
+  // dims); a block id outside the pool makes it absent, as for any key.  Run
+  // by every wave right after its tiles; the merge's first barrier publishes
+  // the scores.
   auto append_key = [&](const Seg& sg) -> bool {
     bool add_new = false;
     if (APPEND && sg.last) {
@@ -543,16 +537,7 @@ __device__ __forceinline__ void decode_line_block(PoolDev pool, const bf16_t* __
           mx = mf;
         }
         const int h = sg.kvh * G + g;
-        if (sg.final_out) {
-          out[((size_t)sg.b * num_q_heads + h) * D + d] = f32_to_bf16(acc / l);
-        } else {
-          const size_t row = sg.prow + (size_t)g * sg.pstride;
-          part_o[row * D + d] = acc;
-          if (d == 0) {
-            part_ml[row * 2 + 0] = mx;
-            part_ml[row * 2 + 1] = l;
-          }
-        }
+        out[((size_t)sg.b * num_q_heads + h) * D + d] = f32_to_bf16(acc / l);
       }
       __syncthreads();                            // the merge buffers are free again
     }
@@ -560,15 +545,12 @@ __device__ __forceinline__ void decode_line_block(PoolDev pool, const bf16_t* __
 
   int L = ctx[b];
   if (L > cap) {                              // past max_context_len: cut, flagged
-    if (threadIdx.x == 0 && split == 0 && kvh == 0) flag_error(pool.err, PKV_ERRBIT_CONTEXT);
+    if (threadIdx.x == 0 && kvh == 0) flag_error(pool.err, PKV_ERRBIT_CONTEXT);
     L = cap;
   }
-  const int start = split * split_tokens;
-  if (start >= L) return;
-  const int stop = min(L, start + split_tokens);
-  const bool last = APPEND && ctx[b] <= cap && stop == L;
-  const Seg sg{b, kvh, start, last ? stop - 1 : stop, L <= split_tokens,
-               ((size_t)b * num_q_heads + (size_t)kvh * G) * num_splits + split, num_splits, last};
+  if (L <= 0) return;
+  const bool last = APPEND && ctx[b] <= cap;
+  const Seg sg{b, kvh, 0, last ? L - 1 : L, last};
   prologue(sg);
   body(sg);
   const bool add_new = append_key(sg);

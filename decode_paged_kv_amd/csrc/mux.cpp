@@ -582,9 +582,10 @@ int run_mux_round(pkv_mux* m, const pkv_decode_step* d, pkv_prefill_job* p, int3
   hipStream_t ds = stream_of(m, level, 1), ps = stream_of(m, level, 0);
 
   // ---- decode step on the decode stream (as the level's graph when on) ----
-  // on a CU-masked stream the equal-splits plan runs the whole-line K
-  // kernel: with part of the CUs, half-line K reads limit the bandwidth
-  plan.line_k = ds != m->whole;
+  // on a CU-masked stream a plan of one split per (request, KV head) runs
+  // the whole-line K kernel: with part of the CUs, half-line K reads limit
+  // the bandwidth
+  plan.line_k = ds != m->whole && plan.stream_wgs == 0 && plan.num_splits == 1;
   if (d) {
     e = m->use_graphs ? run_decode_graph(m, level, d, dpools, plan, ds)
                       : launch_decode_step(d, dpools, plan, ds, m->decode_append);

@@ -110,8 +110,9 @@ struct DecodePlan {
   int split_tokens;   // keys per split (multiple of 32); split plan only
   int num_splits;     // splits per (request, kv head) at max_context_len; split plan only
   int stream_wgs;     // > 0: stream split over this many workgroups instead
-  bool line_k;        // bf16 equal splits: the whole-line K kernel (for a
-                      // launch on part of the CUs); false from plan_decode
+  bool line_k;        // bf16, one split per pair: the whole-line K kernel
+                      // (for a launch on part of the CUs); false from
+                      // plan_decode
   size_t workspace;   // bytes of partial results needed (0: none)
 };
 // stream_ok = false: never the stream split (equal splits instead)
