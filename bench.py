@@ -91,17 +91,17 @@ def relayout_bytes(n, hkv, d, esize=2):
 PMC_SCALE = {"fetch": 2.0, "write": 1.0}
 TRAFFIC = {
     "attn_decode": {"sources": ['decode_paged_kv_amd/csrc/attn_decode.hip', 'decode_paged_kv_amd/csrc/decode_bf16.h', 'decode_paged_kv_amd/csrc/pkv_internal.h'],
-                    "sha256": "d6878f76e0665bc0e6abfc2b0d84f9a50303b24b30f5922736b361e6e1f1ea99",
-                    "fetch_kib": 65946.74, "write_kib": 512.00},
+                    "sha256": "38eca95bf37836ca984a5a9df998d4c0af278d53be9910904805eac4bc941067",
+                    "fetch_kib": 65954.78, "write_kib": 512.00},
     "attn_prefill_chunk": {"sources": ['decode_paged_kv_amd/csrc/attn_prefill.hip', 'decode_paged_kv_amd/csrc/prefill_bf16.h', 'decode_paged_kv_amd/csrc/pkv_internal.h'],
-                           "sha256": "0442718885b929d101243ff1f859a07477bbb8122c3c141c8cf19dbac3738a65",
-                           "fetch_kib": 28005.08, "write_kib": 15974.18},
+                           "sha256": "2eb83c49082171c269c39f44cab447848018e0b872f6cf4536f63d8ccc64aa63",
+                           "fetch_kib": 28005.34, "write_kib": 15974.17},
     "kv_relayout": {"sources": ['decode_paged_kv_amd/csrc/kv_ops.hip', 'decode_paged_kv_amd/csrc/pkv_internal.h'],
-                    "sha256": "b4fc2c35595665667f6ee1c43d0035272138904c17b236794f6195797b4aee74",
-                    "fetch_kib": 8233.69, "write_kib": 16388.01},
+                    "sha256": "2af290f6b8645156babeeffc1daaf7f7995952fecb4c047393f841a8662d15ff",
+                    "fetch_kib": 8233.69, "write_kib": 16386.05},
     "attn_decode_line": {"sources": ['decode_paged_kv_amd/csrc/attn_decode.hip', 'decode_paged_kv_amd/csrc/decode_line.h', 'decode_paged_kv_amd/csrc/decode_bf16.h', 'decode_paged_kv_amd/csrc/pkv_internal.h'],
-                         "sha256": "71a915a977d69f7a7fb1b2f33546e6cc418d7e130a9998a705496b47545c63e5",
-                         "fetch_kib": 525394.48, "write_kib": 1024.00},
+                         "sha256": "fb5a3988b80f2439d7514e980a310ef94774fdbdb2fcb7140b47e3445800e23d",
+                         "fetch_kib": 525399.99, "write_kib": 1024.00},
 }
 
 
