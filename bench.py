@@ -91,8 +91,8 @@ def relayout_bytes(n, hkv, d, esize=2):
 PMC_SCALE = {"fetch": 2.0, "write": 1.0}
 TRAFFIC = {
     "attn_decode": {"sources": ['decode_paged_kv_amd/csrc/attn_decode.hip', 'decode_paged_kv_amd/csrc/decode_bf16.h', 'decode_paged_kv_amd/csrc/pkv_internal.h'],
-                    "sha256": "38eca95bf37836ca984a5a9df998d4c0af278d53be9910904805eac4bc941067",
-                    "fetch_kib": 65954.78, "write_kib": 512.00},
+                    "sha256": "87eb4716c213a5e239fade5d4382f3743e29bd139c7e6f3a7be5af3efa32d5e5",
+                    "fetch_kib": 65947.23, "write_kib": 512.00},
     "attn_prefill_chunk": {"sources": ['decode_paged_kv_amd/csrc/attn_prefill.hip', 'decode_paged_kv_amd/csrc/prefill_bf16.h', 'decode_paged_kv_amd/csrc/pkv_internal.h'],
                            "sha256": "2eb83c49082171c269c39f44cab447848018e0b872f6cf4536f63d8ccc64aa63",
                            "fetch_kib": 28005.34, "write_kib": 15974.17},
@@ -100,8 +100,8 @@ TRAFFIC = {
                     "sha256": "2af290f6b8645156babeeffc1daaf7f7995952fecb4c047393f841a8662d15ff",
                     "fetch_kib": 8233.69, "write_kib": 16386.05},
     "attn_decode_line": {"sources": ['decode_paged_kv_amd/csrc/attn_decode.hip', 'decode_paged_kv_amd/csrc/decode_line.h', 'decode_paged_kv_amd/csrc/decode_bf16.h', 'decode_paged_kv_amd/csrc/pkv_internal.h'],
-                         "sha256": "fb5a3988b80f2439d7514e980a310ef94774fdbdb2fcb7140b47e3445800e23d",
-                         "fetch_kib": 525399.99, "write_kib": 1024.00},
+                         "sha256": "2e41b85238339a36520e1877cb727653f4919edb98c81400a730bcc10138d100",
+                         "fetch_kib": 525629.10, "write_kib": 1024.00},
 }
 
 

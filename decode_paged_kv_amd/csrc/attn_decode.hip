@@ -16,7 +16,7 @@
 // than resident workgroups, the stream split (plans below).  A plan made
 // for a launch on part of the device's CUs (the decode stream of a PD
 // multiplexing level) with one split per (request, KV head) runs the
-// whole-line K form of decode_line.h instead.
+// whole-line form of decode_line.h instead.
 //
 // fp32 (small checks): the kernel in this file.  Inside a workgroup each
 // wave walks 64-key tiles (tile i of the split goes to wave i % 4):

@@ -1,23 +1,27 @@
-// bf16 paged GQA decode attention for one workgroup, the whole-line K form,
+// bf16 paged GQA decode attention for one workgroup, the whole-line form,
 // used where the decode runs on part of the device's CUs (a CU-masked
 // stream beside a prefill).  One workgroup per (KV head, request), all of
 // the request's keys, as decode_bf16.h does for such batches, whose work
-// decomposition, MFMA contraction, softmax and merge this form shares.  What differs is how a tile's K
-// reaches the matrix cores.
+// decomposition, softmax and merge this form shares.  What differs is how a
+// tile's K and V reach the matrix cores.
 //
 // decode_bf16.h loads K straight in the S^T operand layout: one instruction
 // reads 64 bytes of each of 16 key rows, so every 128-byte line takes two
-// instructions.  On half of the CUs such reads reach about 4.1 TB/s where
-// whole-line reads reach about 4.7 (each CU then needs twice the bandwidth,
-// and the half-line requests limit it); on the whole device HBM is the limit
-// and the direct form is faster (it needs no LDS round trip).  Here K is
-// loaded in whole key rows, each instruction 1 KB of whole 128-byte lines,
-// and turned into the operand layout through a 32-key LDS tile the wave
-// owns (written, then read back).  A row's 16-byte chunk c is stored at
-// position c ^ swz(row), so the 16 rows one operand read touches fall in
-// distinct banks.  V is loaded in the P V operand layout as in
-// decode_bf16.h (each instruction 16 whole 32-byte dim rows).  Both carry
-// the non-temporal hint.
+// instructions; and V 8 bytes per lane.  On half of the CUs each CU needs
+// twice the bandwidth and such requests limit it: a loads-only probe reads
+// about 4.1 TB/s with that pattern, 4.8 with K in whole lines and 5.0 with V
+// at 16 bytes per lane as well; on the whole device HBM is the limit and
+// the direct form is faster (it needs no LDS round trip).  Here K is loaded
+// in whole key rows, each instruction 1 KB of whole 128-byte lines, and
+// turned into the operand layout through a 32-key LDS tile the wave owns
+// (written, then read back).  A row's 16-byte chunk c is stored at position
+// c ^ swz(row), so the 16 rows one operand read touches fall in distinct
+// banks.  The rows each S^T MFMA takes are chosen so that a lane's
+// accumulators hold 8 consecutive keys of the tile, the layout in which a
+// 16x16x32 P V MFMA takes P; its V operand is then 8 consecutive keys of one
+// dim row, one 16-byte load per lane (an instruction reads 512 contiguous
+// bytes from each of the tile's two blocks).  Both carry the non-temporal
+// hint.
 //
 // A tile's registers are refilled with the wave's next tile as soon as they
 // are consumed: K right after it is written to LDS, V right after P V, so
@@ -38,16 +42,14 @@ using decode_impl::f32x4_t;
 using decode_impl::kDecodeSlack;
 using decode_impl::kThreads;
 using decode_impl::kWaves;
-using decode_impl::s16x4_t;
-typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ f32x4_t mfma_qk(const u32x4_t& a, const u32x4_t& b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
                                                  0, 0, 0);
 }
-__device__ __forceinline__ f32x4_t mfma_pv(const u32x2_t& a, const uint2& b, f32x4_t c) {
-  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, a), __builtin_bit_cast(s16x4_t, b), c,
-                                                   0, 0, 0);
+__device__ __forceinline__ f32x4_t mfma_pv(const u32x4_t& a, const u32x4_t& b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
+                                                 0, 0, 0);
 }
 
 // The loads of a tile's operands (q, K, V), the LDS transposition of K and
@@ -93,31 +95,25 @@ __device__ __forceinline__ buffer_rsrc_t buffer_rsrc_uniform(const void* base, i
 __device__ __forceinline__ void vload16_nt(u32x4_t& v, buffer_rsrc_t r, int voffset, int soffset) {
   asm volatile("buffer_load_dwordx4 %0, %1, %2, %3 offen nt" : "+v"(v) : "v"(voffset), "s"(r), "s"(soffset) : "memory");
 }
-// 8 bytes per lane of a buffer, non-temporal; valid after a wait naming it
-__device__ __forceinline__ void vload8_nt(u32x2_t& v, buffer_rsrc_t r, int voffset, int soffset) {
-  asm volatile("buffer_load_dwordx2 %0, %1, %2, %3 offen nt" : "+v"(v) : "v"(voffset), "s"(r), "s"(soffset) : "memory");
-}
 // 16 bytes per lane from a global address; valid after a wait naming it
 __device__ __forceinline__ void gload16(u32x4_t& v, const void* p) {
   asm volatile("global_load_dwordx4 %0, %1, off" : "+v"(v) : "v"(p) : "memory");
 }
-// waits that make a tile's V registers (2 x DT) or q's fragments valid
+// the same, non-temporal
+__device__ __forceinline__ void gload16_nt(u32x4_t& v, const void* p) {
+  asm volatile("global_load_dwordx4 %0, %1, off nt" : "+v"(v) : "v"(p) : "memory");
+}
+// waits that make a tile's V registers (DT) or q's fragments valid
 template <int N>
-__device__ __forceinline__ void wait_vm_v(u32x2_t (&v)[2][8]) {
-  asm volatile("s_waitcnt vmcnt(%16)"
-               : "+v"(v[0][0]), "+v"(v[0][1]), "+v"(v[0][2]), "+v"(v[0][3]), "+v"(v[0][4]), "+v"(v[0][5]),
-                 "+v"(v[0][6]), "+v"(v[0][7]), "+v"(v[1][0]), "+v"(v[1][1]), "+v"(v[1][2]), "+v"(v[1][3]),
-                 "+v"(v[1][4]), "+v"(v[1][5]), "+v"(v[1][6]), "+v"(v[1][7])
+__device__ __forceinline__ void wait_vm_v(u32x4_t (&v)[8]) {
+  asm volatile("s_waitcnt vmcnt(%8)"
+               : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]), "+v"(v[6]), "+v"(v[7])
                : "n"(N)
                : "memory");
 }
 template <int N>
-__device__ __forceinline__ void wait_vm_v(u32x2_t (&v)[2][4]) {
-  asm volatile("s_waitcnt vmcnt(%8)"
-               : "+v"(v[0][0]), "+v"(v[0][1]), "+v"(v[0][2]), "+v"(v[0][3]), "+v"(v[1][0]), "+v"(v[1][1]),
-                 "+v"(v[1][2]), "+v"(v[1][3])
-               : "n"(N)
-               : "memory");
+__device__ __forceinline__ void wait_vm_v(u32x4_t (&v)[4]) {
+  asm volatile("s_waitcnt vmcnt(%4)" : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]) : "n"(N) : "memory");
 }
 template <int N>
 __device__ __forceinline__ void wait_vm_k(u32x4_t (&k)[8]) {
@@ -144,15 +140,17 @@ __device__ __forceinline__ void wait_vm_q(u32x4_t (&q)[2]) {
 template <int D>
 struct LineTile {
   u32x4_t k[32 * 2 * D / 1024];   // instruction i, lane t: row RPI i + t / NCH, chunk (t % NCH) ^ swz(row)
-  u32x2_t v[2][D / 16];           // A of O^T: dim 16m + l%16, keys 16h + 4(l/16) .. +3
+  u32x4_t v[D / 16];              // A of O^T: dim 16m + l%16, keys 8(l/16) .. +7 of the tile
   int blk[2];
 };
 
 // The K tile in LDS: row q of a tile is key q (2D bytes), its 16-byte chunk c
-// at position c ^ swz(q % 16), swz(r) = (r >> SWS) & (NCH - 1): with
-// 256-byte rows (D = 128) each row is a whole bank window, with 128-byte rows
-// (D = 64) two rows share one, and either way the 16 rows of an operand read
-// hit 16 distinct 16-byte bank groups.
+// at position c ^ swz(q), swz(q) = (cr(q) >> SWS) & (NCH - 1) with
+// cr(q) = (q & 3) | ((q >> 3) << 2).  The S^T MFMA of key set h reads rows
+// 8(r / 4) + 4h + r % 4 for r = 0..15, whose cr values are the 16 distinct
+// r: with 256-byte rows (D = 128) each row is a whole bank window, with
+// 128-byte rows (D = 64) two rows share one, and either way the 16 rows of
+// an operand read hit 16 distinct 16-byte bank groups.
 template <int D>
 struct LineKCfg {
   static constexpr int NCH = D / 8;                 // 16-byte chunks per row
@@ -162,6 +160,7 @@ struct LineKCfg {
   static constexpr int NLD = 32 / RPI;              // K load instructions per tile
   static constexpr int SWS = NCH == 16 ? 0 : 1;
   static constexpr int REGION = kWaves * TILE;      // the tile of every wave
+  static __device__ __forceinline__ int swz(int q) { return (((q & 3) | ((q >> 3) << 2)) >> SWS) & (NCH - 1); }
 };
 static_assert(LineKCfg<128>::RPI * LineKCfg<128>::NLD == 32 && LineKCfg<64>::RPI * LineKCfg<64>::NLD == 32,
               "K tile loads");
@@ -239,7 +238,9 @@ __device__ __forceinline__ void decode_line_block(PoolDev pool, const bf16_t* __
     for (int c = 0; c < KC; ++c) gload16(qf[c], qrow + 32 * c);
   };
 
-  const int v_voff = (l16 * bs + 4 * j4) * 2;                   // dim l16 of a 16-dim slab, 4 keys
+  // V of lane l: dim l16 of a 16-dim slab, keys 8 j4 .. +7 of the tile: the
+  // 8-key run 8 (j4 % 2) of key half j4 / 2
+  const int v_lane = l16 * bs + 8 * (j4 & 1);                   // elements from the half's first key
   // this wave's K tile in LDS
   char* const ktile = kregion + wave * KCF::TILE;
   // K loads: instruction i reads rows RPI i .. +RPI-1 (all in key half
@@ -249,14 +250,22 @@ __device__ __forceinline__ void decode_line_block(PoolDev pool, const bf16_t* __
   int kdma_voff[KCF::NLD];
 #pragma unroll
   for (int i = 0; i < KCF::NLD; ++i) {
-    const int q16 = (KCF::RPI * i + lane / KCF::NCH) & 15;
-    const int c = (lane % KCF::NCH) ^ ((q16 >> KCF::SWS) & (KCF::NCH - 1));
-    kdma_voff[i] = (q16 * D + 8 * c) * 2;
+    const int row = KCF::RPI * i + lane / KCF::NCH;
+    const int c = (lane % KCF::NCH) ^ KCF::swz(row);
+    kdma_voff[i] = ((row & 15) * D + 8 * c) * 2;
   }
-  // K operand read of lane l: row l16 (+16 per half), chunk 4c + j4 at
-  // position (4c + j4) ^ swz(l16) = byte offset kx ^ 64c
-  const int ksw = (l16 >> KCF::SWS) & (KCF::NCH - 1);
-  const int kx = l16 * KCF::ROWB + 16 * (j4 ^ (ksw & 3)) + 64 * (ksw >> 2);
+  // S^T MFMA h takes the keys 8(r / 4) + 4h + r % 4 as its rows r = 0..15,
+  // so that its accumulator rows 4 j4 .. +3 are keys 8 j4 + 4h .. +3 and a
+  // lane ends up with keys 8 j4 .. +7 of the tile for its head, the layout
+  // in which P V takes P.  K operand read of lane l for set h: that row,
+  // chunk 4c + j4 at position (4c + j4) ^ swz(row) = byte offset kx[h] ^ 64c
+  int kx[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int row = 8 * (l16 >> 2) + 4 * h + (l16 & 3);
+    const int ksw = KCF::swz(row);
+    kx[h] = row * KCF::ROWB + 16 * (j4 ^ (ksw & 3)) + 64 * (ksw >> 2);
+  }
   // block ids of the tile at k0 (-1: past the context or out of range)
   auto fetch_ids = [&](int k0, int (&ids)[2]) {
     bool bad = false;
@@ -284,16 +293,17 @@ __device__ __forceinline__ void decode_line_block(PoolDev pool, const bf16_t* __
       vload16_nt(r.k[i], rs, kdma_voff[i], soff);
     }
   };
+  // V of the tile at k0: one 16-byte load per lane and 16-dim slab, lanes
+  // j4 < 2 from key half 0's block, the others from half 1's (an absent
+  // block's lanes read block 0 of the pool, in bounds, and are zeroed before
+  // use)
   auto issue_v = [&](int k0, LineTile<D>& r) {
+    const int h = j4 >> 1;
+    const int blk = h ? r.blk[1] : r.blk[0];
+    const bf16_t* vp = vpool + head_off + v_lane +
+                       (blk >= 0 ? (size_t)blk * block_stride + ((k0 + 16 * h) & (bs - 1)) : 0);
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const bool ok = r.blk[h] >= 0;
-      const buffer_rsrc_t rs = buffer_rsrc_uniform(vpool + (ok ? (size_t)r.blk[h] * block_stride + head_off : 0),
-                                           ok ? tile_bytes : 0);
-      const int soff = ((k0 + 16 * h) & (bs - 1)) * 2;
-#pragma unroll
-      for (int mm = 0; mm < DT; ++mm) vload8_nt(r.v[h][mm], rs, v_voff, __builtin_amdgcn_readfirstlane(soff + mm * 32 * bs));
-    }
+    for (int mm = 0; mm < DT; ++mm) gload16_nt(r.v[mm], vp + (size_t)mm * 16 * bs);
   };
 
   f32x4_t o[DT];
@@ -310,14 +320,14 @@ __device__ __forceinline__ void decode_line_block(PoolDev pool, const bf16_t* __
   // absent one (past the segment) through a descriptor with no records that
   // reads zeros and touches no memory, and the prologue loads both sets.  So
   // every path issues the same sequence of loads and each wait names a fixed
-  // count: after a tile's K loads come its V loads (2 DT) and the other set's
-  // next tile (NLD + 2 DT); after its V loads, that other tile and this set's
+  // count: after a tile's K loads come its V loads (DT) and the other set's
+  // next tile (NLD + DT); after its V loads, that other tile and this set's
   // next K loads (NLD).  Loads into registers complete in issue order.  (A
   // wait inside a branch would let the compiler copy the named registers
   // before it; loads whose destination is not kept live would let it reuse
   // the register while the load is in flight.)
   auto process = [&](int k0, LineTile<D>& r, int k0_next, int k0_next2) {
-    wait_vm_k<4 * DT + KCF::NLD>(r.k);
+    wait_vm_k<2 * DT + KCF::NLD>(r.k);
     // K rows into the LDS tile, then back in the operand layout (one wave's
     // LDS operations complete in order)
 #pragma unroll
@@ -326,7 +336,7 @@ __device__ __forceinline__ void decode_line_block(PoolDev pool, const bf16_t* __
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int c = 0; c < KC; ++c) kf[h * KC + c] = lds_read16(ktile + h * 16 * KCF::ROWB + (kx ^ (64 * c)));
+      for (int c = 0; c < KC; ++c) kf[h * KC + c] = lds_read16(ktile + (kx[h] ^ (64 * c)));
     if constexpr (KC == 4)
       wait_lds8(kf);
     else
@@ -338,7 +348,8 @@ __device__ __forceinline__ void decode_line_block(PoolDev pool, const bf16_t* __
 #pragma unroll
       for (int c = 0; c < KC; ++c) st[h] = mfma_qk(kf[h * KC + c], qf[c], st[h]);
     }
-    const bool ok0 = r.blk[0] >= 0, ok1 = r.blk[1] >= 0;
+    // this lane's keys 8 j4 .. +7 lie in key half j4 / 2
+    const bool okh = (j4 < 2 ? r.blk[0] : r.blk[1]) >= 0;
     const bool has_next = k0_next >= 0;
     __builtin_amdgcn_sched_barrier(0);
     r.blk[0] = has_next ? ids_next[0] : -1;
@@ -352,8 +363,8 @@ __device__ __forceinline__ void decode_line_block(PoolDev pool, const bf16_t* __
     for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
-        const int key = k0 + 16 * h + 4 * j4 + rr;
-        const bool valid = key < end && (h ? ok1 : ok0);
+        const int key = k0 + 8 * j4 + 4 * h + rr;
+        const bool valid = key < end && okh;
         x[h][rr] = valid ? st[h][rr] : -INFINITY;
         mx = fmaxf(mx, x[h][rr]);
       }
@@ -367,37 +378,34 @@ __device__ __forceinline__ void decode_line_block(PoolDev pool, const bf16_t* __
 #pragma unroll
       for (int mm = 0; mm < DT; ++mm) o[mm] *= alpha;
     }
-    uint2 pb[2];
+    // P of keys 8 j4 .. +7 (set 0's four, then set 1's), the B operand of P V
+    u32x4_t pb;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       float p[4];
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) p[rr] = __builtin_amdgcn_exp2f(fmaf(x[h][rr], scale_log2, -m));
-      pb[h] = make_uint2(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]));
-      lsum = dot2_bf16(pb[h].x, kOnes, lsum);         // the sum of the same bf16 p the MFMA uses
-      lsum = dot2_bf16(pb[h].y, kOnes, lsum);
+      pb[2 * h] = pack_bf16x2(p[0], p[1]);
+      pb[2 * h + 1] = pack_bf16x2(p[2], p[3]);
+      lsum = dot2_bf16(pb[2 * h], kOnes, lsum);       // the sum of the same bf16 p the MFMA uses
+      lsum = dot2_bf16(pb[2 * h + 1], kOnes, lsum);
     }
     // this tile's V
-    wait_vm_v<2 * KCF::NLD + 2 * DT>(r.v);
-    // the request's last tile: V entries of keys past the context hold
-    // arbitrary bits and must be zero (p = 0 times a NaN pattern is NaN).
-    // Each lane masks its 4 keys of a half (all kept before the last tile):
-    // no branch, so the compiler needs no copies of the V registers.
+    wait_vm_v<2 * KCF::NLD + DT>(r.v);
+    // V entries of keys past the context (the request's last tile) and of an
+    // absent block hold arbitrary bits and must be zero (p = 0 times a NaN
+    // pattern is NaN).  Each lane masks its 8 keys (all kept before the last
+    // tile): no branch, so the compiler needs no copies of the V registers.
+    {
+      const int nvalid = okh ? end - (k0 + 8 * j4) : 0;
+      u32x4_t mk;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int nvalid = end - (k0 + 16 * h + 4 * j4);
-      const uint32_t mlo = nvalid >= 2 ? 0xFFFFFFFFu : nvalid == 1 ? 0x0000FFFFu : 0u;
-      const uint32_t mhi = nvalid >= 4 ? 0xFFFFFFFFu : nvalid == 3 ? 0x0000FFFFu : 0u;
+      for (int i = 0; i < 4; ++i) mk[i] = nvalid >= 2 * i + 2 ? 0xFFFFFFFFu : nvalid == 2 * i + 1 ? 0x0000FFFFu : 0u;
 #pragma unroll
-      for (int mm = 0; mm < DT; ++mm) {
-        r.v[h][mm].x &= mlo;
-        r.v[h][mm].y &= mhi;
-      }
+      for (int mm = 0; mm < DT; ++mm) r.v[mm] &= mk;
     }
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int mm = 0; mm < DT; ++mm) o[mm] = mfma_pv(r.v[h][mm], pb[h], o[mm]);
+    for (int mm = 0; mm < DT; ++mm) o[mm] = mfma_pv(r.v[mm], pb, o[mm]);
     __builtin_amdgcn_sched_barrier(0);
     issue_v(has_next ? k0_next : 0, r);
     __builtin_amdgcn_sched_barrier(0);
@@ -429,7 +437,7 @@ __device__ __forceinline__ void decode_line_block(PoolDev pool, const bf16_t* __
     const int start = sg.start;
     const int ntiles = (sg.end - start + TK - 1) / TK;
     // q: its loads are followed by the prologue's two tiles
-    wait_vm_q<2 * (KCF::NLD + 2 * DT)>(qf);
+    wait_vm_q<2 * (KCF::NLD + DT)>(qf);
     if (l16 >= G) {
 #pragma unroll
       for (int c = 0; c < KC; ++c) qf[c] = u32x4_t{0u, 0u, 0u, 0u};

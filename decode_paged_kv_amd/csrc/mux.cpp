@@ -583,8 +583,8 @@ int run_mux_round(pkv_mux* m, const pkv_decode_step* d, pkv_prefill_job* p, int3
 
   // ---- decode step on the decode stream (as the level's graph when on) ----
   // on a CU-masked stream a plan of one split per (request, KV head) runs
-  // the whole-line K kernel: with part of the CUs, half-line K reads limit
-  // the bandwidth
+  // the whole-line kernel: with part of the CUs, half-line K reads and
+  // 8-byte V reads limit the bandwidth
   plan.line_k = ds != m->whole && plan.stream_wgs == 0 && plan.num_splits == 1;
   if (d) {
     e = m->use_graphs ? run_decode_graph(m, level, d, dpools, plan, ds)
