@@ -8,10 +8,11 @@
   stream ("PD multiplexing" page, "SGLang's PD multiplexing": the main
   loop).  Every decode and prefill output is checked against the oracle,
   and the level changes only when the prefill starts and after it finishes.
-* Decode on the CU-masked stream of a split level with the equal-splits
-  plan (the whole-line K kernel): head dims 64 and 128, GQA groups 1 to 16,
-  ragged contexts from 1 key, plain and append steps, eager and as graphs,
-  against the oracle.
+* Decode on the CU-masked stream of a split level with one split per
+  (request, KV head) (the whole-line kernel): head dims 64 and 128, GQA
+  groups 1 to 16, block sizes 16 to 128, 1 to 8 head shards, ragged
+  contexts from 1 key, plain and append steps, eager and as graphs, against
+  the oracle.
 """
 
 import numpy as np
@@ -60,7 +61,7 @@ def test_levels_and_cu_masks():
 class _MuxCase:
     """A few layers with a decode batch and one prompt sharing each layer's pool."""
 
-    def __init__(self, layers=3, hq=8, hkv=2, d=128, bs=16, ctx=(100, 37, 300, 64), prompt=500, seed=31):
+    def __init__(self, layers=3, hq=8, hkv=2, d=128, bs=16, ctx=(100, 37, 300, 64), prompt=500, seed=31, shards=1):
         self.L, self.hq, self.hkv, self.d, self.bs = layers, hq, hkv, d, bs
         self.ctx = list(ctx)
         self.N = prompt
@@ -72,7 +73,7 @@ class _MuxCase:
         self.pools, self.hist_k, self.hist_v = [], [], []
         self.kn, self.vn, self.qd, self.qp, self.kp, self.vp = [], [], [], [], [], []
         for l in range(layers):
-            pool = ops.PagedPool(nblk, bs, hkv, 1, d, "bf16").fill_bits(0x7FBF)
+            pool = ops.PagedPool(nblk, bs, hkv, shards, d, "bf16").fill_bits(0x7FBF)
             hk = [inputs.normal((c - 1, hkv, d), 0.5, "bf16", g(inputs.T_K, r, l)) for r, c in enumerate(self.ctx)]
             hv = [inputs.normal((c - 1, hkv, d), 0.5, "bf16", g(inputs.T_V, r, l)) for r, c in enumerate(self.ctx)]
             start = np.concatenate([[0], np.cumsum([c - 1 for c in self.ctx])]).astype(np.int32)
@@ -279,20 +280,27 @@ def _ragged_contexts(n, hi, seed):
 
 # (q-heads, KV heads, head dim, contexts): 64 x 8 pairs take one split each;
 # the smaller batches have contexts of at most 128 keys, also one split
+# (q-heads, KV heads, head dim, block size, head shards, contexts); a
+# 32-key tile takes two blocks at block size 16 and one block (both halves)
+# above it
 _LINE_CASES = [
-    (32, 8, 128, _ragged_contexts(64, 700, 1)),
-    (8, 8, 128, _ragged_contexts(9, 128, 2)),
-    (16, 1, 128, _ragged_contexts(13, 128, 3)),
-    (16, 2, 64, _ragged_contexts(13, 128, 4)),
-    (4, 2, 64, _ragged_contexts(7, 128, 5)),
+    (32, 8, 128, 16, 1, _ragged_contexts(64, 700, 1)),
+    (8, 8, 128, 16, 1, _ragged_contexts(9, 128, 2)),
+    (16, 1, 128, 16, 1, _ragged_contexts(13, 128, 3)),
+    (16, 2, 64, 16, 1, _ragged_contexts(13, 128, 4)),
+    (4, 2, 64, 16, 1, _ragged_contexts(7, 128, 5)),
+    (32, 8, 128, 32, 4, _ragged_contexts(64, 700, 6)),
+    (16, 2, 64, 64, 2, _ragged_contexts(13, 128, 7)),
+    (8, 8, 128, 128, 8, _ragged_contexts(9, 128, 8)),
 ]
 
 
 @pytest.mark.parametrize("append", [False, True])
-@pytest.mark.parametrize("hq,hkv,d,ctx", _LINE_CASES)
-def test_mux_split_level_decode_matches_the_oracle(hq, hkv, d, ctx, append):
-    print(f"split-level decode hq={hq} hkv={hkv} d={d} batch={len(ctx)} append={append}", flush=True)
-    case = _MuxCase(layers=3, hq=hq, hkv=hkv, d=d, ctx=ctx, prompt=400, seed=40 + hq + d)
+@pytest.mark.parametrize("hq,hkv,d,bs,shards,ctx", _LINE_CASES)
+def test_mux_split_level_decode_matches_the_oracle(hq, hkv, d, bs, shards, ctx, append):
+    print(f"split-level decode hq={hq} hkv={hkv} d={d} bs={bs} shards={shards} batch={len(ctx)} append={append}",
+          flush=True)
+    case = _MuxCase(layers=3, hq=hq, hkv=hkv, d=d, bs=bs, ctx=ctx, prompt=400, seed=40 + hq + d + bs, shards=shards)
     # budget 400 with a 400-token prompt: 1 layer per round, 3 rounds
     mux = ops.Mux(0, cu_granularity=8, min_decode_cus=32, sm_group_num=8, decode_bs_divisor=36, token_budget=400)
     try:
