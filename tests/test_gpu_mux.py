@@ -321,3 +321,44 @@ def test_mux_split_level_decode_matches_the_oracle(hq, hkv, d, bs, shards, ctx, 
         case.check_prefill()
     finally:
         mux.close()
+
+
+def _random_line_case(seed):
+    rng = np.random.default_rng(1000 + seed)
+    d = int(rng.choice([64, 128]))
+    g = int(rng.choice([1, 2, 4, 8, 16]))
+    hkv = int(rng.choice([1, 2, 4, 8]))
+    bs = int(rng.choice([16, 32, 64, 128]))
+    shards = int(rng.choice([s for s in (1, 2, 4, 8) if hkv % s == 0]))
+    # one split per (request, KV head): 512 or more pairs, or contexts of at
+    # most 128 keys
+    if rng.random() < 0.5:
+        batch, hi = int(-(-512 // hkv)), int(rng.integers(33, 400))
+    else:
+        batch, hi = int(rng.integers(1, 24)), 128
+    ctx = tuple(int(c) for c in rng.integers(1, hi + 1, batch))
+    return g * hkv, hkv, d, bs, shards, ctx
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_mux_split_level_decode_random_shapes(seed):
+    hq, hkv, d, bs, shards, ctx = _random_line_case(seed)
+    print(f"random split-level decode seed={seed}: hq={hq} hkv={hkv} d={d} bs={bs} shards={shards} "
+          f"batch={len(ctx)} max ctx={max(ctx)}", flush=True)
+    case = _MuxCase(layers=2, hq=hq, hkv=hkv, d=d, bs=bs, ctx=ctx, prompt=256, seed=500 + seed, shards=shards)
+    mux = ops.Mux(0, cu_granularity=8, min_decode_cus=32, sm_group_num=8, decode_bs_divisor=36, token_budget=256)
+    try:
+        groups = mux.groups()
+        mux.set_decode_append(seed % 2 == 1)
+        for i in range(2):
+            for o in case.o_dec:
+                o.zero_()
+            lvl, _ = mux.run_round(case.decode, case.prefill)
+            torch.cuda.synchronize()
+            assert all(x > 0 for x in groups[lvl]), "a split level"
+            case.check_decode()
+        mux.wait_prefill()
+        torch.cuda.synchronize()
+        case.check_prefill()
+    finally:
+        mux.close()
