@@ -890,34 +890,44 @@ def bench_mfma_peak(args):
     """The device's dense bf16 matrix-core rate and its shader clock while the matrix cores are busy: 512
     workgroups of 4 waves (two per CU, two waves per SIMD), each wave running four independent chains of
     32x32x16 bf16 MFMAs, timed with HIP events on the launching stream; every wave also reads the shader clock
-    counter and the 100 MHz reference counter around its loop (kernel in decode_paged_kv_amd/calib)."""
+    counter and the 100 MHz reference counter around its loop (kernel in decode_paged_kv_amd/calib).  The value
+    is with constant operands; metrics.random_operands is the same stream with operands that change from one
+    MFMA to the next."""
     lib = _calib_lib()
     blocks, iters = 512, 4096
     sink = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
     clocks = torch.zeros(blocks * 4 * 2, dtype=torch.int64, device="cuda")
     stream = torch.cuda.Stream()
-
-    def launch():
-        rc = lib.pkv_calib_mfma(iters, blocks, sink.data_ptr(), clocks.data_ptr(), stream.cuda_stream)
-        if rc != 0:
-            raise RuntimeError(f"pkv_calib_mfma: HIP error {rc}")
-
-    for _ in range(max(1, args.warmup)):
-        launch()
-    torch.cuda.synchronize()
-    times = []
-    for _ in range(max(3, args.steps)):
-        a, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        launch()
-        e.record(stream)
-        torch.cuda.synchronize()
-        times.append(a.elapsed_time(e))
-    ms = float(np.median(times))
     flops = blocks * 4 * iters * 4 * 32 * 32 * 16 * 2
+
+    def run(fn, name):
+        def launch():
+            rc = fn(iters, blocks, sink.data_ptr(), clocks.data_ptr(), stream.cuda_stream)
+            if rc != 0:
+                raise RuntimeError(f"{name}: HIP error {rc}")
+
+        for _ in range(max(1, args.warmup)):
+            launch()
+        torch.cuda.synchronize()
+        times = []
+        for _ in range(max(3, args.steps)):
+            a, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            launch()
+            e.record(stream)
+            torch.cuda.synchronize()
+            times.append(a.elapsed_time(e))
+        ck = clocks.view(-1, 2).cpu().numpy().astype(np.float64)
+        return times, ck[:, 0] / (ck[:, 1] / 100e6) / 1e9
+
+    # operands that change from one MFMA to the next (as in attention), then
+    # the constant operands of the headline calibration (last, so the
+    # kernel trace of this workload ends with it)
+    rtimes, rghz = run(lib.pkv_calib_mfma_random, "pkv_calib_mfma_random")
+    rms = float(np.median(rtimes))
+    times, ghz = run(lib.pkv_calib_mfma, "pkv_calib_mfma")
+    ms = float(np.median(times))
     tflops = flops / (ms * 1e-3) / 1e12
-    ck = clocks.view(-1, 2).cpu().numpy().astype(np.float64)
-    ghz = ck[:, 0] / (ck[:, 1] / 100e6) / 1e9
     clk = float(np.median(ghz))
     # the rate the same MFMA stream would reach at the nominal 2.4 GHz, and the peak at the measured clock
     peak_at_clock = BF16_PEAK_TFLOPS * clk / 2.4
@@ -932,7 +942,12 @@ def bench_mfma_peak(args):
             "metrics": {"shader_clock_ghz_median": round(clk, 3), "shader_clock_ghz_min": round(float(ghz.min()), 3),
                         "shader_clock_ghz_max": round(float(ghz.max()), 3),
                         "peak_at_measured_clock_tflops": round(peak_at_clock, 1),
-                        "frac_of_peak_at_measured_clock": round(tflops / peak_at_clock, 4)}}
+                        "frac_of_peak_at_measured_clock": round(tflops / peak_at_clock, 4),
+                        "random_operands": {"tflops": round(flops / (rms * 1e-3) / 1e12, 1),
+                                            "ms_per_launch": round(rms, 4),
+                                            "shader_clock_ghz_median": round(float(np.median(rghz)), 3),
+                                            "note": "eight pseudo-random bf16 operand pairs cycled through by "
+                                                    "consecutive MFMAs"}}}
 
 
 # ----------------------------------------------------- hbm-ceiling ----
@@ -944,6 +959,8 @@ def _calib_lib():
     lib = C.CDLL(b.CALIB_LIB)
     lib.pkv_calib_mfma.restype = C.c_int
     lib.pkv_calib_mfma.argtypes = [C.c_int, C.c_int, C.c_void_p, C.c_void_p, C.c_void_p]
+    lib.pkv_calib_mfma_random.restype = C.c_int
+    lib.pkv_calib_mfma_random.argtypes = [C.c_int, C.c_int, C.c_void_p, C.c_void_p, C.c_void_p]
     lib.pkv_calib_tiled_read.restype = C.c_int
     lib.pkv_calib_tiled_read.argtypes = [C.c_void_p, C.c_void_p, C.c_int, C.c_int, C.c_int, C.c_void_p, C.c_void_p]
     lib.pkv_calib_tiled_copy.restype = C.c_int
@@ -1059,13 +1076,23 @@ def _free_device():
 
 
 def bench_all(args):
-    """The headline workload (Qwen3-32B-like 16K prompt at chunks 2048 and 512: prefill TFLOP/s is ``value``)
-    and, under ``metrics["workloads"]``, the Llama-3-8B-shaped step (decode GB/s), the 70B relayout (GB/s) and the
+    """The headline workload (Qwen3-32B-like 16K prompt at chunks 2048 and 512: prefill TFLOP/s is ``value``),
+    the matrix-core calibration of the same box (``metrics["mfma_calibration"]``) and, under
+    ``metrics["workloads"]``, the Llama-3-8B-shaped step (decode GB/s), the 70B relayout (GB/s) and the
     PD-multiplexing round (decode step ms), each with its own roofline, traffic and oracle baseline.  The
     workloads run one after the other; each frees its device memory before the next."""
     t0 = time.perf_counter()
     res = bench_qwen3_32b(args)
     _free_device()
+    # the dense bf16 rate this box sustains on a pure MFMA stream, with
+    # constant operands and with operands that change from one MFMA to the
+    # next (the headline's roofline peak stays the published figure)
+    cal = bench_mfma_peak(args)
+    rnd = cal["metrics"]["random_operands"]
+    res["metrics"]["mfma_calibration"] = {
+        "constant_operands_tflops": cal["value"], "constant_operands_clock_ghz": cal["metrics"]["shader_clock_ghz_median"],
+        "random_operands_tflops": rnd["tflops"], "random_operands_clock_ghz": rnd["shader_clock_ghz_median"],
+        "prefill_value_over_random_operands_rate": round(res["value"] / rnd["tflops"], 4)}
     sub = {}
     for name, fn in (("llama3_8b", bench_llama3_8b), ("relayout_70b", bench_relayout_70b), ("pdmux", bench_pdmux)):
         t1 = time.perf_counter()

@@ -55,13 +55,15 @@ def test_calibration_library_exports_and_rejects_bad_arguments():
         pytest.skip("libpkv_calib.so not built")
     out = subprocess.run(["nm", "-D", "--defined-only", b.CALIB_LIB], capture_output=True, text=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
-    assert {"pkv_calib_mfma", "pkv_calib_tiled_read", "pkv_calib_tiled_copy", "pkv_calib_copy"} <= exported
+    assert {"pkv_calib_mfma", "pkv_calib_mfma_random", "pkv_calib_tiled_read", "pkv_calib_tiled_copy",
+            "pkv_calib_copy"} <= exported
     cl = C.CDLL(b.CALIB_LIB)
     cl.pkv_calib_tiled_read.argtypes = [C.c_void_p, C.c_void_p, C.c_int, C.c_int, C.c_int, C.c_void_p, C.c_void_p]
     cl.pkv_calib_tiled_copy.argtypes = [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_int, C.c_int, C.c_int,
                                         C.c_void_p]
     cl.pkv_calib_copy.argtypes = [C.c_void_p, C.c_void_p, C.c_size_t, C.c_int, C.c_void_p]
     cl.pkv_calib_mfma.argtypes = [C.c_int, C.c_int, C.c_void_p, C.c_void_p, C.c_void_p]
+    cl.pkv_calib_mfma_random.argtypes = [C.c_int, C.c_int, C.c_void_p, C.c_void_p, C.c_void_p]
     fake = 0x100000
     assert cl.pkv_calib_tiled_read(None, fake, 1, 1, 8, fake, None) == 1
     assert cl.pkv_calib_tiled_read(fake, fake, 1, 1, 5, fake, None) == 1       # unroll not built
@@ -70,6 +72,7 @@ def test_calibration_library_exports_and_rejects_bad_arguments():
     assert cl.pkv_calib_copy(fake, fake, 24, 1, None) == 1                      # not a multiple of 16
     assert cl.pkv_calib_copy(fake + 8, fake, 32, 1, None) == 1                  # misaligned
     assert cl.pkv_calib_mfma(0, 1, fake, fake, None) == 1
+    assert cl.pkv_calib_mfma_random(12, 1, fake, fake, None) == 1              # not a multiple of 8
 
 
 def _pool(**kw):
