@@ -240,9 +240,10 @@ attn_decode_bf16_kernel(PoolDev pool, const bf16_t* __restrict__ q, bf16_t* __re
                         int num_q_heads, float scale_log2, int split_tokens, int num_splits, int max_len,
                         float* __restrict__ part_o, float* __restrict__ part_ml, const bf16_t* __restrict__ k_new,
                         const bf16_t* __restrict__ v_new) {
+  __shared__ DecodeBf16Smem<D, G> sm;
   decode_bf16_block<D, G, STREAM, APPEND>(pool, q, out, bt, bt_stride, ctx, batch, num_q_heads, scale_log2,
                                           split_tokens, num_splits, max_len, part_o, part_ml, k_new, v_new,
-                                          blockIdx.x, blockIdx.y, blockIdx.z, gridDim.x);
+                                          blockIdx.x, blockIdx.y, blockIdx.z, gridDim.x, sm);
 }
 
 // grid (1, KV heads, requests): one workgroup per (request, KV head)

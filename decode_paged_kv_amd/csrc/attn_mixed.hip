@@ -26,6 +26,14 @@
 namespace pkv {
 namespace {
 
+// A workgroup is either kind, so the two kinds' LDS share one allocation
+// (their sum would leave room for only one workgroup per CU at G >= 8).
+template <int D, int G>
+union MixedSmem {
+  prefill_impl::PrefillSmem<D, 1> prefill;
+  decode_impl::DecodeBf16Smem<D, G> decode;
+};
+
 template <int D, int G>
 __global__ void __launch_bounds__(256, 2)
 attn_mixed_bf16_kernel(PoolDev pool,
@@ -40,10 +48,12 @@ attn_mixed_bf16_kernel(PoolDev pool,
                        int pbt_stride, const int32_t* __restrict__ start_loc, const int32_t* __restrict__ chunk_start,
                        int pbatch, int ntiles, int pf_items, int pf_blocks, int pf_max_total, int num_q_heads,
                        float scale_log2) {
+  __shared__ MixedSmem<D, G> sm;
   if ((int)blockIdx.x < pf_blocks) {
     prefill_impl::prefill_bf16_block<D, 1>(pool, pq, pout, pbt, pbt_stride, start_loc, chunk_start, pbatch, ntiles,
                                            num_q_heads, G, scale_log2, pf_items, pf_max_total, blockIdx.x,
-                                           pf_blocks);
+                                           pf_blocks, sm.prefill.kb0, sm.prefill.kb1, sm.prefill.vb0,
+                                           sm.prefill.vb1);
   } else {
     const int bid = blockIdx.x - pf_blocks;
     const int hkv = num_q_heads / G;
@@ -53,7 +63,7 @@ attn_mixed_bf16_kernel(PoolDev pool,
     const int kvh = rem / num_splits, split = rem - kvh * num_splits;
     decode_impl::decode_bf16_block<D, G, false>(pool, dq, dout, dbt, dbt_stride, ctx, dbatch, num_q_heads,
                                                 scale_log2, split_tokens, num_splits, max_len, part_o, part_ml, nullptr,
-                                                nullptr, split, kvh, b, 0);
+                                                nullptr, split, kvh, b, 0, sm.decode);
   }
 }
 

@@ -47,8 +47,9 @@ attn_prefill_bf16_kernel(PoolDev pool, const bf16_t* __restrict__ q, bf16_t* __r
                          const int32_t* __restrict__ bt, int bt_stride, const int32_t* __restrict__ start_loc,
                          const int32_t* __restrict__ chunk_start, int batch, int ntiles, int num_q_heads,
                          int group, float scale_log2, int total_items, int max_total) {
+  __shared__ __attribute__((aligned(1024))) PrefillTiles<D, NG> kb0, kb1, vb0, vb1;
   prefill_bf16_block<D, NG>(pool, q, out, bt, bt_stride, start_loc, chunk_start, batch, ntiles, num_q_heads, group,
-                            scale_log2, total_items, max_total, blockIdx.x, gridDim.x);
+                            scale_log2, total_items, max_total, blockIdx.x, gridDim.x, kb0, kb1, vb0, vb1);
 }
 
 // fp32: one wave per (query row, q-head); lane owns head-dim columns.

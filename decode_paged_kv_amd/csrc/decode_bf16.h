@@ -169,10 +169,9 @@ __device__ __forceinline__ void decode_bf16_block(PoolDev pool, const bf16_t* __
                                                   int num_splits, int max_len, float* __restrict__ part_o,
                                                   float* __restrict__ part_ml, const bf16_t* __restrict__ k_new,
                                                   const bf16_t* __restrict__ v_new, int bx, int by, int bz,
-                                                  int nbx) {
+                                                  int nbx, DecodeBf16Smem<D, G>& sm) {
   static_assert(G >= 1 && G <= 16, "the q-heads of a KV head are the 16 MFMA columns");
   constexpr int KC = D / 32, DT = D / 16, TK = 32;
-  __shared__ DecodeBf16Smem<D, G> sm;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -221,13 +220,14 @@ __device__ __forceinline__ void decode_bf16_block(PoolDev pool, const bf16_t* __
 
   const int k_voff = (l16 * D + 8 * j4) * 2;                    // bytes within a half's 16 K rows
   const int v_voff = (l16 * bs + 4 * j4) * 2;                   // dim l16 of a 16-dim slab, 4 keys
-  // block ids of the tile at k0 (-1: past the split or out of range)
-  auto fetch_ids = [&](int k0, int (&ids)[2]) {
+  // block ids of the tile at k0 (-1: past the split or out of range) from
+  // the table entries of its two halves (raw, read beforehand)
+  auto ids_from = [&](int k0, const int (&raw)[2], int (&ids)[2]) {
     bool bad = false;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int key16 = k0 + 16 * h;
-      const int blk = key16 < end ? table[key16 >> pool.bs_shift] : -1;
+      const int blk = key16 < end ? raw[h] : -1;
       const bool ok = blk >= 0 && blk < pool.num_blocks;
       bad |= key16 < end && !ok;
       // the id is wave-uniform; saying so keeps the descriptors built from
@@ -235,6 +235,13 @@ __device__ __forceinline__ void decode_bf16_block(PoolDev pool, const bf16_t* __
       ids[h] = __builtin_amdgcn_readfirstlane(ok ? blk : -1);
     }
     if (bad && lane == 0) flag_error(pool.err, PKV_ERRBIT_BLOCK_ID);
+  };
+  // the same, reading the entries
+  auto fetch_ids = [&](int k0, int (&ids)[2]) {
+    int raw[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) raw[h] = k0 + 16 * h < end ? table[(k0 + 16 * h) >> pool.bs_shift] : -1;
+    ids_from(k0, raw, ids);
   };
   auto issue_k = [&](int k0, DecodeTile<D>& r) {
 #pragma unroll
@@ -361,6 +368,23 @@ __device__ __forceinline__ void decode_bf16_block(PoolDev pool, const bf16_t* __
     }
     if (wave + 2 * W < ntiles) fetch_ids(sg.start + (wave + 2 * W) * TK, ids_next);
   };
+  // the same, with the block-table entries of the first three tiles read
+  // ahead (before the context length was known)
+  auto prologue_pre = [&](const Seg& sg, const int (&raw)[3][2]) {
+    bind(sg);
+    const int ntiles = (sg.end - sg.start + TK - 1) / TK;
+    if (wave < ntiles) {
+      ids_from(sg.start + wave * TK, raw[0], ra.blk);
+      issue_k(sg.start + wave * TK, ra);
+      issue_v(sg.start + wave * TK, ra);
+    }
+    if (wave + W < ntiles) {
+      ids_from(sg.start + (wave + W) * TK, raw[1], rb.blk);
+      issue_k(sg.start + (wave + W) * TK, rb);
+      issue_v(sg.start + (wave + W) * TK, rb);
+    }
+    if (wave + 2 * W < ntiles) ids_from(sg.start + (wave + 2 * W) * TK, raw[2], ids_next);
+  };
   // the tiles of the bound segment (its prologue has run)
   auto body = [&](const Seg& sg) {
 #pragma unroll
@@ -468,6 +492,17 @@ __device__ __forceinline__ void decode_bf16_block(PoolDev pool, const bf16_t* __
   if constexpr (!STREAM) {
     // one segment: split bx of (request bz, KV head by)
     const int split = bx, kvh = by, b = bz;
+    // the table entries of this wave's first three tiles do not depend on
+    // the context length: read them together with it
+    int raw[3][2];
+    {
+      const int32_t* tb = bt + (size_t)b * bt_stride;
+#pragma unroll
+      for (int i = 0; i < 3; ++i)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          raw[i][h] = tb[min((split * split_tokens + (wave + i * kWaves) * TK + 16 * h) >> pool.bs_shift, bt_stride - 1)];
+    }
     int L = ctx[b];
     if (L > cap) {                              // past max_context_len: cut, flagged
       if (threadIdx.x == 0 && split == 0 && kvh == 0) flag_error(pool.err, PKV_ERRBIT_CONTEXT);
@@ -479,7 +514,7 @@ __device__ __forceinline__ void decode_bf16_block(PoolDev pool, const bf16_t* __
     const bool last = APPEND && ctx[b] <= cap && end == L;
     const Seg sg{b, kvh, start, last ? end - 1 : end, L <= split_tokens,
                  ((size_t)b * num_q_heads + (size_t)kvh * G) * num_splits + split, num_splits, last};
-    prologue(sg);
+    prologue_pre(sg, raw);
     body(sg);
     const bool add_new = append_key(sg);
     merge(sg, add_new);

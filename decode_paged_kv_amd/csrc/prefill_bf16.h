@@ -114,6 +114,17 @@ struct BlockPlan {
 };
 static_assert(BlockPlan<128>::valid() && BlockPlan<64>::valid(), "block schedule");
 
+// The LDS of one workgroup: double-buffered K and V tiles per key-tile
+// group, four separate arrays so the compiler sees that a DMA into one
+// buffer never overlaps reads of another.  Declared by the kernel (the
+// mixed-batch kernel overlays them with the decode workgroups' LDS).
+template <int D, int NG>
+using PrefillTiles = char[NG][PrefillCfg<D>::TILE];
+template <int D, int NG>
+struct PrefillSmem {
+  __attribute__((aligned(1024))) PrefillTiles<D, NG> kb0, kb1, vb0, vb1;
+};
+
 // One workgroup's work: block `bid` of a grid of `nblocks` (a multiple of
 // the XCD count) over `total_items` work items.  NG = key-tile groups per
 // workgroup.  NG = 1: 4 waves, two workgroups per CU.  NG = 2 (small
@@ -126,14 +137,10 @@ __device__ __forceinline__ void prefill_bf16_block(PoolDev pool, const bf16_t* _
                                                    int bt_stride, const int32_t* __restrict__ start_loc,
                                                    const int32_t* __restrict__ chunk_start, int batch, int ntiles,
                                                    int num_q_heads, int group, float scale_log2, int total_items,
-                                                   int max_total, int bid, int nblocks) {
+                                                   int max_total, int bid, int nblocks,
+                                                   PrefillTiles<D, NG>& kb0, PrefillTiles<D, NG>& kb1,
+                                                   PrefillTiles<D, NG>& vb0, PrefillTiles<D, NG>& vb1) {
   using C = PrefillCfg<D>;
-  // double-buffered K and V tiles; four separate arrays so the compiler
-  // sees that a DMA into one buffer never overlaps reads of another
-  __shared__ __attribute__((aligned(1024))) char kb0[NG][C::TILE];
-  __shared__ __attribute__((aligned(1024))) char kb1[NG][C::TILE];
-  __shared__ __attribute__((aligned(1024))) char vb0[NG][C::TILE];
-  __shared__ __attribute__((aligned(1024))) char vb1[NG][C::TILE];
 
   // ---- work item (XCD-contiguous runs) ----
   const int per_xcd = nblocks / kXcds;
