@@ -91,17 +91,17 @@ def relayout_bytes(n, hkv, d, esize=2):
 PMC_SCALE = {"fetch": 2.0, "write": 1.0}
 TRAFFIC = {
     "attn_decode": {"sources": ['decode_paged_kv_amd/csrc/attn_decode.hip', 'decode_paged_kv_amd/csrc/decode_bf16.h', 'decode_paged_kv_amd/csrc/pkv_internal.h'],
-                    "sha256": "87eb4716c213a5e239fade5d4382f3743e29bd139c7e6f3a7be5af3efa32d5e5",
-                    "fetch_kib": 65947.23, "write_kib": 512.00},
+                    "sha256": "d59f9903fbaf3d3ceb8d6d7f1409f324651dae4daee4c20a6b568c4fea4f6e39",
+                    "fetch_kib": 65947.92, "write_kib": 512.00},
     "attn_prefill_chunk": {"sources": ['decode_paged_kv_amd/csrc/attn_prefill.hip', 'decode_paged_kv_amd/csrc/prefill_bf16.h', 'decode_paged_kv_amd/csrc/pkv_internal.h'],
-                           "sha256": "2eb83c49082171c269c39f44cab447848018e0b872f6cf4536f63d8ccc64aa63",
-                           "fetch_kib": 28005.34, "write_kib": 15974.17},
+                           "sha256": "f1c506b4032bde6f62eabd80daefa7ee583efb0b26015f98ebfe9a76b1e41535",
+                           "fetch_kib": 28005.17, "write_kib": 15974.16},
     "kv_relayout": {"sources": ['decode_paged_kv_amd/csrc/kv_ops.hip', 'decode_paged_kv_amd/csrc/pkv_internal.h'],
                     "sha256": "2af290f6b8645156babeeffc1daaf7f7995952fecb4c047393f841a8662d15ff",
-                    "fetch_kib": 8233.69, "write_kib": 16386.05},
+                    "fetch_kib": 8233.68, "write_kib": 16391.06},
     "attn_decode_line": {"sources": ['decode_paged_kv_amd/csrc/attn_decode.hip', 'decode_paged_kv_amd/csrc/decode_line.h', 'decode_paged_kv_amd/csrc/decode_bf16.h', 'decode_paged_kv_amd/csrc/pkv_internal.h'],
-                         "sha256": "2e41b85238339a36520e1877cb727653f4919edb98c81400a730bcc10138d100",
-                         "fetch_kib": 525629.10, "write_kib": 1024.00},
+                         "sha256": "b7a4c9dad65532bbe3349a13279d35cef7b828d934c263785b782dbc108e233d",
+                         "fetch_kib": 525630.24, "write_kib": 1024.00},
 }
 
 
