@@ -6,7 +6,9 @@ import ctypes as C
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libpkv.so")
+# PKV_LIB_PATH selects another build of the same library (e.g. one whose
+# host code is compiled with sanitizers)
+LIB_PATH = os.environ.get("PKV_LIB_PATH") or os.path.join(HERE, "libpkv.so")
 
 MAX_SHARDS = 16
 F32, BF16, FP8_E4M3 = 0, 1, 2
