@@ -86,6 +86,23 @@ def test_decode_longer_max_context_than_needed():
     assert_close(got, oracle_decode(sc, q), "bf16", "decode(max_ctx 4000)")
 
 
+@pytest.mark.parametrize("bs", [16, 64])
+def test_decode_short_contexts_in_a_table_of_exact_width(bs):
+    # 64 requests x 8 KV heads: one workgroup per pair, whose waves read the
+    # table entries of their first three tiles before the context length is
+    # known; with contexts of 1-100 keys and a table exactly as wide as the
+    # longest needs, most of those entries lie past the context (the reads
+    # are clamped to the table row and discarded)
+    lengths = [int(x) for x in np.random.default_rng(41).integers(1, 101, 64)]
+    sc = Scenario(num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=bs, dtype="bf16", lengths=lengths,
+                  pool_blocks=64 * (-(-100 // bs)) + 8, scale=0.5, seed=41)
+    assert sc.tables.shape[1] == -(-max(lengths) // bs)
+    sc.write_all()
+    q = _q(sc, (64, 32, 128), scale=0.5)
+    got = run_decode(sc, q)
+    assert_close(got, oracle_decode(sc, q), "bf16", f"decode(64 short contexts, bs {bs})")
+
+
 def run_prefill_chunks(sc: Scenario, q_np, chunk, req=0):
     """Write + attend chunk by chunk for one request; returns the stacked GPU rows."""
     n = sc.lengths[req]
