@@ -83,6 +83,9 @@ def _check_oracle(sc, nd, S, chunk, qd, qp, out_d, out_p):
     ("bf16", 32, 8, 128, 16, [int(x) for x in np.random.default_rng(21).integers(1, 700, 64)], 3000, 512),
     # and a chunk of 2048 (16 query tiles x 32 q-heads = 512): same prefill variant as attn_prefill_chunk
     ("bf16", 32, 8, 128, 16, [int(x) for x in np.random.default_rng(22).integers(1, 700, 64)], 6000, 2112),
+    # G = 8 (Qwen3-32B heads) with both parts at full size: 512 pairs and a 2048-token chunk (16 x 64 >= 512);
+    # the two kinds of workgroup share one LDS allocation, so two of either fit on a CU
+    ("bf16", 64, 8, 128, 16, [int(x) for x in np.random.default_rng(23).integers(1, 700, 64)], 6000, 2112),
     # few pairs, long contexts: the decode part takes equal splits and a merge kernel follows
     ("bf16", 64, 8, 128, 16, [4097, 2048, 77, 1500], 2500, 2048),
     ("bf16", 16, 1, 64, 32, [1, 333, 1024], 900, 300),      # G = 16, head dim 64
