@@ -1077,9 +1077,10 @@ def _free_device():
 
 def bench_all(args):
     """The headline workload (Qwen3-32B-like 16K prompt at chunks 2048 and 512: prefill TFLOP/s is ``value``),
-    the matrix-core calibration of the same box (``metrics["mfma_calibration"]``) and, under
-    ``metrics["workloads"]``, the Llama-3-8B-shaped step (decode GB/s), the 70B relayout (GB/s) and the
-    PD-multiplexing round (decode step ms), each with its own roofline, traffic and oracle baseline.  The
+    the matrix-core calibration of the same box (``metrics["mfma_calibration"]``), under
+    ``metrics["workloads"]`` the Llama-3-8B-shaped step (decode GB/s), the 70B relayout (GB/s) and the
+    PD-multiplexing round (decode step ms), each with its own roofline, traffic and oracle baseline, and the HBM
+    calibration at the decode's and the relayout's access patterns (``metrics["hbm_calibration"]``).  The
     workloads run one after the other; each frees its device memory before the next."""
     t0 = time.perf_counter()
     res = bench_qwen3_32b(args)
@@ -1102,6 +1103,18 @@ def bench_all(args):
                                        "roofline", "metrics", "cpu_baseline") if k in r}
         sub[name]["wall_s"] = round(time.perf_counter() - t1, 1)
     res["metrics"]["workloads"] = sub
+    # what HBM delivers on this machine to the decode's and the relayout's own
+    # access patterns (the rooflines' peak stays the published 8 TB/s)
+    hb = bench_hbm_ceiling(args)["metrics"]
+    _free_device()
+    best = lambda prefix: max(v["gbps"] for k, v in hb.items() if k.startswith(prefix))  # noqa: E731
+    r134, r315, ct = best("read_134mb"), best("read_315mb"), best("copy_tiled")
+    res["metrics"]["hbm_calibration"] = {
+        "tiled_read_134mb_gbps": r134, "tiled_read_315mb_gbps": r315, "tiled_copy_16.8mb_gbps": ct,
+        "contiguous_copy_16.8mb_gbps": best("copy_contiguous"),
+        "llama_decode_over_tiled_read": round(sub["llama3_8b"]["value"] / r134, 4),
+        "qwen_decode_over_tiled_read": round(res["metrics"]["decode_attn_gbps"] / r315, 4),
+        "relayout_over_tiled_copy": round(sub["relayout_70b"]["value"] / ct, 4)}
     res["metrics"]["wall_s"] = round(time.perf_counter() - t0, 1)
     return res
 
