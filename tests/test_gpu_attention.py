@@ -119,20 +119,22 @@ def run_prefill_chunks(sc: Scenario, q_np, chunk, req=0):
     return np.concatenate([inputs.as_float(from_dev(o, sc.dtype), sc.dtype) for o in outs])
 
 
-@pytest.mark.parametrize("dtype,hq,hkv,d,bs,n,chunk", [
-    ("f32", 4, 2, 64, 16, 256, 64),          # the tiny check: 4 causal chunks of 64
-    ("bf16", 32, 8, 128, 16, 1024, 512),     # Llama-3-8B shape, 2 chunks of 512 (all rows)
-    ("bf16", 32, 8, 128, 16, 1024, 1024),    # same prompt one-shot
-    ("bf16", 64, 8, 128, 16, 1100, 1100),    # >= 512 workgroups: one key-tile group per workgroup
-    ("bf16", 8, 2, 128, 16, 300, 77),        # ragged chunks and tail
-    ("bf16", 16, 1, 64, 32, 517, 200),       # G = 16, head dim 64
-    ("bf16", 4, 4, 128, 64, 130, 130),       # G = 1, one chunk of 130
-    ("bf16", 8, 8, 64, 128, 1, 1),           # a single token
-    ("f32", 4, 2, 128, 32, 70, 33),
+@pytest.mark.parametrize("dtype,hq,hkv,d,bs,n,chunk,shards", [
+    ("f32", 4, 2, 64, 16, 256, 64, 1),          # the tiny check: 4 causal chunks of 64
+    ("bf16", 32, 8, 128, 16, 1024, 512, 1),     # Llama-3-8B shape, 2 chunks of 512 (all rows)
+    ("bf16", 32, 8, 128, 16, 1024, 1024, 1),    # same prompt one-shot
+    ("bf16", 64, 8, 128, 16, 1100, 1100, 1),    # >= 512 workgroups: one key-tile group per workgroup
+    ("bf16", 8, 2, 128, 16, 300, 77, 1),        # ragged chunks and tail
+    ("bf16", 16, 1, 64, 32, 517, 200, 1),       # G = 16, head dim 64
+    ("bf16", 4, 4, 128, 64, 130, 130, 1),       # G = 1, one chunk of 130
+    ("bf16", 8, 8, 64, 128, 1, 1, 1),           # a single token
+    ("f32", 4, 2, 128, 32, 70, 33, 1),
+    ("bf16", 32, 16, 64, 16, 700, 300, 16),     # the most shards (16 x 1 head), G = 2
+    ("bf16", 64, 8, 128, 32, 1300, 600, 4),     # Qwen3-32B heads in 4 shards of 2
 ])
-def test_chunked_prefill_matches_one_shot_oracle(dtype, hq, hkv, d, bs, n, chunk):
+def test_chunked_prefill_matches_one_shot_oracle(dtype, hq, hkv, d, bs, n, chunk, shards):
     sc = Scenario(num_q_heads=hq, num_kv_heads=hkv, head_dim=d, block_size=bs, dtype=dtype, lengths=[n],
-                  pool_blocks=-(-n // bs) + 2, scale=0.5 if dtype == "bf16" else 1.0, seed=8)
+                  pool_blocks=-(-n // bs) + 2, num_shards=shards, scale=0.5 if dtype == "bf16" else 1.0, seed=8)
     q = _q(sc, (n, hq, d), scale=0.5 if dtype == "bf16" else 1.0)
     got = run_prefill_chunks(sc, q, chunk)
     ref = oa.prefill(inputs.as_float(q, dtype), sc.kf(0), sc.vf(0))
