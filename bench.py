@@ -438,6 +438,60 @@ def bench_qwen3_32b(args):
     return result
 
 
+def bench_stall_free_qwen(args):
+    """One stall-free step of the Qwen3-32B-like batch (G = 8): the 16 decodes and what they leave of a
+    2048-token budget for the 16K prompt at position 8192, every layer's attention as one attn_mixed_batch
+    launch against attn_decode + attn_prefill_chunk.  16 layers (own pools), per-layer times."""
+    w = workloads.QWEN3_32B
+    L, hq, hkv, d, bs = 16, w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size
+    ctxs = [int(x) for x in w.decode_contexts()]
+    B, N = len(ctxs), w.prompt_len
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(w.seed)
+    stream = torch.cuda.Stream()
+    sh = stream.cuda_stream
+    tables = make_tables(w, ctxs + [N], bs, w.pool_blocks)
+    dec_bt, pr_bt = i32(tables[:B]), i32(tables[B:B + 1])
+    pools = [ops.PagedPool(w.pool_blocks, bs, hkv, 1, d, "bf16") for _ in range(L)]
+    for p in pools:
+        fill_pool_random(p, gen)
+    maxc = max(ctxs)
+    s0 = N // 2
+    t = ops.stall_free_chunk(2048, B, N - s0)
+    q_dec = [rand_bf16((B, hq, d), gen) for _ in range(L)]
+    o_dec = [torch.empty((B, hq, d), dtype=torch.bfloat16, device="cuda") for _ in range(L)]
+    q_pr = [rand_bf16((t, hq, d), gen) for _ in range(L)]
+    o_pr = [torch.empty((t, hq, d), dtype=torch.bfloat16, device="cuda") for _ in range(L)]
+    ctx_t, sl, cs = i32(ctxs), i32([0, t]), i32([s0])
+    ws = torch.zeros(max(16, ops.attn_decode_workspace_size(B, hq, maxc, d)), dtype=torch.uint8, device="cuda")
+
+    def step(fused):
+        def run():
+            for l in range(L):
+                if fused:
+                    ops.attn_mixed_batch(pools[l], q_dec[l], o_dec[l], dec_bt, ctx_t, maxc, q_pr[l], o_pr[l], pr_bt,
+                                         sl, cs, t, hq, workspace=ws, stream=sh, max_total_len=N)
+                else:
+                    ops.attn_decode(pools[l], q_dec[l], o_dec[l], dec_bt, ctx_t, maxc, hq, workspace=ws, stream=sh)
+                    ops.attn_prefill_chunk(pools[l], q_pr[l], o_pr[l], pr_bt, sl, cs, t, hq, stream=sh,
+                                           max_total_len=N)
+        return run
+
+    pg = PhaseGraphs(stream)
+    pg.capture("fused", step(True))
+    pg.capture("two_launches", step(False))
+    tm = time_replays(pg, ["fused", "two_launches"], args.steps, args.warmup)
+    fused, two = tm["fused"] / L, tm["two_launches"] / L
+    return {"metric": "stall-free step attention, ms per layer", "value": round(fused, 4), "unit": "ms",
+            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(tm["fused"], 3),
+            "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": f"stall-free step, Qwen3-32B-like heads (64/8, d128, bs16): decode 16 x "
+                                   f"U[2048,8192] + a {t}-token chunk of the 16K prompt at {s0} (budget 2048); "
+                                   f"{L} layers, own pools"},
+            "metrics": {"fused_ms_per_layer": round(fused, 4), "two_launches_ms_per_layer": round(two, 4),
+                        "fused_over_two_launches": round(fused / two, 4), "chunk": t, "chunk_start": s0}}
+
+
 def cpu_baseline_prefill(w, seconds=10.0):
     from oracle import attention as oa
     hq, hkv, d, N = w.num_q_heads, w.num_kv_heads, w.head_dim, w.prompt_len
@@ -1103,6 +1157,10 @@ def bench_all(args):
                                        "roofline", "metrics", "cpu_baseline") if k in r}
         sub[name]["wall_s"] = round(time.perf_counter() - t1, 1)
     res["metrics"]["workloads"] = sub
+    # the fused stall-free launch at G = 8 (the mixed-batch kernel)
+    sf = bench_stall_free_qwen(args)
+    _free_device()
+    res["metrics"]["stall_free_qwen3_32b"] = {**sf["metrics"], "layers": 16}
     # what HBM delivers on this machine to the decode's and the relayout's own
     # access patterns (the rooflines' peak stays the published 8 TB/s)
     hb = bench_hbm_ceiling(args)["metrics"]
@@ -1122,7 +1180,8 @@ def bench_all(args):
 # --------------------------------------------------------------- main ----
 BENCHES = {"all": bench_all, "llama3-8b": bench_llama3_8b, "qwen3-32b": bench_qwen3_32b,
            "relayout-70b": bench_relayout_70b, "pdmux": bench_pdmux, "copy-1gib": bench_copy_1gib,
-           "mfma-peak": bench_mfma_peak, "hbm-ceiling": bench_hbm_ceiling}
+           "mfma-peak": bench_mfma_peak, "hbm-ceiling": bench_hbm_ceiling,
+           "stall-free-qwen3-32b": bench_stall_free_qwen}
 
 
 def main():
